@@ -1,0 +1,340 @@
+"""Seeded synthetic decode-step workloads, shared by the oracle and the HIP path.
+
+This module only draws inputs. It holds none of the decode-step arithmetic
+(no quantization, scoring, selection or attention); both the CPU oracle and
+the GPU path receive exactly the arrays built here.
+
+Five workloads follow the sparse-decode setting the pages evaluate:
+
+* ``tiny``        B1  Hkv1 Hq4  T4096   block budget 8     (3 needle blocks, +2.0)
+* ``llama8b``     B1  Hkv8 Hq32 T32768  block budget 64    (1% needle blocks, norm 3)
+* ``jetqsparse``  B16 Hkv4 Hq16 T131072 block budget 64    (per-channel key offset,
+                  Zipf-profile needles over 2% of blocks); the decode shape of the
+                  Jet-QSparse abstract (128K context, batch 16, 64 blocks per KV head)
+* ``ragged``      the jetqsparse shape with budget 128, lengths uniform in
+                  [64K, 128K], 4 outlier channels x8, and the two newest pages kept
+                  in BF16 (Jet-QSparse abstract: up to two BF16 pages per sequence)
+* ``token``       B8 Hkv8 Hq32 T131072, rank-32 projected keys from a seeded
+                  orthonormal P, top-2048 tokens (JSSA abstract and Figure 1;
+                  1.5625% density of JSSA Figure 3: 2048 of 131072)
+
+Every workload also exists at reduced size (``scale_tokens`` / ``batch``) so the
+oracle finishes in seconds while still spanning many tiles and a ragged tail.
+
+Random streams are drawn per (sequence, KV head) from
+``numpy.random.default_rng([seed, stream, b, h])``, so any unit can be redrawn
+on its own (the full-size sampled checks rely on that).
+
+Calibration inputs (the key-centering vector and the per-KV-head FP32 scale)
+are produced here too: the centering vector is the per-channel mean of the
+keys over the packed region (the tiny workload states exactly that), and the
+per-KV-head scale maps the largest centered key magnitude onto the largest
+NVFP4 magnitude (6 x 448 = 2688), so that no block scale saturates.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK = 128
+# Largest NVFP4 magnitude: E2M1 max (6) times E4M3 max (448).
+NVFP4_MAX = 2688.0
+
+# stream ids for default_rng([seed, stream, ...])
+_S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_OUTLIER, _S_LENS, _S_PROJ = range(1, 9)
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    """Shape and structure of one synthetic workload."""
+
+    name: str
+    seed: int
+    batch: int
+    kv_heads: int
+    q_heads: int
+    max_tokens: int
+    granularity: str  # "block" or "token"
+    budget: int  # blocks (block mode) or tokens (token mode), forced pages included
+    n_tail: int = 0  # BF16 tail pages per (sequence, KV head), always selected
+    needle_count: int = 0  # needle blocks per unit
+    needle_profile: str = "none"  # "const" or "zipf"
+    needle_strength: float = 0.0
+    key_offset_std: float = 0.0  # per (KV head, channel) offset, shared over b and t
+    outlier_channels: int = 0
+    outlier_gain: float = 1.0
+    ragged: bool = False  # lengths uniform in [max_tokens/2, max_tokens]
+    rank: int = 0  # projection rank in token mode
+
+    @property
+    def group(self) -> int:
+        return self.q_heads // self.kv_heads
+
+    @property
+    def max_blocks(self) -> int:
+        return self.max_tokens // BLOCK
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.kv_heads
+
+
+SPECS: Dict[str, Spec] = {
+    "tiny": Spec("tiny", 0, 1, 1, 4, 4096, "block", 8,
+                 needle_count=3, needle_profile="const", needle_strength=2.0),
+    "llama8b": Spec("llama8b", 1, 1, 8, 32, 32768, "block", 64,
+                    needle_count=3, needle_profile="const", needle_strength=3.0),
+    "jetqsparse": Spec("jetqsparse", 2, 16, 4, 16, 131072, "block", 64,
+                       needle_count=20, needle_profile="zipf", needle_strength=3.0,
+                       key_offset_std=2.0),
+    "ragged": Spec("ragged", 3, 16, 4, 16, 131072, "block", 128, n_tail=2,
+                   needle_count=20, needle_profile="zipf", needle_strength=3.0,
+                   key_offset_std=2.0, outlier_channels=4, outlier_gain=8.0, ragged=True),
+    "token": Spec("token", 4, 8, 8, 32, 131072, "token", 2048, rank=32),
+}
+
+ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token"]
+
+
+def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
+            budget: Optional[int] = None) -> Spec:
+    """A smaller copy of a workload: fewer tokens (and optionally sequences).
+
+    Needle counts and token budgets keep the full workload's density.
+    """
+    s = SPECS[name]
+    assert max_tokens % BLOCK == 0
+    frac = max_tokens / s.max_tokens
+    kw = dict(max_tokens=max_tokens, name=f"{s.name}@{max_tokens}")
+    if batch is not None:
+        kw["batch"] = batch
+    if s.needle_count:
+        kw["needle_count"] = max(1, int(round(s.needle_count * frac)))
+    if budget is not None:
+        kw["budget"] = budget
+    elif s.granularity == "token":
+        kw["budget"] = max(1, int(round(s.budget * frac)))
+    else:
+        kw["budget"] = min(s.budget, max(s.n_tail + 1, max_tokens // BLOCK // 4))
+    return dataclasses.replace(s, **kw)
+
+
+@dataclasses.dataclass
+class Workload:
+    spec: Spec
+    q: np.ndarray  # float16 [B, Hq, D]
+    k: np.ndarray  # float16 [B, Hkv, T, D]
+    v: np.ndarray  # float16 [B, Hkv, T, D]
+    seq_lens: np.ndarray  # int32 [B]
+    key_center: np.ndarray  # float32 [Hkv, D]
+    global_scale: np.ndarray  # float32 [Hkv]
+    tail_k: Optional[np.ndarray]  # uint16 BF16 bits [B, Hkv, 2, 128, D]
+    tail_v: Optional[np.ndarray]
+    proj: Optional[np.ndarray]  # float32 [Hkv, D, r]
+    needles: List[List[np.ndarray]]  # [b][h] -> block ids carrying needles
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_DIM)
+
+    def n_pages(self, b: int) -> int:
+        return -(-int(self.seq_lens[b]) // BLOCK)
+
+    def packed_blocks(self, b: int) -> int:
+        """Blocks of sequence b held in the 4-bit copy (all but the tail pages)."""
+        return max(0, self.n_pages(b) - self.spec.n_tail)
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest-even) and return the raw 16-bit patterns."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _seq_lens(spec: Spec) -> np.ndarray:
+    if not spec.ragged:
+        return np.full(spec.batch, spec.max_tokens, dtype=np.int32)
+    rng = np.random.default_rng([spec.seed, _S_LENS])
+    lo = spec.max_tokens // 2
+    return rng.integers(lo, spec.max_tokens, size=spec.batch, endpoint=True).astype(np.int32)
+
+
+def _needle_blocks(spec: Spec, seq_lens: np.ndarray) -> List[List[np.ndarray]]:
+    rng = np.random.default_rng([spec.seed, _S_NEEDLE])
+    out = []
+    for b in range(spec.batch):
+        n_pages = -(-int(seq_lens[b]) // BLOCK)
+        packed = max(0, n_pages - spec.n_tail)
+        row = []
+        for _h in range(spec.kv_heads):
+            cnt = min(spec.needle_count, packed)
+            row.append(np.sort(rng.choice(packed, size=cnt, replace=False)) if cnt else
+                       np.zeros(0, dtype=np.int64))
+        out.append(row)
+    return out
+
+
+def _needle_strengths(spec: Spec, count: int, rng: np.random.Generator) -> np.ndarray:
+    if spec.needle_profile == "zipf":
+        # Rank profile s_i = s_1 * i^-1.1 (a Zipf(1.1) law over needle ranks),
+        # ranks assigned to the needle blocks in random order.
+        s = spec.needle_strength * np.arange(1, count + 1, dtype=np.float64) ** -1.1
+        return rng.permutation(s)
+    return np.full(count, spec.needle_strength, dtype=np.float64)
+
+
+def _unit_keys(spec: Spec, b: int, h: int, qdir: np.ndarray, offset: Optional[np.ndarray],
+               outliers: Optional[np.ndarray], needles: np.ndarray) -> np.ndarray:
+    """float32 keys of one (sequence, KV head) before rounding to the cache dtype."""
+    rng = np.random.default_rng([spec.seed, _S_K, b, h])
+    x = rng.standard_normal((spec.max_tokens, HEAD_DIM), dtype=np.float32)
+    if outliers is not None:
+        x[:, outliers[h]] *= np.float32(spec.outlier_gain)
+    if offset is not None:
+        x += offset[h][None, :]
+    if len(needles):
+        srng = np.random.default_rng([spec.seed, _S_NEEDLE, b, h])
+        strengths = _needle_strengths(spec, len(needles), srng)
+        for blk, s in zip(needles, strengths):
+            x[blk * BLOCK:(blk + 1) * BLOCK] += (s * qdir).astype(np.float32)[None, :]
+    return x
+
+
+def _unit_values(spec: Spec, b: int, h: int) -> np.ndarray:
+    rng = np.random.default_rng([spec.seed, _S_V, b, h])
+    return rng.standard_normal((spec.max_tokens, HEAD_DIM), dtype=np.float32)
+
+
+def _proj(spec: Spec) -> np.ndarray:
+    """One seeded orthonormal P (D x r), shared by all KV heads, columns sign-fixed."""
+    rng = np.random.default_rng([spec.seed, _S_PROJ])
+    g = rng.standard_normal((HEAD_DIM, spec.rank))
+    qm, rm = np.linalg.qr(g)
+    qm = qm * np.sign(np.diag(rm))[None, :]
+    p = qm.astype(np.float32)
+    return np.ascontiguousarray(np.broadcast_to(p, (spec.kv_heads, HEAD_DIM, spec.rank)))
+
+
+def generate(spec: Spec, threads: int = 8) -> Workload:
+    """Draw every input of one workload (deterministic in ``spec``)."""
+    B, Hkv, Hq, T, D = spec.batch, spec.kv_heads, spec.q_heads, spec.max_tokens, HEAD_DIM
+    G = spec.group
+    qrng = np.random.default_rng([spec.seed, _S_Q])
+    q = qrng.standard_normal((B, Hq, D), dtype=np.float32).astype(np.float16)
+    seq_lens = _seq_lens(spec)
+    needles = _needle_blocks(spec, seq_lens)
+    offset = None
+    if spec.key_offset_std:
+        offset = (np.random.default_rng([spec.seed, _S_OFFSET])
+                  .standard_normal((Hkv, D)) * spec.key_offset_std).astype(np.float32)
+    outliers = None
+    if spec.outlier_channels:
+        orng = np.random.default_rng([spec.seed, _S_OUTLIER])
+        outliers = np.stack([np.sort(orng.choice(D, spec.outlier_channels, replace=False))
+                             for _ in range(Hkv)])
+
+    k = np.empty((B, Hkv, T, D), dtype=np.float16)
+    v = np.empty((B, Hkv, T, D), dtype=np.float16)
+    tail_k = tail_v = None
+    if spec.n_tail:
+        tail_k = np.zeros((B, Hkv, spec.n_tail, BLOCK, D), dtype=np.uint16)
+        tail_v = np.zeros_like(tail_k)
+    col_sum = np.zeros((B, Hkv, D), dtype=np.float64)
+    col_cnt = np.zeros((B,), dtype=np.int64)
+
+    def work(bh):
+        b, h = bh
+        qm = q[b, h * G:(h + 1) * G].astype(np.float64).mean(axis=0)
+        qdir = qm / max(np.linalg.norm(qm), 1e-30)
+        xk = _unit_keys(spec, b, h, qdir, offset, outliers, needles[b][h])
+        xv = _unit_values(spec, b, h)
+        k[b, h] = xk.astype(np.float16)
+        v[b, h] = xv.astype(np.float16)
+        n_pages = -(-int(seq_lens[b]) // BLOCK)
+        packed = max(0, n_pages - spec.n_tail)
+        if spec.n_tail:
+            for s in range(spec.n_tail):
+                page = n_pages - spec.n_tail + s
+                if page >= 0:
+                    sl = slice(page * BLOCK, (page + 1) * BLOCK)
+                    tail_k[b, h, s] = _bf16_bits(xk[sl])
+                    tail_v[b, h, s] = _bf16_bits(xv[sl])
+        col_sum[b, h] = k[b, h, :packed * BLOCK].astype(np.float64).sum(axis=0)
+        col_cnt[b] = packed * BLOCK
+
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(work, units))
+
+    proj = None
+    if spec.granularity == "token":
+        key_center = np.zeros((Hkv, D), dtype=np.float32)
+        global_scale = np.ones((Hkv,), dtype=np.float32)
+        proj = _proj(spec)
+    else:
+        total = max(int(col_cnt.sum()), 1)
+        key_center = (col_sum.sum(axis=0) / total).astype(np.float32)
+        global_scale = calibrate_scale(spec, k, seq_lens, key_center, threads)
+    return Workload(spec, q, k, v, seq_lens, key_center, global_scale,
+                    tail_k, tail_v, proj, needles)
+
+
+def calibrate_scale(spec: Spec, k: np.ndarray, seq_lens: np.ndarray,
+                    key_center: np.ndarray, threads: int = 8) -> np.ndarray:
+    """Per-KV-head FP32 scale: largest |key - center| over the packed region / 2688."""
+    Hkv = spec.kv_heads
+    amax = np.zeros((spec.batch, Hkv), dtype=np.float32)
+
+    def work(bh):
+        b, h = bh
+        n_pages = -(-int(seq_lens[b]) // BLOCK)
+        packed = max(0, n_pages - spec.n_tail) * BLOCK
+        if packed:
+            y = k[b, h, :packed].astype(np.float32) - key_center[h][None, :]
+            amax[b, h] = np.abs(y).max()
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(work, [(b, h) for b in range(spec.batch) for h in range(Hkv)]))
+    s = (amax.max(axis=0) / np.float32(NVFP4_MAX)).astype(np.float32)
+    s[s == 0] = np.float32(1.0)
+    return s
+
+
+def algorithmic_bytes(w: Workload) -> Dict[str, int]:
+    """Bytes the method must move per decode step (scan + selected K,V), per stage.
+
+    Block mode: 72 B per scanned token (64 B of E2M1 codes + 8 B of E4M3 scales)
+    and 2 x 256 B per attended token (FP16 K and V rows; BF16 tail rows also
+    count 512 B). Token mode: 2r B per scanned token (BF16 projected key) and
+    512 B per selected token.
+    """
+    s = w.spec
+    scan = attn = 0
+    for b in range(s.batch):
+        L = int(w.seq_lens[b])
+        if s.granularity == "block":
+            packed = w.packed_blocks(b)
+            scanned_tokens = min(packed * BLOCK, L)
+            scan += s.kv_heads * 72 * scanned_tokens
+            n_pages = w.n_pages(b)
+            forced = min(s.n_tail, n_pages)
+            chosen = min(s.budget - s.n_tail, packed) + forced
+            # every chosen page is a full 128-token tile except the newest one
+            tokens = 0
+            for p in range(n_pages - forced, n_pages):
+                tokens += min(BLOCK, L - p * BLOCK)
+            tokens += (chosen - forced) * BLOCK if forced else min(chosen * BLOCK, L)
+            attn += s.kv_heads * 512 * tokens
+        else:
+            scan += s.kv_heads * 2 * s.rank * L
+            attn += s.kv_heads * 512 * min(s.budget, L)
+    q_bytes = s.batch * s.q_heads * HEAD_DIM * 2
+    return {"scan": scan, "attn": attn, "q": q_bytes, "total": scan + attn}

@@ -1,0 +1,379 @@
+"""Decode-step sparse attention, step by step (oracle; test infrastructure only).
+
+Sources (the only specification there is):
+
+* Jet-QSparse (arXiv 2611.01022) abstract: keys are cached as NVFP4; a dense
+  scan scores the full key history every decode step and selects 128-token
+  blocks; the selected blocks' values are aggregated in FP16 with FP32
+  accumulation; calibrated key centering and at most two BF16 pages per
+  sequence and layer absorb quantization error; budgets are counted in blocks
+  per KV head (64 in the speed claim, 128 for the accuracy claim).
+* JSSA (arXiv 2610.19026) abstract and Figure 1: the mean of a KV head's query
+  heads scores a projected-key cache in a shared rank-r subspace, the top-B
+  token positions form one index set per KV head shared by its query heads,
+  and attention reads the original full-dimensional keys and values at those
+  positions without gathering them. Figure 3 fixes the density (2048 of 128K);
+  Figure 10 evaluates BF16 and FP8 projected-key caches; Table 15 shows per-KV-
+  head selection beats a head-shared vote.
+
+Everything is per unit = one (sequence b, KV head h). Query head hq belongs to
+KV head hq // G. Arithmetic is float64 except the steps whose result is a
+stored float32/bfloat16 quantity (the packers), which follow float32 exactly.
+Readings of points the pages leave open are stated where they are used.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import nvfp4
+
+BLOCK = 128  # tokens per selectable block (Jet-QSparse abstract)
+HEAD_DIM = 128
+GROUP = 16  # NVFP4: one E4M3 scale per 16 consecutive channels
+NGROUPS = HEAD_DIM // GROUP
+E2M1_MAX = 6.0
+
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# byte layout of the 4-bit key copy
+#
+# The pages fix only the number format. The library stores, per
+# (sequence, KV head, block), an 8192-byte code record and a 1024-byte scale
+# record. With token tau = 16*i + n (i < 8, n < 16), channel d = 32*j + e
+# (j < 4, e < 32) and scale group g = 2*j + s (s < 2):
+#   code of (tau, d)  -> byte ((i*4 + j)*16 + n)*16 + e//2, low nibble if e even
+#   scale of (tau, g) -> byte ((j*16 + n)*8 + i)*2 + s
+# --------------------------------------------------------------------------
+
+def codes_to_cache_layout(codes: np.ndarray) -> np.ndarray:
+    """[..., 128 tokens, 128 channels] one code per entry -> [..., 8192] bytes."""
+    lead = codes.shape[:-2]
+    c = codes.astype(np.uint8).reshape(*lead, 8, 16, 4, 32)  # i, n, j, e
+    c = np.swapaxes(c, -3, -2)  # i, j, n, e
+    packed = c[..., 0::2] | (c[..., 1::2] << 4)
+    return np.ascontiguousarray(packed).reshape(*lead, 8192)
+
+
+def cache_layout_to_codes(raw: np.ndarray) -> np.ndarray:
+    lead = raw.shape[:-1]
+    c = raw.reshape(*lead, 8, 4, 16, 16)  # i, j, n, byte
+    out = np.empty((*lead, 8, 4, 16, 32), dtype=np.uint8)
+    out[..., 0::2] = c & 0xF
+    out[..., 1::2] = c >> 4
+    out = np.swapaxes(out, -3, -2)  # i, n, j, e
+    return np.ascontiguousarray(out).reshape(*lead, BLOCK, HEAD_DIM)
+
+
+def scales_to_cache_layout(sb: np.ndarray) -> np.ndarray:
+    """[..., 128 tokens, 8 groups] -> [..., 1024] bytes."""
+    lead = sb.shape[:-2]
+    s = sb.astype(np.uint8).reshape(*lead, 8, 16, 4, 2)  # i, n, j, s
+    nd = s.ndim
+    s = np.transpose(s, tuple(range(nd - 4)) + (nd - 2, nd - 3, nd - 4, nd - 1))  # j, n, i, s
+    return np.ascontiguousarray(s).reshape(*lead, 1024)
+
+
+def cache_layout_to_scales(raw: np.ndarray) -> np.ndarray:
+    lead = raw.shape[:-1]
+    s = raw.reshape(*lead, 4, 16, 8, 2)  # j, n, i, s
+    nd = s.ndim
+    s = np.transpose(s, tuple(range(nd - 4)) + (nd - 2, nd - 3, nd - 4, nd - 1))  # i, n, j, s
+    return np.ascontiguousarray(s).reshape(*lead, BLOCK, NGROUPS)
+
+
+# --------------------------------------------------------------------------
+# helpers for the cache dtypes
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 values (bf16 is the top half of an fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even, via torch's CPU conversion."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=F32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def n_pages(seq_len: int) -> int:
+    return -(-int(seq_len) // BLOCK)
+
+
+def packed_blocks(seq_len: int, n_tail: int) -> int:
+    """Blocks held in the 4-bit copy: every page except the newest ``n_tail``."""
+    return max(0, n_pages(seq_len) - n_tail)
+
+
+# --------------------------------------------------------------------------
+# A0: pack keys to the NVFP4 copy (Jet-QSparse abstract: the persistent cache is
+# NVFP4, keys are centered by a calibrated vector first, and the packer reads the
+# 16-bit activations directly)
+#
+# Reading: y = fl32(fl32(k) - c); per 16-channel group the E4M3 scale encodes
+# amax(|y|) / (6 * s_t) so the group's largest element lands on the largest
+# E2M1 magnitude; the effective scale is S = fl32(E4M3(sb) * s_t); each element
+# is E2M1(fl32(y / S)); a group whose scale decodes to 0 stores code 0.
+# --------------------------------------------------------------------------
+
+def pack_nvfp4(k: np.ndarray, center: np.ndarray, global_scale: float
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantize keys [..., 128] of one KV head.
+
+    Returns (codes [..., 128] uint8, one 4-bit code per channel;
+             scale bytes [..., 8] uint8, one E4M3 per 16-channel group).
+    """
+    y = (np.asarray(k).astype(F32) - np.asarray(center, dtype=F32)).astype(F32)
+    yg = y.reshape(*y.shape[:-1], NGROUPS, GROUP)
+    amax = np.abs(yg).max(axis=-1)
+    st = F32(global_scale)
+    six_st = F32(F32(E2M1_MAX) * st)
+    ratio = (amax / six_st).astype(F32)
+    sb = nvfp4.e4m3_encode_nonneg(ratio)
+    S = (nvfp4.e4m3_decode(sb).astype(F32) * st).astype(F32)
+    Sx = np.broadcast_to(S[..., None], yg.shape)
+    x = np.divide(yg, Sx, out=np.zeros_like(yg), where=Sx > 0).astype(F32)
+    codes = nvfp4.e2m1_encode(x)
+    codes[np.broadcast_to((S == 0)[..., None], codes.shape)] = 0
+    return codes.reshape(y.shape), sb
+
+
+def pack_unit_blocks(k_unit: np.ndarray, center: np.ndarray, global_scale: float,
+                     block_begin: int, block_end: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Pack blocks [block_begin, block_end) of one unit's keys [T, 128].
+
+    Returns code records [n, 8192] and scale records [n, 1024].
+    """
+    kb = k_unit[block_begin * BLOCK:block_end * BLOCK].reshape(-1, BLOCK, HEAD_DIM)
+    codes, sb = pack_nvfp4(kb, center, global_scale)
+    return codes_to_cache_layout(codes), scales_to_cache_layout(sb)
+
+
+def dequant_blocks(code_rec: np.ndarray, scale_rec: np.ndarray) -> np.ndarray:
+    """Records [n, 8192] + [n, 1024] -> e2m1 * e4m3 values [n, 128, 128] (float64).
+
+    The per-KV-head FP32 scale and the centering vector are not applied.
+    """
+    codes = cache_layout_to_codes(code_rec)
+    sb = cache_layout_to_scales(scale_rec)
+    return nvfp4.e2m1_decode(codes) * np.repeat(nvfp4.e4m3_decode(sb), GROUP, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# A1: dense block scan (Jet-QSparse abstract: every decode step scores all cached
+# keys from the 4-bit copy, and the scores pick blocks of 128 tokens)
+#
+# Readings: the estimated logit of query head h and token t is
+#   sigma * (s_t * q_h . dequant(k_t) + q_h . c)
+# (the centering vector is added back so the estimate targets q . k); a block's
+# score is the largest estimated logit over the KV head's query heads and the
+# block's valid tokens (t < L). Blocks outside the packed region score -inf.
+# --------------------------------------------------------------------------
+
+def scan_block_unit(q_group: np.ndarray, code_rec: np.ndarray, scale_rec: np.ndarray,
+                    global_scale: float, center: np.ndarray, seq_len: int, n_tail: int,
+                    sigma: float, max_blocks: Optional[int] = None) -> np.ndarray:
+    """Block scores [max_blocks] (float64) of one unit; q_group is [G, 128]."""
+    nb_total = code_rec.shape[0] if max_blocks is None else max_blocks
+    scores = np.full(nb_total, -np.inf)
+    nb = packed_blocks(seq_len, n_tail)
+    if nb == 0:
+        return scores
+    qg = np.asarray(q_group, dtype=np.float64)
+    kd = dequant_blocks(code_rec[:nb], scale_rec[:nb])  # [nb, 128, 128]
+    dots = kd.reshape(-1, HEAD_DIM) @ qg.T  # [nb*128, G]
+    qc = qg @ np.asarray(center, dtype=np.float64)  # [G]
+    logits = sigma * (float(global_scale) * dots + qc[None, :])
+    t = np.arange(nb * BLOCK)
+    logits[t >= seq_len] = -np.inf
+    scores[:nb] = logits.reshape(nb, BLOCK * qg.shape[0]).max(axis=1)
+    return scores
+
+
+# --------------------------------------------------------------------------
+# A2 / A8: top-k selection per KV head
+#
+# Readings: the budget counts the forced BF16 pages (Jet-QSparse abstract: at
+# most two BF16 pages), which are the two newest pages and are always chosen;
+# the remaining budget - n_tail picks go to the highest-scoring candidates,
+# equal scores going to the lower index; output ascending, padded with -1.
+# Token mode (JSSA Figure 1): top-B token positions per KV head, no forced pages.
+# --------------------------------------------------------------------------
+
+def select_unit(scores: np.ndarray, n_candidates: int, budget: int,
+                forced: Sequence[int] = (), picks: Optional[int] = None
+                ) -> Tuple[np.ndarray, int]:
+    """Pick from candidates 0..n_candidates-1; returns (idx [budget] int32, count).
+
+    ``picks`` (default budget - len(forced)) candidates are chosen by score,
+    then the forced entries are added.
+    """
+    if picks is None:
+        picks = budget - len(forced)
+    cand = np.arange(n_candidates)
+    s = np.asarray(scores[:n_candidates], dtype=np.float64)
+    order = np.lexsort((cand, -s))  # primary: score descending; then index ascending
+    chosen = cand[order[:max(0, picks)]]
+    sel = np.sort(np.concatenate([chosen, np.asarray(list(forced), dtype=np.int64)]))
+    out = np.full(budget, -1, dtype=np.int32)
+    out[:len(sel)] = sel
+    return out, int(len(sel))
+
+
+def select_blocks_unit(scores: np.ndarray, seq_len: int, n_tail: int, budget: int
+                       ) -> Tuple[np.ndarray, int]:
+    """Forced tail pages plus the top (budget - n_tail) scanned blocks."""
+    npg = n_pages(seq_len)
+    forced = list(range(max(0, npg - n_tail), npg))
+    return select_unit(scores, packed_blocks(seq_len, n_tail), budget, forced,
+                       picks=budget - n_tail)
+
+
+def select_tokens_unit(scores: np.ndarray, seq_len: int, budget: int) -> Tuple[np.ndarray, int]:
+    return select_unit(scores, min(int(seq_len), scores.shape[0]), budget)
+
+
+# --------------------------------------------------------------------------
+# A3 / A9: sparse attention over the selected rows, split into partials
+# (Jet-QSparse abstract: sparse value aggregation with FP32 accumulation over
+# the selected blocks; JSSA Figure 1: the query heads share the index set and
+# read the original keys and values)
+# --------------------------------------------------------------------------
+
+def gather_rows_block(k_unit, v_unit, blocks: Sequence[int], seq_len: int, n_tail: int,
+                      tail_k_unit=None, tail_v_unit=None) -> Tuple[np.ndarray, np.ndarray]:
+    """float64 K and V rows [n, 128] of the selected blocks, in block order.
+
+    Tail pages (the n_tail newest) come from the BF16 tail store, slot
+    page - (n_pages - n_tail); tokens at or beyond seq_len are left out.
+    """
+    npg = n_pages(seq_len)
+    ks, vs = [], []
+    for blk in blocks:
+        lo, hi = blk * BLOCK, min((blk + 1) * BLOCK, seq_len)
+        if hi <= lo:
+            continue
+        if n_tail and blk >= npg - n_tail:
+            slot = blk - (npg - n_tail)
+            ks.append(bf16_bits_to_f64(tail_k_unit[slot, :hi - lo]))
+            vs.append(bf16_bits_to_f64(tail_v_unit[slot, :hi - lo]))
+        else:
+            ks.append(np.asarray(k_unit[lo:hi], dtype=np.float64))
+            vs.append(np.asarray(v_unit[lo:hi], dtype=np.float64))
+    if not ks:
+        return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def gather_rows_token(k_unit, v_unit, tokens: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    t = np.asarray(tokens, dtype=np.int64)
+    return (np.asarray(k_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM),
+            np.asarray(v_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM))
+
+
+def attend(q_group: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, sigma: float
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(sigma q K^T) V for each query head: (O [G, 128], lse [G]).
+
+    An empty row set gives O = 0 and lse = -inf.
+    """
+    qg = np.asarray(q_group, dtype=np.float64)
+    G = qg.shape[0]
+    if k_rows.shape[0] == 0:
+        return np.zeros((G, HEAD_DIM)), np.full(G, -np.inf)
+    logits = sigma * (qg @ k_rows.T)  # [G, n]
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    z = w.sum(axis=1, keepdims=True)
+    out = (w @ v_rows) / z
+    lse = (m + np.log(z))[:, 0]
+    return out, lse
+
+
+def split_ranges(budget: int, num_splits: int):
+    """Split s covers entries [s*per, min((s+1)*per, budget)) of the index list."""
+    per = -(-budget // num_splits)
+    return [(s * per, min((s + 1) * per, budget)) for s in range(num_splits)]
+
+
+def attend_splits(q_group, idx: np.ndarray, num_splits: int, rows_fn, sigma: float):
+    """Per-split partials (O_s [S, G, 128], lse_s [S, G]) over the index list.
+
+    ``rows_fn(list_of_indices)`` returns the (K, V) rows of those entries.
+    """
+    parts_o, parts_l = [], []
+    for lo, hi in split_ranges(idx.shape[0], num_splits):
+        sel = [int(x) for x in idx[lo:hi] if x >= 0]
+        kr, vr = rows_fn(sel)
+        o, l = attend(q_group, kr, vr, sigma)
+        parts_o.append(o)
+        parts_l.append(l)
+    return np.stack(parts_o), np.stack(parts_l)
+
+
+# --------------------------------------------------------------------------
+# A4: log-sum-exp combine of split partials
+#   lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) * O_s
+# --------------------------------------------------------------------------
+
+def combine(part_o: np.ndarray, part_lse: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """part_o [S, ..., D], part_lse [S, ...] -> (O [..., D], lse [...])."""
+    po = np.asarray(part_o, dtype=np.float64)
+    pl = np.asarray(part_lse, dtype=np.float64)
+    m = pl.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(pl - m_safe[None])
+    z = w.sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, z)))
+    out = (w[..., None] * po).sum(axis=0) / np.where(empty, 1.0, z)[..., None]
+    out[empty] = 0.0
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# A6: projected-key cache for token mode (JSSA Figure 1: a projected-key cache
+# in a shared low-dimensional subspace; Figure 10: BF16 projected-key cache)
+#
+# Reading: kproj[t, j] = BF16(acc), acc the float32 sum over d ascending of
+# fl32(P[d, j] * k[t, d]), each addition rounded to float32, no fused multiply-add.
+# --------------------------------------------------------------------------
+
+def project_keys(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """Keys [n, 128] (fp16 values) and P [128, r] (float32) -> BF16 bits [n, r]."""
+    kf = np.asarray(k_rows).astype(F32)
+    P = np.asarray(proj, dtype=F32)
+    acc = np.zeros((kf.shape[0], P.shape[1]), dtype=F32)
+    for d in range(HEAD_DIM):
+        prod = (kf[:, d:d + 1] * P[d][None, :]).astype(F32)
+        acc = (acc + prod).astype(F32)
+    return f32_to_bf16_bits(acc)
+
+
+# --------------------------------------------------------------------------
+# A7: token scan (JSSA Figure 1: the mean of the KV head's query heads scores
+# the projected keys)
+#   qbar = mean_h q_h,  p = P^T qbar,  score_t = sigma * p . kproj_t   (t < L)
+# --------------------------------------------------------------------------
+
+def scan_token_unit(q_group: np.ndarray, kproj_bits: np.ndarray, proj: np.ndarray,
+                    seq_len: int, sigma: float) -> np.ndarray:
+    qbar = np.asarray(q_group, dtype=np.float64).mean(axis=0)
+    p = np.asarray(proj, dtype=np.float64).T @ qbar  # [r]
+    kt = bf16_bits_to_f64(kproj_bits)  # [T, r]
+    scores = sigma * (kt @ p)
+    scores[np.arange(kt.shape[0]) >= seq_len] = -np.inf
+    return scores
+
+
+def softmax_scale(head_dim: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,207 @@
+"""Pins of the oracle's selection, attention, combine and token path (CPU)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode as O
+
+SIGMA = 1.0 / math.sqrt(128)
+
+
+def _rank_select(scores, n_cand, picks):
+    """Brute force: candidate i is chosen iff fewer than `picks` candidates beat it."""
+    chosen = []
+    for i in range(n_cand):
+        beat = sum(1 for j in range(n_cand)
+                   if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+        if beat < picks:
+            chosen.append(i)
+    return chosen
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_matches_rank_counting_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = 97
+    s = np.round(rng.standard_normal(n) * 2) / 2  # many exact ties
+    for budget in [1, 5, 20, 96, 97, 120]:
+        idx, cnt = O.select_unit(s, n, budget)
+        exp = _rank_select(s, n, budget)
+        assert cnt == len(exp)
+        assert list(idx[:cnt]) == exp  # ascending
+        assert np.all(idx[cnt:] == -1)
+
+
+def test_select_blocks_forced_tail_pages():
+    rng = np.random.default_rng(5)
+    L = 128 * 10 + 7  # 11 pages, the last partial
+    scores = rng.standard_normal(16)
+    idx, cnt = O.select_blocks_unit(scores, L, 2, 5)
+    # 3 picks among the 9 scanned blocks plus pages 9 and 10
+    exp = sorted(_rank_select(scores, 9, 3) + [9, 10])
+    assert cnt == 5 and list(idx) == exp
+    # fewer pages than tail slots
+    idx, cnt = O.select_blocks_unit(scores, 100, 2, 4)
+    assert cnt == 1 and list(idx) == [0, -1, -1, -1]
+    # empty sequence
+    idx, cnt = O.select_blocks_unit(scores, 0, 2, 4)
+    assert cnt == 0 and np.all(idx == -1)
+
+
+def test_budget_all_blocks_is_dense_attention():
+    rng = np.random.default_rng(6)
+    T, G = 1024, 4
+    q = rng.standard_normal((G, 128)).astype(np.float16)
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    idx = np.arange(T // 128)
+    kr, vr = O.gather_rows_block(k, v, idx, T, 0)
+    o, lse = O.attend(q, kr, vr, SIGMA)
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(k.astype(np.float64))
+    vt = torch.from_numpy(v.astype(np.float64))
+    logits = SIGMA * qt @ kt.T
+    ref = torch.softmax(logits, dim=-1) @ vt
+    assert np.abs(o - ref.numpy()).max() < 1e-12
+    assert np.abs(lse - torch.logsumexp(logits, dim=-1).numpy()).max() < 1e-12
+
+
+def test_attention_brute_force_loops():
+    rng = np.random.default_rng(7)
+    T, G = 300, 2
+    q = rng.standard_normal((G, 128)).astype(np.float16)
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    sel = [0, 2]  # blocks 0 and 2 (tokens 0..127, 256..299)
+    kr, vr = O.gather_rows_block(k, v, sel, T, 0)
+    o, lse = O.attend(q, kr, vr, SIGMA)
+    toks = list(range(0, 128)) + list(range(256, 300))
+    for h in range(G):
+        w = [math.exp(SIGMA * sum(float(q[h, d]) * float(k[t, d]) for d in range(128)))
+             for t in toks]
+        z = sum(w)
+        for d in (0, 17, 127):
+            od = sum(wi * float(v[t, d]) for wi, t in zip(w, toks)) / z
+            assert abs(o[h, d] - od) < 1e-12
+        assert abs(lse[h] - math.log(z)) < 1e-12
+
+
+def test_centering_does_not_change_attention():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    k = rng.standard_normal((512, 128))
+    v = rng.standard_normal((512, 128))
+    c = rng.standard_normal(128) * 3
+    o1, _ = O.attend(q, k, v, SIGMA)
+    o2, _ = O.attend(q, k - c[None, :], v, SIGMA)
+    assert np.abs(o1 - o2).max() < 1e-12
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 16])
+def test_combine_independent_of_split_count(splits):
+    rng = np.random.default_rng(9)
+    T = 1280
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    idx = np.array([0, 3, 4, 7, 9, -1, -1], dtype=np.int32)
+    rows = lambda sel: O.gather_rows_block(k, v, sel, T, 0)
+    po, pl = O.attend_splits(q, idx, splits, rows, SIGMA)
+    o, lse = O.combine(po, pl)
+    kr, vr = rows([0, 3, 4, 7, 9])
+    o1, l1 = O.attend(q, kr, vr, SIGMA)
+    assert np.abs(o - o1).max() < 1e-12 and np.abs(lse - l1).max() < 1e-12
+    if splits == 1:
+        assert np.array_equal(po[0], o1)
+
+
+def test_empty_selection_gives_zero_and_minus_inf():
+    q = np.ones((4, 128), np.float16)
+    po, pl = O.attend_splits(q, np.full(4, -1, np.int32), 2,
+                             lambda sel: (np.zeros((0, 128)), np.zeros((0, 128))), SIGMA)
+    o, lse = O.combine(po, pl)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_tail_pages_read_from_bf16_store():
+    rng = np.random.default_rng(10)
+    L = 128 * 5 + 40  # 6 pages; pages 4, 5 live in the tail store
+    T = 1024
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    x = rng.standard_normal((T, 128)).astype(np.float32)
+    xv = rng.standard_normal((T, 128)).astype(np.float32)
+    k = x.astype(np.float16)
+    v = xv.astype(np.float16)
+    tk = np.zeros((2, 128, 128), np.uint16)
+    tv = np.zeros((2, 128, 128), np.uint16)
+    for s, page in enumerate([4, 5]):
+        tk[s] = O.f32_to_bf16_bits(x[page * 128:(page + 1) * 128])
+        tv[s] = O.f32_to_bf16_bits(xv[page * 128:(page + 1) * 128])
+    k[512:] = 1000  # the main buffer at tail pages is never read
+    kr, vr = O.gather_rows_block(k, v, [1, 4, 5], L, 2, tk, tv)
+    assert kr.shape[0] == 128 + 128 + 40
+    assert np.array_equal(kr[128:256], O.bf16_bits_to_f64(tk[0]))
+    assert np.array_equal(kr[256:], O.bf16_bits_to_f64(tk[1, :40]))
+    xk = torch.from_numpy(x[512:512 + 168]).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(kr[128:], xk)
+
+
+# ---------------------------------------------------------------- token path
+
+def test_identity_projection_gives_bf16_keys():
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((300, 128)).astype(np.float16)
+    P = np.eye(128, dtype=np.float32)
+    bits = O.project_keys(k, P)
+    ref = torch.from_numpy(k.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(bits.view(np.int16), ref)
+
+
+def test_projection_within_float32_error_bound():
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((500, 128)).astype(np.float16)
+    g = rng.standard_normal((128, 32))
+    P = np.linalg.qr(g)[0].astype(np.float32)
+    got = O.bf16_bits_to_f64(O.project_keys(k, P))
+    exact = k.astype(np.float64) @ P.astype(np.float64)
+    absterm = np.abs(k.astype(np.float64)) @ np.abs(P.astype(np.float64))
+    u32 = 2.0 ** -24
+    bound = 129 * u32 * absterm + 2.0 ** -8 * np.abs(exact) * 1.01
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_token_scores_follow_mean_query_and_rotation():
+    rng = np.random.default_rng(13)
+    T, G = 400, 4
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    q = rng.standard_normal((G, 128)).astype(np.float16)
+    P = np.linalg.qr(rng.standard_normal((128, 128)))[0].astype(np.float32)
+    s = O.scan_token_unit(q, O.project_keys(k, P), P, T, SIGMA)
+    qbar = q.astype(np.float64).mean(axis=0)
+    exact = SIGMA * (k.astype(np.float64) @ qbar)
+    # full-rank orthonormal P: scores are sigma * qbar . k up to BF16 rounding of P^T k
+    bound = SIGMA * (np.abs(k.astype(np.float64)) @ np.abs(P.astype(np.float64))
+                     ) @ np.abs(P.astype(np.float64).T @ qbar) * 2.0 ** -7
+    assert np.all(np.abs(s - exact) <= bound + 1e-9)
+    # the score depends on the group only through its mean query
+    qm = np.repeat(qbar[None, :], G, axis=0)
+    s2 = O.scan_token_unit(qm, O.project_keys(k, P), P, T, SIGMA)
+    assert np.abs(s - s2).max() < 1e-12
+    # masking beyond the sequence length
+    s3 = O.scan_token_unit(q, O.project_keys(k, P), P, 250, SIGMA)
+    assert np.all(s3[250:] == -np.inf) and np.array_equal(s3[:250], s[:250])
+
+
+def test_token_select_and_gather_free_rows():
+    rng = np.random.default_rng(14)
+    T = 512
+    s = np.round(rng.standard_normal(T), 1)
+    idx, cnt = O.select_tokens_unit(s, 400, 37)
+    assert cnt == 37 and list(idx) == _rank_select(s, 400, 37)
+    k = rng.standard_normal((T, 128)).astype(np.float16)
+    v = rng.standard_normal((T, 128)).astype(np.float16)
+    kr, vr = O.gather_rows_token(k, v, idx[:cnt])
+    assert np.array_equal(kr, k[idx[:cnt]].astype(np.float64))
