@@ -1,0 +1,217 @@
+"""Decode-step throughput of the sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path for one layer: score_scan (4-bit dense
+scan or projected-key scan), select_topk, sparse_decode_attn and combine, over
+a batch of synthetic inputs already resident in HBM. Consecutive steps rotate
+over --layers distinct copies of the KV cache, as consecutive layers of a model
+would, so no step finds the previous step's data in the 256 MB Infinity Cache.
+
+Prints one JSON line. `value` is (batch x KV heads) decode steps per second;
+`pct_hbm_peak` is the step's algorithmic bytes per second over 8 TB/s;
+`roofline` is the dominant kernel (the scan) measured with HIP events on the
+launch stream over the timed region; `cpu_baseline` is the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode-attention steps/sec (batch x KV heads) at 128K; % HBM peak"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="jetqsparse",
+                    choices=["tiny", "llama8b", "jetqsparse", "ragged", "token"])
+    ap.add_argument("--layers", type=int, default=4, help="distinct KV-cache copies rotated per step")
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time only the whole step, without per-kernel events")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, budget_s: float):
+    """Oracle (float64 NumPy) scan + select + attention + combine on sampled units."""
+    import numpy as np
+
+    from oracle import decode as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    s = w.spec
+    G, sigma = s.group, w.softmax_scale
+    units = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
+    done, spent = 0, 0.0
+    for b, h in units:
+        if done and spent >= budget_s:
+            break
+        L = int(w.seq_lens[b])
+        qg = w.q[b, h * G:(h + 1) * G]
+        if s.granularity == "block":
+            rc, rs = O.pack_unit_blocks(w.k[b, h], w.key_center[h], w.global_scale[h], 0,
+                                        s.max_blocks)
+            tk = w.tail_k[b, h] if s.n_tail else None
+            tv = w.tail_v[b, h] if s.n_tail else None
+            t0 = time.perf_counter()
+            sc = O.scan_block_unit(qg, rc, rs, w.global_scale[h], w.key_center[h], L, s.n_tail,
+                                   sigma, s.max_blocks)
+            idx, _ = O.select_blocks_unit(sc, L, s.n_tail, s.budget)
+            rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
+        else:
+            kp = O.project_keys(w.k[b, h], w.proj[h])
+            t0 = time.perf_counter()
+            sc = O.scan_token_unit(qg, kp, w.proj[h], L, sigma)
+            idx, _ = O.select_tokens_unit(sc, L, s.budget)
+            rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L])
+        po, pl = O.attend_splits(qg, idx, 1, rows, sigma)
+        O.combine(po, pl)
+        spent += time.perf_counter() - t0
+        done += 1
+        log(f"[cpu] unit {(b, h)} done, {spent:.1f} s so far")
+    return {"value": done / spent, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV head) units of the same workload, "
+                      f"NumPy float64, pack excluded; {spent:.1f} s"}
+
+
+def main() -> int:
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported "
+              "(the path shards by (sequence, KV head) with no exchange; run one process per GPU)",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_pack_amd import binding, workloads as W
+    from block_sparse_attention_pack_amd.step import upload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    spec = W.SPECS[a.workload]
+    log(f"[bench] generating {spec.name} ...")
+    t0 = time.time()
+    w = W.generate(spec, threads=16)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+    d0 = upload(w, splits=a.splits)
+    d0.pack()
+    torch.cuda.synchronize()
+    layers = [d0]
+    for i in range(1, a.layers):
+        if d0.block_mode:
+            layers.append(dataclasses.replace(d0, k=d0.k.clone(), v=d0.v.clone(),
+                                              codes=d0.codes.clone(), scales=d0.scales.clone()))
+        else:
+            layers.append(dataclasses.replace(d0, k=d0.k.clone(), v=d0.v.clone(),
+                                              kproj=d0.kproj.clone()))
+    torch.cuda.synchronize()
+    log(f"[bench] {a.layers} layer copies resident; warmup {a.warmup}")
+    nbytes = W.algorithmic_bytes(w)
+    stream = torch.cuda.current_stream()
+
+    for i in range(a.warmup):
+        layers[i % len(layers)].run()
+    torch.cuda.synchronize()
+
+    stages = ["scan", "select", "attend", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(a.steps):
+        d = layers[i % len(layers)]
+        if a.no_stage_events:
+            d.run()
+            continue
+        e = ev[i]
+        e[0].record(stream)
+        d.scan()
+        e[1].record(stream)
+        d.select()
+        e[2].record(stream)
+        d.attend()
+        e[3].record(stream)
+        d.combine()
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / a.steps
+    units = spec.batch * spec.kv_heads
+    value = units * a.steps / elapsed
+    stage_us = {}
+    if not a.no_stage_events:
+        for j, name in enumerate(stages):
+            ts = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(a.steps)]
+            stage_us[name] = float(np.mean(ts))
+        step_us = [ev[i][0].elapsed_time(ev[i][4]) * 1e3 for i in range(a.steps)]
+        stage_us["step_events_p50"] = float(np.median(step_us))
+    log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms; stages (us): {stage_us}")
+
+    scan_us = stage_us.get("scan")
+    roofline = None
+    if scan_us:
+        achieved = nbytes["scan"] / (scan_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "scan_block_kernel" if d0.block_mode
+                    else "scan_token_kernel<32>", "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": None, "bytes_per_launch": nbytes["scan"]}
+    step_gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "kv_heads": spec.kv_heads,
+                   "q_heads": spec.q_heads, "context": spec.max_tokens,
+                   "granularity": spec.granularity, "budget": spec.budget,
+                   "tail_pages": spec.n_tail, "splits": d0.splits, "layers_rotated": a.layers,
+                   "scan": "e2m1*e4m3 -> f16 MFMA, f32 acc" if d0.block_mode
+                   else "bf16 rank-%d keys, f32" % spec.rank},
+        "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes_per_step": nbytes["total"],
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "roofline": roofline,
+    }
+    if a.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

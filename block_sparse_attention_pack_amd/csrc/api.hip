@@ -1,0 +1,250 @@
+// C ABI of the sparse decode-attention library: argument checks, error
+// reporting and kernel launches. See include/bsa.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define BSA_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+// Checks shared by every entry point that takes a layout and a selection config.
+int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom* g) {
+  BSA_REQUIRE(L && c, BSA_ERR_INVALID_ARG, "layout and cfg must not be NULL");
+  BSA_REQUIRE(L->head_dim == bsa::kHeadDim, BSA_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported",
+              L->head_dim);
+  BSA_REQUIRE(L->block_size == bsa::kBlock, BSA_ERR_UNSUPPORTED,
+              "block_size %d: only 128 is supported", L->block_size);
+  BSA_REQUIRE(L->batch >= 1 && L->num_kv_heads >= 1 && L->num_q_heads >= 1, BSA_ERR_INVALID_ARG,
+              "batch, num_kv_heads and num_q_heads must be >= 1");
+  BSA_REQUIRE(L->num_q_heads % L->num_kv_heads == 0, BSA_ERR_INVALID_ARG,
+              "num_q_heads %d is not a multiple of num_kv_heads %d", L->num_q_heads, L->num_kv_heads);
+  const int G = L->num_q_heads / L->num_kv_heads;
+  BSA_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, BSA_ERR_UNSUPPORTED,
+              "query heads per KV head %d: supported 1, 2, 4, 8, 16", G);
+  BSA_REQUIRE(L->max_tokens >= bsa::kBlock && L->max_tokens % bsa::kBlock == 0,
+              BSA_ERR_INVALID_ARG, "max_tokens %d must be a positive multiple of 128",
+              L->max_tokens);
+  BSA_REQUIRE(L->max_tokens <= (1 << 26), BSA_ERR_UNSUPPORTED, "max_tokens %d above 2^26",
+              L->max_tokens);
+  BSA_REQUIRE(int64_t(L->batch) * L->num_kv_heads <= 65535, BSA_ERR_UNSUPPORTED,
+              "batch * num_kv_heads above 65535");
+  BSA_REQUIRE(L->kv_stride_t >= bsa::kHeadDim && L->kv_stride_t % 8 == 0 && L->kv_stride_h >= 0 &&
+                  L->kv_stride_h % 8 == 0 && L->kv_stride_b >= 0 && L->kv_stride_b % 8 == 0,
+              BSA_ERR_INVALID_ARG,
+              "strides (b %lld, h %lld, t %lld): t >= 128, all non-negative multiples of 8",
+              (long long)L->kv_stride_b, (long long)L->kv_stride_h, (long long)L->kv_stride_t);
+  BSA_REQUIRE(L->kv_dtype == BSA_DTYPE_F16 || L->kv_dtype == BSA_DTYPE_BF16, BSA_ERR_UNSUPPORTED,
+              "kv_dtype %d", L->kv_dtype);
+  BSA_REQUIRE(c->granularity == BSA_GRANULARITY_BLOCK || c->granularity == BSA_GRANULARITY_TOKEN,
+              BSA_ERR_INVALID_ARG, "granularity %d", c->granularity);
+  BSA_REQUIRE(std::isfinite(c->softmax_scale) && c->softmax_scale > 0.0f, BSA_ERR_INVALID_ARG,
+              "softmax_scale must be finite and > 0");
+  const int NB = L->max_tokens / bsa::kBlock;
+  if (c->granularity == BSA_GRANULARITY_BLOCK) {
+    BSA_REQUIRE(c->n_tail_pages >= 0 && c->n_tail_pages <= 2, BSA_ERR_INVALID_ARG,
+                "n_tail_pages %d must be 0, 1 or 2", c->n_tail_pages);
+    BSA_REQUIRE(c->budget >= 1 && c->budget >= c->n_tail_pages && c->budget <= NB,
+                BSA_ERR_INVALID_ARG, "block budget %d must lie in [max(1, n_tail_pages), %d]",
+                c->budget, NB);
+  } else {
+    BSA_REQUIRE(c->n_tail_pages == 0, BSA_ERR_INVALID_ARG, "token mode takes no tail pages");
+    BSA_REQUIRE(c->budget >= 1 && c->budget <= L->max_tokens, BSA_ERR_INVALID_ARG,
+                "token budget %d must lie in [1, %d]", c->budget, L->max_tokens);
+    const int r = c->proj_rank;
+    BSA_REQUIRE(r == 8 || r == 16 || r == 32 || r == 64 || r == 128, BSA_ERR_UNSUPPORTED,
+                "proj_rank %d: supported 8, 16, 32, 64, 128", r);
+  }
+  g->B = L->batch;
+  g->Hkv = L->num_kv_heads;
+  g->Hq = L->num_q_heads;
+  g->G = G;
+  g->Tmax = L->max_tokens;
+  g->NBmax = NB;
+  g->sb = L->kv_stride_b;
+  g->sh = L->kv_stride_h;
+  g->st = L->kv_stride_t;
+  g->dtype = L->kv_dtype;
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* k,
+                      const float* key_center, const float* global_scale, const float* proj,
+                      int32_t block_begin, int32_t block_end, uint8_t* codes, uint8_t* scales,
+                      uint16_t* kproj, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    BSA_REQUIRE(k && aligned16(k), BSA_ERR_INVALID_ARG, "k must be a 16-byte aligned device pointer");
+    BSA_REQUIRE(0 <= block_begin && block_begin <= block_end && block_end <= g.NBmax,
+                BSA_ERR_INVALID_ARG, "block range [%d, %d) outside [0, %d]", block_begin,
+                block_end, g.NBmax);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (cfg->granularity == BSA_GRANULARITY_BLOCK) {
+      BSA_REQUIRE(global_scale && codes && scales && aligned16(codes), BSA_ERR_INVALID_ARG,
+                  "block mode needs global_scale, codes (16-byte aligned) and scales");
+      return hip_status(bsa::launch_pack_block(g, k, key_center, global_scale, block_begin,
+                                               block_end, codes, scales, s),
+                        "pack_nvfp4");
+    }
+    BSA_REQUIRE(proj && kproj, BSA_ERR_INVALID_ARG, "token mode needs proj and kproj");
+    return hip_status(bsa::launch_pack_proj(g, k, proj, cfg->proj_rank, block_begin, block_end,
+                                            kproj, s),
+                      "pack_proj");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                   const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                   const float* key_center, const uint16_t* kproj, const float* proj,
+                   const int32_t* seq_lens, float* scores, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    BSA_REQUIRE(q && aligned16(q) && seq_lens && scores, BSA_ERR_INVALID_ARG,
+                "q (16-byte aligned), seq_lens and scores are required");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const _Float16* qh = static_cast<const _Float16*>(q);
+    if (cfg->granularity == BSA_GRANULARITY_BLOCK) {
+      BSA_REQUIRE(codes && scales && global_scale && aligned16(codes) && aligned16(scales),
+                  BSA_ERR_INVALID_ARG,
+                  "block mode needs codes, scales (16-byte aligned) and global_scale");
+      return hip_status(bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale, qh,
+                                               codes, scales, global_scale, key_center,
+                                               seq_lens, scores, s),
+                        "scan_block");
+    }
+    BSA_REQUIRE(kproj && proj && aligned16(kproj), BSA_ERR_INVALID_ARG,
+                "token mode needs kproj (16-byte aligned) and proj");
+    return hip_status(bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank, qh, kproj,
+                                             proj, seq_lens, scores, s),
+                      "scan_token");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+size_t bsa_workspace_size(const bsa_kv_layout* layout, const bsa_select_cfg* cfg) {
+  bsa::UnitGeom g;
+  if (check_common(layout, cfg, &g)) return 0;
+  return cfg->granularity == BSA_GRANULARITY_TOKEN ? bsa::token_select_workspace(g) : 0;
+}
+
+int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const float* scores,
+                    const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                    int32_t* idx, int32_t* count, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    BSA_REQUIRE(scores && seq_lens && idx && count, BSA_ERR_INVALID_ARG,
+                "scores, seq_lens, idx and count are required");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (cfg->granularity == BSA_GRANULARITY_BLOCK)
+      return hip_status(bsa::launch_select_block(g, cfg->budget, cfg->n_tail_pages, scores,
+                                                 seq_lens, idx, count, s),
+                        "select_block");
+    const size_t need = bsa::token_select_workspace(g);
+    BSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), BSA_ERR_WORKSPACE,
+                "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    return hip_status(bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx,
+                                               count, s),
+                      "select_token");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                           const void* k, const void* v, const int32_t* seq_lens,
+                           const int32_t* idx, const int32_t* count, const uint16_t* tail_k,
+                           const uint16_t* tail_v, int32_t num_splits, float* part_o,
+                           float* part_lse, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
+                "q, k, v must be 16-byte aligned device pointers");
+    BSA_REQUIRE(seq_lens && idx && count && part_o && part_lse, BSA_ERR_INVALID_ARG,
+                "seq_lens, idx, count, part_o and part_lse are required");
+    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
+                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
+                num_splits);
+    if (cfg->n_tail_pages > 0)
+      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
+                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_attention(g, cfg->granularity, cfg->budget, cfg->n_tail_pages,
+                                            cfg->softmax_scale, static_cast<const _Float16*>(q),
+                                            k, v, seq_lens, idx, count, tail_k, tail_v,
+                                            num_splits, part_o, part_lse, s),
+                      "sparse_decode_attn");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float* part_o,
+                const float* part_lse, float* out, float* out_lse, void* stream) {
+  try {
+    BSA_REQUIRE(head_dim == bsa::kHeadDim, BSA_ERR_UNSUPPORTED, "head_dim %d: only 128", head_dim);
+    BSA_REQUIRE(rows >= 0 && num_splits >= 1 && num_splits <= 1024, BSA_ERR_INVALID_ARG,
+                "rows %d >= 0 and num_splits %d in [1, 1024] required", rows, num_splits);
+    BSA_REQUIRE(rows == 0 || (part_o && part_lse && out), BSA_ERR_INVALID_ARG,
+                "part_o, part_lse and out are required");
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_combine(rows, num_splits, part_o, part_lse, out, out_lse,
+                                          static_cast<hipStream_t>(stream)),
+                      "combine");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+const char* bsa_version(void) { return "bsa 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Shared device and host helpers of the gfx950 sparse decode-attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsa.h"
+
+namespace bsa {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 128;       // tokens per selectable block (Jet-QSparse abstract)
+constexpr int kCodeRecord = 8192; // bytes of E2M1 codes per (unit, block)
+constexpr int kScaleRecord = 1024;// bytes of E4M3 scales per (unit, block)
+constexpr int kWave = 64;
+constexpr int kMaxGroup = 16;     // query heads per KV head held by one MFMA row set
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+
+// --- number formats --------------------------------------------------------
+
+// OCP E4M3FN byte -> float (exact). 0x7F / 0xFF (NaN) never occur in a packed
+// scale: the packer saturates at 0x7E.
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __builtin_ldexpf(float(8u + m), int(e) - 10)  // 2^(e-7) (1 + m/8)
+                      : __builtin_ldexpf(float(m), -9);               // m 2^-9
+  return (b & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t bits) {
+  union { uint16_t u; _Float16 h; } cv;
+  cv.u = bits;
+  return float(cv.h);
+}
+
+// Order-preserving map of a float score to an unsigned key: larger score ->
+// larger key; -0 and +0 share a key; NaN maps to 0, below every number.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) return 0u;
+  if (s == 0.0f) s = 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// --- wave reductions (64 lanes) --------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Maximum over the 16 lanes of a row (lanes 16r .. 16r+15).
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ int clamp_len(int L, int tmax) { return L < 0 ? 0 : (L > tmax ? tmax : L); }
+
+}  // namespace bsa
+
+// --- host launchers (defined in the kernel files, called by api.hip) -------
+
+namespace bsa {
+
+struct UnitGeom {
+  int B, Hkv, Hq, G, Tmax, NBmax;
+  int64_t sb, sh, st;  // K/V strides in elements
+  int dtype;
+};
+
+hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* center,
+                             const float* gscale, int blk0, int blk1, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s);
+hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
+                            int blk0, int blk1, uint16_t* kproj, hipStream_t s);
+hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
+                             const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                             const float* center, const int32_t* seq_lens, float* scores,
+                             hipStream_t s);
+hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, const _Float16* q,
+                             const uint16_t* kproj, const float* proj, const int32_t* seq_lens,
+                             float* scores, hipStream_t s);
+size_t token_select_workspace(const UnitGeom& g);
+hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
+                               const int32_t* seq_lens, int32_t* idx, int32_t* count,
+                               hipStream_t s);
+hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
+                               const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
+                               hipStream_t s);
+hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int n_tail,
+                            float sigma, const _Float16* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
+                            const uint16_t* tail_k, const uint16_t* tail_v, int splits,
+                            float* part_o, float* part_lse, hipStream_t s);
+hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
+                          float* out, float* out_lse, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,175 @@
+// Packers of the key copies (off the timed decode path).
+//
+// Block mode: NVFP4 -- E2M1 elements, one E4M3 scale per 16 channels, one FP32
+// scale per KV head, keys centered first (Jet-QSparse abstract: NVFP4 cache,
+// calibrated key centering, packed straight from the 16-bit activations).
+// Token mode: BF16 projected keys kproj = P^T k (JSSA Figure 1 and Figure 10).
+//
+// Every rounding step is a single IEEE float32 operation (no contraction into
+// fused multiply-adds), so the bytes are reproducible bit for bit.
+#pragma clang fp contract(off)
+
+#include "common.hpp"
+
+namespace bsa {
+namespace {
+
+// Nearest E4M3FN code of r >= 0, ties to the even code, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_from_float(float r) {
+  if (!(r > 0.0f)) return 0u;
+  if (r >= 448.0f) return 0x7Eu;
+  const int e = int((__float_as_uint(r) >> 23) & 0xFFu) - 127;  // r is a normal float here
+  uint32_t code;
+  if (e < -6) {
+    // subnormal range: value = m * 2^-9, m in 0..8 (m = 8 is the smallest normal)
+    code = uint32_t(__builtin_rintf(__builtin_ldexpf(r, 9)));
+  } else {
+    // r = 2^e * (1 + f), mantissa 3 bits: m = rne((r / 2^e - 1) * 8), may carry to 8
+    const float frac = __builtin_ldexpf(r, 3 - e) - 8.0f;  // exact
+    const uint32_t m = uint32_t(__builtin_rintf(frac));
+    code = (uint32_t(e + 7) << 3) + m;
+  }
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Nearest E2M1 code of x (ties to the even code, saturating at 6), sign from x.
+__device__ __forceinline__ uint32_t e2m1_from_float(float x) {
+  const float a = __builtin_fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;        // 0   (0.25 ties to code 0)
+  else if (a < 0.75f) c = 1;    // 0.5
+  else if (a <= 1.25f) c = 2;   // 1   (0.75 and 1.25 tie to code 2)
+  else if (a < 1.75f) c = 3;    // 1.5
+  else if (a <= 2.5f) c = 4;    // 2   (1.75 and 2.5 tie to code 4)
+  else if (a < 3.5f) c = 5;     // 3
+  else if (a <= 5.0f) c = 6;    // 4   (3.5 and 5 tie to code 6)
+  else c = 7;                   // 6   (saturation)
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <int DT>
+__device__ __forceinline__ void load16(const uint16_t* p, float* out) {
+  const uint4v a = *reinterpret_cast<const uint4v*>(p);
+  const uint4v b = *reinterpret_cast<const uint4v*>(p + 8);
+  const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (DT == BSA_DTYPE_F16) {
+      out[2 * i] = half_bits_to_float(uint16_t(w[i] & 0xFFFFu));
+      out[2 * i + 1] = half_bits_to_float(uint16_t(w[i] >> 16));
+    } else {
+      out[2 * i] = bf16_bits_to_float(w[i] & 0xFFFFu);
+      out[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
+    }
+  }
+}
+
+// One work-group packs one (unit, block): 1024 (token, 16-channel group) items,
+// four per thread. Consecutive threads take consecutive groups of one token.
+template <int DT>
+__global__ __launch_bounds__(256) void pack_nvfp4_kernel(
+    const uint16_t* __restrict__ k, const float* __restrict__ center,
+    const float* __restrict__ gscale, int Hkv, int NBmax, int64_t sb, int64_t sh, int64_t st,
+    int blk0, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int blk = blk0 + blockIdx.x;
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv, h = unit % Hkv;
+  const float s_t = gscale[h];
+  const float six_st = 6.0f * s_t;
+  uint8_t* crec = codes + (int64_t(unit) * NBmax + blk) * kCodeRecord;
+  uint8_t* srec = scales + (int64_t(unit) * NBmax + blk) * kScaleRecord;
+  const uint16_t* kb = k + b * sb + h * sh + int64_t(blk) * kBlock * st;
+#pragma unroll 1
+  for (int r = 0; r < 4; ++r) {
+    const int item = threadIdx.x + 256 * r;
+    const int tau = item >> 3, g = item & 7;
+    float y[16];
+    load16<DT>(kb + tau * st + 16 * g, y);
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float c = center ? center[h * kHeadDim + 16 * g + u] : 0.0f;
+      y[u] = y[u] - c;
+      amax = fmaxf(amax, __builtin_fabsf(y[u]));
+    }
+    const uint32_t sbyte = e4m3_from_float(amax / six_st);
+    const float S = e4m3_to_float(sbyte) * s_t;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t c = S > 0.0f ? e2m1_from_float(y[u] / S) : 0u;
+      if (u < 8) lo |= c << (4 * u);
+      else hi |= c << (4 * (u - 8));
+    }
+    const int i = tau >> 4, n = tau & 15, j = g >> 1, s = g & 1;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(crec + ((i * 4 + j) * 16 + n) * 16 + 8 * s);
+    dst[0] = lo;
+    dst[1] = hi;
+    srec[((j * 16 + n) * 8 + i) * 2 + s] = uint8_t(sbyte);
+  }
+}
+
+// Projected keys: one thread per (token, output channel); the float32 sum runs
+// over d in ascending order with separately rounded products and additions.
+template <int DT>
+__global__ __launch_bounds__(256) void pack_proj_kernel(
+    const uint16_t* __restrict__ k, const float* __restrict__ proj, int Hkv, int Tmax,
+    int64_t sb, int64_t sh, int64_t st, int rank, int tok0, int ntok,
+    uint16_t* __restrict__ kproj) {
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv, h = unit % Hkv;
+  const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= int64_t(ntok) * rank) return;
+  const int t = tok0 + int(item / rank), j = int(item % rank);
+  const uint16_t* kr = k + b * sb + h * sh + int64_t(t) * st;
+  const float* P = proj + int64_t(h) * kHeadDim * rank + j;
+  float acc = 0.0f;
+  for (int d = 0; d < kHeadDim; d += 16) {
+    float kv[16];
+    load16<DT>(kr + d, kv);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float prod = P[(d + u) * rank] * kv[u];
+      acc = acc + prod;
+    }
+  }
+  // float32 -> bfloat16, round to nearest even (inputs are finite)
+  const uint32_t u = __float_as_uint(acc);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  kproj[(int64_t(unit) * Tmax + t) * rank + j] = uint16_t(rounded);
+}
+
+}  // namespace
+
+hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* center,
+                             const float* gscale, int blk0, int blk1, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s) {
+  if (blk1 <= blk0) return hipSuccess;
+  dim3 grid(blk1 - blk0, g.B * g.Hkv);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  if (g.dtype == BSA_DTYPE_F16)
+    hipLaunchKernelGGL(pack_nvfp4_kernel<BSA_DTYPE_F16>, grid, dim3(256), 0, s, kp, center,
+                       gscale, g.Hkv, g.NBmax, g.sb, g.sh, g.st, blk0, codes, scales);
+  else
+    hipLaunchKernelGGL(pack_nvfp4_kernel<BSA_DTYPE_BF16>, grid, dim3(256), 0, s, kp, center,
+                       gscale, g.Hkv, g.NBmax, g.sb, g.sh, g.st, blk0, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
+                            int blk0, int blk1, uint16_t* kproj, hipStream_t s) {
+  if (blk1 <= blk0) return hipSuccess;
+  const int tok0 = blk0 * kBlock, ntok = (blk1 - blk0) * kBlock;
+  const int64_t items = int64_t(ntok) * rank;
+  dim3 grid(unsigned((items + 255) / 256), g.B * g.Hkv);
+  const uint16_t* kp = static_cast<const uint16_t*>(k);
+  if (g.dtype == BSA_DTYPE_F16)
+    hipLaunchKernelGGL(pack_proj_kernel<BSA_DTYPE_F16>, grid, dim3(256), 0, s, kp, proj, g.Hkv,
+                       g.Tmax, g.sb, g.sh, g.st, rank, tok0, ntok, kproj);
+  else
+    hipLaunchKernelGGL(pack_proj_kernel<BSA_DTYPE_BF16>, grid, dim3(256), 0, s, kp, proj, g.Hkv,
+                       g.Tmax, g.sb, g.sh, g.st, rank, tok0, ntok, kproj);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

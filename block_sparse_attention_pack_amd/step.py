@@ -1,0 +1,146 @@
+"""Device buffers of one decode step and the four-call hot path.
+
+PyTorch only provides device memory and the stream here; every step of the
+path runs in libbsa.so kernels through :mod:`block_sparse_attention_pack_amd.binding`.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import binding as bsa
+from .workloads import BLOCK, HEAD_DIM, Workload
+
+
+def default_splits(units: int, budget: int, granularity: str) -> int:
+    """Split count that gives the attention launch about 1024 work-groups."""
+    s = max(1, math.ceil(1024 / max(units, 1)))
+    if granularity == "token":
+        s = min(s, max(1, budget // 32))  # at least one 32-row tile per split
+    return max(1, min(s, budget))
+
+
+@dataclasses.dataclass
+class DeviceStep:
+    """Inputs, the key copy and the step's outputs, resident on one GPU."""
+
+    w: Workload
+    layout: bsa.KvLayout
+    cfg: bsa.SelectCfg
+    splits: int
+    q: "torch.Tensor"
+    k: "torch.Tensor"
+    v: "torch.Tensor"
+    seq_lens: "torch.Tensor"
+    key_center: "torch.Tensor"
+    global_scale: "torch.Tensor"
+    tail_k: Optional["torch.Tensor"]
+    tail_v: Optional["torch.Tensor"]
+    proj: Optional["torch.Tensor"]
+    codes: Optional["torch.Tensor"]
+    scales: Optional["torch.Tensor"]
+    kproj: Optional["torch.Tensor"]
+    scores: "torch.Tensor"
+    workspace: Optional["torch.Tensor"]
+    ws_bytes: int
+    idx: "torch.Tensor"
+    count: "torch.Tensor"
+    part_o: "torch.Tensor"
+    part_lse: "torch.Tensor"
+    out: "torch.Tensor"
+    out_lse: "torch.Tensor"
+
+    @property
+    def block_mode(self) -> bool:
+        return self.cfg.granularity == bsa.BLOCK
+
+    # -- the cache build (not part of the timed step) ------------------------
+    def pack(self, stream=None) -> None:
+        nb = self.w.spec.max_blocks
+        bsa.pack_kv_cache(self.layout, self.cfg, self.k, self.key_center, self.global_scale,
+                          self.proj, 0, nb, self.codes, self.scales, self.kproj, stream)
+
+    # -- the decode step ------------------------------------------------------
+    def scan(self, stream=None) -> None:
+        bsa.score_scan(self.layout, self.cfg, self.q, self.codes, self.scales,
+                       self.global_scale, self.key_center, self.kproj, self.proj,
+                       self.seq_lens, self.scores, stream)
+
+    def select(self, stream=None) -> None:
+        bsa.select_topk(self.layout, self.cfg, self.scores, self.seq_lens, self.workspace,
+                        self.ws_bytes, self.idx, self.count, stream)
+
+    def attend(self, stream=None) -> None:
+        bsa.sparse_decode_attn(self.layout, self.cfg, self.q, self.k, self.v, self.seq_lens,
+                               self.idx, self.count, self.tail_k, self.tail_v, self.splits,
+                               self.part_o, self.part_lse, stream)
+
+    def combine(self, stream=None) -> None:
+        rows = self.w.spec.batch * self.w.spec.q_heads
+        bsa.combine(rows, self.splits, HEAD_DIM, self.part_o, self.part_lse, self.out,
+                    self.out_lse, stream)
+
+    def run(self, stream=None) -> None:
+        self.scan(stream)
+        self.select(stream)
+        self.attend(stream)
+        self.combine(stream)
+
+
+def upload(w: Workload, device="cuda", splits: Optional[int] = None,
+           kv_dtype: str = "f16") -> DeviceStep:
+    """Copy a workload to the GPU and allocate every buffer of the step.
+
+    ``kv_dtype="bf16"`` stores K and V as bfloat16 instead (values rounded from
+    the fp16 draws), for the BF16-cache variant.
+    """
+    import torch
+
+    s = w.spec
+    B, Hkv, Hq, T = s.batch, s.kv_heads, s.q_heads, s.max_tokens
+    dev = torch.device(device)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    k = t(w.k)
+    v = t(w.v)
+    if kv_dtype == "bf16":
+        k = k.to(torch.bfloat16)
+        v = v.to(torch.bfloat16)
+    layout = bsa.layout_for(k, Hq)
+    gran = bsa.BLOCK if s.granularity == "block" else bsa.TOKEN
+    cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
+                         w.softmax_scale)
+    if splits is None:
+        splits = default_splits(B * Hkv, s.budget, s.granularity)
+    nb = s.max_blocks
+    codes = scales = kproj = proj = None
+    if gran == bsa.BLOCK:
+        codes = torch.empty((B, Hkv, nb, 8192), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, Hkv, nb, 1024), dtype=torch.uint8, device=dev)
+        scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
+    else:
+        kproj = torch.empty((B, Hkv, T, s.rank), dtype=torch.int16, device=dev)
+        proj = t(w.proj)
+        scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    tail_k = tail_v = None
+    if s.n_tail:
+        tail_k = t(w.tail_k.view(np.int16))
+        tail_v = t(w.tail_v.view(np.int16))
+    ws_bytes = bsa.workspace_size(layout, cfg)
+    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    return DeviceStep(
+        w=w, layout=layout, cfg=cfg, splits=splits,
+        q=t(w.q), k=k, v=v, seq_lens=t(w.seq_lens), key_center=t(w.key_center),
+        global_scale=t(w.global_scale), tail_k=tail_k, tail_v=tail_v, proj=proj,
+        codes=codes, scales=scales, kproj=kproj, scores=scores, workspace=workspace,
+        ws_bytes=ws_bytes,
+        idx=torch.empty((B, Hkv, s.budget), dtype=torch.int32, device=dev),
+        count=torch.empty((B, Hkv), dtype=torch.int32, device=dev),
+        part_o=torch.empty((B, Hq, splits, HEAD_DIM), dtype=torch.float32, device=dev),
+        part_lse=torch.empty((B, Hq, splits), dtype=torch.float32, device=dev),
+        out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev),
+        out_lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
+    )

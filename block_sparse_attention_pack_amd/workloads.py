@@ -71,6 +71,7 @@ class Spec:
     outlier_gain: float = 1.0
     ragged: bool = False  # lengths uniform in [max_tokens/2, max_tokens]
     rank: int = 0  # projection rank in token mode
+    lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
     def group(self) -> int:
@@ -160,6 +161,9 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def _seq_lens(spec: Spec) -> np.ndarray:
+    if spec.lengths is not None:
+        assert len(spec.lengths) == spec.batch
+        return np.asarray(spec.lengths, dtype=np.int32)
     if not spec.ragged:
         return np.full(spec.batch, spec.max_tokens, dtype=np.int32)
     rng = np.random.default_rng([spec.seed, _S_LENS])

@@ -1,0 +1,219 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) sparse decode-attention library.
+ *
+ * One decode step per layer, per unit = one (sequence b, KV head h):
+ *
+ *   score_scan   score every cached key from a 4-bit copy (block mode) or a
+ *                rank-r projected copy (token mode)
+ *   select_topk  choose the budget per KV head: top blocks of 128 tokens (plus
+ *                the forced BF16 tail pages) or top tokens
+ *   sparse_decode_attn
+ *                softmax(sigma q K^T) V over the chosen rows only, read in
+ *                place from the FP16 cache, FP32 accumulation, split into
+ *                num_splits partials per query head
+ *   combine      log-sum-exp merge of the partials
+ *
+ * and, off the timed path, pack_kv_cache builds the 4-bit key copy or the
+ * projected-key copy.
+ *
+ * Sources: Jet-QSparse (arXiv 2611.01022) abstract -- NVFP4 key cache, a dense
+ * scan over the whole history, selection of 128-token blocks with a budget per
+ * KV head, FP16 value aggregation with FP32 accumulation, calibrated key
+ * centering, at most two BF16 pages per sequence; JSSA (arXiv 2610.19026)
+ * abstract and Figure 1 -- the group's mean query scores a projected-key cache,
+ * one top-B token set per KV head shared by its query heads, attention that
+ * reads the selected rows of the standard GQA cache without gathering them.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers are device memory of the current HIP
+ *     device; the caller owns every buffer; the library allocates nothing,
+ *     frees nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns without waiting for it. Inputs must stay valid and outputs
+ *     unread until the stream reaches the work.
+ *   - Same inputs give the same output bits (no float atomics; fixed orders).
+ *   - Return value: BSA_OK, or a negative code with a message readable from
+ *     bsa_last_error() on the calling thread. Argument checks happen before
+ *     anything is enqueued; nothing is enqueued when a check fails.
+ *   - Contents of device buffers are not validated (the library cannot read
+ *     them without synchronizing): seq_lens must lie in [0, max_tokens],
+ *     global_scale must be finite and > 0, idx entries must be -1 or valid.
+ *     Out-of-range seq_lens are clamped to [0, max_tokens]; idx entries outside
+ *     the valid range are skipped; no such input makes a kernel read or write
+ *     outside the buffers described here.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes or strides */
+  BSA_ERR_UNSUPPORTED = -2, /* head_dim or block_size other than 128, group > 16, ... */
+  BSA_ERR_HIP = -3,         /* a HIP launch failed (message names the HIP error) */
+  BSA_ERR_WORKSPACE = -4    /* workspace missing or smaller than bsa_workspace_size() */
+};
+
+enum { BSA_DTYPE_F16 = 0, BSA_DTYPE_BF16 = 1 };
+enum { BSA_GRANULARITY_BLOCK = 0, BSA_GRANULARITY_TOKEN = 1 };
+
+/* Standard GQA KV cache: K and V are [batch][num_kv_heads][max_tokens][head_dim]
+ * through the strides below (in elements, head_dim contiguous). Query head hq
+ * belongs to KV head hq / (num_q_heads / num_kv_heads). */
+typedef struct bsa_kv_layout {
+  int32_t batch;        /* B >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t num_q_heads;  /* Hq, a multiple of Hkv; group G = Hq/Hkv in 1..16 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t block_size;   /* must be 128 */
+  int32_t max_tokens;   /* Tmax: capacity per unit, a multiple of 128 */
+  int64_t kv_stride_b;  /* elements between sequences */
+  int64_t kv_stride_h;  /* elements between KV heads */
+  int64_t kv_stride_t;  /* elements between tokens, >= head_dim, multiple of 8 */
+  int32_t kv_dtype;     /* BSA_DTYPE_F16 or BSA_DTYPE_BF16 (K and V alike) */
+} bsa_kv_layout;
+
+/* Selection rule of the step. */
+typedef struct bsa_select_cfg {
+  int32_t granularity;  /* BSA_GRANULARITY_BLOCK or BSA_GRANULARITY_TOKEN */
+  int32_t budget;       /* per unit: blocks (forced tail pages included) or tokens */
+  int32_t n_tail_pages; /* BLOCK: 0..2 newest pages kept in a BF16 store and always
+                           selected (Jet-QSparse abstract); TOKEN: must be 0 */
+  int32_t proj_rank;    /* TOKEN: r, a multiple of 8 in 8..128; BLOCK: ignored */
+  float softmax_scale;  /* sigma, > 0 (1/sqrt(128) for the standard scale) */
+} bsa_select_cfg;
+
+/* ---------------------------------------------------------------------------
+ * Layout of the 4-bit key copy (BLOCK mode)
+ *
+ * codes  : uint8 [B][Hkv][max_tokens/128][8192]
+ * scales : uint8 [B][Hkv][max_tokens/128][1024]
+ * For token tau = 16 i + n (i < 8, n < 16) of a block and channel d = 32 j + e
+ * (j < 4, e < 32), scale group g = d / 16 = 2 j + s (s < 2):
+ *   E2M1 code of (tau, d)   at byte ((i*4 + j)*16 + n)*16 + e/2 of the code
+ *                           record, low nibble for even e, high nibble for odd e
+ *   E4M3 scale of (tau, g)  at byte ((j*16 + n)*8 + i)*2 + s of the scale record
+ * The order lets one 64-lane wave load 16 tokens x 128 channels with one
+ * contiguous 16-byte load per lane, already in the matrix-core operand order.
+ *
+ * Number format (NVFP4, named by the Jet-QSparse abstract): E2M1 elements,
+ * one E4M3 (OCP E4M3FN) scale per 16 channels, one FP32 scale s_t per KV head.
+ * Packing of key row k with centering vector c:
+ *   y   = fl32(fl32(k) - c[h])
+ *   sb  = E4M3_rne_sat( fl32( max|y over the group| / fl32(6 * s_t[h]) ) )
+ *   S   = fl32(E4M3(sb) * s_t[h])
+ *   code= S > 0 ? E2M1_rne_sat(fl32(y / S)) : 0     (sign copied from y)
+ * The dequantized key is s_t[h] * E2M1(code) * E4M3(sb) + c[h].
+ * ------------------------------------------------------------------------- */
+
+/* Build the key copy for blocks [block_begin, block_end) of every unit.
+ *
+ * BLOCK: k (device, kv_dtype, layout above), key_center (device float
+ *   [Hkv][128], or NULL for no centering), global_scale (device float [Hkv],
+ *   finite > 0) -> codes, scales (device, layout above). proj and kproj unused.
+ * TOKEN: k and proj (device float [Hkv][128][r]) -> kproj (device uint16
+ *   bfloat16 bits [B][Hkv][max_tokens][r]) for tokens [128*block_begin,
+ *   128*block_end): kproj[t][j] = BF16_rne(acc), acc the float32 sum over
+ *   d = 0..127 in ascending order of fl32(P[h][d][j] * k[t][d]), each addition
+ *   rounded to float32 (JSSA Figure 1: projected-key cache; Figure 10: BF16).
+ * Packing all tokens of the blocks regardless of sequence length is the
+ * caller's choice: blocks past a sequence's end are never read by the scan.
+ * Requires 0 <= block_begin <= block_end <= max_tokens/128. */
+int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                      const void* k, const float* key_center, const float* global_scale,
+                      const float* proj, int32_t block_begin, int32_t block_end,
+                      uint8_t* codes, uint8_t* scales, uint16_t* kproj, void* stream);
+
+/* Score the cache for one decode step.
+ *
+ * q: device fp16 [B][Hq][128] contiguous. seq_lens: device int32 [B].
+ * BLOCK (Jet-QSparse abstract: dense scan of the whole history, 128-token
+ *   blocks): for block n < P_b = ceil(L_b/128) - n_tail_pages,
+ *     scores[b][h][n] = max over query heads hq of KV head h and tokens t of
+ *       block n with t < L_b of  sigma * (s_t[h] * q_hq . (E2M1 * E4M3)(t)
+ *                                           + q_hq . c[h])
+ *   (the centering vector is added back so the estimate targets q . k;
+ *   key_center NULL means c = 0); every other block scores -inf.
+ *   codes, scales, global_scale required; kproj, proj unused.
+ * TOKEN (JSSA Figure 1): qbar = mean of the group's query heads,
+ *   p = P[h]^T qbar, scores[b][h][t] = sigma * p . kproj[b][h][t] for t < L_b,
+ *   -inf beyond. kproj, proj required; codes, scales, global_scale unused.
+ * scores: device float [B][Hkv][max_tokens/128] (BLOCK) or [B][Hkv][max_tokens]
+ * (TOKEN); every entry is written. */
+int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                   const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                   const float* key_center, const uint16_t* kproj, const float* proj,
+                   const int32_t* seq_lens, float* scores, void* stream);
+
+/* Bytes of device workspace bsa_select_topk needs for this layout and cfg
+ * (0 for BLOCK granularity). */
+size_t bsa_workspace_size(const bsa_kv_layout* layout, const bsa_select_cfg* cfg);
+
+/* Choose the budget per unit (Jet-QSparse abstract: top blocks per KV head;
+ * JSSA Figure 1 and Table 15: top-B tokens per KV head, shared by its query heads).
+ *
+ * BLOCK: candidates are blocks n < P_b (see score_scan); the
+ *   (budget - n_tail_pages) highest-scoring candidates are taken, plus the
+ *   forced pages max(0, N_b - n_tail_pages) .. N_b - 1, N_b = ceil(L_b/128).
+ * TOKEN: candidates are tokens t < L_b; the budget highest-scoring are taken.
+ * Equal scores go to the lower index; NaN ranks below every number; -0 == +0.
+ * idx: device int32 [B][Hkv][budget], ascending, padded with -1.
+ * count: device int32 [B][Hkv], the number of valid idx entries.
+ * workspace: device memory of at least bsa_workspace_size() bytes (may be NULL
+ * when that is 0); its contents on entry do not matter. */
+int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                    const float* scores, const int32_t* seq_lens, void* workspace,
+                    size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream);
+
+/* Sparse attention over the selected rows, as split partials (Jet-QSparse
+ * abstract: FP16 aggregation with FP32 accumulation over contiguous block
+ * tiles; JSSA Figure 1: gather-free reads of the selected rows).
+ *
+ * For query head hq of KV head h and split s, with per = ceil(budget/S), the
+ * rows are those of idx entries [s*per, min((s+1)*per, budget)) that are not -1:
+ *   BLOCK: the tokens t of each selected block with t < L_b; a block that is one
+ *     of the n_tail_pages newest pages (n >= N_b - n_tail_pages) is read from
+ *     the BF16 tail store, slot n - (N_b - n_tail_pages), else from k, v.
+ *   TOKEN: the tokens idx[...] (those >= L_b are skipped).
+ *   part_o[b][hq][s][:]  = sum_t softmax_t(sigma q . k_t) v_t over the split's rows
+ *   part_lse[b][hq][s]   = log sum_t exp(sigma q . k_t)
+ *   (an empty split writes 0 and -inf).
+ * q: device fp16 [B][Hq][128]. k, v: device, kv_dtype, the layout above.
+ * tail_k, tail_v: device bfloat16 bits [B][Hkv][n_tail_pages][128][128], or
+ * NULL when n_tail_pages is 0. idx, count: as written by bsa_select_topk
+ * (count is read only to skip the work of unused entries).
+ * part_o: device float [B][Hq][S][128]; part_lse: device float [B][Hq][S];
+ * 1 <= num_splits <= budget. */
+int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                           const void* q, const void* k, const void* v,
+                           const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
+                           const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
+                           float* part_o, float* part_lse, void* stream);
+
+/* Log-sum-exp merge of split partials, per row r (a (sequence, query head)):
+ *   lse[r] = log sum_s exp(part_lse[r][s]),
+ *   out[r] = sum_s exp(part_lse[r][s] - lse[r]) * part_o[r][s][:];
+ * rows whose splits are all empty get out = 0 and lse = -inf.
+ * part_o: device float [rows][num_splits][head_dim]; part_lse: device float
+ * [rows][num_splits]; out: device float [rows][head_dim]; out_lse: device
+ * float [rows] (may be NULL). head_dim must be 128. */
+int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float* part_o,
+                const float* part_lse, float* out, float* out_lse, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* Library version string. */
+const char* bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,146 @@
+"""Stage-by-stage comparison of the HIP path with the oracle, one unit at a time.
+
+Tolerances (the oracle is float64):
+  pack           bit-exact bytes
+  block scores   |gpu - oracle| <= 8e-6 * A + 1e-6, A = sigma * (s_t * sum|q| |dequant k|
+                 + sum |q| |c|) maximised over the block: FP32 accumulation of at
+                 most 130 exactly formed products (error <= 130 * 2^-24 * A)
+  token scores   same form with A = sigma * sum_j |p_j| |kproj_j| (float32 p = P^T qbar)
+  selection      integer work: the oracle's selection run on the GPU's own scores
+                 must equal the GPU's bit for bit; against the oracle's scores the
+                 two may differ only on entries whose oracle score lies within
+                 1e-4 relative of the boundary score
+  attention      max |O_gpu - O_oracle| <= 2e-3 and |lse_gpu - lse_oracle| <= 2e-3,
+                 both sides on the GPU's selection
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import decode as O
+from oracle import nvfp4
+
+SCORE_REL = 8e-6
+SCORE_ABS = 1e-6
+BOUNDARY_REL = 1e-4
+OUT_TOL = 2e-3
+
+
+def q_group(w, b, h):
+    G = w.spec.group
+    return w.q[b, h * G:(h + 1) * G]
+
+
+def check_pack_block(w, b, h, codes_gpu, scales_gpu):
+    nb = w.spec.max_blocks
+    rc, rs = O.pack_unit_blocks(w.k[b, h], w.key_center[h], w.global_scale[h], 0, nb)
+    assert np.array_equal(codes_gpu, rc), f"code bytes differ at unit {(b, h)}: " \
+        f"{int((codes_gpu != rc).sum())} of {rc.size}"
+    assert np.array_equal(scales_gpu, rs), f"scale bytes differ at unit {(b, h)}"
+    return rc, rs
+
+
+def check_pack_token(w, b, h, kproj_gpu, tokens=None):
+    k = w.k[b, h] if tokens is None else w.k[b, h][tokens]
+    ref = O.project_keys(k, w.proj[h])
+    got = kproj_gpu if tokens is None else kproj_gpu[tokens]
+    assert np.array_equal(got.view(np.uint16), ref), \
+        f"kproj differs at unit {(b, h)}: {int((got.view(np.uint16) != ref).sum())} entries"
+    return ref
+
+
+def block_score_bound(w, b, h, rc, rs):
+    """Per-block magnitude A of the estimated logits (see the module docstring)."""
+    nb = w.spec.max_blocks
+    qg = np.abs(q_group(w, b, h).astype(np.float64))
+    deq = np.abs(O.dequant_blocks(rc, rs)).reshape(nb, 128, 128)
+    sigma = w.softmax_scale
+    a = sigma * (float(w.global_scale[h]) * (deq @ qg.T) +
+                 (qg @ np.abs(w.key_center[h].astype(np.float64)))[None, None, :])
+    return a.reshape(nb, -1).max(axis=1)
+
+
+def check_block_scores(w, b, h, scores_gpu, rc, rs):
+    s = w.spec
+    ref = O.scan_block_unit(q_group(w, b, h), rc, rs, w.global_scale[h], w.key_center[h],
+                            int(w.seq_lens[b]), s.n_tail, w.softmax_scale, s.max_blocks)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(scores_gpu)), f"-inf pattern differs at {(b, h)}"
+    assert np.all(scores_gpu[~fin] == -np.inf)
+    A = block_score_bound(w, b, h, rc, rs)
+    err = np.abs(scores_gpu[fin].astype(np.float64) - ref[fin])
+    lim = SCORE_REL * A[fin] + SCORE_ABS
+    assert np.all(err <= lim), f"block scores at {(b, h)}: max err {err.max():.3e}, " \
+        f"worst ratio {(err / lim).max():.2f}"
+    return ref
+
+
+def check_token_scores(w, b, h, scores_gpu, kproj_ref):
+    ref = O.scan_token_unit(q_group(w, b, h), kproj_ref, w.proj[h], int(w.seq_lens[b]),
+                            w.softmax_scale)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(scores_gpu))
+    qbar = np.abs(q_group(w, b, h).astype(np.float64)).mean(axis=0)
+    p = np.abs(w.proj[h].astype(np.float64)).T @ qbar
+    A = w.softmax_scale * (np.abs(O.bf16_bits_to_f64(kproj_ref)) @ p)
+    err = np.abs(scores_gpu[fin].astype(np.float64) - ref[fin])
+    lim = SCORE_REL * A[fin] + SCORE_ABS
+    assert np.all(err <= lim), f"token scores at {(b, h)}: max err {err.max():.3e}"
+    return ref
+
+
+def check_selection(w, b, h, idx_gpu, count_gpu, scores_gpu, scores_ref):
+    s = w.spec
+    L = int(w.seq_lens[b])
+    if s.granularity == "block":
+        exact_idx, exact_cnt = O.select_blocks_unit(scores_gpu.astype(np.float64), L, s.n_tail,
+                                                    s.budget)
+        ref_idx, ref_cnt = O.select_blocks_unit(scores_ref, L, s.n_tail, s.budget)
+        picks = s.budget - s.n_tail
+    else:
+        exact_idx, exact_cnt = O.select_tokens_unit(scores_gpu.astype(np.float64), L, s.budget)
+        ref_idx, ref_cnt = O.select_tokens_unit(scores_ref, L, s.budget)
+        picks = s.budget
+    assert int(count_gpu) == exact_cnt == ref_cnt, (b, h, int(count_gpu), exact_cnt, ref_cnt)
+    assert np.array_equal(idx_gpu, exact_idx), f"selection on the GPU's scores differs at {(b, h)}"
+    got = set(int(x) for x in idx_gpu[:exact_cnt])
+    exp = set(int(x) for x in ref_idx[:ref_cnt])
+    diff = got ^ exp
+    if diff:
+        cand = scores_ref[np.isfinite(scores_ref)]
+        tau = np.sort(cand)[::-1][min(picks, cand.size) - 1]
+        for x in diff:
+            assert abs(scores_ref[x] - tau) <= BOUNDARY_REL * abs(tau), \
+                f"selection differs beyond the boundary band at {(b, h)}: entry {x}"
+    return len(diff)
+
+
+def oracle_partials(w, b, h, idx, splits):
+    s = w.spec
+    L = int(w.seq_lens[b])
+    qg = q_group(w, b, h)
+    if s.granularity == "block":
+        tk = w.tail_k[b, h] if s.n_tail else None
+        tv = w.tail_v[b, h] if s.n_tail else None
+        rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
+    else:
+        rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h],
+                                               [t for t in sel if t < L])
+    return O.attend_splits(qg, np.asarray(idx), splits, rows, w.softmax_scale)
+
+
+def check_attention(w, b, h, idx_gpu, splits, part_o_gpu, part_lse_gpu, out_gpu, lse_gpu):
+    """part_o_gpu [G, S, D], part_lse_gpu [G, S], out_gpu [G, D], lse_gpu [G]."""
+    po, pl = oracle_partials(w, b, h, idx_gpu, splits)  # [S, G, D], [S, G]
+    o, lse = O.combine(po, pl)
+    fin = np.isfinite(pl)
+    assert np.array_equal(fin, np.isfinite(part_lse_gpu.T)), f"empty splits differ at {(b, h)}"
+    assert np.abs(part_lse_gpu.T[fin] - pl[fin]).max(initial=0) <= OUT_TOL
+    assert np.abs(np.transpose(part_o_gpu, (1, 0, 2)) - po).max() <= OUT_TOL
+    err = np.abs(out_gpu - o).max()
+    assert err <= OUT_TOL, f"output error {err:.3e} at {(b, h)}"
+    lf = np.isfinite(lse)
+    assert np.array_equal(lf, np.isfinite(lse_gpu))
+    assert np.abs(lse_gpu[lf] - lse[lf]).max(initial=0) <= OUT_TOL
+    return err

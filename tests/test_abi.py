@@ -1,0 +1,113 @@
+"""The C ABI library: builds, loads without a GPU, exports every declared
+entry point and rejects bad arguments before touching the device (CPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_pack_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from block_sparse_attention_pack_amd import build
+
+        build.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(bsa_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["bsa_pack_kv_cache", "bsa_score_scan", "bsa_select_topk",
+              "bsa_sparse_decode_attn", "bsa_combine", "bsa_workspace_size",
+              "bsa_last_error", "bsa_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert "gfx950" in B.version()
+
+
+def _layout(**kw):
+    base = dict(batch=1, num_kv_heads=1, num_q_heads=4, head_dim=128, block_size=128,
+                max_tokens=4096, kv_stride_b=4096 * 128, kv_stride_h=4096 * 128,
+                kv_stride_t=128, kv_dtype=B.DTYPE_F16)
+    base.update(kw)
+    return B.KvLayout(**base)
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails its argument checks
+
+
+def _scan(lib, layout, cfg, q=FAKE):
+    return lib.bsa_score_scan(ctypes.byref(layout), ctypes.byref(cfg), q, FAKE, FAKE, FAKE,
+                              None, None, None, FAKE, FAKE, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -2),
+    (dict(block_size=64), -2),
+    (dict(num_kv_heads=4, num_q_heads=6), -1),
+    (dict(num_q_heads=12), -2),
+    (dict(max_tokens=1000), -1),
+    (dict(kv_stride_t=100), -1),
+    (dict(kv_dtype=7), -2),
+])
+def test_bad_layouts_are_rejected(lib, kw, code):
+    cfg = B.select_cfg(B.BLOCK, 8)
+    assert _scan(lib, _layout(**kw), cfg) == code
+    assert lib.bsa_last_error().decode()
+
+
+@pytest.mark.parametrize("cfg,code", [
+    (B.SelectCfg(B.BLOCK, 0, 0, 0, 0.1), -1),
+    (B.SelectCfg(B.BLOCK, 40, 0, 0, 0.1), -1),  # more blocks than the cache holds
+    (B.SelectCfg(B.BLOCK, 1, 2, 0, 0.1), -1),   # budget below the forced pages
+    (B.SelectCfg(B.BLOCK, 8, 3, 0, 0.1), -1),
+    (B.SelectCfg(B.BLOCK, 8, 0, 0, 0.0), -1),
+    (B.SelectCfg(B.TOKEN, 64, 0, 24, 0.1), -2),  # rank 24 unsupported
+    (B.SelectCfg(B.TOKEN, 64, 1, 32, 0.1), -1),  # token mode has no tail pages
+    (B.SelectCfg(5, 8, 0, 0, 0.1), -1),
+])
+def test_bad_configs_are_rejected(lib, cfg, code):
+    assert _scan(lib, _layout(), cfg) == code
+
+
+def test_null_and_misaligned_pointers_are_rejected(lib):
+    L, cfg = _layout(), B.select_cfg(B.BLOCK, 8)
+    assert _scan(lib, L, cfg, q=None) == -1
+    assert _scan(lib, L, cfg, q=FAKE + 2) == -1
+    rc = lib.bsa_sparse_decode_attn(ctypes.byref(L), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, None, None, 9, FAKE, FAKE, None)
+    assert rc == -1 and "num_splits" in lib.bsa_last_error().decode()
+    tail = B.select_cfg(B.BLOCK, 8, n_tail_pages=2)
+    rc = lib.bsa_sparse_decode_attn(ctypes.byref(L), ctypes.byref(tail), FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, None, None, 2, FAKE, FAKE, None)
+    assert rc == -1 and "tail" in lib.bsa_last_error().decode()
+    rc = lib.bsa_pack_kv_cache(ctypes.byref(L), ctypes.byref(cfg), FAKE, None, FAKE, None,
+                               0, 33, FAKE, FAKE, None, None)
+    assert rc == -1
+    assert lib.bsa_combine(4, 2, 64, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.bsa_combine(4, 0, 128, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.bsa_combine(0, 1, 128, None, None, None, None, None) == 0  # nothing to do
+
+
+def test_workspace_size(lib):
+    L = _layout()
+    assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(B.select_cfg(B.BLOCK, 8))) == 0
+    bad = B.select_cfg(B.BLOCK, 8)
+    bad.budget = -1
+    assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(bad)) == 0

@@ -1,0 +1,215 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, stage by stage.
+
+Every workload runs at a reduced size where the oracle checks every unit
+(several tiles, ragged tails) and, in test_gpu_full_size.py, at its full size
+on sampled units. Edge cases: empty and sub-block sequences, one tail page,
+query-group sizes 1..16, a BF16 cache, exact score ties, all-equal scores,
+budgets at and above the candidate count, one split and one split per entry.
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_attention_pack_amd import workloads as W
+from block_sparse_attention_pack_amd.step import upload
+
+import parity_util as PU
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_sparse_attention_pack_amd import binding
+
+    binding.load()  # fails loudly when the library is missing
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_step(w, splits=None, kv_dtype="f16"):
+    d = upload(w, splits=splits, kv_dtype=kv_dtype)
+    d.pack()
+    d.run()
+    torch.cuda.synchronize()
+    return d
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def check_all(w, d, units=None):
+    """Compare every stage for the given units; w holds the K, V the GPU holds."""
+    s = w.spec
+    G = s.group
+    if units is None:
+        units = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
+    scores = host(d.scores)
+    idx, count = host(d.idx), host(d.count)
+    po, pl = host(d.part_o), host(d.part_lse)
+    out, lse = host(d.out), host(d.out_lse)
+    if s.granularity == "block":
+        codes, scales = host(d.codes), host(d.scales)
+    else:
+        kproj = host(d.kproj)
+    for b, h in units:
+        if s.granularity == "block":
+            rc, rs = PU.check_pack_block(w, b, h, codes[b, h], scales[b, h])
+            ref = PU.check_block_scores(w, b, h, scores[b, h], rc, rs)
+        else:
+            kref = PU.check_pack_token(w, b, h, kproj[b, h])
+            ref = PU.check_token_scores(w, b, h, scores[b, h], kref)
+        PU.check_selection(w, b, h, idx[b, h], count[b, h], scores[b, h], ref)
+        rows = slice(h * G, (h + 1) * G)
+        PU.check_attention(w, b, h, idx[b, h], d.splits, po[b, rows], pl[b, rows],
+                           out[b, rows], lse[b, rows])
+
+
+REDUCED = {
+    "tiny": W.SPECS["tiny"],
+    "llama8b": W.reduced("llama8b", 8192),
+    "jetqsparse": W.reduced("jetqsparse", 8192, batch=2),
+    "ragged": W.reduced("ragged", 16384, batch=3, budget=24),
+    "token": W.reduced("token", 16384, batch=2),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_workloads_match_oracle(name):
+    spec = REDUCED[name]
+    _say(f"[parity] {spec.name}")
+    w = W.generate(spec)
+    d = run_step(w)
+    check_all(w, d)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_split_count_does_not_matter(splits):
+    spec = W.reduced("jetqsparse", 4096, batch=1, budget=8)
+    w = W.generate(spec)
+    d = run_step(w, splits=splits)
+    check_all(w, d)
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_query_group_sizes(G):
+    spec = dataclasses.replace(W.SPECS["tiny"], name=f"group{G}", seed=20 + G, batch=2,
+                               kv_heads=2, q_heads=2 * G, max_tokens=2048, budget=5)
+    w = W.generate(spec)
+    check_all(w, run_step(w))
+    tspec = dataclasses.replace(W.SPECS["token"], name=f"tgroup{G}", seed=30 + G, batch=1,
+                                kv_heads=2, q_heads=2 * G, max_tokens=4096, budget=96)
+    w = W.generate(tspec)
+    check_all(w, run_step(w))
+
+
+def test_short_and_empty_sequences_with_tail_pages():
+    lengths = (0, 1, 127, 128, 129, 300, 2000, 4096)
+    for n_tail in (0, 1, 2):
+        spec = dataclasses.replace(W.SPECS["ragged"], name=f"short{n_tail}", seed=40 + n_tail,
+                                   batch=len(lengths), kv_heads=2, q_heads=8, max_tokens=4096,
+                                   budget=6, n_tail=n_tail, needle_count=2, lengths=lengths)
+        _say(f"[parity] {spec.name}")
+        w = W.generate(spec)
+        d = run_step(w)
+        check_all(w, d)
+        cnt = host(d.count)
+        assert np.all(cnt[0] == 0)  # empty sequence: nothing selected, output 0, lse -inf
+        assert np.all(host(d.out)[0] == 0) and np.all(host(d.out_lse)[0] == -np.inf)
+
+
+def test_token_mode_ragged_lengths():
+    lengths = (0, 5, 100, 4097, 8192)
+    spec = dataclasses.replace(W.SPECS["token"], name="tok_ragged", seed=50, batch=len(lengths),
+                               kv_heads=2, q_heads=8, max_tokens=8192, budget=256,
+                               lengths=lengths)
+    w = W.generate(spec)
+    check_all(w, run_step(w))
+
+
+def test_bf16_cache():
+    spec = W.reduced("jetqsparse", 4096, batch=2, budget=10)
+    w = W.generate(spec)
+    d = run_step(w, kv_dtype="bf16")
+    # the oracle sees the bf16-rounded keys and values the GPU holds
+    w16 = dataclasses.replace(w, k=host(d.k.float()), v=host(d.v.float()))
+    check_all(w16, d)
+
+
+def test_exact_ties_go_to_the_lower_index():
+    spec = dataclasses.replace(W.SPECS["tiny"], name="ties", seed=60, needle_count=0, budget=3)
+    w = W.generate(spec)
+    k = w.k.copy()
+    qm = w.q[0].astype(np.float64).mean(axis=0)
+    k[0, 0, 5 * 128:6 * 128] += (3.0 * qm / np.linalg.norm(qm)).astype(np.float16)
+    # blocks 3, 9, 20 and 30 become copies of block 5: five identical top scores
+    for dst in (3, 9, 20, 30):
+        k[0, 0, dst * 128:(dst + 1) * 128] = k[0, 0, 5 * 128:6 * 128]
+    w = dataclasses.replace(w, k=k)
+    d = run_step(w)
+    sc = host(d.scores)[0, 0]
+    assert len(set(sc[[3, 5, 9, 20, 30]])) == 1 and sc[5] == sc.max()
+    assert list(host(d.idx)[0, 0]) == [3, 5, 9]
+    check_all(w, d)
+
+
+@pytest.mark.parametrize("name", ["tiny", "token"])
+def test_all_equal_scores_take_lowest_indices(name):
+    base = W.SPECS["tiny"] if name == "tiny" else W.reduced("token", 4096, batch=1)
+    w = W.generate(base)
+    w = dataclasses.replace(w, q=np.zeros_like(w.q))
+    d = run_step(w)
+    s = w.spec
+    picks = s.budget - s.n_tail
+    assert list(host(d.idx)[0, 0][:picks]) == list(range(picks))
+    check_all(w, d)
+
+
+def test_budget_at_and_above_candidates():
+    lengths = (128 * 5, 128 * 3 + 7)
+    spec = dataclasses.replace(W.SPECS["ragged"], name="budget_all", seed=70, batch=2,
+                               kv_heads=1, q_heads=4, max_tokens=2048, budget=8, n_tail=2,
+                               needle_count=1, lengths=lengths)
+    w = W.generate(spec)
+    d = run_step(w, splits=8)
+    check_all(w, d)
+    assert list(host(d.count)[:, 0]) == [5, 4]
+    # budget == n_tail: only the tail pages
+    w2 = dataclasses.replace(w, spec=dataclasses.replace(spec, budget=2))
+    d2 = run_step(w2, splits=2)
+    check_all(w2, d2)
+    assert list(host(d2.idx)[0, 0]) == [3, 4]
+
+
+def test_budget_all_blocks_is_dense_attention():
+    spec = dataclasses.replace(W.SPECS["tiny"], name="dense", budget=32)
+    w = W.generate(spec)
+    d = run_step(w, splits=4)
+    check_all(w, d)
+    q = torch.from_numpy(w.q[0].astype(np.float64))
+    k = torch.from_numpy(w.k[0, 0].astype(np.float64))
+    v = torch.from_numpy(w.v[0, 0].astype(np.float64))
+    ref = torch.softmax(w.softmax_scale * q @ k.T, dim=-1) @ v
+    assert np.abs(host(d.out)[0] - ref.numpy()).max() <= PU.OUT_TOL
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = W.generate(W.reduced("ragged", 8192, batch=2, budget=12))
+    d = run_step(w)
+    first = [host(t).copy() for t in (d.scores, d.idx, d.count, d.part_o, d.out, d.out_lse)]
+    for _ in range(3):
+        d.run()
+        torch.cuda.synchronize()
+        again = [host(t) for t in (d.scores, d.idx, d.count, d.part_o, d.out, d.out_lse)]
+        for a, b in zip(first, again):
+            assert np.array_equal(a, b, equal_nan=True)
