@@ -5,25 +5,30 @@
 // JSSA Figure 1: the KV head's query heads share one index set and read the
 // original keys and values at those rows in place (no gather buffer).
 //
-// Work-group = (split s, unit); its 4 waves take the split's tiles round-robin
-// and keep their own online-softmax state, merged through LDS at the end. A
-// tile is one selected block (block mode) or 32 consecutive selected tokens
-// (token mode), processed as groups of 16 rows:
-//   QK^T: v_mfma_f32_16x16x32_f16, A = the group's query heads (rows >= G are
-//         zero), B = 16 key rows, lane l holding row l % 16, channels
-//         32 (l/16) .. +31 -- one 64-byte run of the row per lane. BF16 rows
-//         (tail pages or a BF16 cache) use two bf16 MFMAs with q split exactly
-//         into q_hi + q_lo (an fp16 value is the sum of two bf16 values).
-//   softmax: FP32 in the log2 domain, one max/rescale per tile.
-//   PV: VALU FMAs in FP32; lane owns DPL consecutive channels of one row subset,
-//       so a wave load covers whole 256-byte value rows; probabilities come
-//       from a per-wave LDS table.
+// Work-group = (split s, unit). The split's rows are cut into groups of 16
+// (an eighth of a selected block, or 16 consecutive selected tokens), dealt
+// round-robin to the 4 waves. A wave takes its groups in chunks of up to
+// 1024 / G rows, each in three phases that keep a ring of kDepth groups of
+// loads in flight:
+//   1. keys stream in; QK^T on v_mfma_f32_16x16x32_f16 (A = the group's query
+//      heads, rows >= G zero; B = 16 key rows, lane l holding row l % 16 and,
+//      for MFMA step c, channels 8 (l/16 + 4 c) .. +7, so each wave load reads
+//      64 contiguous bytes of every row); log2-scaled logits to an LDS table. BF16
+//      rows (tail pages or a BF16 cache) take two bf16 MFMAs with q split
+//      exactly into q_hi + q_lo (an fp16 value is the sum of two bf16 values).
+//   2. an exact softmax update over the chunk per head (wave reductions), the
+//      FP32 accumulators rescaled once per chunk.
+//   3. values stream in; PV as FP32 VALU FMAs, a lane owning DPL consecutive
+//      channels of a subset of the rows so one wave load covers whole
+//      256-byte value rows.
+// The waves' states are merged through LDS into one (O, lse) partial per head.
 #include "common.hpp"
 
 namespace bsa {
 namespace {
 
 constexpr int kAttnWaves = 4;
+constexpr int kDepth = 2;  // 16-row groups in flight per wave in each streaming phase
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -32,6 +37,9 @@ struct PvShape {
   static constexpr int DPL = G <= 4 ? 8 : (G == 8 ? 4 : 2);  // channels per lane
   static constexpr int LPR = kHeadDim / DPL;                  // lanes per row
   static constexpr int NQ = kWave / LPR;                      // rows per wave load
+  static constexpr int RPL = 16 / NQ;                         // value rows per lane per group
+  static constexpr int VDW = DPL / 2;                         // dwords of a row per lane
+  static constexpr int CHUNK = 1024 / G;                      // rows per wave per chunk
 };
 
 __device__ __forceinline__ void split_bf16(const half8& q, bf16x8& hi, bf16x8& lo) {
@@ -41,35 +49,6 @@ __device__ __forceinline__ void split_bf16(const half8& q, bf16x8& hi, bf16x8& l
     const __bf16 h = __bf16(f);
     hi[e] = h;
     lo[e] = __bf16(f - float(h));  // exact: f has 11 significant bits, h the top 8
-  }
-}
-
-template <int DPL, bool BF16>
-__device__ __forceinline__ void load_v(const uint16_t* p, float* v) {
-  if constexpr (DPL == 8) {
-    const uint4v w = *reinterpret_cast<const uint4v*>(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (BF16) {
-        v[2 * e] = bf16_bits_to_float(w[e] & 0xFFFFu);
-        v[2 * e + 1] = bf16_bits_to_float(w[e] >> 16);
-      } else {
-        v[2 * e] = half_bits_to_float(uint16_t(w[e] & 0xFFFFu));
-        v[2 * e + 1] = half_bits_to_float(uint16_t(w[e] >> 16));
-      }
-    }
-  } else if constexpr (DPL == 4) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    const uint32_t ww[2] = {w.x, w.y};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      v[2 * e] = BF16 ? bf16_bits_to_float(ww[e] & 0xFFFFu) : half_bits_to_float(uint16_t(ww[e]));
-      v[2 * e + 1] = BF16 ? bf16_bits_to_float(ww[e] >> 16) : half_bits_to_float(uint16_t(ww[e] >> 16));
-    }
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    v[0] = BF16 ? bf16_bits_to_float(w & 0xFFFFu) : half_bits_to_float(uint16_t(w));
-    v[1] = BF16 ? bf16_bits_to_float(w >> 16) : half_bits_to_float(uint16_t(w >> 16));
   }
 }
 
@@ -95,194 +74,359 @@ struct AttnArgs {
   float scale_log2;  // sigma * log2(e)
 };
 
-template <int G, bool MAIN_BF16, int NG>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode) {
+// Per-unit context shared by every row group of the work-group.
+struct UnitCtx {
+  const uint16_t* kunit;  // K and V of this (sequence, KV head)
+  const uint16_t* vunit;
+  const int32_t* uidx;
+  int e0, e1, L, npg, tail0, unit;
+};
+
+// One group of 16 rows: an eighth of a selected block, or 16
+// consecutive selected tokens. Row rho of the group is at kb/vb + off(rho).
+struct GroupRef {
+  const uint16_t* kb;
+  const uint16_t* vb;
+  int64_t rs;       // elements between rows (block mode)
+  int nvalid;       // block mode: rows 0 .. nvalid-1 are valid
+  const int* toks;  // token mode: the group's 16 staged token indices (-1 = masked)
+  bool bf16;
+};
+
+// The selected block ids (block mode) or token indices (token mode) a wave
+// needs for one chunk are staged in LDS before the chunk's streaming loops, so
+// nothing inside them waits on a vector-memory index load (such a wait would
+// also wait for every key and value load in flight).
+//   block mode: stage[t] = block id of the wave's group t (relative to the chunk)
+//   token mode: stage[16 t + rho] = token of row rho of group t, or -1
+// live == false gives a null group: every row masked, addresses inside the unit.
+template <bool MAIN_BF16>
+__device__ __forceinline__ GroupRef describe(const AttnArgs& a, const UnitCtx& u, int q,
+                                             const int* stage, int tl, bool block_mode,
+                                             bool live) {
+  GroupRef r;
+  r.toks = stage;
+  if (!live) {
+    r.kb = u.kunit;
+    r.vb = u.vunit;
+    r.rs = a.st;
+    r.nvalid = 0;
+    r.bf16 = MAIN_BF16;
+    return r;
+  }
+  if (block_mode) {
+    const int blk = stage[tl];
+    const int part = q & 7;
+    const bool ok = blk >= 0 && blk < u.npg;
+    const int b0 = ok ? blk : 0;
+    r.nvalid = ok ? min(16, u.L - b0 * kBlock - 16 * part) : 0;
+    if (a.n_tail > 0 && ok && blk >= u.tail0) {
+      const int64_t off =
+          ((int64_t(u.unit) * a.n_tail + (blk - u.tail0)) * kBlock + 16 * part) * kHeadDim;
+      r.kb = a.tail_k + off;
+      r.vb = a.tail_v + off;
+      r.rs = kHeadDim;
+      r.bf16 = true;
+    } else {
+      const int64_t off = (int64_t(b0) * kBlock + 16 * part) * a.st;
+      r.kb = u.kunit + off;
+      r.vb = u.vunit + off;
+      r.rs = a.st;
+      r.bf16 = MAIN_BF16;
+    }
+  } else {
+    r.kb = u.kunit;
+    r.vb = u.vunit;
+    r.rs = a.st;
+    r.nvalid = 16;
+    r.toks = stage + 16 * tl;
+    r.bf16 = MAIN_BF16;
+  }
+  return r;
+}
+
+// Element offset of group row rho from kb / vb, or -1 when masked.
+__device__ __forceinline__ int64_t row_offset(const GroupRef& r, int rho, bool block_mode) {
+  if (block_mode) return rho < r.nvalid ? int64_t(rho) * r.rs : -1;
+  if (r.nvalid == 0) return -1;  // null group
+  const int tok = r.toks[rho];
+  return tok >= 0 ? int64_t(tok) * r.rs : -1;
+}
+
+// Key registers of one group: lane l holds row l % 16, channels 8 (l/16 + 4 c) .. +7
+// for MFMA step c, so load c of the wave reads 64 contiguous bytes of each row.
+struct KeySlot {
+  uint4v w[4];
+  bool ok, bf16;
+};
+
+template <bool MAIN_BF16>
+__device__ __forceinline__ void issue_keys(KeySlot& ks, const AttnArgs& a, const UnitCtx& u,
+                                           int q, const int* stage, int tl, int lane,
+                                           bool block_mode, bool live) {
+  const GroupRef r = describe<MAIN_BF16>(a, u, q, stage, tl, block_mode, live);
+  const int64_t off = row_offset(r, lane & 15, block_mode);
+  ks.ok = off >= 0;
+  ks.bf16 = r.bf16;
+  // plain loads: each 128-byte line is read by two of the wave's loads, and a
+  // streaming (non-temporal) hint can evict it in between
+  const uint4v* kp = reinterpret_cast<const uint4v*>(r.kb + (off >= 0 ? off : 0) + 8 * (lane >> 4));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ks.w[c] = kp[4 * c];
+}
+
+// Value registers of one group: lane l holds channels (l % LPR) * DPL .. of rows
+// l / LPR + NQ k.
+template <int G>
+struct ValSlot {
+  uint32_t w[PvShape<G>::RPL][PvShape<G>::VDW];
+  bool bf16;
+};
+
+template <int G, bool MAIN_BF16>
+__device__ __forceinline__ void issue_values(ValSlot<G>& vs, const AttnArgs& a, const UnitCtx& u,
+                                             int q, const int* stage, int tl, int lane,
+                                             bool block_mode, bool live) {
   using PV = PvShape<G>;
-  constexpr int DPL = PV::DPL, LPR = PV::LPR, NQ = PV::NQ;
-  constexpr int TROWS = 16 * NG;
-  // the per-wave probability tables and, after the tile loop, the waves'
-  // accumulators share one LDS buffer
-  constexpr int kPFloats = TROWS * G, kAccFloats = G * kHeadDim;
-  constexpr int kShare = kPFloats > kAccFloats ? kPFloats : kAccFloats;
-  __shared__ float pa_lds[kAttnWaves * kShare];
-  __shared__ float alpha_lds[kAttnWaves][16];
-  __shared__ int row_lds[kAttnWaves][TROWS];
+  const GroupRef r = describe<MAIN_BF16>(a, u, q, stage, tl, block_mode, live);
+  vs.bf16 = r.bf16;
+  const int dc = lane % PV::LPR, qsub = lane / PV::LPR;
+#pragma unroll
+  for (int k = 0; k < PV::RPL; ++k) {
+    const int64_t off = row_offset(r, qsub + PV::NQ * k, block_mode);
+    const uint32_t* vp =
+        reinterpret_cast<const uint32_t*>(r.vb + (off >= 0 ? off : 0) + dc * PV::DPL);
+    if constexpr (PV::VDW == 4) {
+      const uint4v x = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(vp));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vs.w[k][e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = __builtin_nontemporal_load(vp + e);
+    }
+  }
+}
+
+// QK^T of one landed key group; the log2-scaled logits of rows 16 g .. +15 go
+// to sc[head * CHUNK + 16 g + row] (masked rows -inf).
+template <int G>
+__device__ __forceinline__ void group_scores(const KeySlot& ks, const half8* qa,
+                                             const bf16x8* qsplit, float scale_log2, float* sc,
+                                             int g, int lane) {
+  constexpr int CHUNK = PvShape<G>::CHUNK;
+  float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!ks.bf16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      half8 kv;
+      __builtin_memcpy(&kv, &ks.w[c], 16);
+      // re-read from LDS every group: keeps the operands out of the registers
+      // the value phase needs
+      const half8 qc = *static_cast<const volatile half8*>(qa + c * kWave + lane);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qc, kv, d, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 kv;
+      __builtin_memcpy(&kv, &ks.w[c], 16);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qsplit[(2 * c) * kWave + lane], kv, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qsplit[(2 * c + 1) * kWave + lane], kv, d, 0, 0, 0);
+    }
+  }
+  const int n16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * j4 + r;
+    if (hh < G) sc[hh * CHUNK + 16 * g + n16] = ks.ok ? d[r] * scale_log2 : -__builtin_inff();
+  }
+}
+
+// acc += p * v over one landed value group (p from sc, masked rows have p = 0).
+template <int G>
+__device__ __forceinline__ void group_pv(float (&acc)[G][PvShape<G>::DPL], const ValSlot<G>& vs,
+                                         const float* sc, int g, int lane) {
+  using PV = PvShape<G>;
+  constexpr int DPL = PV::DPL, CHUNK = PV::CHUNK;
+  const int qsub = lane / PV::LPR;
+#pragma unroll
+  for (int k = 0; k < PV::RPL; ++k) {
+    const int rl = 16 * g + qsub + PV::NQ * k;
+    float vv[DPL];
+#pragma unroll
+    for (int e = 0; e < PV::VDW; ++e) {
+      const uint32_t x = vs.w[k][e];
+      if (vs.bf16) {
+        vv[2 * e] = bf16_bits_to_float(x & 0xFFFFu);
+        vv[2 * e + 1] = bf16_bits_to_float(x >> 16);
+      } else {
+        vv[2 * e] = half_bits_to_float(uint16_t(x & 0xFFFFu));
+        vv[2 * e + 1] = half_bits_to_float(uint16_t(x >> 16));
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float p = sc[hh * CHUNK + rl];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[hh][e] = __builtin_fmaf(p, vv[e], acc[hh][e]);
+    }
+  }
+}
+
+template <int G, bool MAIN_BF16>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i) {
+  using PV = PvShape<G>;
+  constexpr int DPL = PV::DPL, LPR = PV::LPR, CHUNK = PV::CHUNK;
+  const bool block_mode = block_mode_i != 0;
+  // per-wave score / probability tables [head][row]; after the row loop the
+  // same LDS holds the waves' accumulators for the merge
+  constexpr int kScFloats = G * CHUNK, kAccFloats = G * kHeadDim;
+  constexpr int kShare = kScFloats > kAccFloats ? kScFloats : kAccFloats;
+  __shared__ float sc_lds[kAttnWaves * kShare];
   __shared__ float m_lds[kAttnWaves][16], l_lds[kAttnWaves][16];
+  __shared__ half8 qa_lds[4 * kWave];       // q in the MFMA operand order
+  __shared__ bf16x8 qsplit_lds[8 * kWave];  // q = q_hi + q_lo in the MFMA operand order
+  __shared__ int stage_lds[kAttnWaves][CHUNK];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, unit = blockIdx.y;
   const int b = unit / a.Hkv, h = unit % a.Hkv;
-  const int L = clamp_len(a.seq_lens[b], a.Tmax);
-  const int npg = ceil_div(L, kBlock);
-  const int tail0 = npg - a.n_tail;  // first page held in the tail store
+  UnitCtx u;
+  u.unit = unit;
+  u.L = clamp_len(a.seq_lens[b], a.Tmax);
+  u.npg = ceil_div(u.L, kBlock);
+  u.tail0 = u.npg - a.n_tail;  // first page held in the tail store
   const int per = ceil_div(a.budget, a.splits);
   const int cnt = min(max(a.count[unit], 0), a.budget);
-  const int e0 = split * per;
-  const int e1 = min(min(e0 + per, a.budget), cnt);
-  const int32_t* uidx = a.idx + int64_t(unit) * a.budget;
+  u.e0 = split * per;
+  u.e1 = min(min(u.e0 + per, a.budget), cnt);
+  u.uidx = a.idx + int64_t(unit) * a.budget;
+  u.kunit = a.k + b * a.sb + h * a.sh;
+  u.vunit = a.v + b * a.sb + h * a.sh;
 
-  // query operands: lane l holds head row l % 16, channels 32 (l/16) + 8 c .. + 8
+  // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
+  // for MFMA step c (the key layout above), staged once in LDS by wave 0
   const int n16 = lane & 15, j4 = lane >> 4;
-  half8 qa[4];
-  {
+  if (wave == 0) {
     const bool ok = n16 < G;
-    const _Float16* qrow =
-        a.q + (int64_t(b) * a.Hq + h * G + (ok ? n16 : 0)) * kHeadDim + 32 * j4;
+    const _Float16* qrow = a.q + (int64_t(b) * a.Hq + h * G + (ok ? n16 : 0)) * kHeadDim + 8 * j4;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      half8 v = *reinterpret_cast<const half8*>(qrow + 8 * c);
-      qa[c] = ok ? v : half8{};
+      half8 v = *reinterpret_cast<const half8*>(qrow + 32 * c);
+      if (!ok) v = half8{};
+      qa_lds[c * kWave + lane] = v;
+      split_bf16(v, qsplit_lds[(2 * c) * kWave + lane], qsplit_lds[(2 * c + 1) * kWave + lane]);
     }
   }
+  __syncthreads();
 
-  float m[4], lsum[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -__builtin_inff();
-    lsum[r] = 0.0f;
-  }
+  float m[G], lsum[G];  // wave-uniform running max (log2 domain) and sum per head
   float acc[G][DPL];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -__builtin_inff();
+    lsum[hh] = 0.0f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
+  }
+  float* sc = sc_lds + wave * kShare;
 
-  const int dc = lane % LPR, qsub = lane / LPR;
-  float* pw = pa_lds + wave * kShare;
-  int* rw = row_lds[wave];
-
-  // tiles of this split: block mode one entry per tile, token mode TROWS entries
-  const int ent_per_tile = block_mode ? 1 : TROWS;
-  const int ntiles = e1 > e0 ? ceil_div(e1 - e0, ent_per_tile) : 0;
-  for (int tile = wave; tile < ntiles; tile += kAttnWaves) {
-    // ---- row addressing ---------------------------------------------------
-    bool tile_bf16 = MAIN_BF16;
-    const uint16_t* kb = a.k + b * a.sb + h * a.sh;
-    const uint16_t* vb = a.v + b * a.sb + h * a.sh;
-    int64_t rstride = a.st;
-    int nvalid_rows;
+  // 16-row groups of this split, dealt round-robin to the waves: wave w takes
+  // groups w, w + 4, ...; t counts the wave's own groups
+  const int nent = u.e1 > u.e0 ? u.e1 - u.e0 : 0;
+  const int ngroups = block_mode ? 8 * nent : ceil_div(nent, 16);
+  const int nmine = ngroups > wave ? ceil_div(ngroups - wave, kAttnWaves) : 0;
+  constexpr int kChunkGroups = CHUNK / 16;
+#pragma unroll 1
+  for (int t0 = 0; t0 < nmine; t0 += kChunkGroups) {
+    const int tend = min(t0 + kChunkGroups, nmine);
+    int* stage = stage_lds[wave];
     if (block_mode) {
-      const int blk = uidx[e0 + tile];
-      if (blk < 0 || blk >= npg) continue;
-      nvalid_rows = min(kBlock, L - blk * kBlock);
-      if (a.n_tail > 0 && blk >= tail0) {
-        const int64_t off = ((int64_t(unit) * a.n_tail + (blk - tail0)) * kBlock) * kHeadDim;
-        kb = a.tail_k + off;
-        vb = a.tail_v + off;
-        rstride = kHeadDim;
-        tile_bf16 = true;
-      } else {
-        kb += int64_t(blk) * kBlock * a.st;
-        vb += int64_t(blk) * kBlock * a.st;
-      }
-      // rows are tau * rstride for tau < nvalid_rows
-#pragma unroll
-      for (int t = lane; t < TROWS; t += kWave) rw[t] = t < nvalid_rows ? t : -1;
+      for (int t = t0 + lane; t < tend; t += kWave)
+        stage[t - t0] = u.uidx[u.e0 + ((wave + kAttnWaves * t) >> 3)];
     } else {
-      const int t0 = e0 + tile * TROWS;
-      for (int t = lane; t < TROWS; t += kWave) {
-        const int e = t0 + t;
-        const int tok = e < e1 ? uidx[e] : -1;
-        rw[t] = (tok >= 0 && tok < L) ? tok : -1;
-      }
-      nvalid_rows = TROWS;
-    }
-    wave_lds_fence();
-
-    // ---- scores: s[g][r] = log2-scaled logit of head 4 j4 + r, row 16 g + n16
-    float s[NG][4];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const int row = rw[16 * g + n16];
-      const bool ok = row >= 0;
-      const uint16_t* kp = kb + int64_t(ok ? row : 0) * rstride + 32 * j4;
-      uint4v w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[c] = reinterpret_cast<const uint4v*>(kp)[c];
-      float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (!tile_bf16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          half8 kv;
-          __builtin_memcpy(&kv, &w[c], 16);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kv, d, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bf16x8 kv, qh, ql;
-          __builtin_memcpy(&kv, &w[c], 16);
-          split_bf16(qa[c], qh, ql);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kv, d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kv, d, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[g][r] = ok ? d[r] * a.scale_log2 : -__builtin_inff();
-    }
-
-    // ---- online softmax update (per head row r of this lane) ----------------
-    float alpha[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float tm = s[0][r];
-#pragma unroll
-      for (int g = 1; g < NG; ++g) tm = fmaxf(tm, s[g][r]);
-      tm = row16_max(tm);
-      const float mn = fmaxf(m[r], tm);
-      const bool live = mn > -__builtin_inff();
-      alpha[r] = live ? __builtin_amdgcn_exp2f(m[r] - mn) : 1.0f;
-      float ps = 0.0f;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const float p = live ? __builtin_amdgcn_exp2f(s[g][r] - mn) : 0.0f;
-        s[g][r] = p;
-        ps += p;
-      }
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, kWave);
-      lsum[r] = lsum[r] * alpha[r] + ps;
-      m[r] = mn;
-    }
-    // probabilities and rescale factors to LDS (heads < G only)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 4 * j4 + r;
-      if (hh < G) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) pw[(16 * g + n16) * G + hh] = s[g][r];
-        if (n16 == 0) alpha_lds[wave][hh] = alpha[r];
+      for (int i = lane; i < 16 * (tend - t0); i += kWave) {
+        const int t = t0 + (i >> 4);
+        const int e = u.e0 + 16 * (wave + kAttnWaves * t) + (i & 15);
+        const int tok = e < u.e1 ? u.uidx[e] : -1;
+        stage[i] = (tok >= 0 && tok < u.L) ? tok : -1;
       }
     }
     wave_lds_fence();
-
-    // ---- PV: acc[hh][e] = acc * alpha + sum_rows p * v ----------------------
+    // ---- phase 1: keys stream through a ring of kDepth slots; QK^T -> sc ----
+    // Every slot is always issued (groups past the chunk are null groups), so
+    // the ring registers are defined on every path.
+    {
+      KeySlot ring[kDepth];
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k)
+        issue_keys<MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t0 + k), stage, k, lane,
+                              block_mode, t0 + k < tend);
+#pragma unroll 1
+      for (int t = t0; t < tend; t += kDepth) {
+#pragma unroll
+        for (int k = 0; k < kDepth; ++k) {
+          if (t + k < tend) group_scores<G>(ring[k], qa_lds, qsplit_lds, a.scale_log2, sc, t + k - t0, lane);
+          issue_keys<MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t + k + kDepth), stage,
+                                t + k + kDepth - t0, lane, block_mode, t + k + kDepth < tend);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    wave_lds_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase 2: exact softmax update over the chunk, per head -------------
+    const int rows = 16 * (tend - t0);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float al = alpha_lds[wave][hh];
+      float* sh = sc + hh * CHUNK;
+      float mx = -__builtin_inff();
+      for (int r = lane; r < rows; r += kWave) mx = fmaxf(mx, sh[r]);
+      mx = wave_max(mx);
+      const float mn = fmaxf(m[hh], mx);
+      const bool live = mn > -__builtin_inff();
+      const float alpha = live ? __builtin_amdgcn_exp2f(m[hh] - mn) : 1.0f;
+      float ps = 0.0f;
+      for (int r = lane; r < rows; r += kWave) {
+        const float p = live ? __builtin_amdgcn_exp2f(sh[r] - mn) : 0.0f;
+        sh[r] = p;
+        ps += p;
+      }
+      // wave-uniform: keep the running state in scalar registers
+      lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                               __builtin_bit_cast(int, lsum[hh] * alpha + wave_sum(ps))));
+      m[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[hh][e] *= al;
+      for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha;
     }
-#pragma unroll 2
-    for (int rr = qsub; rr < TROWS; rr += NQ) {
-      const int row = rw[rr];
-      if (row < 0) continue;
-      float vv[DPL];
-      const uint16_t* vp = vb + int64_t(row) * rstride + dc * DPL;
-      if (tile_bf16) load_v<DPL, true>(vp, vv);
-      else load_v<DPL, false>(vp, vv);
+    wave_lds_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase 3: values stream through a ring of kDepth slots; PV ----------
+    {
+      ValSlot<G> ring[kDepth];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float p = pw[rr * G + hh];
+      for (int k = 0; k < kDepth; ++k)
+        issue_values<G, MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t0 + k), stage, k, lane,
+                                   block_mode, t0 + k < tend);
+#pragma unroll 1
+      for (int t = t0; t < tend; t += kDepth) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[hh][e] = __builtin_fmaf(p, vv[e], acc[hh][e]);
+        for (int k = 0; k < kDepth; ++k) {
+          if (t + k < tend) group_pv<G>(acc, ring[k], sc, t + k - t0, lane);
+          issue_values<G, MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t + k + kDepth), stage,
+                                     t + k + kDepth - t0, lane, block_mode,
+                                     t + k + kDepth < tend);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     wave_lds_fence();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- merge the waves' states -------------------------------------------
-  __syncthreads();  // every wave is done with its probability table
+  __syncthreads();  // every wave is done with its score table
+  const int dc = lane % LPR, qsub = lane / LPR;
   // rows of one channel chunk are spread over NQ lanes: sum them
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -297,16 +441,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) pa_lds[wave * kShare + hh * kHeadDim + dc * DPL + e] = acc[hh][e];
+      for (int e = 0; e < DPL; ++e)
+        sc_lds[wave * kShare + hh * kHeadDim + dc * DPL + e] = acc[hh][e];
   }
-  if (n16 == 0) {
+  if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 4 * j4 + r;
-      if (hh < G) {
-        m_lds[wave][hh] = m[r];
-        l_lds[wave][hh] = lsum[r];
-      }
+    for (int hh = 0; hh < G; ++hh) {
+      m_lds[wave][hh] = m[hh];
+      l_lds[wave][hh] = lsum[hh];
     }
   }
   __syncthreads();
@@ -320,7 +462,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode) {
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
         const float f = __builtin_amdgcn_exp2f(m_lds[w][hh] - M);
-        num += f * pa_lds[w * kShare + o];
+        num += f * sc_lds[w * kShare + o];
         den += f * l_lds[w][hh];
       }
     }
@@ -333,20 +475,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode) {
   }
 }
 
-template <int G, bool BF16, int NG>
-void launch_one(dim3 grid, hipStream_t s, const AttnArgs& a, int block_mode) {
-  hipLaunchKernelGGL((attn_kernel<G, BF16, NG>), grid, dim3(256), 0, s, a, block_mode);
-}
-
 template <int G>
 void launch_g(dim3 grid, hipStream_t s, const AttnArgs& a, int block_mode, bool bf16) {
-  if (block_mode) {
-    if (bf16) launch_one<G, true, 8>(grid, s, a, 1);
-    else launch_one<G, false, 8>(grid, s, a, 1);
-  } else {
-    if (bf16) launch_one<G, true, 2>(grid, s, a, 0);
-    else launch_one<G, false, 2>(grid, s, a, 0);
-  }
+  if (bf16) hipLaunchKernelGGL((attn_kernel<G, true>), grid, dim3(256), 0, s, a, block_mode);
+  else hipLaunchKernelGGL((attn_kernel<G, false>), grid, dim3(256), 0, s, a, block_mode);
 }
 
 }  // namespace

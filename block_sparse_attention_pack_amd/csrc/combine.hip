@@ -39,8 +39,14 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   float acc = 0.0f;
   if (!empty) {
     const float* po = part_o + int64_t(row) * splits * kHeadDim + d;
-    for (int s = 0; s < splits; ++s) acc += w[s] * po[int64_t(s) * kHeadDim];
-    acc /= sum;
+    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial sums keep loads in flight
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a4[k] += w[s + k] * po[int64_t(s + k) * kHeadDim];
+    }
+    for (; s < splits; ++s) a4[0] += w[s] * po[int64_t(s) * kHeadDim];
+    acc = ((a4[0] + a4[1]) + (a4[2] + a4[3])) / sum;
   }
   out[int64_t(row) * kHeadDim + d] = acc;
   if (out_lse && d == 0) out_lse[row] = empty ? -__builtin_inff() : mx + __logf(sum);

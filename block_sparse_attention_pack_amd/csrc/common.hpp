@@ -65,11 +65,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Maximum over the 16 lanes of a row (lanes 16r .. 16r+15).
+// DPP row rotation (within each 16-lane row) of a float.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Maximum over the 16 lanes of a row (lanes 16r .. 16r+15), in every lane of it.
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+
+// Sum over the 16 lanes of a row; every lane gets a sum (the summation order
+// differs between lanes, so only one lane's value should be kept).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

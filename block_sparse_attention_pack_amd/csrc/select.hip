@@ -17,6 +17,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxDigitBits = 12;
+constexpr int kLdsKeys = 8192;  // candidates staged in LDS (32 KiB) when they fit
 
 struct ScanScratch {
   int wave_tot[kSelWaves];
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     int row_len, int block_mode, int budget, int n_tail, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
   __shared__ uint32_t hist[1 << kMaxDigitBits];
+  __shared__ uint32_t keys_lds[kLdsKeys];
   __shared__ ScanScratch scr;
   __shared__ int sh_beta, sh_above;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -86,6 +88,13 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   }
   picks = max(0, min(picks, C));
   const float* row = scores + int64_t(unit) * row_len;
+  // block-mode rows (and short token rows) are read from global memory once
+  const bool in_lds = C <= kLdsKeys;
+  if (in_lds) {
+    for (int i = tid; i < C; i += kSelThreads) keys_lds[i] = score_key(row[i]);
+    __syncthreads();
+  }
+  auto key_at = [&](int i) -> uint32_t { return in_lds ? keys_lds[i] : score_key(row[i]); };
 
   // --- radix select of the picks-th largest key ---------------------------
   // After the loop every candidate with key > kgt is taken, and of those with
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
       for (int d = tid; d < nb; d += kSelThreads) hist[d] = 0;
       __syncthreads();
       for (int i = tid; i < C; i += kSelThreads) {
-        const uint32_t key = score_key(row[i]);
+        const uint32_t key = key_at(i);
         if (bits == 0 || (key >> (32 - bits)) == prefix)
           atomicAdd(&hist[(key >> shift) & uint32_t(nb - 1)], 1u);
       }
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
       const int i = c0 + 4 * lane + k;
       if (i < s1) {
         bool gt, eq;
-        classify(i, score_key(row[i]), gt, eq);
+        classify(i, key_at(i), gt, eq);
         cg += gt;
         ce += eq;
       }
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     for (int k = 0; k < 4; ++k) {
       const int i = c0 + 4 * lane + k;
       gt[k] = eq[k] = false;
-      if (i < s1) classify(i, score_key(row[i]), gt[k], eq[k]);
+      if (i < s1) classify(i, key_at(i), gt[k], eq[k]);
       ce += eq[k];
     }
     int ce_tot;

@@ -17,10 +17,14 @@ from .workloads import BLOCK, HEAD_DIM, Workload
 
 
 def default_splits(units: int, budget: int, granularity: str) -> int:
-    """Split count that gives the attention launch about 1024 work-groups."""
-    s = max(1, math.ceil(1024 / max(units, 1)))
+    """Split count that gives the attention launch about 512 work-groups.
+
+    The attention kernel runs three waves per SIMD, so 512 four-wave groups are
+    resident on 256 CUs at once; more, smaller splits only add merge work.
+    """
+    s = max(1, math.ceil(512 / max(units, 1)))
     if granularity == "token":
-        s = min(s, max(1, budget // 32))  # at least one 32-row tile per split
+        s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
     return max(1, min(s, budget))
 
 
