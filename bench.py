@@ -48,6 +48,9 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time only the whole step, without per-kernel events")
+    ap.add_argument("--mode", default="fused", choices=["fused", "split"],
+                    help="fused: score_select + attend_combine (2 launches); "
+                         "split: score_scan, select_topk, sparse_decode_attn, combine")
     return ap.parse_args()
 
 
@@ -134,29 +137,32 @@ def main() -> int:
     nbytes = W.algorithmic_bytes(w)
     stream = torch.cuda.current_stream()
 
+    if a.mode == "fused":
+        stages = ["score_select", "attend_combine"]
+        calls = lambda d: [d.score_select, d.attend_combine]
+    else:
+        stages = ["scan", "select", "attend", "combine"]
+        calls = lambda d: [d.scan, d.select, d.attend, d.combine]
     for i in range(a.warmup):
-        layers[i % len(layers)].run()
+        for c in calls(layers[i % len(layers)]):
+            c()
     torch.cuda.synchronize()
 
-    stages = ["scan", "select", "attend", "combine"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    ns = len(stages)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(a.steps):
-        d = layers[i % len(layers)]
+        cs = calls(layers[i % len(layers)])
         if a.no_stage_events:
-            d.run()
+            for c in cs:
+                c()
             continue
         e = ev[i]
         e[0].record(stream)
-        d.scan()
-        e[1].record(stream)
-        d.select()
-        e[2].record(stream)
-        d.attend()
-        e[3].record(stream)
-        d.combine()
-        e[4].record(stream)
+        for j, c in enumerate(cs):
+            c()
+            e[j + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / a.steps
@@ -167,16 +173,19 @@ def main() -> int:
         for j, name in enumerate(stages):
             ts = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(a.steps)]
             stage_us[name] = float(np.mean(ts))
-        step_us = [ev[i][0].elapsed_time(ev[i][4]) * 1e3 for i in range(a.steps)]
+        step_us = [ev[i][0].elapsed_time(ev[i][ns]) * 1e3 for i in range(a.steps)]
         stage_us["step_events_p50"] = float(np.median(step_us))
     log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms; stages (us): {stage_us}")
 
-    scan_us = stage_us.get("scan")
+    scan_us = stage_us.get("scan" if a.mode == "split" or not d0.block_mode else "score_select")
+    if a.mode == "fused" and not d0.block_mode:
+        scan_us = None  # token mode's score_select is two launches; time the split form
     roofline = None
     if scan_us:
         achieved = nbytes["scan"] / (scan_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "kernel": "scan_block_kernel" if d0.block_mode
-                    else "scan_token_kernel<32>", "achieved": round(achieved, 1),
+        kname = ("scan_select_kernel" if a.mode == "fused" else "scan_block_kernel") \
+            if d0.block_mode else "scan_token_kernel<32>"
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": None, "bytes_per_launch": nbytes["scan"]}
     step_gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
@@ -197,6 +206,7 @@ def main() -> int:
                    "q_heads": spec.q_heads, "context": spec.max_tokens,
                    "granularity": spec.granularity, "budget": spec.budget,
                    "tail_pages": spec.n_tail, "splits": d0.splits, "layers_rotated": a.layers,
+                   "calls": a.mode,
                    "scan": "e2m1*e4m3 -> f16 MFMA, f32 acc" if d0.block_mode
                    else "bf16 rank-%d keys, f32" % spec.rank},
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),

@@ -75,6 +75,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "bsa_select_topk": [LP, CP, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
         "bsa_sparse_decode_attn": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
         "bsa_combine": [_I32, _I32, _I32, _P, _P, _P, _P, _P],
+        "bsa_score_select": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                             _P, _P, _P, _P],
+        "bsa_attend_combine": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                               _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -82,6 +86,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.bsa_workspace_size.argtypes = [LP, CP]
     lib.bsa_workspace_size.restype = ctypes.c_size_t
+    lib.bsa_counters_size.argtypes = [LP]
+    lib.bsa_counters_size.restype = ctypes.c_size_t
     lib.bsa_last_error.argtypes = []
     lib.bsa_last_error.restype = ctypes.c_char_p
     lib.bsa_version.argtypes = []
@@ -178,3 +184,26 @@ def combine(rows, num_splits, head_dim, part_o, part_lse, out, out_lse, stream=N
     lib = load()
     _check(lib.bsa_combine(rows, num_splits, head_dim, _ptr(part_o), _ptr(part_lse), _ptr(out),
                            _ptr(out_lse), _stream(stream)))
+
+
+def counters_size(layout) -> int:
+    return int(load().bsa_counters_size(ctypes.byref(layout)))
+
+
+def score_select(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
+                 scores, workspace, workspace_bytes, counters, idx, count, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_score_select(ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(codes),
+                                _ptr(scales), _ptr(global_scale), _ptr(key_center), _ptr(kproj),
+                                _ptr(proj), _ptr(seq_lens), _ptr(scores), _ptr(workspace),
+                                workspace_bytes, _ptr(counters), _ptr(idx), _ptr(count),
+                                _stream(stream)))
+
+
+def attend_combine(layout, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                   part_o, part_lse, counters, out, out_lse, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_attend_combine(ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(seq_lens), _ptr(idx), _ptr(count), _ptr(tail_k),
+                                  _ptr(tail_v), num_splits, _ptr(part_o), _ptr(part_lse),
+                                  _ptr(counters), _ptr(out), _ptr(out_lse), _stream(stream)))

@@ -219,7 +219,8 @@ int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cf
     return hip_status(bsa::launch_attention(g, cfg->granularity, cfg->budget, cfg->n_tail_pages,
                                             cfg->softmax_scale, static_cast<const _Float16*>(q),
                                             k, v, seq_lens, idx, count, tail_k, tail_v,
-                                            num_splits, part_o, part_lse, s),
+                                            num_splits, part_o, part_lse, nullptr, nullptr,
+                                            nullptr, s),
                       "sparse_decode_attn");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -238,6 +239,80 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
     return hip_status(bsa::launch_combine(rows, num_splits, part_o, part_lse, out, out_lse,
                                           static_cast<hipStream_t>(stream)),
                       "combine");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+size_t bsa_counters_size(const bsa_kv_layout* layout) {
+  if (!layout || layout->batch < 1 || layout->num_kv_heads < 1) return 0;
+  return sizeof(uint32_t) * size_t(layout->batch) * size_t(layout->num_kv_heads);
+}
+
+int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                     const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                     const float* key_center, const uint16_t* kproj, const float* proj,
+                     const int32_t* seq_lens, float* scores, void* workspace,
+                     size_t workspace_bytes, uint32_t* counters, int32_t* idx, int32_t* count,
+                     void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    if (cfg->granularity == BSA_GRANULARITY_TOKEN) {
+      rc = bsa_score_scan(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                          seq_lens, scores, stream);
+      if (rc) return rc;
+      return bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx,
+                             count, stream);
+    }
+    BSA_REQUIRE(q && aligned16(q) && seq_lens && scores && idx && count, BSA_ERR_INVALID_ARG,
+                "q (16-byte aligned), seq_lens, scores, idx and count are required");
+    BSA_REQUIRE(codes && scales && global_scale && aligned16(codes) && aligned16(scales),
+                BSA_ERR_INVALID_ARG,
+                "block mode needs codes, scales (16-byte aligned) and global_scale");
+    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "block mode needs the arrival counters");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_scan_select_block(
+                          g, cfg->n_tail_pages, cfg->budget, cfg->softmax_scale,
+                          static_cast<const _Float16*>(q), codes, scales, global_scale,
+                          key_center, seq_lens, scores, counters, idx, count, s),
+                      "scan_select");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                       const void* k, const void* v, const int32_t* seq_lens,
+                       const int32_t* idx, const int32_t* count, const uint16_t* tail_k,
+                       const uint16_t* tail_v, int32_t num_splits, float* part_o,
+                       float* part_lse, uint32_t* counters, float* out, float* out_lse,
+                       void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
+                "q, k, v must be 16-byte aligned device pointers");
+    BSA_REQUIRE(seq_lens && idx && count && part_o && part_lse && out, BSA_ERR_INVALID_ARG,
+                "seq_lens, idx, count, part_o, part_lse and out are required");
+    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
+                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
+                num_splits);
+    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "the arrival counters are required");
+    if (cfg->n_tail_pages > 0)
+      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
+                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_attention(g, cfg->granularity, cfg->budget, cfg->n_tail_pages,
+                                            cfg->softmax_scale, static_cast<const _Float16*>(q),
+                                            k, v, seq_lens, idx, count, tail_k, tail_v,
+                                            num_splits, part_o, part_lse, counters, out, out_lse,
+                                            s),
+                      "attend_combine");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

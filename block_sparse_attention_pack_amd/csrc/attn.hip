@@ -22,6 +22,7 @@
 //      channels of a subset of the rows so one wave load covers whole
 //      256-byte value rows.
 // The waves' states are merged through LDS into one (O, lse) partial per head.
+#include "combine_core.hpp"
 #include "common.hpp"
 
 namespace bsa {
@@ -69,6 +70,9 @@ struct AttnArgs {
   const uint16_t* tail_v;
   float* part_o;
   float* part_lse;
+  uint32_t* counters;  // non-null: the unit's last group also merges the partials
+  float* out;
+  float* out_lse;
   int64_t sb, sh, st;
   int Hkv, Hq, Tmax, budget, n_tail, splits;
   float scale_log2;  // sigma * log2(e)
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   __shared__ half8 qa_lds[4 * kWave];       // q in the MFMA operand order
   __shared__ bf16x8 qsplit_lds[8 * kWave];  // q = q_hi + q_lo in the MFMA operand order
   __shared__ int stage_lds[kAttnWaves][CHUNK];
+  __shared__ int is_last;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, unit = blockIdx.y;
@@ -468,10 +473,30 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
     }
     const int64_t rowq = int64_t(b) * a.Hq + h * G + hh;
     const bool empty = !(den > 0.0f);
-    a.part_o[(rowq * a.splits + split) * kHeadDim + d] = empty ? 0.0f : num / den;
-    if (d == 0)
-      a.part_lse[rowq * a.splits + split] =
-          empty ? -__builtin_inff() : (M + __builtin_amdgcn_logf(den)) * kLn2;
+    const float po = empty ? 0.0f : num / den;
+    const float pl = empty ? -__builtin_inff() : (M + __builtin_amdgcn_logf(den)) * kLn2;
+    float* po_p = a.part_o + (rowq * a.splits + split) * kHeadDim + d;
+    float* pl_p = a.part_lse + rowq * a.splits + split;
+    if (a.counters) {  // read back by the unit's last group
+      store_coherent(po_p, po);
+      if (d == 0) store_coherent(pl_p, pl);
+    } else {
+      *po_p = po;
+      if (d == 0) *pl_p = pl;
+    }
+  }
+  if (!a.counters) return;
+
+  // ---- fused merge: the unit's last group to finish combines the partials --
+  if (!last_group_of_unit(a.counters, unit, a.splits, &is_last)) return;
+  for (int o = threadIdx.x; o < G * kHeadDim; o += 256) {
+    const int hh = o / kHeadDim, d = o % kHeadDim;
+    const int64_t rowq = int64_t(b) * a.Hq + h * G + hh;
+    float val, lse;
+    combine_channel<true>(a.part_lse + rowq * a.splits, a.part_o + rowq * a.splits * kHeadDim,
+                          a.splits, d, val, lse);
+    a.out[rowq * kHeadDim + d] = val;
+    if (d == 0 && a.out_lse) a.out_lse[rowq] = lse;
   }
 }
 
@@ -487,7 +512,8 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
                             float sigma, const _Float16* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
                             const uint16_t* tail_k, const uint16_t* tail_v, int splits,
-                            float* part_o, float* part_lse, hipStream_t s) {
+                            float* part_o, float* part_lse, uint32_t* counters, float* out,
+                            float* out_lse, hipStream_t s) {
   AttnArgs a;
   a.q = q;
   a.k = static_cast<const uint16_t*>(k);
@@ -499,6 +525,9 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
   a.tail_v = tail_v;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  a.counters = counters;
+  a.out = out;
+  a.out_lse = out_lse;
   a.sb = g.sb;
   a.sh = g.sh;
   a.st = g.st;

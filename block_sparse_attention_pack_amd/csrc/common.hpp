@@ -89,6 +89,40 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + row_ror<1>(v);
 }
 
+// --- device-wide hand-off between work-groups of one launch -----------------
+// The fused kernels pass a few values (block scores, split partials) from every
+// work-group of a unit to the unit's last one. Those values are stored and
+// loaded as device-scope atomics, which reach the memory-side coherence point
+// past each XCD's L2, so no L2 write-back fence is needed: a writer waits for
+// its stores to complete before it counts itself in the unit's counter.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Counts the calling work-group in counters[unit]; true in exactly one group,
+// the last of `groups` to arrive, which also returns the counter to zero.
+// Call from every thread after the group's hand-off stores (all threads must
+// reach it: it synchronises the group).
+__device__ __forceinline__ bool last_group_of_unit(uint32_t* counters, int unit, uint32_t groups,
+                                                  int* lds_flag) {
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(&counters[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before == groups - 1;
+    if (last) __hip_atomic_store(&counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = last;
+  }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 __device__ __forceinline__ int clamp_len(int L, int tmax) { return L < 0 ? 0 : (L > tmax ? tmax : L); }
@@ -114,6 +148,12 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,
                              hipStream_t s);
+hipError_t launch_scan_select_block(const UnitGeom& g, int n_tail, int budget, float sigma,
+                                    const _Float16* q, const uint8_t* codes,
+                                    const uint8_t* scales, const float* gscale,
+                                    const float* center, const int32_t* seq_lens, float* scores,
+                                    uint32_t* counters, int32_t* idx, int32_t* count,
+                                    hipStream_t s);
 hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, const _Float16* q,
                              const uint16_t* kproj, const float* proj, const int32_t* seq_lens,
                              float* scores, hipStream_t s);
@@ -128,7 +168,8 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
                             float sigma, const _Float16* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
                             const uint16_t* tail_k, const uint16_t* tail_v, int splits,
-                            float* part_o, float* part_lse, hipStream_t s);
+                            float* part_o, float* part_lse, uint32_t* counters, float* out,
+                            float* out_lse, hipStream_t s);
 hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
                           float* out, float* out_lse, hipStream_t s);
 

@@ -23,6 +23,7 @@
 // p = P^T qbar in FP32 once per work-group, then each token's score is
 // sigma * p . kproj_t, streamed 64 B per token with 16-byte loads.
 #include "common.hpp"
+#include "select_core.hpp"
 
 namespace bsa {
 namespace {
@@ -48,39 +49,47 @@ __device__ __forceinline__ half2v scale_pair(uint32_t byte) {
   return r;
 }
 
-// grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads.
-__global__ __launch_bounds__(256) void scan_block_kernel(
-    const _Float16* __restrict__ q, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
-    const float* __restrict__ center, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int Hkv, int Hq, int G, int NBmax, int Tmax, int n_tail,
-    float sigma, int bpw) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+struct ScanBlockArgs {
+  const _Float16* q;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+  const float* center;
+  const int32_t* seq_lens;
+  float* scores;
+  int Hkv, Hq, G, NBmax, Tmax, n_tail, bpw;
+  float sigma;
+  bool coherent;  // scores are read by another work-group of the same launch
+};
+
+// The scan of one wave: blocks [blk_begin, blk_begin + bpw) of unit blockIdx.y.
+__device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lane, int wave) {
   const int unit = blockIdx.y;
-  const int b = unit / Hkv, h = unit % Hkv;
-  const int L = clamp_len(seq_lens[b], Tmax);
+  const int b = unit / a.Hkv, h = unit % a.Hkv;
+  const int L = clamp_len(a.seq_lens[b], a.Tmax);
   const int npages = ceil_div(L, kBlock);
-  const int packed = npages - n_tail > 0 ? npages - n_tail : 0;
-  const int blk_begin = (blockIdx.x * kScanWaves + wave) * bpw;
-  if (blk_begin >= NBmax) return;
-  const int blk_end = min(blk_begin + bpw, NBmax);
-  float* out = scores + int64_t(unit) * NBmax;
+  const int packed = npages - a.n_tail > 0 ? npages - a.n_tail : 0;
+  const int blk_begin = (blockIdx.x * kScanWaves + wave) * a.bpw;
+  if (blk_begin >= a.NBmax) return;
+  const int blk_end = min(blk_begin + a.bpw, a.NBmax);
+  const int G = a.G;
+  float* out = a.scores + int64_t(unit) * a.NBmax;
 
   const int n = lane & 15, j = lane >> 4;
   // A operand: query head row n (zero beyond the group), channels 32 j + 8 c .. + 8
   half8 qa[4];
   float qc_part = 0.0f;
   const bool row_ok = n < G;
-  const _Float16* qrow = q + (int64_t(b) * Hq + h * G + (row_ok ? n : 0)) * kHeadDim + 32 * j;
+  const _Float16* qrow = a.q + (int64_t(b) * a.Hq + h * G + (row_ok ? n : 0)) * kHeadDim + 32 * j;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     half8 v = *reinterpret_cast<const half8*>(qrow + 8 * c);
     if (!row_ok) v = half8{};
     qa[c] = v;
-    if (center) {
+    if (a.center) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        qc_part += float(v[e]) * center[h * kHeadDim + 32 * j + 8 * c + e];
+        qc_part += float(v[e]) * a.center[h * kHeadDim + 32 * j + 8 * c + e];
     }
   }
   // q . c of head row n: sum over the 4 channel quarters (lanes n, n+16, n+32, n+48)
@@ -94,15 +103,18 @@ __global__ __launch_bounds__(256) void scan_block_kernel(
     qc[r] = __shfl(qc_part, 4 * j + r, kWave);
     head_ok[r] = 4 * j + r < G;
   }
-  const float s_t = gscale[h];
+  const float s_t = a.gscale[h];
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     if (blk >= packed) {
-      if (lane == 0) out[blk] = -__builtin_inff();
+      if (lane == 0) {
+        if (a.coherent) store_coherent(out + blk, -__builtin_inff());
+        else out[blk] = -__builtin_inff();
+      }
       continue;
     }
-    const uint8_t* crec = codes + (int64_t(unit) * NBmax + blk) * kCodeRecord;
-    const uint8_t* srec = scales + (int64_t(unit) * NBmax + blk) * kScaleRecord;
+    const uint8_t* crec = a.codes + (int64_t(unit) * a.NBmax + blk) * kCodeRecord;
+    const uint8_t* srec = a.scales + (int64_t(unit) * a.NBmax + blk) * kScaleRecord;
     uint4v cw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -131,8 +143,36 @@ __global__ __launch_bounds__(256) void scan_block_kernel(
     for (int r = 0; r < 4; ++r)
       if (head_ok[r]) best = fmaxf(best, s_t * m[r] + qc[r]);
     best = wave_max(best);
-    if (lane == 0) out[blk] = sigma * best;
+    if (lane == 0) {
+      if (a.coherent) store_coherent(out + blk, a.sigma * best);
+      else out[blk] = a.sigma * best;
+    }
   }
+}
+
+// grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads.
+__global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
+  scan_wave_blocks(a, threadIdx.x & 63, threadIdx.x >> 6);
+}
+
+// Scan, then selection by the unit's last work-group to finish: every group
+// counts itself in counters[unit] after its scores are stored; the one that
+// sees all the others done reads the unit's scores and writes idx / count, and
+// returns the counter to zero. No group ever waits for another.
+__global__ __launch_bounds__(256) void scan_select_kernel(ScanBlockArgs a, int budget,
+                                                          uint32_t* __restrict__ counters,
+                                                          int32_t* __restrict__ idx,
+                                                          int32_t* __restrict__ count) {
+  __shared__ SelectLds lds;
+  __shared__ int is_last;
+  scan_wave_blocks(a, threadIdx.x & 63, threadIdx.x >> 6);
+  const int unit = blockIdx.y;
+  if (!last_group_of_unit(counters, unit, gridDim.x, &is_last)) return;
+  const int L = clamp_len(a.seq_lens[unit / a.Hkv], a.Tmax);
+  int C, picks, f0, f1;
+  block_candidates(L, a.n_tail, a.NBmax, budget, C, picks, f0, f1);
+  select_unit_rows<true>(a.scores + int64_t(unit) * a.NBmax, C, picks, f0, f1, budget,
+                         idx + int64_t(unit) * budget, count + unit, lds);
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
@@ -214,17 +254,59 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
 
 }  // namespace
 
-hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
+namespace {
+ScanBlockArgs make_scan_args(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,
-                             hipStream_t s) {
+                             dim3& grid) {
   const int units = g.B * g.Hkv;
   // enough work-groups to fill 256 CUs several times over
   int bpw = 4;
   while (bpw > 1 && int64_t(units) * ceil_div(g.NBmax, kScanWaves * bpw) < 2048) bpw >>= 1;
-  dim3 grid(ceil_div(g.NBmax, kScanWaves * bpw), units);
-  hipLaunchKernelGGL(scan_block_kernel, grid, dim3(256), 0, s, q, codes, scales, gscale, center,
-                     seq_lens, scores, g.Hkv, g.Hq, g.G, g.NBmax, g.Tmax, n_tail, sigma, bpw);
+  grid = dim3(ceil_div(g.NBmax, kScanWaves * bpw), units);
+  ScanBlockArgs a;
+  a.q = q;
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.center = center;
+  a.seq_lens = seq_lens;
+  a.scores = scores;
+  a.Hkv = g.Hkv;
+  a.Hq = g.Hq;
+  a.G = g.G;
+  a.NBmax = g.NBmax;
+  a.Tmax = g.Tmax;
+  a.n_tail = n_tail;
+  a.bpw = bpw;
+  a.sigma = sigma;
+  a.coherent = false;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
+                             const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                             const float* center, const int32_t* seq_lens, float* scores,
+                             hipStream_t s) {
+  dim3 grid;
+  const ScanBlockArgs a =
+      make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores, grid);
+  hipLaunchKernelGGL(scan_block_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_select_block(const UnitGeom& g, int n_tail, int budget, float sigma,
+                                    const _Float16* q, const uint8_t* codes,
+                                    const uint8_t* scales, const float* gscale,
+                                    const float* center, const int32_t* seq_lens, float* scores,
+                                    uint32_t* counters, int32_t* idx, int32_t* count,
+                                    hipStream_t s) {
+  dim3 grid;
+  ScanBlockArgs a =
+      make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores, grid);
+  a.coherent = true;
+  hipLaunchKernelGGL(scan_select_kernel, grid, dim3(256), 0, s, a, budget, counters, idx, count);
   return hipGetLastError();
 }
 

@@ -1,15 +1,18 @@
 // Top-k selection per unit (Jet-QSparse abstract: top blocks per KV head;
 // JSSA Figure 1 and Table 15: top-B tokens per KV head, shared by the group).
 //
-// One 1024-thread work-group per unit. Scores become order-preserving 32-bit
-// keys. A radix select finds the exact key kappa of the picks-th largest
-// candidate in at most three histogram passes (12 + 12 + 8 bits, LDS
-// histograms), stopping early once the bucket holding the boundary is taken
-// whole. An index-ordered compaction then writes, in ascending order, every
-// candidate with key > kappa plus the lowest-index candidates with key ==
-// kappa up to the budget -- the ties rule of the oracle -- and appends the
-// forced BF16 tail pages, which always follow the scanned blocks.
+// Block mode: one 256-thread work-group per unit runs select_unit_rows
+// (select_core.hpp).
+//
+// Token mode: one 1024-thread work-group per unit. Scores become
+// order-preserving 32-bit keys. A radix select finds the exact key kappa of the
+// picks-th largest candidate in at most three histogram passes (12 + 12 + 8
+// bits, LDS histograms), stopping early once the bucket holding the boundary is
+// taken whole. An index-ordered compaction then writes, in ascending order,
+// every candidate with key > kappa plus the lowest-index candidates with key ==
+// kappa up to the budget.
 #include "common.hpp"
+#include "select_core.hpp"
 
 namespace bsa {
 namespace {
@@ -251,17 +254,30 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   if (tid == 0) count[unit] = nsel + min(nf, budget - nsel);
 }
 
-}  // namespace
+// Block mode: one 256-thread work-group per unit.
+__global__ __launch_bounds__(kSelectThreads) void select_block_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
+    int NBmax, int budget, int n_tail, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+  __shared__ SelectLds lds;
+  const int unit = blockIdx.x;
+  const int L = clamp_len(seq_lens[unit / Hkv], Tmax);
+  int C, picks, f0, f1;
+  block_candidates(L, n_tail, NBmax, budget, C, picks, f0, f1);
+  select_unit_rows(scores + int64_t(unit) * NBmax, C, picks, f0, f1, budget,
+                   idx + int64_t(unit) * budget, count + unit, lds);
+}
 
-size_t token_select_workspace(const UnitGeom&) { return 0; }
+}  // namespace
 
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
                                const int32_t* seq_lens, int32_t* idx, int32_t* count,
                                hipStream_t s) {
-  hipLaunchKernelGGL(select_topk_kernel, dim3(g.B * g.Hkv), dim3(kSelThreads), 0, s, scores,
-                     seq_lens, g.Hkv, g.Tmax, g.NBmax, 1, budget, n_tail, idx, count);
+  hipLaunchKernelGGL(select_block_kernel, dim3(g.B * g.Hkv), dim3(kSelectThreads), 0, s, scores,
+                     seq_lens, g.Hkv, g.Tmax, g.NBmax, budget, n_tail, idx, count);
   return hipGetLastError();
 }
+
+size_t token_select_workspace(const UnitGeom&) { return 0; }
 
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void*, int32_t* idx, int32_t* count,

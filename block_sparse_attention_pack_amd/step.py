@@ -57,6 +57,7 @@ class DeviceStep:
     part_lse: "torch.Tensor"
     out: "torch.Tensor"
     out_lse: "torch.Tensor"
+    counters: "torch.Tensor"  # arrival counters of the fused calls (zero between calls)
 
     @property
     def block_mode(self) -> bool:
@@ -89,10 +90,29 @@ class DeviceStep:
                     self.out_lse, stream)
 
     def run(self, stream=None) -> None:
+        """The step as four calls: scan, select, attention, combine."""
         self.scan(stream)
         self.select(stream)
         self.attend(stream)
         self.combine(stream)
+
+    # -- the same step as two fused calls -------------------------------------
+    def score_select(self, stream=None) -> None:
+        bsa.score_select(self.layout, self.cfg, self.q, self.codes, self.scales,
+                         self.global_scale, self.key_center, self.kproj, self.proj,
+                         self.seq_lens, self.scores, self.workspace, self.ws_bytes,
+                         self.counters, self.idx, self.count, stream)
+
+    def attend_combine(self, stream=None) -> None:
+        bsa.attend_combine(self.layout, self.cfg, self.q, self.k, self.v, self.seq_lens,
+                           self.idx, self.count, self.tail_k, self.tail_v, self.splits,
+                           self.part_o, self.part_lse, self.counters, self.out, self.out_lse,
+                           stream)
+
+    def run_fused(self, stream=None) -> None:
+        """The step as two calls: score_select, attend_combine."""
+        self.score_select(stream)
+        self.attend_combine(stream)
 
 
 def upload(w: Workload, device="cuda", splits: Optional[int] = None,
@@ -147,4 +167,5 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         part_lse=torch.empty((B, Hq, splits), dtype=torch.float32, device=dev),
         out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev),
         out_lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
+        counters=torch.zeros((bsa.counters_size(layout) // 4,), dtype=torch.int32, device=dev),
     )
