@@ -14,6 +14,7 @@
 namespace bsa {
 
 constexpr int kSelectThreads = 256;
+constexpr int kSelectRegKeys = 8;  // rows up to 2048 candidates stay in registers
 
 struct SelectLds {
   uint32_t hist[256];
@@ -58,6 +59,23 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
   picks = max(0, min(picks, C));
   const int per = ceil_div(C, kSelectThreads);
   const int i0 = min(C, tid * per), i1 = min(C, i0 + per);
+  // Up to kSelectRegKeys candidates per thread are read once and kept in
+  // registers; longer rows are re-read from memory on every pass.
+  const bool in_regs = per <= kSelectRegKeys;
+  uint32_t rk[kSelectRegKeys];
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kSelectRegKeys; ++j) rk[j] = i0 + j < i1 ? score_key(score_at(i0 + j)) : 0u;
+  }
+  auto for_each_key = [&](auto&& f) {
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kSelectRegKeys; ++j)
+        if (i0 + j < i1) f(i0 + j, rk[j]);
+    } else {
+      for (int i = i0; i < i1; ++i) f(i, score_key(score_at(i)));
+    }
+  };
 
   // keys taken: key > kgt, plus the first r_eq (by index) with key == keq;
   // or every key >= kge when a whole bucket is taken
@@ -72,15 +90,18 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
       const int shift = 24 - bits;
       s.hist[tid] = 0;
       __syncthreads();
-      for (int i = i0; i < i1; ++i) {
-        const uint32_t key = score_key(score_at(i));
+      for_each_key([&](int, uint32_t key) {
         if (bits == 0 || (key >> (shift + 8)) == prefix)
           atomicAdd(&s.hist[(key >> shift) & 0xFFu], 1u);
-      }
+      });
       __syncthreads();
       // thread t looks at bin d = 255 - t; the inclusive scan counts bins >= d
       const int d = 255 - tid;
       const int hd = int(s.hist[d]);
+      if (tid == 0) {  // defined results even if no bin qualifies (ordered by the scan's barriers)
+        s.beta = 0;
+        s.above = 0;
+      }
       int total;
       const int ge = select_block_scan(hd, s, total);
       const int above = ge - hd;  // keys in bins above d
@@ -114,29 +135,27 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
 
   // counts of this thread's range: taken by key, and tied at kappa
   int ngt = 0, neq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(score_at(i));
+  for_each_key([&](int, uint32_t key) {
     ngt += taken_by_key(key);
     neq += tied(key);
-  }
+  });
   int tot_gt, tot_eq;
   const int gt_before = select_block_scan(ngt, s, tot_gt) - ngt;
   const int eq_before = select_block_scan(neq, s, tot_eq) - neq;
-  const int nsel = min(tot_gt + min(tot_eq, r_eq), budget);
+  const int nsel = max(0, min(tot_gt + min(tot_eq, r_eq), budget));
   int pos = gt_before + min(eq_before, r_eq);
   int eq_seen = eq_before;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(score_at(i));
+  for_each_key([&](int i, uint32_t key) {
     bool take = taken_by_key(key);
     if (tied(key)) {
       take = eq_seen < r_eq;
       ++eq_seen;
     }
     if (take) {
-      if (pos < budget) out[pos] = i;  // always true; guards the write
+      if (pos >= 0 && pos < budget) out[pos] = i;  // always true; guards the write
       ++pos;
     }
-  }
+  });
   const int nf = max(0, f1 - f0);
   for (int k = tid; k < budget - nsel; k += kSelectThreads) out[nsel + k] = k < nf ? f0 + k : -1;
   if (tid == 0) *count = nsel + min(nf, budget - nsel);

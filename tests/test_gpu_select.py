@@ -1,0 +1,139 @@
+"""select_topk on crafted score rows, through the C ABI, against the oracle.
+
+The scores are written straight into the score buffer, so the selection is
+tested on rows no scan would give: exact ties spread over many 8192-key chunks,
+keys that differ only in their lowest bits (every radix digit is needed), NaN,
+signed zeros, infinities and subnormals, all-equal rows, and budgets from 1 to
+above the candidate count. The result must be bit-exact: the same indices, in
+ascending order, and the same count.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_attention_pack_amd import binding as bsa
+
+from oracle import decode as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bsa.load()
+
+
+def _layout(B, Hkv, T):
+    # select_topk reads no K: a contiguous [B, Hkv, T, 128] layout with no buffer
+    return bsa.KvLayout(B, Hkv, Hkv, 128, 128, T, Hkv * T * 128, T * 128, 128, bsa.DTYPE_F16)
+
+
+def _rows(pattern, n, rng):
+    if pattern == "random":
+        return rng.standard_normal(n).astype(np.float32)
+    if pattern == "low_bits":  # one exponent, 700 neighbouring mantissas, each ~n/700 times
+        return (np.float32(1.5) + (rng.integers(0, 700, n) * np.float32(2.0 ** -23))).astype(np.float32)
+    if pattern == "few_values":  # four values: every boundary is a tie spread over all chunks
+        return rng.integers(0, 4, n).astype(np.float32)
+    if pattern == "specials":
+        pool = np.array([np.nan, -0.0, 0.0, -np.inf, np.inf, 1e-45, -1e-45, 3.0, -3.0, 1e30,
+                         -1e30, 2.0 ** -126], dtype=np.float32)
+        return pool[rng.integers(0, len(pool), n)]
+    if pattern == "all_equal":
+        return np.full(n, 0.25, dtype=np.float32)
+    raise ValueError(pattern)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
+@pytest.mark.parametrize("budget", [1, 300, 2048, 40000])
+def test_token_select_matches_oracle(pattern, budget):
+    T = 40960  # five 8192-key chunks
+    lengths = [T, 40001, 8193, 8192, 8191, 2049, 1, 0]
+    B, Hkv = len(lengths), 2
+    rng = np.random.default_rng([7, budget, len(pattern)])
+    scores = np.stack([_rows(pattern, T, rng) for _ in range(B * Hkv)]).reshape(B, Hkv, T)
+    _say(f"[select] token pattern={pattern} budget={budget} T={T}")
+    layout = _layout(B, Hkv, T)
+    cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1)
+    ws_bytes = bsa.workspace_size(layout, cfg)
+    dev = torch.device("cuda")
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=dev)  # contents must not matter
+    sc = torch.from_numpy(scores).to(dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
+    count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
+    for rep in range(2):  # a second call on the same workspace
+        bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
+        torch.cuda.synchronize()
+        gi, gc = idx.cpu().numpy(), count.cpu().numpy()
+        for b in range(B):
+            for h in range(Hkv):
+                ri, rc = O.select_tokens_unit(scores[b, h].astype(np.float64), lengths[b], budget)
+                assert int(gc[b, h]) == rc, (pattern, budget, b, h, rep)
+                assert np.array_equal(gi[b, h], ri), (pattern, budget, b, h, rep)
+
+
+@pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
+@pytest.mark.parametrize("nb,budget,n_tail", [(1024, 64, 0), (2048, 130, 2), (4096, 1000, 1),
+                                              (4096, 4096, 0)])
+def test_block_select_matches_oracle(pattern, nb, budget, n_tail):
+    T = nb * 128  # 2048 blocks fill the per-thread registers; 4096 re-read memory
+    lengths = [T, T - 1, T // 2 + 5, 129, 128, 1, 0]
+    B, Hkv = len(lengths), 2
+    rng = np.random.default_rng([8, nb, budget, len(pattern)])
+    scores = np.stack([_rows(pattern, nb, rng) for _ in range(B * Hkv)]).reshape(B, Hkv, nb)
+    _say(f"[select] block pattern={pattern} blocks={nb} budget={budget} tail={n_tail}")
+    layout = _layout(B, Hkv, T)
+    cfg = bsa.select_cfg(bsa.BLOCK, budget, n_tail, 0, 0.1)
+    dev = torch.device("cuda")
+    sc = torch.from_numpy(scores).to(dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
+    count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
+    bsa.select_topk(layout, cfg, sc, lens, None, 0, idx, count)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), count.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            ri, rc = O.select_blocks_unit(scores[b, h].astype(np.float64), lengths[b], n_tail,
+                                          budget)
+            assert int(gc[b, h]) == rc, (pattern, b, h)
+            assert np.array_equal(gi[b, h], ri), (pattern, b, h)
+
+
+@pytest.mark.parametrize("pattern", ["random", "few_values"])
+def test_token_select_over_several_bitmap_windows(pattern):
+    """Rows longer than 131072 tokens: the bitmaps are compacted in several windows."""
+    T = 262144
+    lengths = [T, 140000, 131073]
+    B, Hkv, budget = len(lengths), 2, 3000
+    rng = np.random.default_rng([9, len(pattern)])
+    scores = np.stack([_rows(pattern, T, rng) for _ in range(B * Hkv)]).reshape(B, Hkv, T)
+    _say(f"[select] token windows pattern={pattern} T={T}")
+    layout = _layout(B, Hkv, T)
+    cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1)
+    ws_bytes = bsa.workspace_size(layout, cfg)
+    dev = torch.device("cuda")
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=dev)
+    sc = torch.from_numpy(scores).to(dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
+    count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
+    bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), count.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            ri, rc = O.select_tokens_unit(scores[b, h].astype(np.float64), lengths[b], budget)
+            assert int(gc[b, h]) == rc, (pattern, b, h)
+            assert np.array_equal(gi[b, h], ri), (pattern, b, h)
