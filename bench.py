@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time only the whole step, without per-kernel events")
     ap.add_argument("--mode", default="fused", choices=["fused", "split"],
-                    help="fused: score_select + attend_combine (2 launches); "
+                    help="fused: score_scan, select_topk, attend_combine; "
                          "split: score_scan, select_topk, sparse_decode_attn, combine")
     return ap.parse_args()
 
@@ -138,8 +138,8 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     if a.mode == "fused":
-        stages = ["score_select", "attend_combine"]
-        calls = lambda d: [d.score_select, d.attend_combine]
+        stages = ["scan", "select", "attend_combine"]
+        calls = lambda d: [d.scan, d.select, d.attend_combine]
     else:
         stages = ["scan", "select", "attend", "combine"]
         calls = lambda d: [d.scan, d.select, d.attend, d.combine]
@@ -177,14 +177,11 @@ def main() -> int:
         stage_us["step_events_p50"] = float(np.median(step_us))
     log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms; stages (us): {stage_us}")
 
-    scan_us = stage_us.get("scan" if a.mode == "split" or not d0.block_mode else "score_select")
-    if a.mode == "fused" and not d0.block_mode:
-        scan_us = None  # token mode's score_select is two launches; time the split form
+    scan_us = stage_us.get("scan")
     roofline = None
     if scan_us:
         achieved = nbytes["scan"] / (scan_us * 1e-6) / 1e9
-        kname = ("scan_select_kernel" if a.mode == "fused" else "scan_block_kernel") \
-            if d0.block_mode else "scan_token_kernel<32>"
+        kname = "scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d>" % spec.rank
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": None, "bytes_per_launch": nbytes["scan"]}

@@ -64,6 +64,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     path = path or LIB_PATH
+    try:
+        # PyTorch ships its own libamdhip64.so.7; this library binds to whichever
+        # copy the process loads first, and torch's kernels only run on its own
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m block_sparse_attention_pack_amd.build`")
@@ -76,7 +82,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "bsa_sparse_decode_attn": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
         "bsa_combine": [_I32, _I32, _I32, _P, _P, _P, _P, _P],
         "bsa_score_select": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
-                             _P, _P, _P, _P],
+                             _P, _P, _P],
         "bsa_attend_combine": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                _P],
     }
@@ -191,13 +197,12 @@ def counters_size(layout) -> int:
 
 
 def score_select(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
-                 scores, workspace, workspace_bytes, counters, idx, count, stream=None) -> None:
+                 scores, workspace, workspace_bytes, idx, count, stream=None) -> None:
     lib = load()
     _check(lib.bsa_score_select(ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(codes),
                                 _ptr(scales), _ptr(global_scale), _ptr(key_center), _ptr(kproj),
                                 _ptr(proj), _ptr(seq_lens), _ptr(scores), _ptr(workspace),
-                                workspace_bytes, _ptr(counters), _ptr(idx), _ptr(count),
-                                _stream(stream)))
+                                workspace_bytes, _ptr(idx), _ptr(count), _stream(stream)))
 
 
 def attend_combine(layout, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,

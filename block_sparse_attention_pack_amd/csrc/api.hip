@@ -9,6 +9,9 @@
 
 namespace {
 
+// attend_combine merges in the attention launch's last group up to this many splits
+constexpr int kFusedMergeMaxSplits = 8;
+
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -253,35 +256,12 @@ int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
                      const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                      const float* key_center, const uint16_t* kproj, const float* proj,
                      const int32_t* seq_lens, float* scores, void* workspace,
-                     size_t workspace_bytes, uint32_t* counters, int32_t* idx, int32_t* count,
-                     void* stream) {
-  try {
-    bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    if (cfg->granularity == BSA_GRANULARITY_TOKEN) {
-      rc = bsa_score_scan(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
-                          seq_lens, scores, stream);
-      if (rc) return rc;
-      return bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx,
-                             count, stream);
-    }
-    BSA_REQUIRE(q && aligned16(q) && seq_lens && scores && idx && count, BSA_ERR_INVALID_ARG,
-                "q (16-byte aligned), seq_lens, scores, idx and count are required");
-    BSA_REQUIRE(codes && scales && global_scale && aligned16(codes) && aligned16(scales),
-                BSA_ERR_INVALID_ARG,
-                "block mode needs codes, scales (16-byte aligned) and global_scale");
-    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "block mode needs the arrival counters");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    return hip_status(bsa::launch_scan_select_block(
-                          g, cfg->n_tail_pages, cfg->budget, cfg->softmax_scale,
-                          static_cast<const _Float16*>(q), codes, scales, global_scale,
-                          key_center, seq_lens, scores, counters, idx, count, s),
-                      "scan_select");
-  } catch (...) {
-    return fail(BSA_ERR_HIP, "unexpected exception");
-  }
+                     size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream) {
+  const int rc = bsa_score_scan(layout, cfg, q, codes, scales, global_scale, key_center, kproj,
+                                proj, seq_lens, scores, stream);
+  if (rc) return rc;
+  return bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count,
+                         stream);
 }
 
 int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
@@ -307,12 +287,16 @@ int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, c
                   "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    return hip_status(bsa::launch_attention(g, cfg->granularity, cfg->budget, cfg->n_tail_pages,
-                                            cfg->softmax_scale, static_cast<const _Float16*>(q),
-                                            k, v, seq_lens, idx, count, tail_k, tail_v,
-                                            num_splits, part_o, part_lse, counters, out, out_lse,
-                                            s),
-                      "attend_combine");
+    // The last group's merge reads every split's partials one after another;
+    // past a few splits the separate merge launch, parallel over rows, is faster.
+    const bool merge_in_last_group = num_splits <= kFusedMergeMaxSplits;
+    hipError_t e = bsa::launch_attention(
+        g, cfg->granularity, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
+        static_cast<const _Float16*>(q), k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+        part_o, part_lse, merge_in_last_group ? counters : nullptr, out, out_lse, s);
+    if (e == hipSuccess && !merge_in_last_group)
+      e = bsa::launch_combine(g.B * g.Hq, num_splits, part_o, part_lse, out, out_lse, s);
+    return hip_status(e, "attend_combine");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

@@ -148,12 +148,6 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,
                              hipStream_t s);
-hipError_t launch_scan_select_block(const UnitGeom& g, int n_tail, int budget, float sigma,
-                                    const _Float16* q, const uint8_t* codes,
-                                    const uint8_t* scales, const float* gscale,
-                                    const float* center, const int32_t* seq_lens, float* scores,
-                                    uint32_t* counters, int32_t* idx, int32_t* count,
-                                    hipStream_t s);
 hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, const _Float16* q,
                              const uint16_t* kproj, const float* proj, const int32_t* seq_lens,
                              float* scores, hipStream_t s);

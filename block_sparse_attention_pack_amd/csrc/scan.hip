@@ -59,7 +59,6 @@ struct ScanBlockArgs {
   float* scores;
   int Hkv, Hq, G, NBmax, Tmax, n_tail, bpw;
   float sigma;
-  bool coherent;  // scores are read by another work-group of the same launch
 };
 
 // The scan of one wave: blocks [blk_begin, blk_begin + bpw) of unit blockIdx.y.
@@ -107,10 +106,7 @@ __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lan
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     if (blk >= packed) {
-      if (lane == 0) {
-        if (a.coherent) store_coherent(out + blk, -__builtin_inff());
-        else out[blk] = -__builtin_inff();
-      }
+      if (lane == 0) out[blk] = -__builtin_inff();
       continue;
     }
     const uint8_t* crec = a.codes + (int64_t(unit) * a.NBmax + blk) * kCodeRecord;
@@ -143,36 +139,13 @@ __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lan
     for (int r = 0; r < 4; ++r)
       if (head_ok[r]) best = fmaxf(best, s_t * m[r] + qc[r]);
     best = wave_max(best);
-    if (lane == 0) {
-      if (a.coherent) store_coherent(out + blk, a.sigma * best);
-      else out[blk] = a.sigma * best;
-    }
+    if (lane == 0) out[blk] = a.sigma * best;
   }
 }
 
 // grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads.
 __global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
   scan_wave_blocks(a, threadIdx.x & 63, threadIdx.x >> 6);
-}
-
-// Scan, then selection by the unit's last work-group to finish: every group
-// counts itself in counters[unit] after its scores are stored; the one that
-// sees all the others done reads the unit's scores and writes idx / count, and
-// returns the counter to zero. No group ever waits for another.
-__global__ __launch_bounds__(256) void scan_select_kernel(ScanBlockArgs a, int budget,
-                                                          uint32_t* __restrict__ counters,
-                                                          int32_t* __restrict__ idx,
-                                                          int32_t* __restrict__ count) {
-  __shared__ SelectLds lds;
-  __shared__ int is_last;
-  scan_wave_blocks(a, threadIdx.x & 63, threadIdx.x >> 6);
-  const int unit = blockIdx.y;
-  if (!last_group_of_unit(counters, unit, gridDim.x, &is_last)) return;
-  const int L = clamp_len(a.seq_lens[unit / a.Hkv], a.Tmax);
-  int C, picks, f0, f1;
-  block_candidates(L, a.n_tail, a.NBmax, budget, C, picks, f0, f1);
-  select_unit_rows<true>(a.scores + int64_t(unit) * a.NBmax, C, picks, f0, f1, budget,
-                         idx + int64_t(unit) * budget, count + unit, lds);
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
@@ -280,7 +253,6 @@ ScanBlockArgs make_scan_args(const UnitGeom& g, int n_tail, float sigma, const _
   a.n_tail = n_tail;
   a.bpw = bpw;
   a.sigma = sigma;
-  a.coherent = false;
   return a;
 }
 }  // namespace
@@ -293,20 +265,6 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _
   const ScanBlockArgs a =
       make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores, grid);
   hipLaunchKernelGGL(scan_block_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_scan_select_block(const UnitGeom& g, int n_tail, int budget, float sigma,
-                                    const _Float16* q, const uint8_t* codes,
-                                    const uint8_t* scales, const float* gscale,
-                                    const float* center, const int32_t* seq_lens, float* scores,
-                                    uint32_t* counters, int32_t* idx, int32_t* count,
-                                    hipStream_t s) {
-  dim3 grid;
-  ScanBlockArgs a =
-      make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores, grid);
-  a.coherent = true;
-  hipLaunchKernelGGL(scan_select_kernel, grid, dim3(256), 0, s, a, budget, counters, idx, count);
   return hipGetLastError();
 }
 

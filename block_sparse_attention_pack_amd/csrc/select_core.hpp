@@ -48,13 +48,10 @@ __device__ __forceinline__ int select_block_scan(int v, SelectLds& s, int& total
 // first among equal ones), appends the forced entries f0 .. f1-1, writes them
 // ascending to out[0 .. budget) padded with -1, and the number chosen to *count.
 // Every thread of the work-group must call it (it synchronises the group).
-// COHERENT: read the scores with device-scope loads (they were written by other
-// work-groups of the same launch).
-template <bool COHERENT = false>
 __device__ __forceinline__ void select_unit_rows(const float* row, int C, int picks, int f0,
                                                  int f1, int budget, int32_t* out,
                                                  int32_t* count, SelectLds& s) {
-  auto score_at = [&](int i) -> float { return COHERENT ? load_coherent(row + i) : row[i]; };
+  auto score_at = [&](int i) -> float { return row[i]; };
   const int tid = threadIdx.x;
   picks = max(0, min(picks, C));
   const int per = ceil_div(C, kSelectThreads);

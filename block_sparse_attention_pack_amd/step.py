@@ -20,11 +20,14 @@ def default_splits(units: int, budget: int, granularity: str) -> int:
     """Split count that gives the attention launch about 512 work-groups.
 
     The attention kernel runs three waves per SIMD, so 512 four-wave groups are
-    resident on 256 CUs at once; more, smaller splits only add merge work.
+    resident on 256 CUs at once; more, smaller splits only add merge work. A
+    split keeps at least two blocks (block mode) or 64 tokens (token mode).
     """
     s = max(1, math.ceil(512 / max(units, 1)))
     if granularity == "token":
         s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
+    else:
+        s = min(s, max(1, budget // 2))
     return max(1, min(s, budget))
 
 
@@ -57,7 +60,7 @@ class DeviceStep:
     part_lse: "torch.Tensor"
     out: "torch.Tensor"
     out_lse: "torch.Tensor"
-    counters: "torch.Tensor"  # arrival counters of the fused calls (zero between calls)
+    counters: "torch.Tensor"  # arrival counters of attend_combine (zero between calls)
 
     @property
     def block_mode(self) -> bool:
@@ -96,12 +99,12 @@ class DeviceStep:
         self.attend(stream)
         self.combine(stream)
 
-    # -- the same step as two fused calls -------------------------------------
+    # -- the same step as two combined calls ----------------------------------
     def score_select(self, stream=None) -> None:
         bsa.score_select(self.layout, self.cfg, self.q, self.codes, self.scales,
                          self.global_scale, self.key_center, self.kproj, self.proj,
                          self.seq_lens, self.scores, self.workspace, self.ws_bytes,
-                         self.counters, self.idx, self.count, stream)
+                         self.idx, self.count, stream)
 
     def attend_combine(self, stream=None) -> None:
         bsa.attend_combine(self.layout, self.cfg, self.q, self.k, self.v, self.seq_lens,

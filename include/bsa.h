@@ -207,31 +207,29 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
                 const float* part_lse, float* out, float* out_lse, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Fused forms of the step (same results, fewer launches)
+ * Combined forms of the step (same results, fewer calls)
  *
  * bsa_score_select = bsa_score_scan followed by bsa_select_topk, and
  * bsa_attend_combine = bsa_sparse_decode_attn followed by bsa_combine over the
  * num_splits partials of each (sequence, query head), with identical outputs.
- * In block mode the selection runs in the last scan work-group of each unit to
- * finish, and the merge in the last attention work-group of each unit, so their
- * latency hides behind other units' work. The last group is found with one
- * arrival counter per unit in `counters` (device, bsa_counters_size bytes): it
- * must be zero-filled before its first use, every call that completes leaves it
- * zero, and calls that share it must not run concurrently. No work-group ever
- * waits for another. Token mode runs the two unfused calls (counters unused by
- * bsa_score_select).
+ With at most 8 splits bsa_attend_combine merges in the last attention
+ * work-group of each unit to finish, so the merge hides behind other units'
+ * attention (with more it launches the merge separately). That group is found
+ * with one arrival counter per unit in `counters` (device, bsa_counters_size
+ * bytes): it must be zero-filled before its first use, every call that
+ * completes leaves it zero, and calls that share it must not run concurrently.
+ * No work-group ever waits for another.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of the arrival counters: 4 * batch * num_kv_heads (0 for a bad layout). */
 size_t bsa_counters_size(const bsa_kv_layout* layout);
 
-/* bsa_score_scan then bsa_select_topk; arguments as there, plus `counters`. */
+/* bsa_score_scan then bsa_select_topk; arguments as there. */
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                      const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                      const float* key_center, const uint16_t* kproj, const float* proj,
                      const int32_t* seq_lens, float* scores, void* workspace,
-                     size_t workspace_bytes, uint32_t* counters, int32_t* idx, int32_t* count,
-                     void* stream);
+                     size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream);
 
 /* bsa_sparse_decode_attn then bsa_combine: part_o / part_lse are filled as by
  * bsa_sparse_decode_attn, out [B][Hq][128] and out_lse [B][Hq] (may be NULL) as

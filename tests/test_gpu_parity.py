@@ -244,3 +244,20 @@ def test_fused_calls_with_short_sequences_and_many_splits():
     d.run_fused()
     torch.cuda.synchronize()
     check_all(w, d)
+
+
+@pytest.mark.parametrize("splits", [8, 9, 16])
+def test_attend_combine_on_both_sides_of_the_merge_limit(splits):
+    """Up to 8 splits the merge runs in the attention launch, beyond in its own."""
+    w = W.generate(W.reduced("ragged", 8192, batch=2, budget=24))
+    d = run_step(w, splits=splits)
+    ref = [host(t).copy() for t in (d.out, d.out_lse)]
+    for t in (d.out, d.out_lse):
+        t.fill_(7)
+    for rep in range(2):
+        d.attend_combine()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (host(d.out), host(d.out_lse))):
+            assert np.array_equal(a, b, equal_nan=True), (splits, rep)
+        assert int(d.counters.abs().sum()) == 0
+    check_all(w, d)
