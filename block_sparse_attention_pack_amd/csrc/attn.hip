@@ -309,6 +309,30 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   u.kunit = a.k + b * a.sb + h * a.sh;
   u.vunit = a.v + b * a.sb + h * a.sh;
 
+  // 16-row groups of this split, dealt round-robin to the waves: wave w takes
+  // groups w, w + 4, ...; t counts the wave's own groups
+  const int nent = u.e1 > u.e0 ? u.e1 - u.e0 : 0;
+  const int ngroups = block_mode ? 8 * nent : ceil_div(nent, 16);
+  const int nmine = ngroups > wave ? ceil_div(ngroups - wave, kAttnWaves) : 0;
+  constexpr int kChunkGroups = CHUNK / 16;
+  // stage the block ids / tokens of the wave's groups t0 .. tend-1
+  auto stage_chunk = [&](int t0, int tend) {
+    int* stage = stage_lds[wave];
+    if (block_mode) {
+      for (int t = t0 + lane; t < tend; t += kWave)
+        stage[t - t0] = u.uidx[u.e0 + ((wave + kAttnWaves * t) >> 3)];
+    } else {
+      for (int i = lane; i < 16 * (tend - t0); i += kWave) {
+        const int t = t0 + (i >> 4);
+        const int e = u.e0 + 16 * (wave + kAttnWaves * t) + (i & 15);
+        const int tok = e < u.e1 ? u.uidx[e] : -1;
+        stage[i] = (tok >= 0 && tok < u.L) ? tok : -1;
+      }
+    }
+  };
+  // the first chunk's index loads overlap the query loads below
+  if (nmine > 0) stage_chunk(0, min(kChunkGroups, nmine));
+
   // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
   // for MFMA step c (the key layout above), staged once in LDS by wave 0
   const int n16 = lane & 15, j4 = lane >> 4;
@@ -336,27 +360,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   }
   float* sc = sc_lds + wave * kShare;
 
-  // 16-row groups of this split, dealt round-robin to the waves: wave w takes
-  // groups w, w + 4, ...; t counts the wave's own groups
-  const int nent = u.e1 > u.e0 ? u.e1 - u.e0 : 0;
-  const int ngroups = block_mode ? 8 * nent : ceil_div(nent, 16);
-  const int nmine = ngroups > wave ? ceil_div(ngroups - wave, kAttnWaves) : 0;
-  constexpr int kChunkGroups = CHUNK / 16;
 #pragma unroll 1
   for (int t0 = 0; t0 < nmine; t0 += kChunkGroups) {
     const int tend = min(t0 + kChunkGroups, nmine);
     int* stage = stage_lds[wave];
-    if (block_mode) {
-      for (int t = t0 + lane; t < tend; t += kWave)
-        stage[t - t0] = u.uidx[u.e0 + ((wave + kAttnWaves * t) >> 3)];
-    } else {
-      for (int i = lane; i < 16 * (tend - t0); i += kWave) {
-        const int t = t0 + (i >> 4);
-        const int e = u.e0 + 16 * (wave + kAttnWaves * t) + (i & 15);
-        const int tok = e < u.e1 ? u.uidx[e] : -1;
-        stage[i] = (tok >= 0 && tok < u.L) ? tok : -1;
-      }
-    }
+    if (t0 > 0) stage_chunk(t0, tend);  // the first chunk was staged before the loop
     wave_lds_fence();
     // ---- phase 1: keys stream through a ring of kDepth slots; QK^T -> sc ----
     // Every slot is always issued (groups past the chunk are null groups), so
@@ -379,6 +387,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
       }
     }
     wave_lds_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    // the value ring's first groups go out now, so their latency overlaps the
+    // softmax (every slot is issued; groups past the chunk are null groups)
+    ValSlot<G> vring[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      issue_values<G, MAIN_BF16>(vring[k], a, u, wave + kAttnWaves * (t0 + k), stage, k, lane,
+                                 block_mode, t0 + k < tend);
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase 2: exact softmax update over the chunk, per head -------------
     const int rows = 16 * (tend - t0);
@@ -406,13 +422,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
     }
     wave_lds_fence();
     __builtin_amdgcn_sched_barrier(0);
-    // ---- phase 3: values stream through a ring of kDepth slots; PV ----------
+    // ---- phase 3: values stream through the ring; PV -----------------------
     {
-      ValSlot<G> ring[kDepth];
-#pragma unroll
-      for (int k = 0; k < kDepth; ++k)
-        issue_values<G, MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t0 + k), stage, k, lane,
-                                   block_mode, t0 + k < tend);
+      ValSlot<G>(&ring)[kDepth] = vring;
 #pragma unroll 1
       for (int t = t0; t < tend; t += kDepth) {
 #pragma unroll
