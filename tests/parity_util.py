@@ -144,3 +144,26 @@ def check_attention(w, b, h, idx_gpu, splits, part_o_gpu, part_lse_gpu, out_gpu,
     assert np.array_equal(lf, np.isfinite(lse_gpu))
     assert np.abs(lse_gpu[lf] - lse[lf]).max(initial=0) <= OUT_TOL
     return err
+
+
+def check_units(w, d, units=None):
+    """Compare every stage of a DeviceStep with the oracle for the given units
+    (all by default); w must hold the K and V the GPU holds. Device buffers are
+    copied to the host one unit at a time."""
+    s = w.spec
+    G = s.group
+    if units is None:
+        units = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
+    host = lambda t: t.cpu().numpy()
+    for b, h in units:
+        scores = host(d.scores[b, h])
+        if s.granularity == "block":
+            rc, rs = check_pack_block(w, b, h, host(d.codes[b, h]), host(d.scales[b, h]))
+            ref = check_block_scores(w, b, h, scores, rc, rs)
+        else:
+            kref = check_pack_token(w, b, h, host(d.kproj[b, h]))
+            ref = check_token_scores(w, b, h, scores, kref)
+        check_selection(w, b, h, host(d.idx[b, h]), host(d.count[b, h]), scores, ref)
+        rows = slice(h * G, (h + 1) * G)
+        check_attention(w, b, h, host(d.idx[b, h]), d.splits, host(d.part_o[b, rows]),
+                        host(d.part_lse[b, rows]), host(d.out[b, rows]), host(d.out_lse[b, rows]))

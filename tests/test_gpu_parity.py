@@ -49,30 +49,7 @@ def host(t):
 
 
 def check_all(w, d, units=None):
-    """Compare every stage for the given units; w holds the K, V the GPU holds."""
-    s = w.spec
-    G = s.group
-    if units is None:
-        units = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
-    scores = host(d.scores)
-    idx, count = host(d.idx), host(d.count)
-    po, pl = host(d.part_o), host(d.part_lse)
-    out, lse = host(d.out), host(d.out_lse)
-    if s.granularity == "block":
-        codes, scales = host(d.codes), host(d.scales)
-    else:
-        kproj = host(d.kproj)
-    for b, h in units:
-        if s.granularity == "block":
-            rc, rs = PU.check_pack_block(w, b, h, codes[b, h], scales[b, h])
-            ref = PU.check_block_scores(w, b, h, scores[b, h], rc, rs)
-        else:
-            kref = PU.check_pack_token(w, b, h, kproj[b, h])
-            ref = PU.check_token_scores(w, b, h, scores[b, h], kref)
-        PU.check_selection(w, b, h, idx[b, h], count[b, h], scores[b, h], ref)
-        rows = slice(h * G, (h + 1) * G)
-        PU.check_attention(w, b, h, idx[b, h], d.splits, po[b, rows], pl[b, rows],
-                           out[b, rows], lse[b, rows])
+    PU.check_units(w, d, units)
 
 
 REDUCED = {
