@@ -1,8 +1,9 @@
 """Decode-step throughput of the sparse attention hot path on one MI355X.
 
 A step is one pass of the whole path for one layer: score_scan (4-bit dense
-scan or projected-key scan), select_topk, sparse_decode_attn and combine, over
-a batch of synthetic inputs already resident in HBM. Consecutive steps rotate
+scan or projected-key scan), select_topk, sparse_decode_attn and combine (by
+default as two calls: score_scan and select_attend_combine), over a batch of
+synthetic inputs already resident in HBM. Consecutive steps rotate
 over --layers distinct copies of the KV cache, as consecutive layers of a model
 would, so no step finds the previous step's data in the 256 MB Infinity Cache.
 
@@ -54,8 +55,9 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time only the whole step, without per-kernel events")
-    ap.add_argument("--mode", default="fused", choices=["fused", "split"],
-                    help="fused: score_scan, select_topk, attend_combine; "
+    ap.add_argument("--mode", default="fused", choices=["fused", "three", "split"],
+                    help="fused: score_scan, select_attend_combine; "
+                         "three: score_scan, select_topk, attend_combine; "
                          "split: score_scan, select_topk, sparse_decode_attn, combine")
     return ap.parse_args()
 
@@ -184,6 +186,9 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     if a.mode == "fused":
+        stages = ["scan", "select_attend_combine"]
+        calls = lambda d: [d.scan, d.select_attend_combine]
+    elif a.mode == "three":
         stages = ["scan", "select", "attend_combine"]
         calls = lambda d: [d.scan, d.select, d.attend_combine]
     else:

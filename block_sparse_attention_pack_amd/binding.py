@@ -85,6 +85,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                              _P, _P, _P],
         "bsa_attend_combine": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
                                _P],
+        "bsa_select_attend_combine": [LP, CP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
+                                      _I32, _P, _P, _P, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -212,3 +214,14 @@ def attend_combine(layout, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, n
                                   _ptr(v), _ptr(seq_lens), _ptr(idx), _ptr(count), _ptr(tail_k),
                                   _ptr(tail_v), num_splits, _ptr(part_o), _ptr(part_lse),
                                   _ptr(counters), _ptr(out), _ptr(out_lse), _stream(stream)))
+
+
+def select_attend_combine(layout, cfg, q, k, v, seq_lens, scores, workspace, workspace_bytes,
+                          tail_k, tail_v, num_splits, idx, count, part_o, part_lse, counters, out,
+                          out_lse, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_select_attend_combine(
+        ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens),
+        _ptr(scores), _ptr(workspace), workspace_bytes, _ptr(tail_k), _ptr(tail_v), num_splits,
+        _ptr(idx), _ptr(count), _ptr(part_o), _ptr(part_lse), _ptr(counters), _ptr(out),
+        _ptr(out_lse), _stream(stream)))

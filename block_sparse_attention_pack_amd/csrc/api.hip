@@ -102,6 +102,32 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
 
 }  // namespace
 
+namespace {
+
+// Attention, then the merge: in the attention launch's last group up to
+// kFusedMergeMaxSplits splits (its merge reads every split's partials one after
+// another), in the row-parallel merge launch beyond. With sel_scores the
+// attention launch also selects the blocks (block mode).
+hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
+                            const void* k, const void* v, const int32_t* seq_lens,
+                            const int32_t* idx, const int32_t* count, const uint16_t* tail_k,
+                            const uint16_t* tail_v, int32_t num_splits, float* part_o,
+                            float* part_lse, uint32_t* counters, float* out, float* out_lse,
+                            const float* sel_scores, int32_t* sel_idx, int32_t* sel_count,
+                            hipStream_t s) {
+  const bool merge_in_last_group = num_splits <= kFusedMergeMaxSplits;
+  hipError_t e = bsa::launch_attention(
+      g, cfg->granularity, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
+      static_cast<const _Float16*>(q), k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+      part_o, part_lse, merge_in_last_group ? counters : nullptr, out, out_lse, sel_scores,
+      sel_idx, sel_count, s);
+  if (e == hipSuccess && !merge_in_last_group)
+    e = bsa::launch_combine(g.B * g.Hq, num_splits, part_o, part_lse, out, out_lse, s);
+  return e;
+}
+
+}  // namespace
+
 extern "C" {
 
 int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* k,
@@ -223,7 +249,7 @@ int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cf
                                             cfg->softmax_scale, static_cast<const _Float16*>(q),
                                             k, v, seq_lens, idx, count, tail_k, tail_v,
                                             num_splits, part_o, part_lse, nullptr, nullptr,
-                                            nullptr, s),
+                                            nullptr, nullptr, nullptr, nullptr, s),
                       "sparse_decode_attn");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -287,16 +313,53 @@ int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, c
                   "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    // The last group's merge reads every split's partials one after another;
-    // past a few splits the separate merge launch, parallel over rows, is faster.
-    const bool merge_in_last_group = num_splits <= kFusedMergeMaxSplits;
-    hipError_t e = bsa::launch_attention(
-        g, cfg->granularity, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
-        static_cast<const _Float16*>(q), k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-        part_o, part_lse, merge_in_last_group ? counters : nullptr, out, out_lse, s);
-    if (e == hipSuccess && !merge_in_last_group)
-      e = bsa::launch_combine(g.B * g.Hq, num_splits, part_o, part_lse, out, out_lse, s);
-    return hip_status(e, "attend_combine");
+    return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
+                                       num_splits, part_o, part_lse, counters, out, out_lse,
+                                       nullptr, nullptr, nullptr, s),
+                      "attend_combine");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, const float* scores, void* workspace,
+                              size_t workspace_bytes, const uint16_t* tail_k,
+                              const uint16_t* tail_v, int32_t num_splits, int32_t* idx,
+                              int32_t* count, float* part_o, float* part_lse,
+                              uint32_t* counters, float* out, float* out_lse, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    int rc = check_common(layout, cfg, &g);
+    if (rc) return rc;
+    const bool in_attention =
+        cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax;
+    if (!in_attention) {
+      rc = bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count,
+                           stream);
+      if (rc) return rc;
+      return bsa_attend_combine(layout, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
+                                num_splits, part_o, part_lse, counters, out, out_lse, stream);
+    }
+    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
+                "q, k, v must be 16-byte aligned device pointers");
+    BSA_REQUIRE(seq_lens && scores && idx && count && part_o && part_lse && out,
+                BSA_ERR_INVALID_ARG,
+                "seq_lens, scores, idx, count, part_o, part_lse and out are required");
+    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
+                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
+                num_splits);
+    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "the arrival counters are required");
+    if (cfg->n_tail_pages > 0)
+      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
+                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
+                                       num_splits, part_o, part_lse, counters, out, out_lse,
+                                       scores, idx, count, s),
+                      "select_attend_combine");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

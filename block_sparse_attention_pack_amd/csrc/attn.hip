@@ -22,8 +22,14 @@
 //      channels of a subset of the rows so one wave load covers whole
 //      256-byte value rows.
 // The waves' states are merged through LDS into one (O, lse) partial per head.
+//
+// With block scores given, every work-group of a unit first selects the unit's
+// blocks itself (select_unit_rows, the same selection select_topk makes) into
+// LDS, and the split-0 group also writes idx / count: the selection's latency
+// then overlaps nothing but saves its own launch.
 #include "combine_core.hpp"
 #include "common.hpp"
+#include "select_core.hpp"
 
 namespace bsa {
 namespace {
@@ -73,6 +79,9 @@ struct AttnArgs {
   uint32_t* counters;  // non-null: the unit's last group also merges the partials
   float* out;
   float* out_lse;
+  const float* sel_scores;  // non-null: select the blocks in the prologue (block mode)
+  int32_t* sel_idx;         // where split 0 writes the selection, and its count
+  int32_t* sel_count;
   int64_t sb, sh, st;
   int Hkv, Hq, Tmax, budget, n_tail, splits;
   float scale_log2;  // sigma * log2(e)
@@ -292,6 +301,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   __shared__ bf16x8 qsplit_lds[8 * kWave];  // q = q_hi + q_lo in the MFMA operand order
   __shared__ int stage_lds[kAttnWaves][CHUNK];
   __shared__ int is_last;
+  __shared__ int32_t sel_lds[kFusedSelectMax];
+  __shared__ SelectLds sel_s;
+  __shared__ int32_t sel_cnt;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, unit = blockIdx.y;
@@ -301,11 +313,47 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   u.L = clamp_len(a.seq_lens[b], a.Tmax);
   u.npg = ceil_div(u.L, kBlock);
   u.tail0 = u.npg - a.n_tail;  // first page held in the tail store
+  // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
+  // for MFMA step c (the key layout above). For G <= 4 wave 0 issues the loads
+  // first, so their latency overlaps the selection and the index loads below
+  // (for larger groups the registers are needed there).
+  constexpr bool kEarlyQ = G <= 4;
+  const int n16 = lane & 15, j4 = lane >> 4;
+  half8 qv[4];
+  auto load_q = [&]() {
+    const bool ok = n16 < G;
+    const _Float16* qrow = a.q + (int64_t(b) * a.Hq + h * G + (ok ? n16 : 0)) * kHeadDim + 8 * j4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qv[c] = *reinterpret_cast<const half8*>(qrow + 32 * c);
+      if (!ok) qv[c] = half8{};
+    }
+  };
+  if (kEarlyQ && wave == 0) load_q();
+  int cnt;
+  if (a.sel_scores) {
+    // the unit's selection, made by every group of the unit alike
+    const int nb = a.Tmax / kBlock;
+    int C, picks, f0, f1;
+    block_candidates(u.L, a.n_tail, nb, a.budget, C, picks, f0, f1);
+    select_unit_rows(a.sel_scores + int64_t(unit) * nb, C, picks, f0, f1, a.budget, sel_lds,
+                     &sel_cnt, sel_s);
+    __syncthreads();
+    cnt = sel_cnt;
+    u.uidx = sel_lds;
+    if (split == 0) {
+      for (int i = threadIdx.x; i < a.budget; i += 256)
+        a.sel_idx[int64_t(unit) * a.budget + i] = sel_lds[i];
+      if (threadIdx.x == 0) a.sel_count[unit] = cnt;
+    }
+  } else {
+    cnt = a.count[unit];
+    u.uidx = a.idx + int64_t(unit) * a.budget;
+  }
+  cnt = min(max(cnt, 0), a.budget);
   const int per = ceil_div(a.budget, a.splits);
-  const int cnt = min(max(a.count[unit], 0), a.budget);
   u.e0 = split * per;
   u.e1 = min(min(u.e0 + per, a.budget), cnt);
-  u.uidx = a.idx + int64_t(unit) * a.budget;
   u.kunit = a.k + b * a.sb + h * a.sh;
   u.vunit = a.v + b * a.sb + h * a.sh;
 
@@ -333,18 +381,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
   // the first chunk's index loads overlap the query loads below
   if (nmine > 0) stage_chunk(0, min(kChunkGroups, nmine));
 
-  // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
-  // for MFMA step c (the key layout above), staged once in LDS by wave 0
-  const int n16 = lane & 15, j4 = lane >> 4;
+  // query operands: staged once in LDS by wave 0
   if (wave == 0) {
-    const bool ok = n16 < G;
-    const _Float16* qrow = a.q + (int64_t(b) * a.Hq + h * G + (ok ? n16 : 0)) * kHeadDim + 8 * j4;
+    if (!kEarlyQ) load_q();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      half8 v = *reinterpret_cast<const half8*>(qrow + 32 * c);
-      if (!ok) v = half8{};
-      qa_lds[c * kWave + lane] = v;
-      split_bf16(v, qsplit_lds[(2 * c) * kWave + lane], qsplit_lds[(2 * c + 1) * kWave + lane]);
+      qa_lds[c * kWave + lane] = qv[c];
+      split_bf16(qv[c], qsplit_lds[(2 * c) * kWave + lane], qsplit_lds[(2 * c + 1) * kWave + lane]);
     }
   }
   __syncthreads();
@@ -525,8 +568,14 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
                             const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
                             const uint16_t* tail_k, const uint16_t* tail_v, int splits,
                             float* part_o, float* part_lse, uint32_t* counters, float* out,
-                            float* out_lse, hipStream_t s) {
+                            float* out_lse, const float* sel_scores, int32_t* sel_idx,
+                            int32_t* sel_count, hipStream_t s) {
+  if (sel_scores && (granularity != BSA_GRANULARITY_BLOCK || budget > kFusedSelectMax))
+    return hipErrorInvalidValue;
   AttnArgs a;
+  a.sel_scores = sel_scores;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
   a.q = q;
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);

@@ -158,12 +158,16 @@ hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const 
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
                                hipStream_t s);
+// Largest budget for which the attention launch selects the blocks itself.
+constexpr int kFusedSelectMax = 1024;
+
 hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int n_tail,
                             float sigma, const _Float16* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
                             const uint16_t* tail_k, const uint16_t* tail_v, int splits,
                             float* part_o, float* part_lse, uint32_t* counters, float* out,
-                            float* out_lse, hipStream_t s);
+                            float* out_lse, const float* sel_scores, int32_t* sel_idx,
+                            int32_t* sel_count, hipStream_t s);
 hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
                           float* out, float* out_lse, hipStream_t s);
 

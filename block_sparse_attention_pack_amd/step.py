@@ -112,6 +112,17 @@ class DeviceStep:
                            self.part_o, self.part_lse, self.counters, self.out, self.out_lse,
                            stream)
 
+    def select_attend_combine(self, stream=None) -> None:
+        bsa.select_attend_combine(self.layout, self.cfg, self.q, self.k, self.v, self.seq_lens,
+                                  self.scores, self.workspace, self.ws_bytes, self.tail_k,
+                                  self.tail_v, self.splits, self.idx, self.count, self.part_o,
+                                  self.part_lse, self.counters, self.out, self.out_lse, stream)
+
+    def run_two(self, stream=None) -> None:
+        """The step as two calls: score_scan, select_attend_combine."""
+        self.scan(stream)
+        self.select_attend_combine(stream)
+
     def run_fused(self, stream=None) -> None:
         """The step as two calls: score_select, attend_combine."""
         self.score_select(stream)

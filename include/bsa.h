@@ -241,6 +241,21 @@ int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, c
                        float* part_lse, uint32_t* counters, float* out, float* out_lse,
                        void* stream);
 
+/* bsa_select_topk then bsa_attend_combine, with identical outputs: idx and count
+ * as written by bsa_select_topk, part_o / part_lse / out / out_lse as by
+ * bsa_attend_combine. In block mode with budget <= 1024 a single attention
+ * launch does both: every work-group of a unit makes the unit's selection in
+ * its prologue (Jet-QSparse abstract: selection by score, then sparse
+ * aggregation), and the split-0 group writes idx and count. Otherwise (token
+ * mode, larger budgets) it runs the two calls; workspace is bsa_select_topk's. */
+int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, const float* scores, void* workspace,
+                              size_t workspace_bytes, const uint16_t* tail_k,
+                              const uint16_t* tail_v, int32_t num_splits, int32_t* idx,
+                              int32_t* count, float* part_o, float* part_lse,
+                              uint32_t* counters, float* out, float* out_lse, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* bsa_last_error(void);
 

@@ -1,8 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is drawn at its full size (up to 128K tokens, batch 16), packed,
-and run through the same calls bench.py times: score_scan, select_topk and
-attend_combine with the default split count. Every stage of a few sampled units
+and run through the same calls bench.py times: score_scan and
+select_attend_combine with the default split count. Every stage of a few sampled units
 (the first, the last and one in between) is then checked against the oracle:
 pack bytes bit-exact, scores within the FP32 accumulation bound, the selection
 bit-exact on the GPU's own scores, outputs within 2e-3.
@@ -44,8 +44,7 @@ def test_full_size_sampled_units(name):
     d = upload(w)  # the default split count, as bench.py uses
     d.pack()
     d.scan()
-    d.select()
-    d.attend_combine()
+    d.select_attend_combine()
     torch.cuda.synchronize()
     assert int(d.counters.abs().sum()) == 0
     units = _sampled_units(spec)

@@ -194,33 +194,41 @@ def test_repeat_runs_are_bitwise_identical():
 
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_fused_calls_match_the_four_calls(name):
-    """score_select + attend_combine give the four calls' bits, call after call."""
+    """score_select + attend_combine, and score_scan + select_attend_combine,
+    give the four calls' bits, call after call."""
     w = W.generate(REDUCED[name])
     d = run_step(w)
     ref = [host(t).copy() for t in (d.scores, d.idx, d.count, d.out, d.out_lse)]
     for t in (d.scores, d.idx, d.count, d.out, d.out_lse):
         t.fill_(7)
-    for rep in range(3):  # the arrival counters must return to zero every call
-        d.run_fused()
-        torch.cuda.synchronize()
-        got = [host(t) for t in (d.scores, d.idx, d.count, d.out, d.out_lse)]
-        for a, b in zip(ref, got):
-            assert np.array_equal(a, b, equal_nan=True), (name, rep)
-        assert int(d.counters.abs().sum()) == 0
+    for run in (d.run_fused, d.run_two):
+        for rep in range(3):  # the arrival counters must return to zero every call
+            for t in (d.idx, d.count, d.out, d.out_lse):
+                t.fill_(7)
+            run()
+            torch.cuda.synchronize()
+            got = [host(t) for t in (d.scores, d.idx, d.count, d.out, d.out_lse)]
+            for a, b in zip(ref, got):
+                assert np.array_equal(a, b, equal_nan=True), (name, run.__name__, rep)
+            assert int(d.counters.abs().sum()) == 0
     check_all(w, d)
 
 
 def test_fused_calls_with_short_sequences_and_many_splits():
     lengths = (0, 1, 129, 300, 2000, 4096)
     spec = dataclasses.replace(W.SPECS["ragged"], name="fused_short", seed=80, batch=len(lengths),
-                               kv_heads=2, q_heads=8, max_tokens=4096, budget=6, n_tail=2,
+                               kv_heads=2, q_heads=8, max_tokens=4096, budget=12, n_tail=2,
                                needle_count=2, lengths=lengths)
     w = W.generate(spec)
-    d = upload(w, splits=6)
-    d.pack()
-    d.run_fused()
-    torch.cuda.synchronize()
-    check_all(w, d)
+    for splits in (6, 12):
+        d = upload(w, splits=splits)
+        d.pack()
+        d.run_fused()
+        torch.cuda.synchronize()
+        check_all(w, d)
+        d.run_two()
+        torch.cuda.synchronize()
+        check_all(w, d)
 
 
 @pytest.mark.parametrize("splits", [8, 9, 16])
