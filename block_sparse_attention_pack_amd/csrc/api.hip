@@ -9,9 +9,6 @@
 
 namespace {
 
-// attend_combine merges in the attention launch's last group up to this many splits
-constexpr int kFusedMergeMaxSplits = 8;
-
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -104,10 +101,10 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
 
 namespace {
 
-// Attention, then the merge: in the attention launch's last group up to
-// kFusedMergeMaxSplits splits (its merge reads every split's partials one after
-// another), in the row-parallel merge launch beyond. With sel_scores the
-// attention launch also selects the blocks (block mode).
+// Attention, then the merge: in the attention launch's last group of each unit
+// up to bsa::kFusedMergeMaxSplits splits, in the row-parallel merge launch
+// beyond. With sel_scores the attention launch also selects the blocks (block
+// mode).
 hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
                             const void* k, const void* v, const int32_t* seq_lens,
                             const int32_t* idx, const int32_t* count, const uint16_t* tail_k,
@@ -115,7 +112,7 @@ hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
                             float* part_lse, uint32_t* counters, float* out, float* out_lse,
                             const float* sel_scores, int32_t* sel_idx, int32_t* sel_count,
                             hipStream_t s) {
-  const bool merge_in_last_group = num_splits <= kFusedMergeMaxSplits;
+  const bool merge_in_last_group = num_splits <= bsa::kFusedMergeMaxSplits;
   hipError_t e = bsa::launch_attention(
       g, cfg->granularity, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
       static_cast<const _Float16*>(q), k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,

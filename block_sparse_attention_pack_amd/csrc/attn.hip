@@ -221,7 +221,8 @@ __device__ __forceinline__ void issue_values(ValSlot<G>& vs, const AttnArgs& a, 
 }
 
 // QK^T of one landed key group; the log2-scaled logits of rows 16 g .. +15 go
-// to sc[head * CHUNK + 16 g + row] (masked rows -inf).
+// to sc[head * CHUNK + 16 g + row] (masked rows -inf). qa: this lane's four
+// FP16 query operands (registers); qsplit: the BF16 halves, in LDS.
 template <int G>
 __device__ __forceinline__ void group_scores(const KeySlot& ks, const half8* qa,
                                              const bf16x8* qsplit, float scale_log2, float* sc,
@@ -233,10 +234,7 @@ __device__ __forceinline__ void group_scores(const KeySlot& ks, const half8* qa,
     for (int c = 0; c < 4; ++c) {
       half8 kv;
       __builtin_memcpy(&kv, &ks.w[c], 16);
-      // re-read from LDS every group: keeps the operands out of the registers
-      // the value phase needs
-      const half8 qc = *static_cast<const volatile half8*>(qa + c * kWave + lane);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qc, kv, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kv, d, 0, 0, 0);
     }
   } else {
 #pragma unroll
@@ -418,11 +416,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
       for (int k = 0; k < kDepth; ++k)
         issue_keys<MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t0 + k), stage, k, lane,
                               block_mode, t0 + k < tend);
+      // the FP16 query operands stay in registers for the key phase only
+      half8 qreg[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qreg[c] = qa_lds[c * kWave + lane];
 #pragma unroll 1
       for (int t = t0; t < tend; t += kDepth) {
 #pragma unroll
         for (int k = 0; k < kDepth; ++k) {
-          if (t + k < tend) group_scores<G>(ring[k], qa_lds, qsplit_lds, a.scale_log2, sc, t + k - t0, lane);
+          if (t + k < tend) group_scores<G>(ring[k], qreg, qsplit_lds, a.scale_log2, sc, t + k - t0, lane);
           issue_keys<MAIN_BF16>(ring[k], a, u, wave + kAttnWaves * (t + k + kDepth), stage,
                                 t + k + kDepth - t0, lane, block_mode, t + k + kDepth < tend);
           __builtin_amdgcn_sched_barrier(0);
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
       float* sh = sc + hh * CHUNK;
       float mx = -__builtin_inff();
       for (int r = lane; r < rows; r += kWave) mx = fmaxf(mx, sh[r]);
-      mx = wave_max(mx);
+      mx = wave_max_uniform(mx);
       const float mn = fmaxf(m[hh], mx);
       const bool live = mn > -__builtin_inff();
       const float alpha = live ? __builtin_amdgcn_exp2f(m[hh] - mn) : 1.0f;
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
       }
       // wave-uniform: keep the running state in scalar registers
       lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                               __builtin_bit_cast(int, lsum[hh] * alpha + wave_sum(ps))));
+                                               __builtin_bit_cast(int, lsum[hh] * alpha + wave_sum_uniform(ps))));
       m[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha;
@@ -548,8 +550,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i)
     const int hh = o / kHeadDim, d = o % kHeadDim;
     const int64_t rowq = int64_t(b) * a.Hq + h * G + hh;
     float val, lse;
-    combine_channel<true>(a.part_lse + rowq * a.splits, a.part_o + rowq * a.splits * kHeadDim,
-                          a.splits, d, val, lse);
+    if (a.splits <= kFusedMergeMaxSplits)  // always, as launched
+      combine_channel_few<kFusedMergeMaxSplits, true>(
+          a.part_lse + rowq * a.splits, a.part_o + rowq * a.splits * kHeadDim, a.splits, d, val,
+          lse);
+    else
+      combine_channel<true>(a.part_lse + rowq * a.splits, a.part_o + rowq * a.splits * kHeadDim,
+                            a.splits, d, val, lse);
     a.out[rowq * kHeadDim + d] = val;
     if (d == 0 && a.out_lse) a.out_lse[rowq] = lse;
   }

@@ -89,6 +89,26 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + row_ror<1>(v);
 }
 
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Maximum over the wave, as a wave-uniform value: DPP within the 16-lane rows,
+// then the four row results. Every lane of the wave must be active.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// Sum over the wave, as a wave-uniform value, in a fixed order (rows as
+// row16_sum's lane 16r sums them, then (r0 + r1) + (r2 + r3)). Every lane of
+// the wave must be active.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // --- device-wide hand-off between work-groups of one launch -----------------
 // The fused kernels pass a few values (block scores, split partials) from every
 // work-group of a unit to the unit's last one. Those values are stored and
@@ -160,6 +180,8 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                hipStream_t s);
 // Largest budget for which the attention launch selects the blocks itself.
 constexpr int kFusedSelectMax = 1024;
+// The attention launch merges the splits in its last group up to this many.
+constexpr int kFusedMergeMaxSplits = 8;
 
 hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int n_tail,
                             float sigma, const _Float16* q, const void* k, const void* v,

@@ -138,7 +138,7 @@ __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lan
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (head_ok[r]) best = fmaxf(best, s_t * m[r] + qc[r]);
-    best = wave_max(best);
+    best = wave_max_uniform(best);
     if (lane == 0) out[blk] = a.sigma * best;
   }
 }
