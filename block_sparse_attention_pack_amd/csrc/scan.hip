@@ -149,10 +149,12 @@ __global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
-// scores kTokPerWg / 4 tokens. R / 8 lanes share one token row (16 bytes each),
-// so one wave load covers 64 * 16 B of consecutive rows; the partial products
-// of a row are summed across its lanes. Four loads are in flight per step.
-constexpr int kTokPerWg = 4096;
+// scores kTokPerWg / 4 consecutive tokens, one token per lane and step: a lane
+// reads its token's whole projected row (R bf16 = R / 8 16-byte loads; together
+// the wave's loads cover 64 consecutive rows, whole cache lines) and forms the
+// dot product with p in its own registers, so the 64 scores of a step leave in
+// one coalesced store.
+constexpr int kTokPerWg = 16384;
 
 template <int R>
 __global__ __launch_bounds__(256) void scan_token_kernel(
@@ -160,67 +162,84 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
     const float* __restrict__ proj, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma) {
   static_assert(R % 8 == 0 && R <= 128, "rank");
-  constexpr int kLanesPerTok = R / 8;           // lanes sharing one token row
-  constexpr int kTokPerStep = 64 / kLanesPerTok;
-  __shared__ float p_lds[R];
+  constexpr int kVec = R / 8;               // 16-byte loads per token row
+  constexpr bool kPinReg = R <= 32;         // p in registers (else read from LDS)
+  constexpr int kUnroll = 1;                // tokens per lane in flight
+  __shared__ float qbar[kHeadDim];
   __shared__ float part[256];
+  __shared__ float p_lds[R];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit % Hkv;
   const int L = clamp_len(seq_lens[b], Tmax);
 
-  // p = P^T qbar, qbar = (sum of the group's queries) / G, all in float32.
+  // qbar = (sum of the group's queries) / G, then p = sigma * P^T qbar, in
+  // float32; every thread issues all its loads of a stage before using them.
+  if (threadIdx.x < kHeadDim) {
+    const _Float16* qd = q + (int64_t(b) * Hq + h * G) * kHeadDim + threadIdx.x;
+    float qs = 0.0f;
+    for (int g = 0; g < G; ++g) qs += float(qd[int64_t(g) * kHeadDim]);
+    qbar[threadIdx.x] = qs * (1.0f / float(G));
+  }
+  __syncthreads();
   {
-    const float invG = 1.0f / float(G);
     constexpr int kChunks = 256 / R;  // threads per output channel
-    const int jj = threadIdx.x % R, ch = threadIdx.x / R;
     constexpr int kDPer = kHeadDim / kChunks;
+    const int jj = threadIdx.x % R, ch = threadIdx.x / R;
+    constexpr int kBatch = kDPer < 16 ? kDPer : 16;
+    const float* pc = proj + (int64_t(h) * kHeadDim + ch * kDPer) * R + jj;
     float acc = 0.0f;
-    for (int d = ch * kDPer; d < (ch + 1) * kDPer; ++d) {
-      float qs = 0.0f;
-      for (int g = 0; g < G; ++g) qs += float(q[(int64_t(b) * Hq + h * G + g) * kHeadDim + d]);
-      acc += proj[(int64_t(h) * kHeadDim + d) * R + jj] * (qs * invG);
+    for (int i0 = 0; i0 < kDPer; i0 += kBatch) {
+      float pv[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) pv[i] = pc[int64_t(i0 + i) * R];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) acc += pv[i] * qbar[ch * kDPer + i0 + i];
     }
     part[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x < R) {
-      float s = 0.0f;
-      for (int c = 0; c < kChunks; ++c) s += part[c * R + threadIdx.x];
-      p_lds[threadIdx.x] = s * sigma;
+      float sum = 0.0f;
+      for (int c = 0; c < kChunks; ++c) sum += part[c * R + threadIdx.x];
+      p_lds[threadIdx.x] = sum * sigma;
     }
     __syncthreads();
   }
-  const int sub = lane % kLanesPerTok;
-  float p[8];
+  float p[kPinReg ? R : 1];
+  if constexpr (kPinReg) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = p_lds[8 * sub + e];
+    for (int j = 0; j < R; ++j) p[j] = p_lds[j];
+  }
 
   const int t_wave = blockIdx.x * kTokPerWg + wave * (kTokPerWg / 4);
   const uint16_t* base = kproj + int64_t(unit) * Tmax * R;
   float* out = scores + int64_t(unit) * Tmax;
   const int t_end = min(t_wave + kTokPerWg / 4, Tmax);
-  constexpr int kUnroll = 4;
-  for (int t0 = t_wave; t0 < t_end; t0 += kUnroll * kTokPerStep) {
-    uint4v w[kUnroll];
+  for (int t0 = t_wave; t0 < t_end; t0 += kUnroll * kWave) {
+    uint4v w[kUnroll][kVec];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kTokPerStep + lane / kLanesPerTok;
-      w[u] = t < t_end ? __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(
-                             base + int64_t(t) * R + 8 * sub))
-                       : uint4v{0u, 0u, 0u, 0u};
+      const int t = t0 + u * kWave + lane;
+      const uint4v* row = reinterpret_cast<const uint4v*>(base + int64_t(t < t_end ? t : t_wave) * R);
+#pragma unroll
+      for (int c = 0; c < kVec; ++c) w[u][c] = row[c];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kTokPerStep + lane / kLanesPerTok;
+      const int t = t0 + u * kWave + lane;
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s += p[2 * e] * bf16_bits_to_float(w[u][e] & 0xFFFFu);
-        s += p[2 * e + 1] * bf16_bits_to_float(w[u][e] >> 16);
-      }
+      for (int c = 0; c < kVec; ++c) {
 #pragma unroll
-      for (int off = 1; off < kLanesPerTok; off <<= 1) s += __shfl_xor(s, off, kWave);
-      if (t < t_end && sub == 0) out[t] = t < L ? s : -__builtin_inff();
+        for (int e = 0; e < 4; ++e) {
+          const int j = 8 * c + 2 * e;
+          const float p0 = kPinReg ? p[kPinReg ? j : 0] : p_lds[j];
+          const float p1 = kPinReg ? p[kPinReg ? j + 1 : 0] : p_lds[j + 1];
+          s = __builtin_fmaf(p0, bf16_bits_to_float(w[u][c][e] & 0xFFFFu), s);
+          s = __builtin_fmaf(p1, bf16_bits_to_float(w[u][c][e] >> 16), s);
+        }
+      }
+      if (t < t_end) out[t] = t < L ? s : -__builtin_inff();
     }
   }
 }
