@@ -420,43 +420,75 @@ __global__ __launch_bounds__(kSelectThreads) void tok_finish_kernel(
   // it is in the bucket with a key above kb (>= kb when ge); of the tokens tied
   // at kb the first r_eq in index order are taken. Its output position is the
   // number of tokens taken by key before it plus min(ties before it, r_eq).
+  // With the bucket listed in LDS (in token order), each window's bucket
+  // entries are one contiguous range of the list; its threads classify them
+  // in parallel into the window's taken bitmap (wgt) and a tie bitmap (wbk,
+  // free once the list is built). Otherwise each thread walks its own words'
+  // bucket bits and reads their scores.
   int32_t* out = idx + int64_t(unit) * budget;
-  int gt_run = 0, eq_run = 0, list_run = 0;
+  int gt_run = 0, eq_run = 0;
+  auto lower_bound = [&](int tok) {  // first list entry with token >= tok
+    int lo = 0, hi = listed;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (stok[mid] < tok) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
   for (int w0 = 0; w0 < Wc; w0 += kTokWin) {
     __syncthreads();
     load_window(u.gt, wgt, w0);
-    if (bucket && !(staged && one_window)) load_window(u.bk, wbk, w0);
-    __syncthreads();
-    uint32_t tk[kTokWpt], te[kTokWpt], m[kTokWpt];
-    int nbk = 0;
-    if (bucket) nbk = my_bucket_words(m);
-    else {
-#pragma unroll
-      for (int j = 0; j < kTokWpt; ++j) m[j] = 0u;
-    }
-    int off = 0, tot_bk = 0;
-    if (bucket && staged) off = list_run + select_block_scan(nbk, lds, tot_bk) - nbk;
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int j = 0; j < kTokWpt; ++j) {
-      uint32_t taken = wgt[tok_pad(tid * kTokWpt + j)], tie = 0u, b = m[j];
-      while (b) {
-        const int bit = __builtin_ctz(b);
-        b &= b - 1;
-        const int t = (w0 + tid * kTokWpt + j) * 32 + bit;
-        uint32_t key = 0u;
-        if (staged) key = off < listed ? skey[off] : 0u;
-        else key = t < C ? score_key(row[t]) : 0u;
-        ++off;
-        if (ge ? key >= kb : key > kb) taken |= 1u << bit;
-        else if (!ge && key == kb) tie |= 1u << bit;
+    if (bucket) {
+      if (staged) {
+        for (int k = tid; k < kTokWinPad; k += kSelectThreads) wbk[k] = 0u;
+      } else {
+        load_window(u.bk, wbk, w0);
       }
-      tk[j] = taken;
-      te[j] = tie;
-      ngt += __popc(taken);
-      neq += __popc(tie);
     }
-    list_run += tot_bk;
+    __syncthreads();
+    if (bucket && staged) {
+      const int lo = lower_bound(w0 * 32), hi = lower_bound((w0 + kTokWin) * 32);
+      for (int k = lo + tid; k < hi; k += kSelectThreads) {
+        const uint32_t key = skey[k];
+        const int t = stok[k];
+        const int wl = (t >> 5) - w0;  // in [0, kTokWin): t lies in this window
+        const uint32_t bit = 1u << (t & 31);
+        if (ge ? key >= kb : key > kb) atomicOr(&wgt[tok_pad(wl)], bit);
+        else if (!ge && key == kb) atomicOr(&wbk[tok_pad(wl)], bit);
+      }
+      __syncthreads();
+    }
+    uint32_t tk[kTokWpt], te[kTokWpt];
+    int ngt = 0, neq = 0;
+    if (bucket && !staged) {
+      uint32_t m[kTokWpt];
+      my_bucket_words(m);
+#pragma unroll
+      for (int j = 0; j < kTokWpt; ++j) {
+        uint32_t taken = wgt[tok_pad(tid * kTokWpt + j)], tie = 0u, b = m[j];
+        while (b) {
+          const int bit = __builtin_ctz(b);
+          b &= b - 1;
+          const int t = (w0 + tid * kTokWpt + j) * 32 + bit;
+          const uint32_t key = t < C ? score_key(row[t]) : 0u;
+          if (ge ? key >= kb : key > kb) taken |= 1u << bit;
+          else if (!ge && key == kb) tie |= 1u << bit;
+        }
+        tk[j] = taken;
+        te[j] = tie;
+        ngt += __popc(taken);
+        neq += __popc(tie);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTokWpt; ++j) {
+        tk[j] = wgt[tok_pad(tid * kTokWpt + j)];
+        te[j] = bucket ? wbk[tok_pad(tid * kTokWpt + j)] : 0u;
+        ngt += __popc(tk[j]);
+        neq += __popc(te[j]);
+      }
+    }
     int win_gt, win_eq;
     const int gt_before = gt_run + select_block_scan(ngt, lds, win_gt) - ngt;
     int eq_seen = eq_run + select_block_scan(neq, lds, win_eq) - neq;
