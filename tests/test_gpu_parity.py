@@ -83,11 +83,38 @@ def test_query_group_sizes(G):
     spec = dataclasses.replace(W.SPECS["tiny"], name=f"group{G}", seed=20 + G, batch=2,
                                kv_heads=2, q_heads=2 * G, max_tokens=2048, budget=5)
     w = W.generate(spec)
-    check_all(w, run_step(w))
+    d = run_step(w)
+    check_all(w, d)
+    _two_calls_match(d)
     tspec = dataclasses.replace(W.SPECS["token"], name=f"tgroup{G}", seed=30 + G, batch=1,
                                 kv_heads=2, q_heads=2 * G, max_tokens=4096, budget=96)
     w = W.generate(tspec)
-    check_all(w, run_step(w))
+    d = run_step(w)
+    check_all(w, d)
+    _two_calls_match(d)
+
+
+def _two_calls_match(d):
+    """score_scan + select_attend_combine reproduce the four calls' bits."""
+    ref = [host(t).copy() for t in (d.idx, d.count, d.out, d.out_lse)]
+    for t in (d.idx, d.count, d.out, d.out_lse):
+        t.fill_(7)
+    d.run_two()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (host(d.idx), host(d.count), host(d.out), host(d.out_lse))):
+        assert np.array_equal(a, b, equal_nan=True)
+    assert int(d.counters.abs().sum()) == 0
+
+
+def test_select_attend_combine_above_the_in_kernel_budget():
+    """Budgets above 1024 blocks select in their own launch; same results."""
+    spec = dataclasses.replace(W.SPECS["jetqsparse"], name="big_budget", seed=90, batch=1,
+                               kv_heads=1, q_heads=4, max_tokens=1280 * 128, budget=1100,
+                               needle_count=5, key_offset_std=0.0)
+    w = W.generate(spec)
+    d = run_step(w, splits=8)
+    check_all(w, d)
+    _two_calls_match(d)
 
 
 def test_short_and_empty_sequences_with_tail_pages():
