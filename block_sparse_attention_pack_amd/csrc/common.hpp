@@ -110,7 +110,7 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
 }
 
 // --- device-wide hand-off between work-groups of one launch -----------------
-// The fused kernels pass a few values (block scores, split partials) from every
+// The attention kernel's merge passes the split partials from every
 // work-group of a unit to the unit's last one. Those values are stored and
 // loaded as device-scope atomics, which reach the memory-side coherence point
 // past each XCD's L2, so no L2 write-back fence is needed: a writer waits for

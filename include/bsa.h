@@ -16,11 +16,13 @@
  * and, off the timed path, pack_kv_cache builds the 4-bit key copy or the
  * projected-key copy.
  *
- * Sources: Jet-QSparse (arXiv 2611.01022) abstract -- NVFP4 key cache, a dense
- * scan over the whole history, selection of 128-token blocks with a budget per
- * KV head, FP16 value aggregation with FP32 accumulation, calibrated key
- * centering, at most two BF16 pages per sequence; JSSA (arXiv 2610.19026)
- * abstract and Figure 1 -- the group's mean query scores a projected-key cache,
+ * Sources: "Jet-QSparse: Accelerating Agentic LLM Inference with 4-Bit Sparse
+ * Attention", abstract -- NVFP4 key cache, a dense scan over the whole history,
+ * selection of 128-token blocks with a budget per KV head, FP16 products summed
+ * in FP32 over the chosen values, calibrated key centering, up to two newest
+ * pages per sequence kept in BF16; "Joint Subspace Sparse Attention for
+ * Efficient Long-Context Decoding" (JSSA), Abstract and Figure 1 -- the group's
+ * mean query scores a projected-key cache,
  * one top-B token set per KV head shared by its query heads, attention that
  * reads the selected rows of the standard GQA cache without gathering them.
  *

@@ -2,19 +2,21 @@
 
 Sources (the only specification there is):
 
-* Jet-QSparse (arXiv 2611.01022) abstract: keys are cached as NVFP4; a dense
-  scan scores the full key history every decode step and selects 128-token
-  blocks; the selected blocks' values are aggregated in FP16 with FP32
-  accumulation; calibrated key centering and at most two BF16 pages per
-  sequence and layer absorb quantization error; budgets are counted in blocks
-  per KV head (64 in the speed claim, 128 for the accuracy claim).
-* JSSA (arXiv 2610.19026) abstract and Figure 1: the mean of a KV head's query
-  heads scores a projected-key cache in a shared rank-r subspace, the top-B
-  token positions form one index set per KV head shared by its query heads,
-  and attention reads the original full-dimensional keys and values at those
-  positions without gathering them. Figure 3 fixes the density (2048 of 128K);
-  Figure 10 evaluates BF16 and FP8 projected-key caches; Table 15 shows per-KV-
-  head selection beats a head-shared vote.
+* "Jet-QSparse: Accelerating Agentic LLM Inference with 4-Bit Sparse
+  Attention", abstract (Key points, Full text): the key history is stored as
+  NVFP4 and scanned densely at every decode step to pick 128-token blocks;
+  only those blocks' values enter the output, multiplied in FP16 and summed in
+  FP32; keys are centered by a calibrated vector, and up to two of each
+  sequence's newest pages stay in BF16; the budget is a block count per KV
+  head (64 in the speed claim, 128 for the accuracy claim).
+* "Joint Subspace Sparse Attention for Efficient Long-Context Decoding" (JSSA),
+  Abstract and Figure 1: per KV head, the average of its query heads is
+  compared with keys projected to a common rank-r basis; the B best positions
+  become one index list that all of that head's queries use, and attention then
+  reads the unprojected keys and values at those positions in place. Figure 3
+  fixes the density (2048 of 128K); Figure 10 evaluates BF16 and FP8
+  projected-key caches; Table 15 shows per-KV-head selection beats a
+  head-shared vote.
 
 Everything is per unit = one (sequence b, KV head h). Query head hq belongs to
 KV head hq // G. Arithmetic is float64 except the steps whose result is a
@@ -341,8 +343,8 @@ def combine(part_o: np.ndarray, part_lse: np.ndarray) -> Tuple[np.ndarray, np.nd
 
 
 # --------------------------------------------------------------------------
-# A6: projected-key cache for token mode (JSSA Figure 1: a projected-key cache
-# in a shared low-dimensional subspace; Figure 10: BF16 projected-key cache)
+# A6: projected-key cache for token mode (JSSA Figure 1: keys projected onto a
+# rank-r basis common to the heads; Figure 10: the cache held in BF16)
 #
 # Reading: kproj[t, j] = BF16(acc), acc the float32 sum over d ascending of
 # fl32(P[d, j] * k[t, d]), each addition rounded to float32, no fused multiply-add.
