@@ -9,7 +9,9 @@ would, so no step finds the previous step's data in the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is (batch x KV heads) decode steps per second;
 `pct_hbm_peak` is the step's algorithmic bytes per second over 8 TB/s;
-`roofline` is the dominant kernel (the scan) measured with HIP events on the
+`dense_same_gpu` is dense FP16 attention (every block selected) on the same
+cache and kernels, with the sparse step's speedup over it. `roofline` is the
+dominant kernel (the scan) measured with HIP events on the
 launch stream over the timed region (recorded on every --event-stride-th step,
 since each event record costs the GPU a marker); `cpu_baseline` is the CPU oracle timed on
 a bounded sample of the same workload.
@@ -52,6 +54,8 @@ def parse():
                     choices=["tiny", "llama8b", "jetqsparse", "ragged", "token"])
     ap.add_argument("--layers", type=int, default=4, help="distinct KV-cache copies rotated per step")
     ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--no-dense", dest="dense", action="store_false",
+                    help="skip the dense-attention reference on the same GPU")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-stage-events", action="store_true",
@@ -83,6 +87,33 @@ def measured_traffic(kernel: str, workload: str):
     if fields.get("source_sha256") != h.hexdigest():
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
+
+
+def dense_same_gpu(d0, sparse_ms: float, steps: int = 10):
+    """Dense FP16 attention on the same GPU and cache: the same kernels with the
+    budget set to every block (every token in token mode), timed per step."""
+    import torch
+
+    s = d0.w.spec
+    full = s.max_blocks if d0.block_mode else s.max_tokens
+    dd = d0.with_budget(full)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dd.select_attend_combine()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        dd.select_attend_combine()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    dense_bytes = s.kv_heads * 512 * int(d0.w.seq_lens.astype("int64").sum())  # every K, V row
+    del dd
+    return {"ms_per_step": round(ms, 4), "steps": steps, "budget": full,
+            "bytes_per_step": dense_bytes,
+            "pct_hbm_peak": round(100.0 * dense_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 2),
+            "sparse_speedup": round(ms / sparse_ms, 3)}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -270,6 +301,9 @@ def main() -> int:
         "stage_events": None if a.no_stage_events else f"every {stride}th timed step",
         "roofline": roofline,
     }
+    if a.dense:
+        log("[bench] timing dense attention on the same GPU")
+        out["dense_same_gpu"] = dense_same_gpu(d0, ms_per_step)
     if a.cpu_seconds > 0:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

@@ -123,6 +123,31 @@ class DeviceStep:
         self.scan(stream)
         self.select_attend_combine(stream)
 
+    def with_budget(self, budget: int, splits: Optional[int] = None) -> "DeviceStep":
+        """The same cache and inputs with another budget (new selection and
+        partial buffers); budget = every block or token gives dense attention."""
+        import torch
+
+        L = self.layout
+        B, Hkv, Hq = L.batch, L.num_kv_heads, L.num_q_heads
+        gran = "block" if self.block_mode else "token"
+        cfg = bsa.select_cfg(self.cfg.granularity, budget, self.cfg.n_tail_pages,
+                             self.cfg.proj_rank, self.cfg.softmax_scale)
+        if splits is None:
+            splits = default_splits(B * Hkv, budget, gran)
+        dev = self.q.device
+        ws_bytes = bsa.workspace_size(L, cfg)
+        return dataclasses.replace(
+            self, cfg=cfg, splits=splits,
+            workspace=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None,
+            ws_bytes=ws_bytes,
+            idx=torch.empty((B, Hkv, budget), dtype=torch.int32, device=dev),
+            count=torch.empty((B, Hkv), dtype=torch.int32, device=dev),
+            part_o=torch.empty((B, Hq, splits, HEAD_DIM), dtype=torch.float32, device=dev),
+            part_lse=torch.empty((B, Hq, splits), dtype=torch.float32, device=dev),
+            out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev),
+            out_lse=torch.empty((B, Hq), dtype=torch.float32, device=dev))
+
     def run_fused(self, stream=None) -> None:
         """The step as two calls: score_select, attend_combine."""
         self.score_select(stream)
