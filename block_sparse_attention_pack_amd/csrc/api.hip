@@ -123,6 +123,86 @@ hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
   return e;
 }
 
+// Argument checks of each stage, run before anything is enqueued (the combined
+// calls run every stage's checks first).
+int check_scan_args(const bsa_select_cfg* cfg, const void* q, const uint8_t* codes,
+                    const uint8_t* scales, const float* global_scale, const uint16_t* kproj,
+                    const float* proj, const int32_t* seq_lens, const float* scores) {
+  BSA_REQUIRE(q && aligned16(q) && seq_lens && scores, BSA_ERR_INVALID_ARG,
+              "q (16-byte aligned), seq_lens and scores are required");
+  if (cfg->granularity == BSA_GRANULARITY_BLOCK)
+    BSA_REQUIRE(codes && scales && global_scale && aligned16(codes) && aligned16(scales),
+                BSA_ERR_INVALID_ARG,
+                "block mode needs codes, scales (16-byte aligned) and global_scale");
+  else
+    BSA_REQUIRE(kproj && proj && aligned16(kproj), BSA_ERR_INVALID_ARG,
+                "token mode needs kproj (16-byte aligned) and proj");
+  return BSA_OK;
+}
+
+int check_select_args(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const float* scores,
+                      const int32_t* seq_lens, const void* workspace, size_t workspace_bytes,
+                      const int32_t* idx, const int32_t* count) {
+  BSA_REQUIRE(scores && seq_lens && idx && count, BSA_ERR_INVALID_ARG,
+              "scores, seq_lens, idx and count are required");
+  if (cfg->granularity == BSA_GRANULARITY_TOKEN) {
+    const size_t need = bsa::token_select_workspace(g);
+    BSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), BSA_ERR_WORKSPACE,
+                "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  }
+  return BSA_OK;
+}
+
+int check_attend_args(const bsa_select_cfg* cfg, const void* q, const void* k, const void* v,
+                      const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
+                      const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
+                      const float* part_o, const float* part_lse) {
+  BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
+              "q, k, v must be 16-byte aligned device pointers");
+  BSA_REQUIRE(seq_lens && idx && count && part_o && part_lse, BSA_ERR_INVALID_ARG,
+              "seq_lens, idx, count, part_o and part_lse are required");
+  BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
+              BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
+              num_splits);
+  if (cfg->n_tail_pages > 0)
+    BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
+                "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+  return BSA_OK;
+}
+
+int check_merge_args(const float* out, const uint32_t* counters) {
+  BSA_REQUIRE(out, BSA_ERR_INVALID_ARG, "out is required");
+  BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "the arrival counters are required");
+  return BSA_OK;
+}
+
+hipError_t launch_scan(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
+                       const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                       const float* key_center, const uint16_t* kproj, const float* proj,
+                       const int32_t* seq_lens, float* scores, hipStream_t s) {
+  const _Float16* qh = static_cast<const _Float16*>(q);
+  if (cfg->granularity == BSA_GRANULARITY_BLOCK)
+    return bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale, qh, codes, scales,
+                                  global_scale, key_center, seq_lens, scores, s);
+  return bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank, qh, kproj, proj, seq_lens,
+                                scores, s);
+}
+
+hipError_t launch_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const float* scores,
+                         const int32_t* seq_lens, void* workspace, int32_t* idx, int32_t* count,
+                         hipStream_t s) {
+  if (cfg->granularity == BSA_GRANULARITY_BLOCK)
+    return bsa::launch_select_block(g, cfg->budget, cfg->n_tail_pages, scores, seq_lens, idx,
+                                    count, s);
+  return bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx, count, s);
+}
+
+#define BSA_CHECK(expr)   \
+  do {                    \
+    const int rc_ = (expr); \
+    if (rc_) return rc_;  \
+  } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -163,27 +243,12 @@ int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const
                    const int32_t* seq_lens, float* scores, void* stream) {
   try {
     bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    BSA_REQUIRE(q && aligned16(q) && seq_lens && scores, BSA_ERR_INVALID_ARG,
-                "q (16-byte aligned), seq_lens and scores are required");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
     (void)hipGetLastError();
-    const _Float16* qh = static_cast<const _Float16*>(q);
-    if (cfg->granularity == BSA_GRANULARITY_BLOCK) {
-      BSA_REQUIRE(codes && scales && global_scale && aligned16(codes) && aligned16(scales),
-                  BSA_ERR_INVALID_ARG,
-                  "block mode needs codes, scales (16-byte aligned) and global_scale");
-      return hip_status(bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale, qh,
-                                               codes, scales, global_scale, key_center,
-                                               seq_lens, scores, s),
-                        "scan_block");
-    }
-    BSA_REQUIRE(kproj && proj && aligned16(kproj), BSA_ERR_INVALID_ARG,
-                "token mode needs kproj (16-byte aligned) and proj");
-    return hip_status(bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank, qh, kproj,
-                                             proj, seq_lens, scores, s),
-                      "scan_token");
+    return hip_status(launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                                  seq_lens, scores, static_cast<hipStream_t>(stream)),
+                      "score_scan");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }
@@ -200,22 +265,12 @@ int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
                     int32_t* idx, int32_t* count, void* stream) {
   try {
     bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    BSA_REQUIRE(scores && seq_lens && idx && count, BSA_ERR_INVALID_ARG,
-                "scores, seq_lens, idx and count are required");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     (void)hipGetLastError();
-    if (cfg->granularity == BSA_GRANULARITY_BLOCK)
-      return hip_status(bsa::launch_select_block(g, cfg->budget, cfg->n_tail_pages, scores,
-                                                 seq_lens, idx, count, s),
-                        "select_block");
-    const size_t need = bsa::token_select_workspace(g);
-    BSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), BSA_ERR_WORKSPACE,
-                "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-    return hip_status(bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx,
-                                               count, s),
-                      "select_token");
+    return hip_status(launch_select(g, cfg, scores, seq_lens, workspace, idx, count,
+                                    static_cast<hipStream_t>(stream)),
+                      "select_topk");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }
@@ -228,25 +283,16 @@ int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cf
                            float* part_lse, void* stream) {
   try {
     bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
-                "q, k, v must be 16-byte aligned device pointers");
-    BSA_REQUIRE(seq_lens && idx && count && part_o && part_lse, BSA_ERR_INVALID_ARG,
-                "seq_lens, idx, count, part_o and part_lse are required");
-    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
-                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
-                num_splits);
-    if (cfg->n_tail_pages > 0)
-      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
-                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                                part_o, part_lse));
     (void)hipGetLastError();
     return hip_status(bsa::launch_attention(g, cfg->granularity, cfg->budget, cfg->n_tail_pages,
                                             cfg->softmax_scale, static_cast<const _Float16*>(q),
                                             k, v, seq_lens, idx, count, tail_k, tail_v,
                                             num_splits, part_o, part_lse, nullptr, nullptr,
-                                            nullptr, nullptr, nullptr, nullptr, s),
+                                            nullptr, nullptr, nullptr, nullptr,
+                                            static_cast<hipStream_t>(stream)),
                       "sparse_decode_attn");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -280,11 +326,20 @@ int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
                      const float* key_center, const uint16_t* kproj, const float* proj,
                      const int32_t* seq_lens, float* scores, void* workspace,
                      size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream) {
-  const int rc = bsa_score_scan(layout, cfg, q, codes, scales, global_scale, key_center, kproj,
-                                proj, seq_lens, scores, stream);
-  if (rc) return rc;
-  return bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count,
-                         stream);
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
+    BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                               seq_lens, scores, s);
+    if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
+    return hip_status(e, "score_select");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
 }
 
 int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
@@ -295,24 +350,15 @@ int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, c
                        void* stream) {
   try {
     bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
-                "q, k, v must be 16-byte aligned device pointers");
-    BSA_REQUIRE(seq_lens && idx && count && part_o && part_lse && out, BSA_ERR_INVALID_ARG,
-                "seq_lens, idx, count, part_o, part_lse and out are required");
-    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
-                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
-                num_splits);
-    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "the arrival counters are required");
-    if (cfg->n_tail_pages > 0)
-      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
-                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                                part_o, part_lse));
+    BSA_CHECK(check_merge_args(out, counters));
     (void)hipGetLastError();
     return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
                                        num_splits, part_o, part_lse, counters, out, out_lse,
-                                       nullptr, nullptr, nullptr, s),
+                                       nullptr, nullptr, nullptr,
+                                       static_cast<hipStream_t>(stream)),
                       "attend_combine");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -328,35 +374,27 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
                               uint32_t* counters, float* out, float* out_lse, void* stream) {
   try {
     bsa::UnitGeom g;
-    int rc = check_common(layout, cfg, &g);
-    if (rc) return rc;
-    const bool in_attention =
-        cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax;
-    if (!in_attention) {
-      rc = bsa_select_topk(layout, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count,
-                           stream);
-      if (rc) return rc;
-      return bsa_attend_combine(layout, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
-                                num_splits, part_o, part_lse, counters, out, out_lse, stream);
-    }
-    BSA_REQUIRE(q && k && v && aligned16(q) && aligned16(k) && aligned16(v), BSA_ERR_INVALID_ARG,
-                "q, k, v must be 16-byte aligned device pointers");
-    BSA_REQUIRE(seq_lens && scores && idx && count && part_o && part_lse && out,
-                BSA_ERR_INVALID_ARG,
-                "seq_lens, scores, idx, count, part_o, part_lse and out are required");
-    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
-                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
-                num_splits);
-    BSA_REQUIRE(counters, BSA_ERR_WORKSPACE, "the arrival counters are required");
-    if (cfg->n_tail_pages > 0)
-      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
-                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
+    BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                                part_o, part_lse));
+    BSA_CHECK(check_merge_args(out, counters));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
-                                       num_splits, part_o, part_lse, counters, out, out_lse,
-                                       scores, idx, count, s),
-                      "select_attend_combine");
+    const bool in_attention =
+        cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax;
+    hipError_t e;
+    if (in_attention) {
+      e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                           part_o, part_lse, counters, out, out_lse, scores, idx, count, s);
+    } else {
+      e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
+      if (e == hipSuccess)
+        e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                             part_o, part_lse, counters, out, out_lse, nullptr, nullptr, nullptr,
+                             s);
+    }
+    return hip_status(e, "select_attend_combine");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

@@ -111,3 +111,32 @@ def test_workspace_size(lib):
     bad = B.select_cfg(B.BLOCK, 8)
     bad.budget = -1
     assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(bad)) == 0
+
+
+def test_combined_calls_check_their_arguments(lib):
+    L, cfg = _layout(), B.select_cfg(B.BLOCK, 8)
+    tok = B.select_cfg(B.TOKEN, 64, 0, 32)
+    ws = lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(tok))
+    assert ws > 0  # token selection needs its workspace
+    # score_select: token mode without its workspace
+    rc = lib.bsa_score_select(ctypes.byref(L), ctypes.byref(tok), FAKE, None, None, None, None,
+                              FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None)
+    assert rc == -4 and "workspace" in lib.bsa_last_error().decode()
+    # attend_combine: the arrival counters are required
+    rc = lib.bsa_attend_combine(ctypes.byref(L), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, None, 2, FAKE, FAKE, None, FAKE, None, None)
+    assert rc == -4
+    # select_attend_combine (block mode, selection in the attention launch)
+    args = lambda scores, splits, counters: (
+        ctypes.byref(L), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, scores, None, 0, None, None,
+        splits, FAKE, FAKE, FAKE, FAKE, counters, FAKE, None, None)
+    assert lib.bsa_select_attend_combine(*args(None, 2, FAKE)) == -1
+    assert "scores" in lib.bsa_last_error().decode()
+    assert lib.bsa_select_attend_combine(*args(FAKE, 9, FAKE)) == -1  # more splits than budget
+    assert lib.bsa_select_attend_combine(*args(FAKE, 2, None)) == -4
+    # token mode goes through select_topk first: its workspace check comes first
+    rc = lib.bsa_select_attend_combine(ctypes.byref(L), ctypes.byref(tok), FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, None, 0, None, None, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, None, None)
+    assert rc == -4
+    assert lib.bsa_counters_size(ctypes.byref(L)) == 4
