@@ -1,9 +1,10 @@
 """Decode-step throughput of the sparse attention hot path on one MI355X.
 
 A step is one pass of the whole path for one layer: score_scan (4-bit dense
-scan or projected-key scan), select_topk, sparse_decode_attn and combine (by
-default as two calls: score_scan and select_attend_combine), over a batch of
-synthetic inputs already resident in HBM. Consecutive steps rotate
+scan or projected-key scan), select_topk, sparse_decode_attn and combine, over a batch of
+synthetic inputs already resident in HBM. By default (--mode auto) a block-mode
+step with at least 16384 scanned blocks is one decode_step launch, every other
+step two calls, score_scan and select_attend_combine. Consecutive steps rotate
 over --layers distinct copies of the KV cache, as consecutive layers of a model
 would, so no step finds the previous step's data in the 256 MB Infinity Cache.
 
@@ -11,7 +12,8 @@ Prints one JSON line. `value` is (batch x KV heads) decode steps per second;
 `pct_hbm_peak` is the step's algorithmic bytes per second over 8 TB/s;
 `dense_same_gpu` is dense FP16 attention (every block selected) on the same
 cache and kernels, with the sparse step's speedup over it. `roofline` is the
-dominant kernel (the scan) measured with HIP events on the
+dominant kernel (the one-launch step kernel, which is the whole step, or else the
+scan) measured with HIP events on the
 launch stream over the timed region (recorded on every --event-stride-th step,
 since each event record costs the GPU a marker); `cpu_baseline` is the CPU oracle timed on
 a bounded sample of the same workload.
@@ -35,10 +37,14 @@ if ROOT not in sys.path:
 
 METRIC = "sparse decode-attention steps/sec (batch x KV heads) at 128K; % HBM peak"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-# rocprofv3 counter summary of the scan kernel's HBM traffic (FETCH_SIZE + WRITE_SIZE,
-# calibrated on a copy of known size), valid while the kernel's sources are unchanged
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_block_kernel.jetqsparse.traffic.md")
-TRAFFIC_SOURCES = ["scan.hip", "common.hpp"]
+# rocprofv3 counter summaries of a kernel's HBM traffic (FETCH_SIZE + WRITE_SIZE,
+# calibrated on a copy of known size) in profiles/<kernel>.<workload>.traffic.md,
+# valid while the kernel's sources (listed here) are unchanged
+TRAFFIC_SOURCES = {
+    "scan_block_kernel": ["scan.hip", "scan_core.hpp", "common.hpp"],
+    "step_kernel": ["step.hip", "scan_core.hpp", "attn_core.hpp", "select_core.hpp",
+                    "combine_core.hpp", "common.hpp"],
+}
 
 
 def log(*a):
@@ -60,11 +66,14 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time only the whole step, without per-kernel events")
-    ap.add_argument("--event-stride", type=int, default=5,
+    ap.add_argument("--event-stride", type=int, default=25,
                     help="record the per-kernel events on every n-th timed step (each event "
                          "record costs the GPU a marker packet)")
-    ap.add_argument("--mode", default="fused", choices=["fused", "three", "split"],
-                    help="fused: score_scan, select_attend_combine; "
+    ap.add_argument("--mode", default="auto", choices=["auto", "step", "fused", "three", "split"],
+                    help="auto: step where the one-launch step pays off (block mode, "
+                         ">= 16384 scanned blocks), else fused; "
+                         "step: decode_step (one launch in block mode); "
+                         "fused: score_scan, select_attend_combine; "
                          "three: score_scan, select_topk, attend_combine; "
                          "split: score_scan, select_topk, sparse_decode_attn, combine")
     return ap.parse_args()
@@ -73,11 +82,13 @@ def parse():
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when it
     covers another kernel or workload, or the kernel's sources changed since."""
+    if kernel not in TRAFFIC_SOURCES:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.md")) as f:
             fields = dict(re.findall(r"^(\w+): (\S+)$", f.read(), re.M))
         h = hashlib.sha256()
-        for name in TRAFFIC_SOURCES:
+        for name in TRAFFIC_SOURCES[kernel]:
             with open(os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", name), "rb") as f:
                 h.update(f.read())
     except OSError:
@@ -195,7 +206,7 @@ def main() -> int:
     import torch
 
     from block_sparse_attention_pack_amd import binding, workloads as W
-    from block_sparse_attention_pack_amd.step import upload
+    from block_sparse_attention_pack_amd.step import one_launch_pays, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
@@ -204,7 +215,9 @@ def main() -> int:
     t0 = time.time()
     w = W.generate(spec, threads=16)
     log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
-    d0 = upload(w, splits=a.splits)
+    if a.mode == "auto":
+        a.mode = "step" if one_launch_pays(spec.units, spec.max_blocks, spec.granularity) else "fused"
+    d0 = upload(w, splits=a.splits, one_launch=a.mode == "step")
     d0.pack()
     torch.cuda.synchronize()
     layers = [d0]
@@ -220,7 +233,10 @@ def main() -> int:
     nbytes = W.algorithmic_bytes(w)
     stream = torch.cuda.current_stream()
 
-    if a.mode == "fused":
+    if a.mode == "step":
+        stages = ["decode_step"]
+        calls = lambda d: [d.decode_step]
+    elif a.mode == "fused":
         stages = ["scan", "select_attend_combine"]
         calls = lambda d: [d.scan, d.select_attend_combine]
     elif a.mode == "three":
@@ -265,15 +281,21 @@ def main() -> int:
         stage_us["step_events_p50"] = float(np.median(step_us))
     log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms; stages (us): {stage_us}")
 
-    scan_us = stage_us.get("scan")
+    # the dominant kernel: the whole step when it is one launch, else the scan
+    one_launch = a.mode == "step" and d0.block_mode
+    kern_us = stage_us.get("decode_step" if one_launch else "scan")
+    kbytes = nbytes["total" if one_launch else "scan"]
     roofline = None
-    if scan_us:
-        achieved = nbytes["scan"] / (scan_us * 1e-6) / 1e9
-        kname = "scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d>" % spec.rank
+    if kern_us:
+        achieved = kbytes / (kern_us * 1e-6) / 1e9
+        if one_launch:
+            kname = "step_kernel"
+        else:
+            kname = "scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d>" % spec.rank
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(kname, spec.name),
-                    "bytes_per_launch": nbytes["scan"]}
+                    "bytes_per_launch": kbytes}
     step_gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,

@@ -87,6 +87,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                _P],
         "bsa_select_attend_combine": [LP, CP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P,
                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P],
+        "bsa_decode_step": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
+                            ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -225,3 +227,15 @@ def select_attend_combine(layout, cfg, q, k, v, seq_lens, scores, workspace, wor
         _ptr(scores), _ptr(workspace), workspace_bytes, _ptr(tail_k), _ptr(tail_v), num_splits,
         _ptr(idx), _ptr(count), _ptr(part_o), _ptr(part_lse), _ptr(counters), _ptr(out),
         _ptr(out_lse), _stream(stream)))
+
+
+def decode_step(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj, k, v,
+                seq_lens, tail_k, tail_v, num_splits, scores, workspace, workspace_bytes, idx,
+                count, part_o, part_lse, counters, out, out_lse, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_decode_step(
+        ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(codes), _ptr(scales),
+        _ptr(global_scale), _ptr(key_center), _ptr(kproj), _ptr(proj), _ptr(k), _ptr(v),
+        _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), num_splits, _ptr(scores), _ptr(workspace),
+        workspace_bytes, _ptr(idx), _ptr(count), _ptr(part_o), _ptr(part_lse), _ptr(counters),
+        _ptr(out), _ptr(out_lse), _stream(stream)))

@@ -318,7 +318,9 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
 
 size_t bsa_counters_size(const bsa_kv_layout* layout) {
   if (!layout || layout->batch < 1 || layout->num_kv_heads < 1) return 0;
-  return sizeof(uint32_t) * size_t(layout->batch) * size_t(layout->num_kv_heads);
+  const int64_t units = int64_t(layout->batch) * layout->num_kv_heads;
+  if (units > 65535) return 0;  // no call accepts such a layout
+  return sizeof(uint32_t) * size_t(bsa::step_counter_words(int(units)));
 }
 
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
@@ -395,6 +397,45 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
                              s);
     }
     return hip_status(e, "select_attend_combine");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                    const float* key_center, const uint16_t* kproj, const float* proj,
+                    const void* k, const void* v, const int32_t* seq_lens,
+                    const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
+                    float* scores, void* workspace, size_t workspace_bytes, int32_t* idx,
+                    int32_t* count, float* part_o, float* part_lse, uint32_t* counters,
+                    float* out, float* out_lse, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
+    BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
+    BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                                part_o, part_lse));
+    BSA_CHECK(check_merge_args(out, counters));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e;
+    if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
+      e = bsa::launch_step(g, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
+                           static_cast<const _Float16*>(q), codes, scales, global_scale,
+                           key_center, k, v, seq_lens, tail_k, tail_v, num_splits, scores, idx,
+                           count, part_o, part_lse, counters, out, out_lse, s);
+    } else {
+      e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
+                      scores, s);
+      if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
+      if (e == hipSuccess)
+        e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                             part_o, part_lse, counters, out, out_lse, nullptr, nullptr, nullptr,
+                             s);
+    }
+    return hip_status(e, "decode_step");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

@@ -121,6 +121,12 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -192,5 +198,15 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
                             int32_t* sel_count, hipStream_t s);
 hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
                           float* out, float* out_lse, hipStream_t s);
+// The block-mode decode step in one launch (scan, selection, attention, merge).
+// Its counters: step_counter_words(units) 32-bit words, zero before the launch.
+int step_counter_words(int units);
+hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, const _Float16* q,
+                       const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                       const float* center, const void* k, const void* v,
+                       const int32_t* seq_lens, const uint16_t* tail_k, const uint16_t* tail_v,
+                       int splits, float* scores, int32_t* idx, int32_t* count, float* part_o,
+                       float* part_lse, uint32_t* counters, float* out, float* out_lse,
+                       hipStream_t st);
 
 }  // namespace bsa

@@ -48,10 +48,13 @@ __device__ __forceinline__ int select_block_scan(int v, SelectLds& s, int& total
 // first among equal ones), appends the forced entries f0 .. f1-1, writes them
 // ascending to out[0 .. budget) padded with -1, and the number chosen to *count.
 // Every thread of the work-group must call it (it synchronises the group).
+// COHERENT: read the scores as device-scope loads (they were stored by other
+// work-groups of the same launch).
+template <bool COHERENT = false>
 __device__ __forceinline__ void select_unit_rows(const float* row, int C, int picks, int f0,
                                                  int f1, int budget, int32_t* out,
                                                  int32_t* count, SelectLds& s) {
-  auto score_at = [&](int i) -> float { return row[i]; };
+  auto score_at = [&](int i) -> float { return COHERENT ? load_coherent(row + i) : row[i]; };
   const int tid = threadIdx.x;
   picks = max(0, min(picks, C));
   const int per = ceil_div(C, kSelectThreads);
@@ -61,8 +64,21 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
   const bool in_regs = per <= kSelectRegKeys;
   uint32_t rk[kSelectRegKeys];
   if (in_regs) {
+    if constexpr (COHERENT) {
+      // device-scope loads are not reordered by the compiler: issue them all
+      // before the first is used (indices past the thread's range are clamped
+      // into the row and their values dropped)
+      float f[kSelectRegKeys];
+      const int last = max(C - 1, 0);
 #pragma unroll
-    for (int j = 0; j < kSelectRegKeys; ++j) rk[j] = i0 + j < i1 ? score_key(score_at(i0 + j)) : 0u;
+      for (int j = 0; j < kSelectRegKeys; ++j) f[j] = score_at(min(i0 + j, last));
+#pragma unroll
+      for (int j = 0; j < kSelectRegKeys; ++j) rk[j] = i0 + j < i1 ? score_key(f[j]) : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelectRegKeys; ++j)
+        rk[j] = i0 + j < i1 ? score_key(score_at(i0 + j)) : 0u;
+    }
   }
   auto for_each_key = [&](auto&& f) {
     if (in_regs) {

@@ -16,19 +16,34 @@ from . import binding as bsa
 from .workloads import BLOCK, HEAD_DIM, Workload
 
 
-def default_splits(units: int, budget: int, granularity: str) -> int:
-    """Split count that gives the attention launch about 512 work-groups.
+def default_splits(units: int, budget: int, granularity: str, one_launch: bool = False) -> int:
+    """Split count of the attention.
 
-    The attention kernel runs three waves per SIMD, so 512 four-wave groups are
-    resident on 256 CUs at once; more, smaller splits only add merge work. A
-    split keeps at least two blocks (block mode) or 64 tokens (token mode).
+    Separate attention launch: about 512 work-groups. The kernel runs three
+    waves per SIMD, so 512 four-wave groups are resident on 256 CUs at once;
+    more, smaller splits only add merge work (and, with the selection in the
+    attention prologue, more copies of it). A split keeps at least two blocks
+    (block mode) or 64 tokens (token mode).
+
+    One-launch decode step (block mode): four blocks per split. The selection
+    is made once per unit there, and short attention items shorten the end of
+    the launch, when the last units' attention runs after their scan.
     """
+    if one_launch and granularity != "token":
+        return max(1, min(budget // 4, 1024))
     s = max(1, math.ceil(512 / max(units, 1)))
     if granularity == "token":
         s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
     else:
         s = min(s, max(1, budget // 2))
     return max(1, min(s, budget))
+
+
+def one_launch_pays(units: int, max_blocks: int, granularity: str) -> bool:
+    """Whether the one-launch decode step beats scan + select_attend_combine:
+    in block mode once the scan covers at least 16384 blocks (measured on
+    MI355X: +0.4% at 64 x 1024 blocks, +6% with ragged lengths, -23% at 8 x 256)."""
+    return granularity != "token" and units * max_blocks >= 16384
 
 
 @dataclasses.dataclass
@@ -60,7 +75,7 @@ class DeviceStep:
     part_lse: "torch.Tensor"
     out: "torch.Tensor"
     out_lse: "torch.Tensor"
-    counters: "torch.Tensor"  # arrival counters of attend_combine (zero between calls)
+    counters: "torch.Tensor"  # counters of attend_combine / decode_step (zero between calls)
 
     @property
     def block_mode(self) -> bool:
@@ -153,13 +168,24 @@ class DeviceStep:
         self.score_select(stream)
         self.attend_combine(stream)
 
+    # -- the whole step as one call -------------------------------------------
+    def decode_step(self, stream=None) -> None:
+        """bsa_decode_step: one launch in block mode."""
+        bsa.decode_step(self.layout, self.cfg, self.q, self.codes, self.scales,
+                        self.global_scale, self.key_center, self.kproj, self.proj, self.k,
+                        self.v, self.seq_lens, self.tail_k, self.tail_v, self.splits,
+                        self.scores, self.workspace, self.ws_bytes, self.idx, self.count,
+                        self.part_o, self.part_lse, self.counters, self.out, self.out_lse,
+                        stream)
+
 
 def upload(w: Workload, device="cuda", splits: Optional[int] = None,
-           kv_dtype: str = "f16") -> DeviceStep:
+           kv_dtype: str = "f16", one_launch: bool = False) -> DeviceStep:
     """Copy a workload to the GPU and allocate every buffer of the step.
 
     ``kv_dtype="bf16"`` stores K and V as bfloat16 instead (values rounded from
-    the fp16 draws), for the BF16-cache variant.
+    the fp16 draws), for the BF16-cache variant. ``one_launch`` picks the
+    default split count for decode_step's single launch.
     """
     import torch
 
@@ -177,7 +203,7 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
                          w.softmax_scale)
     if splits is None:
-        splits = default_splits(B * Hkv, s.budget, s.granularity)
+        splits = default_splits(B * Hkv, s.budget, s.granularity, one_launch)
     nb = s.max_blocks
     codes = scales = kproj = proj = None
     if gran == bsa.BLOCK:

@@ -218,12 +218,15 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
  * work-group of each unit to finish, so the merge hides behind other units'
  * attention (with more it launches the merge separately). That group is found
  * with one arrival counter per unit in `counters` (device, bsa_counters_size
- * bytes): it must be zero-filled before its first use, every call that
- * completes leaves it zero, and calls that share it must not run concurrently.
- * No work-group ever waits for another.
+ * bytes, of which these calls use the first 4 * batch * num_kv_heads): it must
+ * be zero-filled before its first use, every call that completes leaves it
+ * zero, and calls that share it must not run concurrently. In these calls no
+ * work-group ever waits for another; bsa_decode_step's waits are described
+ * there.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of the arrival counters: 4 * batch * num_kv_heads (0 for a bad layout). */
+/* Bytes of the counters: 4 * (33 * batch * num_kv_heads + 257) (0 for a bad
+ * layout). */
 size_t bsa_counters_size(const bsa_kv_layout* layout);
 
 /* bsa_score_scan then bsa_select_topk; arguments as there. */
@@ -257,6 +260,35 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
                               const uint16_t* tail_v, int32_t num_splits, int32_t* idx,
                               int32_t* count, float* part_o, float* part_lse,
                               uint32_t* counters, float* out, float* out_lse, void* stream);
+
+/* One whole decode step: bsa_score_scan, bsa_select_topk and
+ * bsa_attend_combine, with identical outputs (scores, idx, count, part_o,
+ * part_lse, out, out_lse); arguments as there, the block-mode key copy (codes,
+ * scales, global_scale, key_center) or the token-mode one (kproj, proj) as the
+ * granularity needs. counters: bsa_counters_size bytes, zero-filled before the
+ * first use.
+ *
+ * In block mode with budget <= 1024 this is one launch (Jet-QSparse abstract:
+ * a dense scan of the 4-bit keys, a per-KV-head block selection, then sparse
+ * aggregation of the chosen blocks). Its work-groups take work items in the
+ * order of a ticket counter, the scan items ahead of the attention items; a
+ * unit's attention items poll until the unit's scan items have stored their
+ * scores. Those scan items hold earlier tickets, so they are already running
+ * and never wait themselves: every wait ends. A wait is also bounded (about a
+ * second, far beyond any correct run); past the bound the launch still ends,
+ * its outputs are undefined, and the last counter word is set and stays set
+ * (all other words return to zero). Calls sharing counters
+ * must not run concurrently. Otherwise (token mode, larger budgets) it runs
+ * the three calls in turn; workspace is bsa_select_topk's (unused in block
+ * mode). */
+int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                    const float* key_center, const uint16_t* kproj, const float* proj,
+                    const void* k, const void* v, const int32_t* seq_lens,
+                    const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
+                    float* scores, void* workspace, size_t workspace_bytes, int32_t* idx,
+                    int32_t* count, float* part_o, float* part_lse, uint32_t* counters,
+                    float* out, float* out_lse, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* bsa_last_error(void);

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["bsa_pack_kv_cache", "bsa_score_scan", "bsa_select_topk",
               "bsa_sparse_decode_attn", "bsa_combine", "bsa_workspace_size",
-              "bsa_last_error", "bsa_version"]:
+              "bsa_decode_step", "bsa_last_error", "bsa_version"]:
         assert n in names, n
 
 
@@ -139,4 +139,29 @@ def test_combined_calls_check_their_arguments(lib):
                                        FAKE, None, 0, None, None, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        FAKE, None, None)
     assert rc == -4
-    assert lib.bsa_counters_size(ctypes.byref(L)) == 4
+    # per unit: a merge arrival word and a 128-byte scan-done line; 8 ticket
+    # lines; the fault flag
+    assert lib.bsa_counters_size(ctypes.byref(L)) == 4 * (33 + 257)
+    assert lib.bsa_counters_size(ctypes.byref(_layout(batch=3, num_kv_heads=2))) == 4 * (198 + 257)
+
+
+def test_decode_step_checks_every_stage_first(lib):
+    L, cfg = _layout(), B.select_cfg(B.BLOCK, 8)
+    tok = B.select_cfg(B.TOKEN, 64, 0, 32)
+
+    def step(c, codes=FAKE, kproj=None, splits=2, scores=FAKE, ws_bytes=0, counters=FAKE,
+             out=FAKE, k=FAKE):
+        return lib.bsa_decode_step(
+            ctypes.byref(L), ctypes.byref(c), FAKE, codes, FAKE, FAKE, None, kproj, FAKE, k,
+            FAKE, FAKE, None, None, splits, scores, None, ws_bytes, FAKE, FAKE, FAKE, FAKE,
+            counters, out, None, None)
+
+    assert step(cfg, codes=None) == -1  # the scan's key copy
+    assert "codes" in lib.bsa_last_error().decode()
+    assert step(cfg, scores=None) == -1
+    assert step(cfg, k=FAKE + 2) == -1  # attention operands
+    assert step(cfg, splits=9) == -1 and "num_splits" in lib.bsa_last_error().decode()
+    assert step(cfg, counters=None) == -4
+    assert step(cfg, out=None) == -1
+    assert step(tok, codes=None, kproj=FAKE) == -4  # token mode: the selection's workspace
+    assert step(tok, codes=None, kproj=None) == -1

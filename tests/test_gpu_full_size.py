@@ -1,8 +1,9 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Each workload is drawn at its full size (up to 128K tokens, batch 16), packed,
-and run through the same calls bench.py times: score_scan and
-select_attend_combine with the default split count. Every stage of a few sampled units
+and run through the same calls bench.py times by default, with its default split
+count: one decode_step launch where that pays off (block mode, at least 16384
+scanned blocks), else score_scan and select_attend_combine. Every stage of a few sampled units
 (the first, the last and one in between) is then checked against the oracle:
 pack bytes bit-exact, scores within the FP32 accumulation bound, the selection
 bit-exact on the GPU's own scores, outputs within 2e-3.
@@ -15,7 +16,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from block_sparse_attention_pack_amd import workloads as W
-from block_sparse_attention_pack_amd.step import upload
+from block_sparse_attention_pack_amd.step import one_launch_pays, upload
 
 import parity_util as PU
 
@@ -41,14 +42,19 @@ def test_full_size_sampled_units(name):
     spec = W.SPECS[name]
     print(f"[full] {name}: generating", flush=True)
     w = W.generate(spec, threads=16)
-    d = upload(w)  # the default split count, as bench.py uses
+    one = one_launch_pays(spec.units, spec.max_blocks, spec.granularity)
+    d = upload(w, one_launch=one)  # the default split count, as bench.py uses
     d.pack()
-    d.scan()
-    d.select_attend_combine()
+    if one:
+        d.decode_step()
+    else:
+        d.scan()
+        d.select_attend_combine()
     torch.cuda.synchronize()
     assert int(d.counters.abs().sum()) == 0
     units = _sampled_units(spec)
-    print(f"[full] {name}: splits {d.splits}, checking units {units}", flush=True)
+    print(f"[full] {name}: {'decode_step' if one else 'two calls'}, splits {d.splits}, "
+          f"checking units {units}", flush=True)
     sys.stdout.flush()
     PU.check_units(w, d, units)
     del d

@@ -94,16 +94,21 @@ def test_query_group_sizes(G):
     _two_calls_match(d)
 
 
+STEP_OUT = ("scores", "idx", "count", "part_o", "part_lse", "out", "out_lse")
+
+
 def _two_calls_match(d):
-    """score_scan + select_attend_combine reproduce the four calls' bits."""
-    ref = [host(t).copy() for t in (d.idx, d.count, d.out, d.out_lse)]
-    for t in (d.idx, d.count, d.out, d.out_lse):
-        t.fill_(7)
-    d.run_two()
-    torch.cuda.synchronize()
-    for a, b in zip(ref, (host(d.idx), host(d.count), host(d.out), host(d.out_lse))):
-        assert np.array_equal(a, b, equal_nan=True)
-    assert int(d.counters.abs().sum()) == 0
+    """score_scan + select_attend_combine, and decode_step, reproduce the four
+    calls' bits (and leave every counter at zero)."""
+    ref = [host(getattr(d, n)).copy() for n in STEP_OUT]
+    for run in (d.run_two, d.decode_step):
+        for n in STEP_OUT:
+            getattr(d, n).fill_(7)
+        run()
+        torch.cuda.synchronize()
+        for n, a in zip(STEP_OUT, ref):
+            assert np.array_equal(a, host(getattr(d, n)), equal_nan=True), (run.__name__, n)
+        assert int(d.counters.abs().sum()) == 0
 
 
 def test_select_attend_combine_above_the_in_kernel_budget():
@@ -228,7 +233,7 @@ def test_fused_calls_match_the_four_calls(name):
     ref = [host(t).copy() for t in (d.scores, d.idx, d.count, d.out, d.out_lse)]
     for t in (d.scores, d.idx, d.count, d.out, d.out_lse):
         t.fill_(7)
-    for run in (d.run_fused, d.run_two):
+    for run in (d.run_fused, d.run_two, d.decode_step):
         for rep in range(3):  # the arrival counters must return to zero every call
             for t in (d.idx, d.count, d.out, d.out_lse):
                 t.fill_(7)
@@ -272,4 +277,43 @@ def test_attend_combine_on_both_sides_of_the_merge_limit(splits):
         for a, b in zip(ref, (host(d.out), host(d.out_lse))):
             assert np.array_equal(a, b, equal_nan=True), (splits, rep)
         assert int(d.counters.abs().sum()) == 0
+    check_all(w, d)
+
+
+def test_decode_step_with_short_sequences_tails_and_many_splits():
+    """One launch: empty, sub-block and ragged sequences, 0-2 tail pages, and
+    split counts on both sides of the merge's fast path, call after call."""
+    lengths = (0, 1, 129, 300, 2000, 4096)
+    for n_tail in (0, 2):
+        spec = dataclasses.replace(W.SPECS["ragged"], name=f"step_short{n_tail}", seed=85 + n_tail,
+                                   batch=len(lengths), kv_heads=2, q_heads=8, max_tokens=4096,
+                                   budget=12, n_tail=n_tail, needle_count=2, lengths=lengths)
+        w = W.generate(spec)
+        for splits in (1, 6, 12):
+            _say(f"[parity] {spec.name} splits {splits}")
+            d = run_step(w, splits=splits)
+            _two_calls_match(d)
+            _two_calls_match(d)
+            check_all(w, d)
+
+
+def test_decode_step_bf16_cache_and_large_group():
+    for G, kv_dtype in ((4, "bf16"), (16, "f16")):
+        spec = dataclasses.replace(W.reduced("jetqsparse", 8192, batch=2), name=f"step_g{G}",
+                                   seed=95 + G, q_heads=4 * G)
+        w = W.generate(spec)
+        d = run_step(w, kv_dtype=kv_dtype)
+        _two_calls_match(d)
+        # the oracle sees the keys and values the GPU holds
+        check_all(dataclasses.replace(w, k=host(d.k.float()), v=host(d.v.float())), d)
+
+
+@pytest.mark.parametrize("splits", [16, 32, 64])
+def test_decode_step_merges_many_splits(splits):
+    """The one-launch step merges up to 16 and 32 splits in one pass, more in
+    two: the four calls' bits either way."""
+    spec = W.reduced("jetqsparse", 16384, batch=2, budget=64)
+    w = W.generate(spec)
+    d = run_step(w, splits=splits)
+    _two_calls_match(d)
     check_all(w, d)
