@@ -40,10 +40,11 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # rocprofv3 counter summaries of a kernel's HBM traffic (FETCH_SIZE + WRITE_SIZE,
 # calibrated on a copy of known size) in profiles/<kernel>.<workload>.traffic.md,
 # valid while the kernel's sources (listed here) are unchanged
-TRAFFIC_SOURCES = {
-    "scan_block_kernel": ["scan.hip", "scan_core.hpp", "common.hpp"],
-    "step_kernel": ["step.hip", "scan_core.hpp", "attn_core.hpp", "select_core.hpp",
-                    "combine_core.hpp", "common.hpp"],
+TRAFFIC_SOURCES = {  # kernel: (file name stem, sources)
+    "scan_block_kernel": ("scan_block_kernel", ["scan.hip", "scan_core.hpp", "common.hpp"]),
+    "scan_token_kernel<32>": ("scan_token_kernel_r32", ["scan.hip", "common.hpp"]),
+    "step_kernel": ("step_kernel", ["step.hip", "scan_core.hpp", "attn_core.hpp",
+                                    "select_core.hpp", "combine_core.hpp", "common.hpp"]),
 }
 
 
@@ -84,11 +85,12 @@ def measured_traffic(kernel: str, workload: str):
     covers another kernel or workload, or the kernel's sources changed since."""
     if kernel not in TRAFFIC_SOURCES:
         return None
+    stem, sources = TRAFFIC_SOURCES[kernel]
     try:
-        with open(os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.md")) as f:
+        with open(os.path.join(ROOT, "profiles", f"{stem}.{workload}.traffic.md")) as f:
             fields = dict(re.findall(r"^(\w+): (\S+)$", f.read(), re.M))
         h = hashlib.sha256()
-        for name in TRAFFIC_SOURCES[kernel]:
+        for name in sources:
             with open(os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", name), "rb") as f:
                 h.update(f.read())
     except OSError:
