@@ -135,8 +135,8 @@ int check_scan_args(const bsa_select_cfg* cfg, const void* q, const uint8_t* cod
                 BSA_ERR_INVALID_ARG,
                 "block mode needs codes, scales (16-byte aligned) and global_scale");
   else
-    BSA_REQUIRE(kproj && proj && aligned16(kproj), BSA_ERR_INVALID_ARG,
-                "token mode needs kproj (16-byte aligned) and proj");
+    BSA_REQUIRE(kproj && proj && aligned16(kproj) && aligned16(scores), BSA_ERR_INVALID_ARG,
+                "token mode needs kproj and scores (16-byte aligned) and proj");
   return BSA_OK;
 }
 

@@ -61,11 +61,6 @@ __device__ __forceinline__ void split_bf16(const half8& q, bf16x8& hi, bf16x8& l
   }
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 struct AttnArgs {
   const _Float16* q;
@@ -471,7 +466,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, bool block_mode, in
     const int tend = min(t0 + kChunkGroups, nmine);
     int* stage = stage_lds[wave];
     if (t0 > 0) stage_chunk(t0, tend);  // the first chunk was staged before the loop
-    wave_lds_fence();
+    wave_lds_sync();
     // ---- phase 1: keys stream through a ring of kDepth slots; QK^T -> sc ----
     // Every slot is always issued (groups past the chunk are null groups), so
     // the ring registers are defined on every path.
@@ -496,7 +491,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, bool block_mode, in
         }
       }
     }
-    wave_lds_fence();
+    wave_lds_sync();
     __builtin_amdgcn_sched_barrier(0);
     // the value ring's first groups go out now, so their latency overlaps the
     // softmax (every slot is issued; groups past the chunk are null groups)
@@ -530,7 +525,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, bool block_mode, in
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha;
     }
-    wave_lds_fence();
+    wave_lds_sync();
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase 3: values stream through the ring; PV -----------------------
     {
@@ -547,7 +542,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, bool block_mode, in
         }
       }
     }
-    wave_lds_fence();
+    wave_lds_sync();
     __builtin_amdgcn_sched_barrier(0);
   }
 

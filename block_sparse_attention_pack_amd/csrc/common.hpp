@@ -109,6 +109,13 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// Orders a wave's LDS writes before its later LDS reads (of other lanes' data).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // --- device-wide hand-off between work-groups of one launch -----------------
 // The attention kernel's merge passes the split partials from every
 // work-group of a unit to the unit's last one. Those values are stored and

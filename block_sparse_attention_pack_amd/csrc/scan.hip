@@ -2,7 +2,7 @@
 //
 // Token mode (JSSA Figure 1): qbar = mean of the group's query heads,
 // p = P^T qbar in FP32 once per work-group, then each token's score is
-// sigma * p . kproj_t, streamed 64 B per token with 16-byte loads.
+// sigma * p . kproj_t, streamed 2R bytes per token in contiguous 1 KiB loads.
 #include "scan_core.hpp"
 #include "select_core.hpp"
 
@@ -15,11 +15,17 @@ __global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
-// scores kTokPerWg / 4 consecutive tokens, one token per lane and step: a lane
-// reads its token's whole projected row (R bf16 = R / 8 16-byte loads; together
-// the wave's loads cover 64 consecutive rows, whole cache lines) and forms the
-// dot product with p in its own registers, so the 64 scores of a step leave in
-// one coalesced store.
+// scores kTokPerWg / 4 consecutive tokens, 64 per step. A token's projected row
+// is R bf16, i.e. R / 8 pieces of 16 bytes, and a step's 64 rows are R / 8
+// contiguous 1 KiB slices: lane l loads piece l % (R / 8) of token l / (R / 8)
+// of each slice, so every load instruction reads one contiguous KiB. A lane
+// forms the dot product of its piece with the matching 8 entries of p, the
+// R / 8 lanes of a token add theirs, and one exchange per slice moves token
+// t's score to lane t. The scores collect in LDS and leave after the
+// work-group's last read, in contiguous 16-byte-per-lane stores: stores
+// spread among the reads cost the HBM far more than their own bytes (23 us of
+// 120 at 128K context, batch 8, 8 KV heads). The next step's rows are loaded
+// before the current ones are scored, and the first step's before p is formed.
 constexpr int kTokPerWg = 16384;
 
 template <int R>
@@ -28,19 +34,49 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
     const float* __restrict__ proj, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma) {
   static_assert(R % 8 == 0 && R <= 128, "rank");
-  constexpr int kVec = R / 8;               // 16-byte loads per token row
-  constexpr bool kPinReg = R <= 32;         // p in registers (else read from LDS)
-  constexpr int kUnroll = 1;                // tokens per lane in flight
+  constexpr int kLpt = R / 8;         // lanes per token (one 16-byte piece each)
+  constexpr int kTps = kWave / kLpt;  // tokens per 1 KiB slice
+  constexpr int kSlices = kLpt;       // slices per 64-token step
+  constexpr int kPerWave = kTokPerWg / 4;
   __shared__ float qbar[kHeadDim];
   __shared__ float part[256];
   __shared__ float p_lds[R];
+  __shared__ __attribute__((aligned(16))) float keep[4][kPerWave];  // the scores, until the end
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit % Hkv;
   const int L = clamp_len(seq_lens[b], Tmax);
+  const int t_wave = blockIdx.x * kTokPerWg + wave * kPerWave;
+  const int t_end = min(t_wave + kPerWave, Tmax);
+  const uint16_t* base = kproj + int64_t(unit) * Tmax * R;
+  float* out = scores + int64_t(unit) * Tmax;
+  const int piece = lane % kLpt, tok_in_slice = lane / kLpt;
+
+  // the 16-byte pieces this lane holds of the step at t0 (rows past t_end,
+  // only possible in a partial last step, read row t0 instead and are dropped)
+  auto load_step = [&](uint4v (&w)[kSlices], int t0) {
+#pragma unroll
+    for (int c = 0; c < kSlices; ++c) {
+      const int t = t0 + c * kTps + tok_in_slice;
+      w[c] = reinterpret_cast<const uint4v*>(base + int64_t(t < t_end ? t : t0) * R)[piece];
+    }
+  };
+  // the first step's rows are in flight while p is formed
+  uint4v wa[kSlices], wb[kSlices];
+  if (t_wave < t_end) load_step(wa, t_wave);
 
   // qbar = (sum of the group's queries) / G, then p = sigma * P^T qbar, in
-  // float32; every thread issues all its loads of a stage before using them.
+  // float32. The thread's entries of P are loaded with the queries, before
+  // the first barrier.
+  constexpr int kChunks = 256 / R;  // threads per output channel
+  constexpr int kDPer = kHeadDim / kChunks;
+  const int jj = threadIdx.x % R, ch = threadIdx.x / R;
+  float pv[kDPer];
+  {
+    const float* pc = proj + (int64_t(h) * kHeadDim + ch * kDPer) * R + jj;
+#pragma unroll
+    for (int i = 0; i < kDPer; ++i) pv[i] = pc[int64_t(i) * R];
+  }
   if (threadIdx.x < kHeadDim) {
     const _Float16* qd = q + (int64_t(b) * Hq + h * G) * kHeadDim + threadIdx.x;
     float qs = 0.0f;
@@ -49,19 +85,9 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   }
   __syncthreads();
   {
-    constexpr int kChunks = 256 / R;  // threads per output channel
-    constexpr int kDPer = kHeadDim / kChunks;
-    const int jj = threadIdx.x % R, ch = threadIdx.x / R;
-    constexpr int kBatch = kDPer < 16 ? kDPer : 16;
-    const float* pc = proj + (int64_t(h) * kHeadDim + ch * kDPer) * R + jj;
     float acc = 0.0f;
-    for (int i0 = 0; i0 < kDPer; i0 += kBatch) {
-      float pv[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) pv[i] = pc[int64_t(i0 + i) * R];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) acc += pv[i] * qbar[ch * kDPer + i0 + i];
-    }
+    for (int i = 0; i < kDPer; ++i) acc += pv[i] * qbar[ch * kDPer + i];
     part[threadIdx.x] = acc;
     __syncthreads();
     if (threadIdx.x < R) {
@@ -71,41 +97,47 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
     }
     __syncthreads();
   }
-  float p[kPinReg ? R : 1];
-  if constexpr (kPinReg) {
+  float pq[8];  // the entries of p that meet this lane's piece
 #pragma unroll
-    for (int j = 0; j < R; ++j) p[j] = p_lds[j];
-  }
+  for (int e = 0; e < 8; ++e) pq[e] = p_lds[8 * piece + e];
 
-  const int t_wave = blockIdx.x * kTokPerWg + wave * (kTokPerWg / 4);
-  const uint16_t* base = kproj + int64_t(unit) * Tmax * R;
-  float* out = scores + int64_t(unit) * Tmax;
-  const int t_end = min(t_wave + kTokPerWg / 4, Tmax);
-  for (int t0 = t_wave; t0 < t_end; t0 += kUnroll * kWave) {
-    uint4v w[kUnroll][kVec];
+  // the 64 scores of the step at t0 from its landed pieces, stored by lane t
+  auto score_step = [&](const uint4v (&w)[kSlices], int t0) {
+    float mine = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kWave + lane;
-      const uint4v* row = reinterpret_cast<const uint4v*>(base + int64_t(t < t_end ? t : t_wave) * R);
-#pragma unroll
-      for (int c = 0; c < kVec; ++c) w[u][c] = row[c];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kWave + lane;
+    for (int c = 0; c < kSlices; ++c) {
       float s = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kVec; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 8 * c + 2 * e;
-          const float p0 = kPinReg ? p[kPinReg ? j : 0] : p_lds[j];
-          const float p1 = kPinReg ? p[kPinReg ? j + 1 : 0] : p_lds[j + 1];
-          s = __builtin_fmaf(p0, bf16_bits_to_float(w[u][c][e] & 0xFFFFu), s);
-          s = __builtin_fmaf(p1, bf16_bits_to_float(w[u][c][e] >> 16), s);
-        }
+      for (int e = 0; e < 4; ++e) {
+        s = __builtin_fmaf(pq[2 * e], bf16_bits_to_float(w[c][e] & 0xFFFFu), s);
+        s = __builtin_fmaf(pq[2 * e + 1], bf16_bits_to_float(w[c][e] >> 16), s);
       }
-      if (t < t_end) out[t] = t < L ? s : -__builtin_inff();
+#pragma unroll
+      for (int off = 1; off < kLpt; off <<= 1) s += __shfl_xor(s, off, kWave);
+      // token c * kTps + k is complete in lane k * kLpt
+      const float v = __shfl(s, (lane % kTps) * kLpt, kWave);
+      if (lane / kTps == c) mine = v;
+    }
+    const int t = t0 + lane;
+    if (t < t_end) keep[wave][t - t_wave] = t < L ? mine : -__builtin_inff();
+  };
+  // the next step's rows are in flight while a step is scored (a deeper
+  // pipeline measured slower)
+  for (int t0 = t_wave; t0 < t_end; t0 += 2 * kWave) {
+    if (t0 + kWave < t_end) load_step(wb, t0 + kWave);
+    score_step(wa, t0);
+    if (t0 + kWave >= t_end) break;
+    if (t0 + 2 * kWave < t_end) load_step(wa, t0 + 2 * kWave);
+    score_step(wb, t0 + kWave);
+  }
+  // the wave's scores, 1 KiB per store instruction (its own LDS rows: no barrier)
+  wave_lds_sync();
+  const int n = t_end > t_wave ? t_end - t_wave : 0;
+  for (int i = 4 * lane; i < n; i += 4 * kWave) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<float4v*>(out + t_wave + i) = *reinterpret_cast<const float4v*>(&keep[wave][i]);
+    } else {
+      for (int k = i; k < n; ++k) out[t_wave + k] = keep[wave][k];
     }
   }
 }

@@ -147,7 +147,7 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  *   p = P[h]^T qbar, scores[b][h][t] = sigma * p . kproj[b][h][t] for t < L_b,
  *   -inf beyond. kproj, proj required; codes, scales, global_scale unused.
  * scores: device float [B][Hkv][max_tokens/128] (BLOCK) or [B][Hkv][max_tokens]
- * (TOKEN); every entry is written. */
+ * (TOKEN, 16-byte aligned); every entry is written. */
 int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                    const float* key_center, const uint16_t* kproj, const float* proj,
