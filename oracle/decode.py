@@ -344,21 +344,46 @@ def combine(part_o: np.ndarray, part_lse: np.ndarray) -> Tuple[np.ndarray, np.nd
 
 # --------------------------------------------------------------------------
 # A6: projected-key cache for token mode (JSSA Figure 1: keys projected onto a
-# rank-r basis common to the heads; Figure 10: the cache held in BF16)
+# rank-r basis common to the heads; Figure 10: the cache held in BF16 or FP8)
 #
-# Reading: kproj[t, j] = BF16(acc), acc the float32 sum over d ascending of
-# fl32(P[d, j] * k[t, d]), each addition rounded to float32, no fused multiply-add.
+# Reading: acc[t, j] is the float32 sum over d ascending of fl32(P[d, j] *
+# k[t, d]), each addition rounded to float32, no fused multiply-add; the cache
+# holds BF16(acc) (round to nearest even), or for the FP8 cache E4M3FN(acc)
+# element by element (nearest, ties to even, saturating at 448, no further
+# scale: the figure names only the storage precision).
 # --------------------------------------------------------------------------
 
-def project_keys(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
-    """Keys [n, 128] (fp16 values) and P [128, r] (float32) -> BF16 bits [n, r]."""
+PROJ_FORMATS = ("bf16", "fp8")
+
+
+def project_keys_f32(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """Keys [n, 128] (fp16 values) and P [128, r] (float32) -> float32 acc [n, r]."""
     kf = np.asarray(k_rows).astype(F32)
     P = np.asarray(proj, dtype=F32)
     acc = np.zeros((kf.shape[0], P.shape[1]), dtype=F32)
     for d in range(HEAD_DIM):
         prod = (kf[:, d:d + 1] * P[d][None, :]).astype(F32)
         acc = (acc + prod).astype(F32)
+    return acc
+
+
+def project_keys(k_rows: np.ndarray, proj: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """The cache entries: BF16 bits (uint16) or E4M3 codes (uint8), [n, r]."""
+    acc = project_keys_f32(k_rows, proj)
+    if fmt == "fp8":
+        return nvfp4.e4m3_encode(acc)
+    if fmt != "bf16":
+        raise ValueError(fmt)
     return f32_to_bf16_bits(acc)
+
+
+def proj_values(kproj: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """Real values of cache entries."""
+    if fmt == "fp8":
+        return nvfp4.e4m3_decode(kproj)
+    if fmt != "bf16":
+        raise ValueError(fmt)
+    return bf16_bits_to_f64(kproj)
 
 
 # --------------------------------------------------------------------------
@@ -367,11 +392,11 @@ def project_keys(k_rows: np.ndarray, proj: np.ndarray) -> np.ndarray:
 #   qbar = mean_h q_h,  p = P^T qbar,  score_t = sigma * p . kproj_t   (t < L)
 # --------------------------------------------------------------------------
 
-def scan_token_unit(q_group: np.ndarray, kproj_bits: np.ndarray, proj: np.ndarray,
-                    seq_len: int, sigma: float) -> np.ndarray:
+def scan_token_unit(q_group: np.ndarray, kproj: np.ndarray, proj: np.ndarray,
+                    seq_len: int, sigma: float, fmt: str = "bf16") -> np.ndarray:
     qbar = np.asarray(q_group, dtype=np.float64).mean(axis=0)
     p = np.asarray(proj, dtype=np.float64).T @ qbar  # [r]
-    kt = bf16_bits_to_f64(kproj_bits)  # [T, r]
+    kt = proj_values(kproj, fmt)  # [T, r]
     scores = sigma * (kt @ p)
     scores[np.arange(kt.shape[0]) >= seq_len] = -np.inf
     return scores

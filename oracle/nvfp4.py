@@ -87,6 +87,18 @@ def e2m1_encode(x) -> np.ndarray:
     return code.astype(np.uint8).reshape(x.shape)
 
 
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3FN code of a signed value (ties to even, saturating at 448,
+    never NaN); the sign bit is copied from x, so -0 is 0x80."""
+    x = np.asarray(x, dtype=np.float32)
+    if np.any(np.isnan(x)):
+        raise ValueError("no NaN input")
+    mag = np.minimum(np.abs(x.astype(np.float64)).ravel(), _E4M3_POS_VALUES[-1])
+    idx = _nearest_even(mag, _E4M3_POS_VALUES, _E4M3_POS_CODES)
+    code = _E4M3_POS_CODES[idx] | (np.signbit(x.ravel()).astype(np.int64) << 7)
+    return code.astype(np.uint8).reshape(x.shape)
+
+
 def e4m3_encode_nonneg(x) -> np.ndarray:
     """Nearest non-negative E4M3FN code (ties to even, saturating at 448)."""
     x = np.asarray(x, dtype=np.float64)

@@ -92,3 +92,34 @@ def test_e2m1_sign_copied_and_negative_zero():
     assert int(nvfp4.e2m1_encode(np.float32(-0.0))) == 8
     assert int(nvfp4.e2m1_encode(np.float32(-0.2))) == 8
     assert int(nvfp4.e2m1_encode(np.float32(0.2))) == 0
+
+
+def test_signed_e4m3_encode_points():
+    for x, code in _golden("e4m3s_enc"):
+        got = int(nvfp4.e4m3_encode(np.float32(float(x))))
+        assert got == int(code, 16), (x, code, got)
+
+
+def test_signed_e4m3_every_finite_code_round_trips():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        v = nvfp4.e4m3_value(c)
+        assert int(nvfp4.e4m3_encode(np.float32(-0.0 if c == 0x80 else v))) == c
+
+
+def test_signed_e4m3_is_nearest_with_even_ties_brute_force():
+    # the definition, written out: the finite value nearest to x, the code with
+    # an even mantissa among equally near ones, the sign of x
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(3000) * 3, rng.uniform(-500, 500, 1000),
+                        rng.uniform(-0.02, 0.02, 1000),
+                        (rng.integers(-900, 900, 1000) * 2.0 ** -10)]).astype(np.float32)
+    mags = [nvfp4.e4m3_value(c) for c in range(0x7F)]
+    for xi, ci in zip(x, nvfp4.e4m3_encode(x)):
+        a = min(abs(float(xi)), 448.0)
+        d = [abs(a - m) for m in mags]
+        best = [c for c in range(0x7F) if d[c] == min(d)]
+        want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        want |= 0x80 if np.signbit(xi) else 0
+        assert int(ci) == want, (float(xi), int(ci), want)

@@ -205,3 +205,59 @@ def test_token_select_and_gather_free_rows():
     v = rng.standard_normal((T, 128)).astype(np.float16)
     kr, vr = O.gather_rows_token(k, v, idx[:cnt])
     assert np.array_equal(kr, k[idx[:cnt]].astype(np.float64))
+
+
+# ---------------------------------------------------------------- FP8 projected cache
+
+def _e4m3_nearest_even(x):
+    """Brute-force E4M3FN encode of float32 values (the format definition)."""
+    from oracle import nvfp4
+
+    mags = np.array([nvfp4.e4m3_value(c) for c in range(0x7F)])
+    out = []
+    for xi in np.asarray(x, dtype=np.float32).ravel():
+        a = min(abs(float(xi)), 448.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+        out.append(c | (0x80 if np.signbit(xi) else 0))
+    return np.array(out, dtype=np.uint8).reshape(np.shape(x))
+
+
+def test_fp8_identity_projection_gives_e4m3_of_keys():
+    rng = np.random.default_rng(21)
+    k = (rng.standard_normal((200, 128)) * np.array([0.01, 1.0, 40.0, 600.0]).repeat(32)
+         ).astype(np.float16)
+    P = np.eye(128, dtype=np.float32)[:, :32]
+    got = O.project_keys(k, P, "fp8")
+    assert got.dtype == np.uint8 and np.array_equal(got, _e4m3_nearest_even(k[:, :32]))
+
+
+def test_fp8_projection_within_error_bound():
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((500, 128)).astype(np.float16)
+    P = np.linalg.qr(rng.standard_normal((128, 32)))[0].astype(np.float32)
+    got = O.proj_values(O.project_keys(k, P, "fp8"), "fp8")
+    exact = k.astype(np.float64) @ P.astype(np.float64)
+    absterm = np.abs(k.astype(np.float64)) @ np.abs(P.astype(np.float64))
+    # float32 accumulation, then E4M3: half a unit in the last place (2^-4
+    # relative for normal values, 2^-10 absolute among subnormals)
+    acc_err = 129 * 2.0 ** -24 * absterm
+    bound = acc_err + 2.0 ** -4 * (np.abs(exact) + acc_err) + 2.0 ** -10
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_fp8_token_scores_exact_for_representable_keys():
+    from oracle import nvfp4
+
+    rng = np.random.default_rng(23)
+    T, G = 300, 4
+    finite = np.array([nvfp4.e4m3_value(c) for c in range(256) if c not in (0x7F, 0xFF)])
+    k = np.zeros((T, 128), dtype=np.float16)
+    k[:, :32] = rng.choice(finite, size=(T, 32)).astype(np.float16)  # exact in fp16
+    q = rng.standard_normal((G, 128)).astype(np.float16)
+    P = np.eye(128, dtype=np.float32)[:, :32]
+    s = O.scan_token_unit(q, O.project_keys(k, P, "fp8"), P, 250, SIGMA, "fp8")
+    qbar = q.astype(np.float64).mean(axis=0)
+    exact = SIGMA * (k[:, :32].astype(np.float64) @ qbar[:32])
+    assert np.abs(s[:250] - exact[:250]).max() < 1e-12 and np.all(s[250:] == -np.inf)
