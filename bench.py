@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="jetqsparse",
-                    choices=["tiny", "llama8b", "jetqsparse", "ragged", "token"])
+                    choices=["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8"])
     ap.add_argument("--layers", type=int, default=4, help="distinct KV-cache copies rotated per step")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-dense", dest="dense", action="store_false",
@@ -161,7 +161,7 @@ def cpu_baseline(w, budget_s: float):
             rec = O.pack_unit_blocks(w.k[b, h], w.key_center[h], w.global_scale[h], 0,
                                      s.max_blocks)
         else:
-            rec = O.project_keys(w.k[b, h], w.proj[h])
+            rec = O.project_keys(w.k[b, h], w.proj[h], s.proj_fmt)
         packed.append((b, h, rec))
     log(f"[cpu] {len(packed)} units packed in {time.perf_counter() - t_start:.1f} s")
 
@@ -177,7 +177,7 @@ def cpu_baseline(w, budget_s: float):
             idx, _ = O.select_blocks_unit(sc, L, s.n_tail, s.budget)
             rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
         else:
-            sc = O.scan_token_unit(qg, rec, w.proj[h], L, sigma)
+            sc = O.scan_token_unit(qg, rec, w.proj[h], L, sigma, s.proj_fmt)
             idx, _ = O.select_tokens_unit(sc, L, s.budget)
             rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L])
         po, pl = O.attend_splits(qg, idx, 1, rows, sigma)
@@ -293,7 +293,8 @@ def main() -> int:
         if one_launch:
             kname = "step_kernel"
         else:
-            kname = "scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d>" % spec.rank
+            kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"
+                     % (spec.rank, ", fp8" if spec.proj_fmt == "fp8" else ""))
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(kname, spec.name),
@@ -318,7 +319,7 @@ def main() -> int:
                    "tail_pages": spec.n_tail, "splits": d0.splits, "layers_rotated": a.layers,
                    "calls": a.mode,
                    "scan": "e2m1*e4m3 -> f16 MFMA, f32 acc" if d0.block_mode
-                   else "bf16 rank-%d keys, f32" % spec.rank},
+                   else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank)},
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": nbytes["total"],
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libbsa.so")
 
 DTYPE_F16, DTYPE_BF16 = 0, 1
 BLOCK, TOKEN = 0, 1
+PROJ_BF16, PROJ_FP8 = 0, 1
 
 ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "WORKSPACE"}
 
@@ -50,6 +51,7 @@ class SelectCfg(ctypes.Structure):
         ("n_tail_pages", ctypes.c_int32),
         ("proj_rank", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("proj_dtype", ctypes.c_int32),
     ]
 
 
@@ -142,10 +144,11 @@ def layout_for(k, num_q_heads: int, dtype: Optional[int] = None) -> KvLayout:
 
 
 def select_cfg(granularity: int, budget: int, n_tail_pages: int = 0, proj_rank: int = 0,
-               softmax_scale: Optional[float] = None, head_dim: int = 128) -> SelectCfg:
+               softmax_scale: Optional[float] = None, head_dim: int = 128,
+               proj_dtype: int = PROJ_BF16) -> SelectCfg:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
-    return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale)
+    return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale, proj_dtype)
 
 
 def version() -> str:

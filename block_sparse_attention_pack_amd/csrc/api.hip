@@ -83,7 +83,14 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
     const int r = c->proj_rank;
     BSA_REQUIRE(r == 8 || r == 16 || r == 32 || r == 64 || r == 128, BSA_ERR_UNSUPPORTED,
                 "proj_rank %d: supported 8, 16, 32, 64, 128", r);
+    BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16 || c->proj_dtype == BSA_PROJ_FP8,
+                BSA_ERR_UNSUPPORTED, "proj_dtype %d", c->proj_dtype);
+    BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16 || r >= 16, BSA_ERR_UNSUPPORTED,
+                "an FP8 projected cache needs proj_rank >= 16");
   }
+  if (c->granularity == BSA_GRANULARITY_BLOCK)
+    BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16, BSA_ERR_INVALID_ARG,
+                "proj_dtype applies to token mode only (must be 0 in block mode)");
   g->B = L->batch;
   g->Hkv = L->num_kv_heads;
   g->Hq = L->num_q_heads;
@@ -126,7 +133,7 @@ hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
 // Argument checks of each stage, run before anything is enqueued (the combined
 // calls run every stage's checks first).
 int check_scan_args(const bsa_select_cfg* cfg, const void* q, const uint8_t* codes,
-                    const uint8_t* scales, const float* global_scale, const uint16_t* kproj,
+                    const uint8_t* scales, const float* global_scale, const void* kproj,
                     const float* proj, const int32_t* seq_lens, const float* scores) {
   BSA_REQUIRE(q && aligned16(q) && seq_lens && scores, BSA_ERR_INVALID_ARG,
               "q (16-byte aligned), seq_lens and scores are required");
@@ -178,13 +185,14 @@ int check_merge_args(const float* out, const uint32_t* counters) {
 
 hipError_t launch_scan(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
                        const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                       const float* key_center, const uint16_t* kproj, const float* proj,
+                       const float* key_center, const void* kproj, const float* proj,
                        const int32_t* seq_lens, float* scores, hipStream_t s) {
   const _Float16* qh = static_cast<const _Float16*>(q);
   if (cfg->granularity == BSA_GRANULARITY_BLOCK)
     return bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale, qh, codes, scales,
                                   global_scale, key_center, seq_lens, scores, s);
-  return bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank, qh, kproj, proj, seq_lens,
+  return bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank,
+                                cfg->proj_dtype == BSA_PROJ_FP8, qh, kproj, proj, seq_lens,
                                 scores, s);
 }
 
@@ -210,7 +218,7 @@ extern "C" {
 int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* k,
                       const float* key_center, const float* global_scale, const float* proj,
                       int32_t block_begin, int32_t block_end, uint8_t* codes, uint8_t* scales,
-                      uint16_t* kproj, void* stream) {
+                      void* kproj, void* stream) {
   try {
     bsa::UnitGeom g;
     int rc = check_common(layout, cfg, &g);
@@ -229,8 +237,9 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, co
                         "pack_nvfp4");
     }
     BSA_REQUIRE(proj && kproj, BSA_ERR_INVALID_ARG, "token mode needs proj and kproj");
-    return hip_status(bsa::launch_pack_proj(g, k, proj, cfg->proj_rank, block_begin, block_end,
-                                            kproj, s),
+    return hip_status(bsa::launch_pack_proj(g, k, proj, cfg->proj_rank,
+                                            cfg->proj_dtype == BSA_PROJ_FP8, block_begin,
+                                            block_end, kproj, s),
                       "pack_proj");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -239,7 +248,7 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, co
 
 int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                   const float* key_center, const uint16_t* kproj, const float* proj,
+                   const float* key_center, const void* kproj, const float* proj,
                    const int32_t* seq_lens, float* scores, void* stream) {
   try {
     bsa::UnitGeom g;
@@ -325,7 +334,7 @@ size_t bsa_counters_size(const bsa_kv_layout* layout) {
 
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                      const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                     const float* key_center, const uint16_t* kproj, const float* proj,
+                     const float* key_center, const void* kproj, const float* proj,
                      const int32_t* seq_lens, float* scores, void* workspace,
                      size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream) {
   try {
@@ -404,7 +413,7 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
 
 int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                     const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                    const float* key_center, const uint16_t* kproj, const float* proj,
+                    const float* key_center, const void* kproj, const float* proj,
                     const void* k, const void* v, const int32_t* seq_lens,
                     const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
                     float* scores, void* workspace, size_t workspace_bytes, int32_t* idx,

@@ -19,6 +19,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 
 // --- number formats --------------------------------------------------------
@@ -176,14 +177,14 @@ hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* cent
                              const float* gscale, int blk0, int blk1, uint8_t* codes,
                              uint8_t* scales, hipStream_t s);
 hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
-                            int blk0, int blk1, uint16_t* kproj, hipStream_t s);
+                            bool fp8, int blk0, int blk1, void* kproj, hipStream_t s);
 hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,
                              hipStream_t s);
-hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, const _Float16* q,
-                             const uint16_t* kproj, const float* proj, const int32_t* seq_lens,
-                             float* scores, hipStream_t s);
+hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
+                             const _Float16* q, const void* kproj, const float* proj,
+                             const int32_t* seq_lens, float* scores, hipStream_t s);
 size_t token_select_workspace(const UnitGeom& g);
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
                                const int32_t* seq_lens, int32_t* idx, int32_t* count,

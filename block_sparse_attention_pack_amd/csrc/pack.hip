@@ -3,7 +3,8 @@
 // Block mode: NVFP4 -- E2M1 elements, one E4M3 scale per 16 channels, one FP32
 // scale per KV head, keys centered first (Jet-QSparse abstract: NVFP4 cache,
 // calibrated key centering, packed straight from the 16-bit activations).
-// Token mode: BF16 projected keys kproj = P^T k (JSSA Figure 1 and Figure 10).
+// Token mode: projected keys kproj = P^T k, stored as BF16 or as E4M3FN bytes
+// (JSSA Figure 1 and Figure 10).
 //
 // Every rounding step is a single IEEE float32 operation (no contraction into
 // fused multiply-adds), so the bytes are reproducible bit for bit.
@@ -111,11 +112,11 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(
 
 // Projected keys: one thread per (token, output channel); the float32 sum runs
 // over d in ascending order with separately rounded products and additions.
-template <int DT>
+template <int DT, bool FP8>
 __global__ __launch_bounds__(256) void pack_proj_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ proj, int Hkv, int Tmax,
     int64_t sb, int64_t sh, int64_t st, int rank, int tok0, int ntok,
-    uint16_t* __restrict__ kproj) {
+    void* __restrict__ kproj) {
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit % Hkv;
   const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -133,10 +134,17 @@ __global__ __launch_bounds__(256) void pack_proj_kernel(
       acc = acc + prod;
     }
   }
-  // float32 -> bfloat16, round to nearest even (inputs are finite)
+  const int64_t at = (int64_t(unit) * Tmax + t) * rank + j;
   const uint32_t u = __float_as_uint(acc);
-  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  kproj[(int64_t(unit) * Tmax + t) * rank + j] = uint16_t(rounded);
+  if constexpr (FP8) {
+    // nearest E4M3FN code of |acc|, sign bit copied (inputs are finite)
+    const uint32_t code = e4m3_from_float(__builtin_fabsf(acc)) | ((u >> 24) & 0x80u);
+    static_cast<uint8_t*>(kproj)[at] = uint8_t(code);
+  } else {
+    // float32 -> bfloat16, round to nearest even (inputs are finite)
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    static_cast<uint16_t*>(kproj)[at] = uint16_t(rounded);
+  }
 }
 
 }  // namespace
@@ -157,18 +165,23 @@ hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* cent
 }
 
 hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
-                            int blk0, int blk1, uint16_t* kproj, hipStream_t s) {
+                            bool fp8, int blk0, int blk1, void* kproj, hipStream_t s) {
   if (blk1 <= blk0) return hipSuccess;
   const int tok0 = blk0 * kBlock, ntok = (blk1 - blk0) * kBlock;
   const int64_t items = int64_t(ntok) * rank;
   dim3 grid(unsigned((items + 255) / 256), g.B * g.Hkv);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
-  if (g.dtype == BSA_DTYPE_F16)
-    hipLaunchKernelGGL(pack_proj_kernel<BSA_DTYPE_F16>, grid, dim3(256), 0, s, kp, proj, g.Hkv,
-                       g.Tmax, g.sb, g.sh, g.st, rank, tok0, ntok, kproj);
-  else
-    hipLaunchKernelGGL(pack_proj_kernel<BSA_DTYPE_BF16>, grid, dim3(256), 0, s, kp, proj, g.Hkv,
-                       g.Tmax, g.sb, g.sh, g.st, rank, tok0, ntok, kproj);
+#define BSA_PACK_PROJ(DT, F8)                                                                \
+  hipLaunchKernelGGL((pack_proj_kernel<DT, F8>), grid, dim3(256), 0, s, kp, proj, g.Hkv, g.Tmax, \
+                     g.sb, g.sh, g.st, rank, tok0, ntok, kproj)
+  if (g.dtype == BSA_DTYPE_F16) {
+    if (fp8) BSA_PACK_PROJ(BSA_DTYPE_F16, true);
+    else BSA_PACK_PROJ(BSA_DTYPE_F16, false);
+  } else {
+    if (fp8) BSA_PACK_PROJ(BSA_DTYPE_BF16, true);
+    else BSA_PACK_PROJ(BSA_DTYPE_BF16, false);
+  }
+#undef BSA_PACK_PROJ
   return hipGetLastError();
 }
 

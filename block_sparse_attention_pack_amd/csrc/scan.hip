@@ -2,7 +2,9 @@
 //
 // Token mode (JSSA Figure 1): qbar = mean of the group's query heads,
 // p = P^T qbar in FP32 once per work-group, then each token's score is
-// sigma * p . kproj_t, streamed 2R bytes per token in contiguous 1 KiB loads.
+// sigma * p . kproj_t, streamed in contiguous 1 KiB loads: 2R bytes per token
+// from a BF16 cache, R from an FP8 one (JSSA Figure 10), whose E4M3 bytes the
+// gfx950 convert widens exactly (scale 1).
 #include "scan_core.hpp"
 #include "select_core.hpp"
 
@@ -16,25 +18,27 @@ __global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
 // scores kTokPerWg / 4 consecutive tokens, 64 per step. A token's projected row
-// is R bf16, i.e. R / 8 pieces of 16 bytes, and a step's 64 rows are R / 8
-// contiguous 1 KiB slices: lane l loads piece l % (R / 8) of token l / (R / 8)
-// of each slice, so every load instruction reads one contiguous KiB. A lane
-// forms the dot product of its piece with the matching 8 entries of p, the
-// R / 8 lanes of a token add theirs, and one exchange per slice moves token
-// t's score to lane t. The scores collect in LDS and leave after the
+// (2R bytes in BF16, R in FP8) is a run of 16-byte pieces, and a step's 64 rows
+// are contiguous 1 KiB slices: lane l loads piece l % P of token l / P of each
+// slice (P pieces per row), so every load instruction reads one contiguous
+// KiB. A lane forms the dot product of its piece with the matching entries of
+// p (8 in BF16, 16 in FP8), the P lanes of a token add theirs, and one
+// exchange per slice moves token t's score to lane t. The scores collect in LDS and leave after the
 // work-group's last read, in contiguous 16-byte-per-lane stores: stores
 // spread among the reads cost the HBM far more than their own bytes (23 us of
 // 120 at 128K context, batch 8, 8 KV heads). The next step's rows are loaded
 // before the current ones are scored, and the first step's before p is formed.
 constexpr int kTokPerWg = 16384;
 
-template <int R>
+template <int R, bool FP8>
 __global__ __launch_bounds__(256) void scan_token_kernel(
-    const _Float16* __restrict__ q, const uint16_t* __restrict__ kproj,
+    const _Float16* __restrict__ q, const void* __restrict__ kproj,
     const float* __restrict__ proj, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma) {
-  static_assert(R % 8 == 0 && R <= 128, "rank");
-  constexpr int kLpt = R / 8;         // lanes per token (one 16-byte piece each)
+  constexpr int kRowBytes = FP8 ? R : 2 * R;
+  constexpr int kPer = FP8 ? 16 : 8;      // entries of a row per 16-byte piece
+  static_assert(kRowBytes % 16 == 0 && kRowBytes <= 256, "rank");
+  constexpr int kLpt = kRowBytes / 16;    // lanes per token (one 16-byte piece each)
   constexpr int kTps = kWave / kLpt;  // tokens per 1 KiB slice
   constexpr int kSlices = kLpt;       // slices per 64-token step
   constexpr int kPerWave = kTokPerWg / 4;
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   const int L = clamp_len(seq_lens[b], Tmax);
   const int t_wave = blockIdx.x * kTokPerWg + wave * kPerWave;
   const int t_end = min(t_wave + kPerWave, Tmax);
-  const uint16_t* base = kproj + int64_t(unit) * Tmax * R;
+  const uint8_t* base = static_cast<const uint8_t*>(kproj) + int64_t(unit) * Tmax * kRowBytes;
   float* out = scores + int64_t(unit) * Tmax;
   const int piece = lane % kLpt, tok_in_slice = lane / kLpt;
 
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
 #pragma unroll
     for (int c = 0; c < kSlices; ++c) {
       const int t = t0 + c * kTps + tok_in_slice;
-      w[c] = reinterpret_cast<const uint4v*>(base + int64_t(t < t_end ? t : t0) * R)[piece];
+      w[c] = reinterpret_cast<const uint4v*>(base + int64_t(t < t_end ? t : t0) * kRowBytes)[piece];
     }
   };
   // the first step's rows are in flight while p is formed
@@ -97,9 +101,9 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
     }
     __syncthreads();
   }
-  float pq[8];  // the entries of p that meet this lane's piece
+  float pq[kPer];  // the entries of p that meet this lane's piece
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pq[e] = p_lds[8 * piece + e];
+  for (int e = 0; e < kPer; ++e) pq[e] = p_lds[kPer * piece + e];
 
   // the 64 scores of the step at t0 from its landed pieces, stored by lane t
   auto score_step = [&](const uint4v (&w)[kSlices], int t0) {
@@ -109,8 +113,18 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s = __builtin_fmaf(pq[2 * e], bf16_bits_to_float(w[c][e] & 0xFFFFu), s);
-        s = __builtin_fmaf(pq[2 * e + 1], bf16_bits_to_float(w[c][e] >> 16), s);
+        if constexpr (FP8) {
+          // bytes 0, 1 and 2, 3 of the dword are entries 4 e .. 4 e + 3
+          const float2v lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[c][e], 1.0f, false);
+          const float2v hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[c][e], 1.0f, true);
+          s = __builtin_fmaf(pq[4 * e], lo[0], s);
+          s = __builtin_fmaf(pq[4 * e + 1], lo[1], s);
+          s = __builtin_fmaf(pq[4 * e + 2], hi[0], s);
+          s = __builtin_fmaf(pq[4 * e + 3], hi[1], s);
+        } else {
+          s = __builtin_fmaf(pq[2 * e], bf16_bits_to_float(w[c][e] & 0xFFFFu), s);
+          s = __builtin_fmaf(pq[2 * e + 1], bf16_bits_to_float(w[c][e] >> 16), s);
+        }
       }
 #pragma unroll
       for (int off = 1; off < kLpt; off <<= 1) s += __shfl_xor(s, off, kWave);
@@ -155,23 +169,30 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _
   return hipGetLastError();
 }
 
-hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, const _Float16* q,
-                             const uint16_t* kproj, const float* proj, const int32_t* seq_lens,
-                             float* scores, hipStream_t s) {
+hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
+                             const _Float16* q, const void* kproj, const float* proj,
+                             const int32_t* seq_lens, float* scores, hipStream_t s) {
   dim3 grid(ceil_div(g.Tmax, kTokPerWg), g.B * g.Hkv);
-#define BSA_SCAN_TOKEN(RK)                                                                     \
-  case RK:                                                                                     \
-    hipLaunchKernelGGL(scan_token_kernel<RK>, grid, dim3(256), 0, s, q, kproj, proj, seq_lens, \
-                       scores, g.Hkv, g.Hq, g.G, g.Tmax, sigma);                               \
-    break;
-  switch (rank) {
-    BSA_SCAN_TOKEN(8)
-    BSA_SCAN_TOKEN(16)
-    BSA_SCAN_TOKEN(32)
-    BSA_SCAN_TOKEN(64)
-    BSA_SCAN_TOKEN(128)
-    default:
-      return hipErrorInvalidValue;
+#define BSA_SCAN_TOKEN(RK, F8)                                                                  \
+  hipLaunchKernelGGL((scan_token_kernel<RK, F8>), grid, dim3(256), 0, s, q, kproj, proj,         \
+                     seq_lens, scores, g.Hkv, g.Hq, g.G, g.Tmax, sigma)
+  if (fp8) {
+    switch (rank) {
+      case 16: BSA_SCAN_TOKEN(16, true); break;
+      case 32: BSA_SCAN_TOKEN(32, true); break;
+      case 64: BSA_SCAN_TOKEN(64, true); break;
+      case 128: BSA_SCAN_TOKEN(128, true); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (rank) {
+      case 8: BSA_SCAN_TOKEN(8, false); break;
+      case 16: BSA_SCAN_TOKEN(16, false); break;
+      case 32: BSA_SCAN_TOKEN(32, false); break;
+      case 64: BSA_SCAN_TOKEN(64, false); break;
+      case 128: BSA_SCAN_TOKEN(128, false); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef BSA_SCAN_TOKEN
   return hipGetLastError();

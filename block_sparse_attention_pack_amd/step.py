@@ -147,7 +147,8 @@ class DeviceStep:
         B, Hkv, Hq = L.batch, L.num_kv_heads, L.num_q_heads
         gran = "block" if self.block_mode else "token"
         cfg = bsa.select_cfg(self.cfg.granularity, budget, self.cfg.n_tail_pages,
-                             self.cfg.proj_rank, self.cfg.softmax_scale)
+                             self.cfg.proj_rank, self.cfg.softmax_scale,
+                             proj_dtype=self.cfg.proj_dtype)
         if splits is None:
             splits = default_splits(B * Hkv, budget, gran)
         dev = self.q.device
@@ -192,7 +193,7 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
     s = w.spec
     B, Hkv, Hq, T = s.batch, s.kv_heads, s.q_heads, s.max_tokens
     dev = torch.device(device)
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    t = lambda a: torch.from_numpy(np.array(a, order="C")).to(dev)  # a writable copy
     k = t(w.k)
     v = t(w.v)
     if kv_dtype == "bf16":
@@ -200,8 +201,9 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         v = v.to(torch.bfloat16)
     layout = bsa.layout_for(k, Hq)
     gran = bsa.BLOCK if s.granularity == "block" else bsa.TOKEN
+    fp8 = gran == bsa.TOKEN and s.proj_fmt == "fp8"
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
-                         w.softmax_scale)
+                         w.softmax_scale, proj_dtype=bsa.PROJ_FP8 if fp8 else bsa.PROJ_BF16)
     if splits is None:
         splits = default_splits(B * Hkv, s.budget, s.granularity, one_launch)
     nb = s.max_blocks
@@ -211,7 +213,8 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         scales = torch.empty((B, Hkv, nb, 1024), dtype=torch.uint8, device=dev)
         scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
     else:
-        kproj = torch.empty((B, Hkv, T, s.rank), dtype=torch.int16, device=dev)
+        kproj = torch.empty((B, Hkv, T, s.rank), dtype=torch.uint8 if fp8 else torch.int16,
+                            device=dev)
         proj = t(w.proj)
         scores = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
     tail_k = tail_v = None

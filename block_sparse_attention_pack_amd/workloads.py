@@ -71,6 +71,7 @@ class Spec:
     outlier_gain: float = 1.0
     ragged: bool = False  # lengths uniform in [max_tokens/2, max_tokens]
     rank: int = 0  # projection rank in token mode
+    proj_fmt: str = "bf16"  # token mode: projected-key cache storage, "bf16" or "fp8"
     lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
@@ -98,9 +99,12 @@ SPECS: Dict[str, Spec] = {
                    needle_count=20, needle_profile="zipf", needle_strength=3.0,
                    key_offset_std=2.0, outlier_channels=4, outlier_gain=8.0, ragged=True),
     "token": Spec("token", 4, 8, 8, 32, 131072, "token", 2048, rank=32),
+    # the token workload's inputs (same seed) with an FP8 projected-key cache
+    "token_fp8": Spec("token_fp8", 4, 8, 8, 32, 131072, "token", 2048, rank=32,
+                      proj_fmt="fp8"),
 }
 
-ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token"]
+ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
@@ -317,8 +321,8 @@ def algorithmic_bytes(w: Workload) -> Dict[str, int]:
 
     Block mode: 72 B per scanned token (64 B of E2M1 codes + 8 B of E4M3 scales)
     and 2 x 256 B per attended token (FP16 K and V rows; BF16 tail rows also
-    count 512 B). Token mode: 2r B per scanned token (BF16 projected key) and
-    512 B per selected token.
+    count 512 B). Token mode: 2r B (BF16) or r B (FP8) per scanned token (the
+    projected key) and 512 B per selected token.
     """
     s = w.spec
     scan = attn = 0
@@ -338,7 +342,7 @@ def algorithmic_bytes(w: Workload) -> Dict[str, int]:
             tokens += (chosen - forced) * BLOCK if forced else min(chosen * BLOCK, L)
             attn += s.kv_heads * 512 * tokens
         else:
-            scan += s.kv_heads * 2 * s.rank * L
+            scan += s.kv_heads * (1 if s.proj_fmt == "fp8" else 2) * s.rank * L
             attn += s.kv_heads * 512 * min(s.budget, L)
     q_bytes = s.batch * s.q_heads * HEAD_DIM * 2
     return {"scan": scan, "attn": attn, "q": q_bytes, "total": scan + attn}

@@ -65,6 +65,10 @@ enum {
 enum { BSA_DTYPE_F16 = 0, BSA_DTYPE_BF16 = 1 };
 enum { BSA_GRANULARITY_BLOCK = 0, BSA_GRANULARITY_TOKEN = 1 };
 
+/* Storage of the projected-key cache (TOKEN mode; JSSA Figure 10 evaluates
+ * both): BF16, or FP8 as OCP E4M3FN bytes. */
+enum { BSA_PROJ_BF16 = 0, BSA_PROJ_FP8 = 1 };
+
 /* Standard GQA KV cache: K and V are [batch][num_kv_heads][max_tokens][head_dim]
  * through the strides below (in elements, head_dim contiguous). Query head hq
  * belongs to KV head hq / (num_q_heads / num_kv_heads). */
@@ -87,8 +91,9 @@ typedef struct bsa_select_cfg {
   int32_t budget;       /* per unit: blocks (forced tail pages included) or tokens */
   int32_t n_tail_pages; /* BLOCK: 0..2 newest pages kept in a BF16 store and always
                            selected (Jet-QSparse abstract); TOKEN: must be 0 */
-  int32_t proj_rank;    /* TOKEN: r in {8, 16, 32, 64, 128}; BLOCK: ignored */
+  int32_t proj_rank;    /* TOKEN: r in {8, 16, 32, 64, 128} (16 .. 128 for FP8); BLOCK: ignored */
   float softmax_scale;  /* sigma, > 0 (1/sqrt(128) for the standard scale) */
+  int32_t proj_dtype;   /* TOKEN: BSA_PROJ_BF16 or BSA_PROJ_FP8; BLOCK: must be BSA_PROJ_BF16 (0) */
 } bsa_select_cfg;
 
 /* ---------------------------------------------------------------------------
@@ -119,18 +124,22 @@ typedef struct bsa_select_cfg {
  * BLOCK: k (device, kv_dtype, layout above), key_center (device float
  *   [Hkv][128], or NULL for no centering), global_scale (device float [Hkv],
  *   finite > 0) -> codes, scales (device, layout above). proj and kproj unused.
- * TOKEN: k and proj (device float [Hkv][128][r]) -> kproj (device uint16
- *   bfloat16 bits [B][Hkv][max_tokens][r]) for tokens [128*block_begin,
- *   128*block_end): kproj[t][j] = BF16_rne(acc), acc the float32 sum over
+ * TOKEN: k and proj (device float [Hkv][128][r]) -> kproj [B][Hkv][max_tokens][r]
+ *   for tokens [128*block_begin, 128*block_end), from acc, the float32 sum over
  *   d = 0..127 in ascending order of fl32(P[h][d][j] * k[t][d]), each addition
- *   rounded to float32 (JSSA Figure 1: projected-key cache; Figure 10: BF16).
+ *   rounded to float32 (JSSA Figure 1: projected-key cache; Figure 10: BF16 or
+ *   FP8 storage):
+ *     BSA_PROJ_BF16: uint16 bfloat16 bits, kproj[t][j] = BF16_rne(acc);
+ *     BSA_PROJ_FP8:  uint8 E4M3FN codes, kproj[t][j] = nearest E4M3FN value
+ *                    to acc (ties to the even code, saturating at 448, sign
+ *                    bit copied from acc; no further scale).
  * Packing all tokens of the blocks regardless of sequence length is the
  * caller's choice: blocks past a sequence's end are never read by the scan.
  * Requires 0 <= block_begin <= block_end <= max_tokens/128. */
 int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
                       const void* k, const float* key_center, const float* global_scale,
                       const float* proj, int32_t block_begin, int32_t block_end,
-                      uint8_t* codes, uint8_t* scales, uint16_t* kproj, void* stream);
+                      uint8_t* codes, uint8_t* scales, void* kproj, void* stream);
 
 /* Score the cache for one decode step.
  *
@@ -150,7 +159,7 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  * (TOKEN, 16-byte aligned); every entry is written. */
 int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                   const float* key_center, const uint16_t* kproj, const float* proj,
+                   const float* key_center, const void* kproj, const float* proj,
                    const int32_t* seq_lens, float* scores, void* stream);
 
 /* Bytes of device workspace bsa_select_topk needs for this layout and cfg
@@ -232,7 +241,7 @@ size_t bsa_counters_size(const bsa_kv_layout* layout);
 /* bsa_score_scan then bsa_select_topk; arguments as there. */
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                      const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                     const float* key_center, const uint16_t* kproj, const float* proj,
+                     const float* key_center, const void* kproj, const float* proj,
                      const int32_t* seq_lens, float* scores, void* workspace,
                      size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream);
 
@@ -283,7 +292,7 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
  * mode). */
 int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                     const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                    const float* key_center, const uint16_t* kproj, const float* proj,
+                    const float* key_center, const void* kproj, const float* proj,
                     const void* k, const void* v, const int32_t* seq_lens,
                     const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
                     float* scores, void* workspace, size_t workspace_bytes, int32_t* idx,

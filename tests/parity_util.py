@@ -42,11 +42,13 @@ def check_pack_block(w, b, h, codes_gpu, scales_gpu):
 
 
 def check_pack_token(w, b, h, kproj_gpu, tokens=None):
+    fmt = w.spec.proj_fmt
     k = w.k[b, h] if tokens is None else w.k[b, h][tokens]
-    ref = O.project_keys(k, w.proj[h])
+    ref = O.project_keys(k, w.proj[h], fmt)
     got = kproj_gpu if tokens is None else kproj_gpu[tokens]
-    assert np.array_equal(got.view(np.uint16), ref), \
-        f"kproj differs at unit {(b, h)}: {int((got.view(np.uint16) != ref).sum())} entries"
+    got = got.view(ref.dtype)
+    assert np.array_equal(got, ref), \
+        f"kproj differs at unit {(b, h)}: {int((got != ref).sum())} entries"
     return ref
 
 
@@ -77,13 +79,14 @@ def check_block_scores(w, b, h, scores_gpu, rc, rs):
 
 
 def check_token_scores(w, b, h, scores_gpu, kproj_ref):
+    fmt = w.spec.proj_fmt
     ref = O.scan_token_unit(q_group(w, b, h), kproj_ref, w.proj[h], int(w.seq_lens[b]),
-                            w.softmax_scale)
+                            w.softmax_scale, fmt)
     fin = np.isfinite(ref)
     assert np.array_equal(fin, np.isfinite(scores_gpu))
     qbar = np.abs(q_group(w, b, h).astype(np.float64)).mean(axis=0)
     p = np.abs(w.proj[h].astype(np.float64)).T @ qbar
-    A = w.softmax_scale * (np.abs(O.bf16_bits_to_f64(kproj_ref)) @ p)
+    A = w.softmax_scale * (np.abs(O.proj_values(kproj_ref, fmt)) @ p)
     err = np.abs(scores_gpu[fin].astype(np.float64) - ref[fin])
     lim = SCORE_REL * A[fin] + SCORE_ABS
     assert np.all(err <= lim), f"token scores at {(b, h)}: max err {err.max():.3e}"

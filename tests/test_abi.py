@@ -165,3 +165,14 @@ def test_decode_step_checks_every_stage_first(lib):
     assert step(cfg, out=None) == -1
     assert step(tok, codes=None, kproj=FAKE) == -4  # token mode: the selection's workspace
     assert step(tok, codes=None, kproj=None) == -1
+
+
+def test_projected_cache_format_is_checked(lib):
+    L = _layout()
+    fp8 = B.select_cfg(B.TOKEN, 64, 0, 32, proj_dtype=B.PROJ_FP8)
+    assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(fp8)) > 0  # a valid cfg
+    assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 8, proj_dtype=B.PROJ_FP8)) == -2
+    assert "FP8" in lib.bsa_last_error().decode()
+    assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 32, proj_dtype=7)) == -2
+    assert _scan(lib, L, B.select_cfg(B.BLOCK, 8, proj_dtype=B.PROJ_FP8)) == -1
+

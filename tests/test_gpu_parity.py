@@ -58,6 +58,7 @@ REDUCED = {
     "jetqsparse": W.reduced("jetqsparse", 8192, batch=2),
     "ragged": W.reduced("ragged", 16384, batch=3, budget=24),
     "token": W.reduced("token", 16384, batch=2),
+    "token_fp8": W.reduced("token_fp8", 16384, batch=2),
 }
 
 
@@ -317,3 +318,20 @@ def test_decode_step_merges_many_splits(splits):
     d = run_step(w, splits=splits)
     _two_calls_match(d)
     check_all(w, d)
+
+
+def test_fp8_projected_cache_decodes_every_code():
+    """The scan widens every finite E4M3 code exactly: crafted cache rows, token t
+    holding code t (NaN codes replaced by 0) in every column, against the oracle."""
+    spec = dataclasses.replace(W.SPECS["token_fp8"], name="fp8_codes", batch=1, kv_heads=1,
+                               q_heads=4, max_tokens=512, budget=32)
+    w = W.generate(spec)
+    d = run_step(w)
+    codes = np.arange(512, dtype=np.int64) % 256
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0
+    rows = np.repeat(codes.astype(np.uint8)[:, None], spec.rank, axis=1)
+    d.kproj[0, 0].copy_(torch.from_numpy(rows))
+    d.scan()
+    torch.cuda.synchronize()
+    PU.check_token_scores(w, 0, 0, host(d.scores[0, 0]), rows)
+
