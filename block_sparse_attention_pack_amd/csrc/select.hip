@@ -6,18 +6,20 @@
 //
 // Token mode: a unit has up to max_tokens candidates (131072 at 128K context),
 // too many for one work-group to read fast, so the selection is spread over
-// kTokChunk-key chunks, one work-group each, in four launches:
-//   init    zeroes each unit's histogram;
+// kTokChunk-key chunks, one work-group each, in three launches:
 //   hist    every group adds the histogram of its keys' top 12 bits (of the
-//           order-preserving key) to its unit's, with device-scope atomics;
+//           order-preserving key) to its unit's, with device-scope atomics
+//           (the histogram is zero on entry: the finish of the previous call
+//           leaves it so);
 //   filter  every group finds from that histogram the top digit beta that
 //           holds the picks-th largest key and writes two bitmaps of its keys:
 //           those with a larger top digit (taken), and those with top digit
 //           beta (the bucket: usually about 1% of the keys);
 //   finish  one group per unit lists the bucket's keys in token order, finds
 //           the exact boundary key among them (radix select over the remaining
-//           20 bits), and compacts the taken tokens in index order: those
-//           above the boundary key, and of its ties the lowest indices.
+//           20 bits), compacts the taken tokens in index order (those above
+//           the boundary key, and of its ties the lowest indices), and returns
+//           the unit's histogram to zero.
 #include "common.hpp"
 #include "select_core.hpp"
 
@@ -103,12 +105,6 @@ __device__ __forceinline__ void tok_counts(const int32_t* seq_lens, int unit, in
                                            int budget, int& C, int& picks) {
   C = clamp_len(seq_lens[unit / Hkv], Tmax);
   picks = max(0, min(budget, C));
-}
-
-// grid (B * Hkv), 256 threads: zero the histogram.
-__global__ __launch_bounds__(kSelectThreads) void tok_init_kernel(TokGeom tg, void* ws) {
-  const TokUnit u = tok_unit(ws, tg, blockIdx.x);
-  for (int d = threadIdx.x; d < kTokBins; d += kSelectThreads) u.hist[d] = 0u;
 }
 
 // Histogram of the top 12 key bits of the unit's candidates.
@@ -516,6 +512,8 @@ __global__ __launch_bounds__(kSelectThreads) void tok_finish_kernel(
   const int nsel = max(0, min(gt_run + min(eq_run, r_eq), budget));
   for (int k = nsel + tid; k < budget; k += kSelectThreads) out[k] = -1;
   if (tid == 0) count[unit] = nsel;
+  // the unit's histogram back to zero for the next call (saves a launch)
+  for (int d = tid; d < kTokBins; d += kSelectThreads) u.hist[d] = 0u;
 }
 
 }  // namespace
@@ -538,7 +536,6 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
   const TokGeom tg = tok_geom(g.Tmax);
   const int units = g.B * g.Hkv;
   const dim3 grid(ceil_div(g.Tmax, kTokChunk), units), block(kSelectThreads);
-  hipLaunchKernelGGL(tok_init_kernel, dim3(units), block, 0, s, tg, ws);
   hipLaunchKernelGGL(tok_hist_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
                      tg, ws);
   hipLaunchKernelGGL(tok_filter_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,

@@ -155,7 +155,7 @@ class DeviceStep:
         ws_bytes = bsa.workspace_size(L, cfg)
         return dataclasses.replace(
             self, cfg=cfg, splits=splits,
-            workspace=torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None,
+            workspace=torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None,
             ws_bytes=ws_bytes,
             idx=torch.empty((B, Hkv, budget), dtype=torch.int32, device=dev),
             count=torch.empty((B, Hkv), dtype=torch.int32, device=dev),
@@ -222,7 +222,8 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         tail_k = t(w.tail_k.view(np.int16))
         tail_v = t(w.tail_v.view(np.int16))
     ws_bytes = bsa.workspace_size(layout, cfg)
-    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    # zero before the first use; every call leaves it so
+    workspace = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
     return DeviceStep(
         w=w, layout=layout, cfg=cfg, splits=splits,
         q=t(w.q), k=k, v=v, seq_lens=t(w.seq_lens), key_center=t(w.key_center),

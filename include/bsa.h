@@ -177,7 +177,10 @@ size_t bsa_workspace_size(const bsa_kv_layout* layout, const bsa_select_cfg* cfg
  * idx: device int32 [B][Hkv][budget], ascending, padded with -1.
  * count: device int32 [B][Hkv], the number of valid idx entries.
  * workspace: device memory of at least bsa_workspace_size() bytes (may be NULL
- * when that is 0); its contents on entry do not matter. */
+ * when that is 0). TOKEN: zero-fill it before its first use; every call that
+ * completes leaves the part that must start at zero (the histograms) zeroed
+ * again, so it is reused as is; calls that share it must not run
+ * concurrently. */
 int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
                     const float* scores, const int32_t* seq_lens, void* workspace,
                     size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream);

@@ -54,6 +54,17 @@ def _say(*a):
     sys.stdout.flush()
 
 
+def _histograms_back_at_zero(ws, units, T):
+    """After a call each unit's histogram in the token workspace is zero again
+    (per unit: 4096 histogram words, a 64-word slot, two bitmaps of
+    ceil(T/64)*2 words rounded up to 64)."""
+    w = ws.view(torch.int32).cpu().numpy()
+    W = -(-T // 64) * 2
+    per = 4096 + 64 + 2 * (-(-W // 64) * 64)
+    for u in range(units):
+        assert not w[u * per:u * per + 4096].any(), f"histogram of unit {u}"
+
+
 @pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
 @pytest.mark.parametrize("budget", [1, 300, 2048, 40000])
 def test_token_select_matches_oracle(pattern, budget):
@@ -67,7 +78,7 @@ def test_token_select_matches_oracle(pattern, budget):
     cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1)
     ws_bytes = bsa.workspace_size(layout, cfg)
     dev = torch.device("cuda")
-    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=dev)  # contents must not matter
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)  # zero before the first use
     sc = torch.from_numpy(scores).to(dev)
     lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
     idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
@@ -75,6 +86,7 @@ def test_token_select_matches_oracle(pattern, budget):
     for rep in range(2):  # a second call on the same workspace
         bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
         torch.cuda.synchronize()
+        _histograms_back_at_zero(ws, B * Hkv, T)
         gi, gc = idx.cpu().numpy(), count.cpu().numpy()
         for b in range(B):
             for h in range(Hkv):
@@ -124,13 +136,14 @@ def test_token_select_over_several_bitmap_windows(pattern):
     cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1)
     ws_bytes = bsa.workspace_size(layout, cfg)
     dev = torch.device("cuda")
-    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=dev)
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
     sc = torch.from_numpy(scores).to(dev)
     lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
     idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
     count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
     bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
     torch.cuda.synchronize()
+    _histograms_back_at_zero(ws, B * Hkv, T)
     gi, gc = idx.cpu().numpy(), count.cpu().numpy()
     for b in range(B):
         for h in range(Hkv):
