@@ -616,12 +616,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, bool block_mode, in
     float val, lse;
     const float* pl = a.part_lse + rowq * a.splits;
     const float* po = a.part_o + rowq * a.splits * kHeadDim;
-    if (a.splits <= kFusedMergeMaxSplits)
-      combine_channel_few<kFusedMergeMaxSplits, true>(pl, po, a.splits, d, val, lse);
-    else if (STEP && a.splits <= 2 * kFusedMergeMaxSplits)
-      combine_channel_few<2 * kFusedMergeMaxSplits, true>(pl, po, a.splits, d, val, lse);
-    else if (STEP && a.splits <= 4 * kFusedMergeMaxSplits)
-      combine_channel_few<4 * kFusedMergeMaxSplits, true>(pl, po, a.splits, d, val, lse);
+    // up to 8 splits as launched by the attention entry points; the decode
+    // step always merges here, in one pass up to 32 splits
+    static_assert(kFusedMergeMaxSplits == 8, "the one-pass forms below");
+    if (a.splits <= 8)
+      combine_channel_few<8, true>(pl, po, a.splits, d, val, lse);
+    else if (STEP && a.splits <= 16)
+      combine_channel_few<16, true>(pl, po, a.splits, d, val, lse);
+    else if (STEP && a.splits <= 32)
+      combine_channel_few<32, true>(pl, po, a.splits, d, val, lse);
     else
       combine_channel<true>(pl, po, a.splits, d, val, lse);
     a.out[rowq * kHeadDim + d] = val;

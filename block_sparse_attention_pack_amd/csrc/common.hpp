@@ -194,7 +194,8 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                hipStream_t s);
 // Largest budget for which the attention launch selects the blocks itself.
 constexpr int kFusedSelectMax = 1024;
-// The attention launch merges the splits in its last group up to this many.
+// The attention launch merges the splits in its last group up to this many
+// (more, up to 32, measured slower than the separate merge launch).
 constexpr int kFusedMergeMaxSplits = 8;
 
 hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int n_tail,

@@ -23,7 +23,8 @@ def default_splits(units: int, budget: int, granularity: str, one_launch: bool =
     waves per SIMD, so 512 four-wave groups are resident on 256 CUs at once;
     more, smaller splits only add merge work (and, with the selection in the
     attention prologue, more copies of it). A split keeps at least two blocks
-    (block mode) or 64 tokens (token mode).
+    (block mode, from 8 units up; fewer units are latency-bound and gain from
+    one block per split) or 64 tokens (token mode).
 
     One-launch decode step (block mode): four blocks per split. The selection
     is made once per unit there, and short attention items shorten the end of
@@ -34,7 +35,7 @@ def default_splits(units: int, budget: int, granularity: str, one_launch: bool =
     s = max(1, math.ceil(512 / max(units, 1)))
     if granularity == "token":
         s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
-    else:
+    elif units >= 8:
         s = min(s, max(1, budget // 2))
     return max(1, min(s, budget))
 

@@ -264,10 +264,11 @@ def test_fused_calls_with_short_sequences_and_many_splits():
         check_all(w, d)
 
 
-@pytest.mark.parametrize("splits", [8, 9, 16])
+@pytest.mark.parametrize("splits", [8, 9, 16, 17, 32, 33, 48])
 def test_attend_combine_on_both_sides_of_the_merge_limit(splits):
-    """Up to 8 splits the merge runs in the attention launch, beyond in its own."""
-    w = W.generate(W.reduced("ragged", 8192, batch=2, budget=24))
+    """Up to 8 splits the merge runs in the attention launch, beyond in its own
+    launch: the same bits either way."""
+    w = W.generate(W.reduced("ragged", 16384, batch=2, budget=48))
     d = run_step(w, splits=splits)
     ref = [host(t).copy() for t in (d.out, d.out_lse)]
     for t in (d.out, d.out_lse):
