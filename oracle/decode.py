@@ -276,6 +276,32 @@ def gather_rows_block(k_unit, v_unit, blocks: Sequence[int], seq_len: int, n_tai
     return np.concatenate(ks), np.concatenate(vs)
 
 
+# --------------------------------------------------------------------------
+# Decode-time state of the cache after L tokens (the Jet-QSparse abstract: the
+# newest pages stay in BF16, older ones are packed into NVFP4 from the
+# full-precision keys). Reading for appends: the BF16 tail store holds BF16
+# roundings of the full-precision cache rows; slot s holds page
+# n_pages(L) - n_tail + s, rows at or beyond L (and slots of pages below 0)
+# are zero. The 4-bit records of a token depend on that token's row only (its
+# scales cover 16 channels of one token), so the copy of every token < L is
+# its bulk pack.
+# --------------------------------------------------------------------------
+
+def tail_store_from_cache(rows: np.ndarray, seq_len: int, n_tail: int) -> np.ndarray:
+    """BF16 bits [n_tail, 128, 128] of the tail pages of one unit's cache rows
+    [T, 128] (fp16 or bf16 values) at length seq_len."""
+    out = np.zeros((n_tail, BLOCK, HEAD_DIM), dtype=np.uint16)
+    npg = n_pages(seq_len)
+    for s in range(n_tail):
+        page = npg - n_tail + s
+        if page < 0:
+            continue
+        lo, hi = page * BLOCK, min((page + 1) * BLOCK, seq_len)
+        if hi > lo:
+            out[s, :hi - lo] = f32_to_bf16_bits(np.asarray(rows[lo:hi], dtype=F32))
+    return out
+
+
 def gather_rows_token(k_unit, v_unit, tokens: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
     t = np.asarray(tokens, dtype=np.int64)
     return (np.asarray(k_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM),

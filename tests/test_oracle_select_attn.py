@@ -261,3 +261,19 @@ def test_fp8_token_scores_exact_for_representable_keys():
     qbar = q.astype(np.float64).mean(axis=0)
     exact = SIGMA * (k[:, :32].astype(np.float64) @ qbar[:32])
     assert np.abs(s[:250] - exact[:250]).max() < 1e-12 and np.all(s[250:] == -np.inf)
+
+
+def test_tail_store_from_cache_worked_example():
+    # 130 tokens, two tail pages: slot 0 is page 0 (rows 0..127), slot 1 page 1
+    # (rows 128, 129, then zeros); one tail page at 128 tokens is page 0 whole
+    rows = (np.arange(300 * 128).reshape(300, 128) % 97 - 48).astype(np.float16)
+    t = O.tail_store_from_cache(rows, 130, 2)
+    bf = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(t[0], bf(rows[:128]))
+    assert np.array_equal(t[1, :2], bf(rows[128:130])) and not t[1, 2:].any()
+    t1 = O.tail_store_from_cache(rows, 128, 1)
+    assert np.array_equal(t1[0], bf(rows[:128]))
+    # fewer pages than slots: the leading slots stay zero
+    t3 = O.tail_store_from_cache(rows, 5, 2)
+    assert not t3[0].any() and np.array_equal(t3[1, :5], bf(rows[:5])) and not t3[1, 5:].any()
+
