@@ -91,6 +91,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P],
         "bsa_decode_step": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
                             ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P],
+        "bsa_append_token": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -242,3 +243,12 @@ def decode_step(layout, cfg, q, codes, scales, global_scale, key_center, kproj, 
         _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), num_splits, _ptr(scores), _ptr(workspace),
         workspace_bytes, _ptr(idx), _ptr(count), _ptr(part_o), _ptr(part_lse), _ptr(counters),
         _ptr(out), _ptr(out_lse), _stream(stream)))
+
+
+def append_token(layout, cfg, k_new, v_new, seq_lens, k, v, key_center, global_scale, proj,
+                 codes, scales, kproj, tail_k, tail_v, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_append_token(
+        ctypes.byref(layout), ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+        _ptr(k), _ptr(v), _ptr(key_center), _ptr(global_scale), _ptr(proj), _ptr(codes),
+        _ptr(scales), _ptr(kproj), _ptr(tail_k), _ptr(tail_v), _stream(stream)))

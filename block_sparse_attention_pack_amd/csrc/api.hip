@@ -246,6 +246,41 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, co
   }
 }
 
+int bsa_append_token(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* k_new,
+                     const void* v_new, const int32_t* seq_lens, void* k, void* v,
+                     const float* key_center, const float* global_scale, const float* proj,
+                     uint8_t* codes, uint8_t* scales, void* kproj, uint16_t* tail_k,
+                     uint16_t* tail_v, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_REQUIRE(k_new && v_new && aligned16(k_new) && aligned16(v_new) && k && v && seq_lens,
+                BSA_ERR_INVALID_ARG,
+                "k_new, v_new (16-byte aligned), k, v and seq_lens are required");
+    const bool block = cfg->granularity == BSA_GRANULARITY_BLOCK;
+    if (block)
+      BSA_REQUIRE(codes && scales && global_scale, BSA_ERR_INVALID_ARG,
+                  "block mode needs codes, scales and global_scale");
+    else
+      BSA_REQUIRE(proj && kproj, BSA_ERR_INVALID_ARG, "token mode needs proj and kproj");
+    if (block && cfg->n_tail_pages > 0)
+      BSA_REQUIRE(tail_k && tail_v && aligned16(tail_k) && aligned16(tail_v), BSA_ERR_INVALID_ARG,
+                  "n_tail_pages > 0 needs 16-byte aligned tail_k and tail_v");
+    (void)hipGetLastError();
+    return hip_status(
+        bsa::launch_append(g, block ? cfg->n_tail_pages : 0, block ? 0 : cfg->proj_rank,
+                           cfg->proj_dtype == BSA_PROJ_FP8, k_new, v_new, seq_lens, k, v,
+                           block ? key_center : nullptr, block ? global_scale : nullptr,
+                           block ? codes : nullptr, block ? scales : nullptr,
+                           block ? nullptr : proj, block ? nullptr : kproj,
+                           block ? tail_k : nullptr, block ? tail_v : nullptr,
+                           static_cast<hipStream_t>(stream)),
+        "append_token");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
 int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                    const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                    const float* key_center, const void* kproj, const float* proj,

@@ -178,6 +178,11 @@ hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* cent
                              uint8_t* scales, hipStream_t s);
 hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
                             bool fp8, int blk0, int blk1, void* kproj, hipStream_t s);
+hipError_t launch_append(const UnitGeom& g, int n_tail, int rank, bool fp8, const void* k_new,
+                         const void* v_new, const int32_t* seq_lens, void* k, void* v,
+                         const float* center, const float* gscale, uint8_t* codes,
+                         uint8_t* scales, const float* proj, void* kproj, uint16_t* tail_k,
+                         uint16_t* tail_v, hipStream_t s);
 hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,

@@ -147,7 +147,171 @@ __global__ __launch_bounds__(256) void pack_proj_kernel(
   }
 }
 
+// Decode-time append, one work-group per unit: the new token's cache rows, its
+// 4-bit records (block mode; a token's records depend on its own row only) or
+// projected key (token mode), and the BF16 tail store (slot s holds page
+// n_pages - n_tail + s: a token that starts a page shifts the slots down by
+// one, and the last slot then takes the new page).
+struct AppendArgs {
+  const uint16_t* k_new;  // [B][Hkv][128], cache dtype
+  const uint16_t* v_new;
+  const int32_t* seq_lens;
+  uint16_t* k;
+  uint16_t* v;
+  int64_t sb, sh, st;
+  const float* center;
+  const float* gscale;
+  uint8_t* codes;   // block mode (else null)
+  uint8_t* scales;
+  const float* proj;  // token mode (else null)
+  void* kproj;
+  bool fp8;
+  uint16_t* tail_k;  // n_tail > 0 (else null)
+  uint16_t* tail_v;
+  int Hkv, Tmax, NBmax, rank, n_tail;
+};
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {  // finite x
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int b = unit / a.Hkv, h = unit % a.Hkv;
+  const int L = a.seq_lens[b];
+  if (L < 0 || L >= a.Tmax) return;  // a full (or invalid) sequence is left unchanged
+  const uint16_t* kn = a.k_new + int64_t(unit) * kHeadDim;
+  const uint16_t* vn = a.v_new + int64_t(unit) * kHeadDim;
+  // the cache rows
+  if (tid < kHeadDim) {
+    a.k[b * a.sb + h * a.sh + int64_t(L) * a.st + tid] = kn[tid];
+    a.v[b * a.sb + h * a.sh + int64_t(L) * a.st + tid] = vn[tid];
+  }
+  // block mode: the token's records, as pack_nvfp4_kernel writes them
+  if (a.codes && tid < 8) {
+    const int g = tid, blk = L / kBlock, tau = L % kBlock;
+    const float s_t = a.gscale[h];
+    float y[16];
+    load16<DT>(kn + 16 * g, y);
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float c = a.center ? a.center[h * kHeadDim + 16 * g + u] : 0.0f;
+      y[u] = y[u] - c;
+      amax = fmaxf(amax, __builtin_fabsf(y[u]));
+    }
+    const uint32_t sbyte = e4m3_from_float(amax / (6.0f * s_t));
+    const float S = e4m3_to_float(sbyte) * s_t;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t c = S > 0.0f ? e2m1_from_float(y[u] / S) : 0u;
+      if (u < 8) lo |= c << (4 * u);
+      else hi |= c << (4 * (u - 8));
+    }
+    uint8_t* crec = a.codes + (int64_t(unit) * a.NBmax + blk) * kCodeRecord;
+    uint8_t* srec = a.scales + (int64_t(unit) * a.NBmax + blk) * kScaleRecord;
+    const int i = tau >> 4, n = tau & 15, j = g >> 1, s = g & 1;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(crec + ((i * 4 + j) * 16 + n) * 16 + 8 * s);
+    dst[0] = lo;
+    dst[1] = hi;
+    srec[((j * 16 + n) * 8 + i) * 2 + s] = uint8_t(sbyte);
+  }
+  // token mode: the projected key, as pack_proj_kernel forms it
+  if (a.kproj && tid < a.rank) {
+    const int j = tid;
+    const float* P = a.proj + int64_t(h) * kHeadDim * a.rank + j;
+    float acc = 0.0f;
+    for (int d = 0; d < kHeadDim; d += 16) {
+      float kv[16];
+      load16<DT>(kn + d, kv);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float prod = P[(d + u) * a.rank] * kv[u];
+        acc = acc + prod;
+      }
+    }
+    const int64_t at = (int64_t(unit) * a.Tmax + L) * a.rank + j;
+    if (a.fp8) {
+      const uint32_t code = e4m3_from_float(__builtin_fabsf(acc)) | ((__float_as_uint(acc) >> 24) & 0x80u);
+      static_cast<uint8_t*>(a.kproj)[at] = uint8_t(code);
+    } else {
+      static_cast<uint16_t*>(a.kproj)[at] = bf16_rne_bits(acc);
+    }
+  }
+  // the BF16 tail store
+  if (a.n_tail > 0) {
+    constexpr int kSlotVec = kBlock * kHeadDim / 8;  // 16-byte vectors per slot
+    uint4v* tk = reinterpret_cast<uint4v*>(a.tail_k + int64_t(unit) * a.n_tail * kBlock * kHeadDim);
+    uint4v* tv = reinterpret_cast<uint4v*>(a.tail_v + int64_t(unit) * a.n_tail * kBlock * kHeadDim);
+    if (L % kBlock == 0) {  // a new page: slots down by one, the last one cleared
+      for (int sl = 0; sl + 1 < a.n_tail; ++sl) {
+        for (int e = tid; e < kSlotVec; e += 256) {
+          const uint4v xk = tk[(sl + 1) * kSlotVec + e], xv = tv[(sl + 1) * kSlotVec + e];
+          tk[sl * kSlotVec + e] = xk;
+          tv[sl * kSlotVec + e] = xv;
+        }
+        __syncthreads();  // slot sl + 1 is read before it is overwritten
+      }
+      const uint4v z = {0u, 0u, 0u, 0u};
+      for (int e = tid; e < kSlotVec; e += 256) {
+        tk[(a.n_tail - 1) * kSlotVec + e] = z;
+        tv[(a.n_tail - 1) * kSlotVec + e] = z;
+      }
+      __syncthreads();  // cleared before the new row lands
+    }
+    if (tid < kHeadDim) {
+      const int64_t at = (int64_t(unit) * a.n_tail + a.n_tail - 1) * kBlock * kHeadDim +
+                         int64_t(L % kBlock) * kHeadDim + tid;
+      if (DT == BSA_DTYPE_F16) {
+        a.tail_k[at] = bf16_rne_bits(half_bits_to_float(kn[tid]));
+        a.tail_v[at] = bf16_rne_bits(half_bits_to_float(vn[tid]));
+      } else {
+        a.tail_k[at] = kn[tid];
+        a.tail_v[at] = vn[tid];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append(const UnitGeom& g, int n_tail, int rank, bool fp8, const void* k_new,
+                         const void* v_new, const int32_t* seq_lens, void* k, void* v,
+                         const float* center, const float* gscale, uint8_t* codes,
+                         uint8_t* scales, const float* proj, void* kproj, uint16_t* tail_k,
+                         uint16_t* tail_v, hipStream_t s) {
+  AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seq_lens = seq_lens;
+  a.k = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.sb = g.sb;
+  a.sh = g.sh;
+  a.st = g.st;
+  a.center = center;
+  a.gscale = gscale;
+  a.codes = codes;
+  a.scales = scales;
+  a.proj = proj;
+  a.kproj = kproj;
+  a.fp8 = fp8;
+  a.tail_k = tail_k;
+  a.tail_v = tail_v;
+  a.Hkv = g.Hkv;
+  a.Tmax = g.Tmax;
+  a.NBmax = g.NBmax;
+  a.rank = rank;
+  a.n_tail = n_tail;
+  if (g.dtype == BSA_DTYPE_F16)
+    hipLaunchKernelGGL(append_kernel<BSA_DTYPE_F16>, dim3(g.B * g.Hkv), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<BSA_DTYPE_BF16>, dim3(g.B * g.Hkv), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* center,
                              const float* gscale, int blk0, int blk1, uint8_t* codes,

@@ -170,6 +170,14 @@ class DeviceStep:
         self.score_select(stream)
         self.attend_combine(stream)
 
+    # -- decode-time cache maintenance (not part of the timed step) -----------
+    def append(self, k_new, v_new, stream=None) -> None:
+        """bsa_append_token: one new token per sequence at seq_lens (the caller
+        advances seq_lens afterwards)."""
+        bsa.append_token(self.layout, self.cfg, k_new, v_new, self.seq_lens, self.k, self.v,
+                         self.key_center, self.global_scale, self.proj, self.codes,
+                         self.scales, self.kproj, self.tail_k, self.tail_v, stream)
+
     # -- the whole step as one call -------------------------------------------
     def decode_step(self, stream=None) -> None:
         """bsa_decode_step: one launch in block mode."""

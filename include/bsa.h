@@ -141,6 +141,33 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
                       const float* proj, int32_t block_begin, int32_t block_end,
                       uint8_t* codes, uint8_t* scales, void* kproj, void* stream);
 
+/* Append one decode step's token to every sequence's cache (the cache
+ * lifecycle of the Jet-QSparse abstract: the newest pages kept in BF16, the key
+ * copy packed straight from the full-precision keys; JSSA Figure 1: projected
+ * keys of new tokens).
+ *
+ * For each sequence b with length L_b = seq_lens[b] before the append
+ * (0 <= L_b < max_tokens; other sequences are left unchanged) and KV head h,
+ * with k_new, v_new device [B][Hkv][128] in kv_dtype (16-byte aligned):
+ *   k[b][h][L_b] = k_new[b][h], v[b][h][L_b] = v_new[b][h];
+ *   BLOCK: the token's E2M1 codes and E4M3 scales in codes, scales, exactly as
+ *     bsa_pack_kv_cache packs that token (a token's records depend on its own
+ *     row only), from key_center (or NULL) and global_scale;
+ *   BLOCK with n_tail_pages > 0: the BF16 tail store (tail_k, tail_v, layout
+ *     as in bsa_sparse_decode_attn: slot s holds page ceil(L/128) -
+ *     n_tail_pages + s) is kept in step: a token that starts a new page
+ *     (L_b % 128 == 0) shifts the slots down by one and clears the last slot;
+ *     then the last slot's row L_b % 128 takes the BF16 (round to nearest
+ *     even) of the new key and value;
+ *   TOKEN: kproj[b][h][L_b] = the projected key of k_new, exactly as
+ *     bsa_pack_kv_cache forms it (proj required).
+ * seq_lens is read, not written: the caller advances it after the call. */
+int bsa_append_token(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* k_new,
+                     const void* v_new, const int32_t* seq_lens, void* k, void* v,
+                     const float* key_center, const float* global_scale, const float* proj,
+                     uint8_t* codes, uint8_t* scales, void* kproj, uint16_t* tail_k,
+                     uint16_t* tail_v, void* stream);
+
 /* Score the cache for one decode step.
  *
  * q: device fp16 [B][Hq][128] contiguous. seq_lens: device int32 [B].

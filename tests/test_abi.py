@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["bsa_pack_kv_cache", "bsa_score_scan", "bsa_select_topk",
               "bsa_sparse_decode_attn", "bsa_combine", "bsa_workspace_size",
-              "bsa_decode_step", "bsa_last_error", "bsa_version"]:
+              "bsa_decode_step", "bsa_append_token", "bsa_last_error", "bsa_version"]:
         assert n in names, n
 
 
@@ -176,3 +176,23 @@ def test_projected_cache_format_is_checked(lib):
     assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 32, proj_dtype=7)) == -2
     assert _scan(lib, L, B.select_cfg(B.BLOCK, 8, proj_dtype=B.PROJ_FP8)) == -1
 
+
+
+def test_append_checks_its_arguments(lib):
+    L = _layout()
+    blk = B.select_cfg(B.BLOCK, 8)
+    tail = B.select_cfg(B.BLOCK, 8, n_tail_pages=2)
+    tok = B.select_cfg(B.TOKEN, 64, 0, 32)
+
+    def app(c, k_new=FAKE, codes=FAKE, proj=None, kproj=None, tail_k=None):
+        return lib.bsa_append_token(ctypes.byref(L), ctypes.byref(c), k_new, FAKE, FAKE, FAKE,
+                                    FAKE, None, FAKE, proj, codes, FAKE, kproj, tail_k, tail_k,
+                                    None)
+
+    assert app(blk, k_new=None) == -1
+    assert app(blk, k_new=FAKE + 2) == -1  # 16-byte alignment
+    assert app(blk, codes=None) == -1 and "codes" in lib.bsa_last_error().decode()
+    assert app(tail) == -1 and "tail" in lib.bsa_last_error().decode()
+    assert app(tail, tail_k=FAKE + 8) == -1
+    assert app(tok, codes=None) == -1 and "proj" in lib.bsa_last_error().decode()
+    assert app(tok, codes=None, proj=FAKE) == -1

@@ -336,3 +336,90 @@ def test_fp8_projected_cache_decodes_every_code():
     torch.cuda.synchronize()
     PU.check_token_scores(w, 0, 0, host(d.scores[0, 0]), rows)
 
+
+
+APPEND_CASES = {
+    # name: (spec, cache dtype)
+    "block": (dataclasses.replace(W.SPECS["ragged"], name="append_block", seed=111, batch=5,
+                                  kv_heads=2, q_heads=8, max_tokens=2048, budget=8, n_tail=0,
+                                  needle_count=2, lengths=(0, 127, 250, 1900, 2048)), "f16"),
+    "block_tail1": (dataclasses.replace(W.SPECS["ragged"], name="append_tail1", seed=112, batch=5,
+                                        kv_heads=2, q_heads=8, max_tokens=2048, budget=8,
+                                        n_tail=1, needle_count=2,
+                                        lengths=(0, 127, 250, 1900, 2048)), "f16"),
+    "block_tail2_bf16": (dataclasses.replace(W.SPECS["ragged"], name="append_tail2", seed=113,
+                                             batch=5, kv_heads=2, q_heads=8, max_tokens=2048,
+                                             budget=8, n_tail=2, needle_count=2,
+                                             lengths=(0, 127, 250, 1900, 2048)), "bf16"),
+    "token": (dataclasses.replace(W.SPECS["token"], name="append_token", seed=114, batch=3,
+                                  kv_heads=2, q_heads=8, max_tokens=2048, budget=256,
+                                  lengths=(0, 1000, 2000)), "f16"),
+    "token_fp8": (dataclasses.replace(W.SPECS["token_fp8"], name="append_fp8", seed=115, batch=3,
+                                      kv_heads=2, q_heads=8, max_tokens=2048, budget=256,
+                                      lengths=(0, 1000, 2000)), "f16"),
+}
+
+
+@pytest.mark.parametrize("case", list(APPEND_CASES))
+def test_append_tokens_match_the_bulk_build(case):
+    """bsa_append_token, one call per decode step, from lengths that start empty,
+    inside a page, at a page edge and full (page starts, tail shifts, sequences
+    that fill up on the way): the cache rows, the key copy and the BF16 tail
+    store end bit-identical to the oracle's build of the final cache, and a step
+    on the appended cache matches the oracle."""
+    from oracle import decode as O
+
+    spec, kv_dtype = APPEND_CASES[case]
+    w = W.generate(spec)
+    d = upload(w, kv_dtype=kv_dtype)
+    d.pack()
+    B, Hkv, T, nt = spec.batch, spec.kv_heads, spec.max_tokens, spec.n_tail
+    lens = np.asarray(w.seq_lens, dtype=np.int64).copy()
+    k_exp = d.k.cpu().clone()  # the cache dtype
+    v_exp = d.v.cpu().clone()
+    if nt:  # the tail store the appends keep up: BF16 pages of the cache rows
+        kf, vf = k_exp.float().numpy(), v_exp.float().numpy()
+        for name, rows in (("tail_k", kf), ("tail_v", vf)):
+            st = np.stack([np.stack([O.tail_store_from_cache(rows[b, h], int(lens[b]), nt)
+                                     for h in range(Hkv)]) for b in range(B)])
+            getattr(d, name).copy_(torch.from_numpy(st.view(np.int16)))
+    n_app = 300
+    rng = np.random.default_rng([spec.seed, 7])
+    dt = d.k.dtype
+    k_new = torch.from_numpy(rng.standard_normal((n_app, B, Hkv, 128), dtype=np.float32)).to(dt)
+    v_new = torch.from_numpy(rng.standard_normal((n_app, B, Hkv, 128), dtype=np.float32)).to(dt)
+    k_new_d, v_new_d = k_new.cuda(), v_new.cuda()
+    _say(f"[append] {case}: {n_app} tokens from lengths {lens.tolist()}")
+    for i in range(n_app):
+        d.append(k_new_d[i], v_new_d[i])
+        for b in range(B):
+            if lens[b] < T:
+                k_exp[b, :, lens[b]] = k_new[i, b]
+                v_exp[b, :, lens[b]] = v_new[i, b]
+        lens = np.minimum(lens + 1, T)
+        d.seq_lens.add_(1).clamp_(max=T)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(d.seq_lens), lens)
+    assert torch.equal(d.k.cpu(), k_exp) and torch.equal(d.v.cpu(), v_exp)
+    kf, vf = k_exp.float().numpy(), v_exp.float().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            if spec.granularity == "block":
+                # every token's records: the appended ones and those the bulk pack wrote
+                PU.check_pack_block(dataclasses.replace(w, k=kf), b, h, host(d.codes[b, h]),
+                                    host(d.scales[b, h]))
+            else:
+                PU.check_pack_token(dataclasses.replace(w, k=kf), b, h, host(d.kproj[b, h]))
+            if nt:
+                for name, rows in (("tail_k", kf), ("tail_v", vf)):
+                    exp = O.tail_store_from_cache(rows[b, h], int(lens[b]), nt)
+                    got = host(getattr(d, name)[b, h]).view(np.uint16)
+                    assert np.array_equal(got, exp), f"{name} differs at {(b, h)}"
+    # a decode step on the appended cache
+    tails = {}
+    if nt:
+        tails = dict(tail_k=host(d.tail_k).view(np.uint16), tail_v=host(d.tail_v).view(np.uint16))
+    w2 = dataclasses.replace(w, k=kf, v=vf, seq_lens=lens.astype(np.int32), **tails)
+    d.run()
+    torch.cuda.synchronize()
+    check_all(w2, d)
