@@ -181,6 +181,53 @@ def dequant_blocks(code_rec: np.ndarray, scale_rec: np.ndarray) -> np.ndarray:
 # block's valid tokens (t < L). Blocks outside the packed region score -inf.
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# A1q: NVFP4 query for the scan (Jet-QSparse abstract: the scan's query-key
+# products run natively in FP4, on 4-bit operands on both sides)
+#
+# Reading: the pages give no query format or scale rule. Each query head's 128
+# channels are quantized as the keys are (A0), without centering, with a
+# per-head FP32 scale s_q = fl32(amax / 2688) -- amax / (6 * 448), so the group
+# that holds the head's largest magnitude gets the largest E4M3 scale. A head of
+# zeros quantizes to zeros. The scan then scores the dequantized query
+# qtilde = e2m1 * e4m3 * s_q in place of q in both of its terms; attention keeps
+# the FP16 query (the output is formed in FP16 on the pages).
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def quantize_query(q_group: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """q_group [G, 128] (fp16 values) -> (codes [G, 128], scale bytes [G, 8],
+    per-head scales s_q [G] float32)."""
+    q = np.asarray(q_group).astype(F32)
+    G = q.shape[0]
+    codes = np.zeros((G, HEAD_DIM), dtype=np.uint8)
+    sb = np.zeros((G, NGROUPS), dtype=np.uint8)
+    s_q = np.zeros(G, dtype=F32)
+    for h in range(G):
+        amax = F32(np.abs(q[h]).max())
+        s_q[h] = F32(amax / F32(E2M1_MAX * E4M3_MAX))
+        if s_q[h] > 0:  # else: every code and scale stays 0
+            codes[h], sb[h] = pack_nvfp4(q[h], np.zeros(HEAD_DIM, dtype=F32), float(s_q[h]))
+    return codes, sb, s_q
+
+
+def dequant_query(codes: np.ndarray, sb: np.ndarray, s_q: np.ndarray) -> np.ndarray:
+    """qtilde [G, 128] float64: e2m1 * e4m3 * s_q, exact."""
+    e = nvfp4.e2m1_decode(codes) * np.repeat(nvfp4.e4m3_decode(sb), GROUP, axis=-1)
+    return e * np.asarray(s_q, dtype=np.float64)[:, None]
+
+
+def scan_query(q_group: np.ndarray, query_fmt: str = "f16") -> np.ndarray:
+    """The query the block scan scores with: q itself, or qtilde for "nvfp4"."""
+    if query_fmt == "f16":
+        return np.asarray(q_group, dtype=np.float64)
+    if query_fmt != "nvfp4":
+        raise ValueError(query_fmt)
+    return dequant_query(*quantize_query(q_group))
+
+
 def scan_block_unit(q_group: np.ndarray, code_rec: np.ndarray, scale_rec: np.ndarray,
                     global_scale: float, center: np.ndarray, seq_len: int, n_tail: int,
                     sigma: float, max_blocks: Optional[int] = None) -> np.ndarray:

@@ -157,3 +157,100 @@ def test_scan_max_over_group_heads():
     per_head = np.stack([O.scan_block_unit(q[h:h + 1], rc, rs, st, c, 256, 0, SIGMA)
                          for h in range(4)])
     assert np.array_equal(full, per_head.max(axis=0))
+
+
+# ---- the NVFP4 query (scan only) -------------------------------------------
+
+def _exact_query(rng, G, sq_exp=-12):
+    """Heads whose values are exactly e2m1 * e4m3 * 2^sq_exp, every group holding
+    a +-6 and one group per head at scale 448, so amax = 2688 * 2^sq_exp and
+    s_q = 2^sq_exp."""
+    sb = rng.integers(0x08, 0x7E, (G, 8))
+    top = rng.integers(0, 8, G)
+    sb[np.arange(G), top] = 0x7E
+    e = rng.integers(0, 16, (G, 8, 16))
+    e[e == 8] = 0  # no -0
+    # every group holds a +-6, so its amax sets its scale
+    e[np.arange(G)[:, None], np.arange(8)[None, :], rng.integers(0, 16, (G, 8))] = \
+        7 + 8 * rng.integers(0, 2, (G, 8))
+    vals = nvfp4.e2m1_decode(e) * nvfp4.e4m3_decode(sb)[..., None] * 2.0 ** sq_exp
+    q = vals.reshape(G, 128).astype(np.float16)
+    assert np.array_equal(q.astype(np.float64), vals.reshape(G, 128))  # exact in fp16
+    return q, e.reshape(G, 128).astype(np.uint8), sb.astype(np.uint8)
+
+
+def test_query_quantizer_round_trips_representable_heads():
+    rng = np.random.default_rng(11)
+    q, e, sb = _exact_query(rng, 16)
+    codes, scales, s_q = O.quantize_query(q)
+    assert np.array_equal(s_q, np.full(16, 2.0 ** -12, np.float32))
+    assert np.array_equal(scales, sb)
+    assert np.array_equal(codes, e)
+    assert np.array_equal(O.dequant_query(codes, scales, s_q), q.astype(np.float64))
+    assert np.array_equal(O.scan_query(q, "nvfp4"), q.astype(np.float64))
+
+
+def test_query_scale_puts_the_largest_group_at_448():
+    rng = np.random.default_rng(12)
+    q = (rng.standard_normal((64, 128)) * rng.uniform(0.01, 30, (64, 1))).astype(np.float16)
+    codes, sb, s_q = O.quantize_query(q)
+    amax = np.abs(q.astype(np.float32)).max(axis=1)
+    assert np.array_equal(s_q, (amax / np.float32(2688.0)).astype(np.float32))
+    g = np.abs(q.astype(np.float32)).reshape(64, 8, 16).max(axis=2).argmax(axis=1)
+    assert np.all(sb[np.arange(64), g] == 0x7E)
+    assert np.all(sb <= 0x7E)
+
+
+def test_query_quantizer_is_scale_invariant_by_powers_of_two():
+    rng = np.random.default_rng(13)
+    q = (rng.standard_normal((8, 128)) * 0.5).astype(np.float16)
+    c0, s0, q0 = O.quantize_query(q)
+    for k in (-3, 2, 5):
+        c1, s1, q1 = O.quantize_query((q.astype(np.float32) * 2.0 ** k).astype(np.float16))
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+        assert np.array_equal(q1, (q0 * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def test_query_quantizer_error_bound():
+    rng = np.random.default_rng(14)
+    q = (rng.standard_normal((256, 128)) * 2).astype(np.float16)
+    codes, sb, s_q = O.quantize_query(q)
+    S = nvfp4.e4m3_decode(sb) * s_q.astype(np.float64)[:, None]
+    x = q.astype(np.float64) / np.repeat(S, 16, axis=1)
+    xq = nvfp4.e2m1_decode(codes)
+    assert np.all(np.abs(x) <= 6 * (1 + 2 ** -3))
+    gap = np.where(np.abs(xq) < 2, 0.25, np.where(np.abs(xq) < 4, 0.5, 1.0))
+    assert np.all(np.abs(x - xq) <= gap + 1e-6)
+    qt = O.scan_query(q, "nvfp4")
+    assert np.all(np.abs(qt - q) <= np.repeat(S, 16, axis=1) * (gap + 1e-6))
+
+
+def test_zero_query_head_scores_zero():
+    rng = np.random.default_rng(15)
+    k = rng.standard_normal((256, 128)).astype(np.float16)
+    c = rng.standard_normal(128).astype(np.float32)
+    codes, sb, s_q = O.quantize_query(np.zeros((2, 128), np.float16))
+    assert not codes.any() and not sb.any() and not s_q.any()
+    st = np.float32(2.0 ** -6)
+    rc, rs = O.pack_unit_blocks(k, c, st, 0, 2)
+    s = O.scan_block_unit(O.scan_query(np.zeros((2, 128), np.float16), "nvfp4"), rc, rs, st, c,
+                          256, 0, SIGMA)
+    assert np.array_equal(s, np.zeros(2))
+
+
+def test_quantized_query_scan_equals_exact_logits():
+    """Representable keys and a non-representable query: the scores are the exact
+    logits of qtilde, which differ from those of q."""
+    rng = np.random.default_rng(16)
+    st = 2.0 ** -6
+    center = rng.integers(-4, 5, 128) * 0.125
+    k, _, _, _ = _exact_keys(rng, 256, center, st)
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    qt = O.scan_query(q, "nvfp4")
+    rc, rs = O.pack_unit_blocks(k, center.astype(np.float32), st, 0, 2)
+    s = O.scan_block_unit(qt, rc, rs, st, center.astype(np.float32), 256, 0, SIGMA)
+    for blk in range(2):
+        rows = k[blk * 128:(blk + 1) * 128].astype(np.float64)
+        best = SIGMA * (rows @ qt.T).max()
+        assert abs(s[blk] - best) <= 1e-12 * max(1.0, abs(best))
+        assert best != SIGMA * (rows @ q.astype(np.float64).T).max()
