@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="jetqsparse",
-                    choices=["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8"])
+    from block_sparse_attention_pack_amd.workloads import ORDER
+
+    ap.add_argument("--workload", default="jetqsparse", choices=ORDER)
     ap.add_argument("--layers", type=int, default=4, help="distinct KV-cache copies rotated per step")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-dense", dest="dense", action="store_false",
@@ -172,8 +173,8 @@ def cpu_baseline(w, budget_s: float):
             rc, rs = rec
             tk = w.tail_k[b, h] if s.n_tail else None
             tv = w.tail_v[b, h] if s.n_tail else None
-            sc = O.scan_block_unit(qg, rc, rs, w.global_scale[h], w.key_center[h], L, s.n_tail,
-                                   sigma, s.max_blocks)
+            sc = O.scan_block_unit(O.scan_query(qg, s.query_fmt), rc, rs, w.global_scale[h],
+                                   w.key_center[h], L, s.n_tail, sigma, s.max_blocks)
             idx, _ = O.select_blocks_unit(sc, L, s.n_tail, s.budget)
             rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
         else:
@@ -318,7 +319,8 @@ def main() -> int:
                    "granularity": spec.granularity, "budget": spec.budget,
                    "tail_pages": spec.n_tail, "splits": d0.splits, "layers_rotated": a.layers,
                    "calls": a.mode,
-                   "scan": "e2m1*e4m3 -> f16 MFMA, f32 acc" if d0.block_mode
+                   "scan": ("%s query, e2m1*e4m3 keys -> f16 MFMA, f32 acc" % spec.query_fmt)
+                   if d0.block_mode
                    else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank)},
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": nbytes["total"],

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libbsa.so")
 DTYPE_F16, DTYPE_BF16 = 0, 1
 BLOCK, TOKEN = 0, 1
 PROJ_BF16, PROJ_FP8 = 0, 1
+QUERY_F16, QUERY_NVFP4 = 0, 1
 
 ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "WORKSPACE"}
 
@@ -52,6 +53,7 @@ class SelectCfg(ctypes.Structure):
         ("proj_rank", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("proj_dtype", ctypes.c_int32),
+        ("query_dtype", ctypes.c_int32),
     ]
 
 
@@ -146,10 +148,11 @@ def layout_for(k, num_q_heads: int, dtype: Optional[int] = None) -> KvLayout:
 
 def select_cfg(granularity: int, budget: int, n_tail_pages: int = 0, proj_rank: int = 0,
                softmax_scale: Optional[float] = None, head_dim: int = 128,
-               proj_dtype: int = PROJ_BF16) -> SelectCfg:
+               proj_dtype: int = PROJ_BF16, query_dtype: int = QUERY_F16) -> SelectCfg:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
-    return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale, proj_dtype)
+    return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale, proj_dtype,
+                     query_dtype)
 
 
 def version() -> str:

@@ -88,9 +88,15 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
     BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16 || r >= 16, BSA_ERR_UNSUPPORTED,
                 "an FP8 projected cache needs proj_rank >= 16");
   }
-  if (c->granularity == BSA_GRANULARITY_BLOCK)
+  if (c->granularity == BSA_GRANULARITY_BLOCK) {
     BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16, BSA_ERR_INVALID_ARG,
                 "proj_dtype applies to token mode only (must be 0 in block mode)");
+    BSA_REQUIRE(c->query_dtype == BSA_QUERY_F16 || c->query_dtype == BSA_QUERY_NVFP4,
+                BSA_ERR_UNSUPPORTED, "query_dtype %d", c->query_dtype);
+  } else {
+    BSA_REQUIRE(c->query_dtype == BSA_QUERY_F16, BSA_ERR_INVALID_ARG,
+                "query_dtype applies to block mode only (must be 0 in token mode)");
+  }
   g->B = L->batch;
   g->Hkv = L->num_kv_heads;
   g->Hq = L->num_q_heads;
@@ -189,7 +195,8 @@ hipError_t launch_scan(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const 
                        const int32_t* seq_lens, float* scores, hipStream_t s) {
   const _Float16* qh = static_cast<const _Float16*>(q);
   if (cfg->granularity == BSA_GRANULARITY_BLOCK)
-    return bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale, qh, codes, scales,
+    return bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale,
+                                  cfg->query_dtype == BSA_QUERY_NVFP4, qh, codes, scales,
                                   global_scale, key_center, seq_lens, scores, s);
   return bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank,
                                 cfg->proj_dtype == BSA_PROJ_FP8, qh, kproj, proj, seq_lens,
@@ -467,7 +474,7 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
     hipError_t e;
     if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
       e = bsa::launch_step(g, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
-                           static_cast<const _Float16*>(q), codes, scales, global_scale,
+                           cfg->query_dtype == BSA_QUERY_NVFP4, static_cast<const _Float16*>(q), codes, scales, global_scale,
                            key_center, k, v, seq_lens, tail_k, tail_v, num_splits, scores, idx,
                            count, part_o, part_lse, counters, out, out_lse, s);
     } else {

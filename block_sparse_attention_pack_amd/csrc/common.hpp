@@ -33,6 +33,46 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
+// Nearest E4M3FN code of r >= 0, ties to the even code, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_from_float(float r) {
+  if (!(r > 0.0f)) return 0u;
+  if (r >= 448.0f) return 0x7Eu;
+  const int e = int((__float_as_uint(r) >> 23) & 0xFFu) - 127;  // r is a normal float here
+  uint32_t code;
+  if (e < -6) {
+    // subnormal range: value = m * 2^-9, m in 0..8 (m = 8 is the smallest normal)
+    code = uint32_t(__builtin_rintf(__builtin_ldexpf(r, 9)));
+  } else {
+    // r = 2^e * (1 + f), mantissa 3 bits: m = rne((r / 2^e - 1) * 8), may carry to 8
+    const float frac = __builtin_ldexpf(r, 3 - e) - 8.0f;  // exact
+    const uint32_t m = uint32_t(__builtin_rintf(frac));
+    code = (uint32_t(e + 7) << 3) + m;
+  }
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Nearest E2M1 code of x (ties to the even code, saturating at 6), sign from x.
+__device__ __forceinline__ uint32_t e2m1_from_float(float x) {
+  const float a = __builtin_fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;        // 0   (0.25 ties to code 0)
+  else if (a < 0.75f) c = 1;    // 0.5
+  else if (a <= 1.25f) c = 2;   // 1   (0.75 and 1.25 tie to code 2)
+  else if (a < 1.75f) c = 3;    // 1.5
+  else if (a <= 2.5f) c = 4;    // 2   (1.75 and 2.5 tie to code 4)
+  else if (a < 3.5f) c = 5;     // 3
+  else if (a <= 5.0f) c = 6;    // 4   (3.5 and 5 tie to code 6)
+  else c = 7;                   // 6   (saturation)
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// Value of an E2M1 code (sign in bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_to_float(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e ? __builtin_ldexpf(float(2u + m), int(e) - 2) : 0.5f * float(m);
+  return (c & 8u) ? -mag : mag;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -183,10 +223,10 @@ hipError_t launch_append(const UnitGeom& g, int n_tail, int rank, bool fp8, cons
                          const float* center, const float* gscale, uint8_t* codes,
                          uint8_t* scales, const float* proj, void* kproj, uint16_t* tail_k,
                          uint16_t* tail_v, hipStream_t s);
-hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
-                             const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                             const float* center, const int32_t* seq_lens, float* scores,
-                             hipStream_t s);
+hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, bool query_nvfp4,
+                             const _Float16* q, const uint8_t* codes, const uint8_t* scales,
+                             const float* gscale, const float* center, const int32_t* seq_lens,
+                             float* scores, hipStream_t s);
 hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
                              const _Float16* q, const void* kproj, const float* proj,
                              const int32_t* seq_lens, float* scores, hipStream_t s);
@@ -215,7 +255,8 @@ hipError_t launch_combine(int rows, int splits, const float* part_o, const float
 // The block-mode decode step in one launch (scan, selection, attention, merge).
 // Its counters: step_counter_words(units) 32-bit words, zero before the launch.
 int step_counter_words(int units);
-hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, const _Float16* q,
+hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, bool query_nvfp4,
+                       const _Float16* q,
                        const uint8_t* codes, const uint8_t* scales, const float* gscale,
                        const float* center, const void* k, const void* v,
                        const int32_t* seq_lens, const uint16_t* tail_k, const uint16_t* tail_v,

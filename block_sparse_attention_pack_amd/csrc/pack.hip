@@ -15,39 +15,6 @@
 namespace bsa {
 namespace {
 
-// Nearest E4M3FN code of r >= 0, ties to the even code, saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_from_float(float r) {
-  if (!(r > 0.0f)) return 0u;
-  if (r >= 448.0f) return 0x7Eu;
-  const int e = int((__float_as_uint(r) >> 23) & 0xFFu) - 127;  // r is a normal float here
-  uint32_t code;
-  if (e < -6) {
-    // subnormal range: value = m * 2^-9, m in 0..8 (m = 8 is the smallest normal)
-    code = uint32_t(__builtin_rintf(__builtin_ldexpf(r, 9)));
-  } else {
-    // r = 2^e * (1 + f), mantissa 3 bits: m = rne((r / 2^e - 1) * 8), may carry to 8
-    const float frac = __builtin_ldexpf(r, 3 - e) - 8.0f;  // exact
-    const uint32_t m = uint32_t(__builtin_rintf(frac));
-    code = (uint32_t(e + 7) << 3) + m;
-  }
-  return code > 0x7Eu ? 0x7Eu : code;
-}
-
-// Nearest E2M1 code of x (ties to the even code, saturating at 6), sign from x.
-__device__ __forceinline__ uint32_t e2m1_from_float(float x) {
-  const float a = __builtin_fabsf(x);
-  uint32_t c;
-  if (a <= 0.25f) c = 0;        // 0   (0.25 ties to code 0)
-  else if (a < 0.75f) c = 1;    // 0.5
-  else if (a <= 1.25f) c = 2;   // 1   (0.75 and 1.25 tie to code 2)
-  else if (a < 1.75f) c = 3;    // 1.5
-  else if (a <= 2.5f) c = 4;    // 2   (1.75 and 2.5 tie to code 4)
-  else if (a < 3.5f) c = 5;     // 3
-  else if (a <= 5.0f) c = 6;    // 4   (3.5 and 5 tie to code 6)
-  else c = 7;                   // 6   (saturation)
-  return c | ((__float_as_uint(x) >> 28) & 8u);
-}
-
 template <int DT>
 __device__ __forceinline__ void load16(const uint16_t* p, float* out) {
   const uint4v a = *reinterpret_cast<const uint4v*>(p);

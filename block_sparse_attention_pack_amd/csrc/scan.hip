@@ -11,9 +11,13 @@
 namespace bsa {
 namespace {
 
-// grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads.
-__global__ __launch_bounds__(256) void scan_block_kernel(ScanBlockArgs a) {
-  scan_wave_blocks<false>(a, threadIdx.x & 63, threadIdx.x >> 6, blockIdx.y, blockIdx.x);
+// grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads. Q4: the
+// NVFP4 query (a.query_nvfp4).
+template <bool Q4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void scan_block_kernel(ScanBlockArgs a) {
+  __shared__ ScanQueryLds ql;
+  scan_wave_blocks<false, false, Q4>(a, threadIdx.x & 63, threadIdx.x >> 6, blockIdx.y,
+                                     blockIdx.x, ql);
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
@@ -158,14 +162,15 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
 
 }  // namespace
 
-hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
-                             const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                             const float* center, const int32_t* seq_lens, float* scores,
-                             hipStream_t s) {
+hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, bool query_nvfp4,
+                             const _Float16* q, const uint8_t* codes, const uint8_t* scales,
+                             const float* gscale, const float* center, const int32_t* seq_lens,
+                             float* scores, hipStream_t s) {
   dim3 grid;
-  const ScanBlockArgs a =
-      make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores, grid);
-  hipLaunchKernelGGL(scan_block_kernel, grid, dim3(256), 0, s, a);
+  const ScanBlockArgs a = make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center,
+                                         seq_lens, scores, grid, 4, query_nvfp4);
+  if (query_nvfp4) hipLaunchKernelGGL(scan_block_kernel<true>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(scan_block_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

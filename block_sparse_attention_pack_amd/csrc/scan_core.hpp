@@ -62,6 +62,7 @@ struct ScanBlockArgs {
   const int32_t* seq_lens;
   float* scores;
   int Hkv, Hq, G, NBmax, Tmax, n_tail, bpw;
+  int query_nvfp4;  // score with the NVFP4-quantized query (BSA_QUERY_NVFP4)
   float sigma;
 };
 
@@ -87,38 +88,91 @@ struct ScanQuery {
   half8 qa[4];      // A operand: head row n = lane % 16 (zero beyond the group)
   float qc[4];      // q . c of the heads this output lane holds
   bool head_ok[4];
-  float s_t;
+  float sc[4];      // s_t (times the head's query scale s_q for an NVFP4 query)
 };
 
+// NVFP4 query (Jet-QSparse abstract: FP4 operands on both sides of the scan's
+// query-key products). Each head is quantized as the packer quantizes a key
+// (no centering): per-head scale s_q = amax / 2688, per 16 channels the E4M3
+// scale of amax_g / (6 s_q), elements E2M1(q / (e4m3 * s_q)); every step one
+// correctly rounded float32 operation. The work-group does it once per item,
+// 16 threads per head with 8 channels each, and leaves e2m1 * e4m3 (exact in
+// f16) and s_q in LDS; s_q multiplies the dot products instead.
+struct ScanQueryLds {
+  half8 q[kMaxGroup * 16];  // head n, channels 8 c .. 8 c + 7 at q[16 n + c]
+  float s_q[kMaxGroup];
+};
+
+// Every thread of the work-group calls it (it ends with a barrier).
+__device__ __forceinline__ void stage_nvfp4_query(const ScanBlockArgs& a, int b, int h,
+                                                  ScanQueryLds& ql) {
+#pragma clang fp contract(off)
+  const int t = threadIdx.x, head = t >> 4, chunk = t & 15;
+  const bool ok = head < a.G;
+  half8 v = half8{};
+  if (ok) v = *reinterpret_cast<const half8*>(a.q + (int64_t(b) * a.Hq + h * a.G + head) * kHeadDim +
+                                               8 * chunk);
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = fmaxf(am, __builtin_fabsf(float(v[e])));
+  const float ag = fmaxf(am, __shfl_xor(am, 1, kWave));  // the 16-channel group
+  float amax = ag;                                        // the head: 16 threads
+#pragma unroll
+  for (int off = 2; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  const float s_q = amax / 2688.0f;
+  const uint32_t sb = e4m3_from_float(ag / (6.0f * s_q));  // 0 for a head of zeros
+  const float e4 = e4m3_to_float(sb);
+  const float S = e4 * s_q;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t code = S > 0.0f ? e2m1_from_float(float(v[e]) / S) : 0u;
+    v[e] = _Float16(e2m1_to_float(code) * e4);
+  }
+  if (ok) {
+    ql.q[t] = v;
+    if (chunk == 0) ql.s_q[head] = s_q;
+  }
+  __syncthreads();
+}
+
+// ql: the staged NVFP4 query (query_nvfp4), else null.
 __device__ __forceinline__ void scan_query(ScanQuery& sq, const ScanBlockArgs& a, int b, int h,
-                                           int lane) {
+                                           int lane, const ScanQueryLds* ql) {
   const int n = lane & 15, j = lane >> 4;
   const int G = a.G;
   // A operand: query head row n, channels 32 j + 8 c .. + 8
   float qc_part = 0.0f;
   const bool row_ok = n < G;
   const _Float16* qrow = a.q + (int64_t(b) * a.Hq + h * G + (row_ok ? n : 0)) * kHeadDim + 32 * j;
+  half8 v[4];
+  float s_q = 1.0f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    half8 v = *reinterpret_cast<const half8*>(qrow + 8 * c);
-    if (!row_ok) v = half8{};
-    sq.qa[c] = v;
+    v[c] = ql ? ql->q[16 * (row_ok ? n : 0) + 4 * j + c] : *reinterpret_cast<const half8*>(qrow + 8 * c);
+    if (!row_ok) v[c] = half8{};
+  }
+  if (ql) s_q = row_ok ? ql->s_q[n] : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sq.qa[c] = v[c];
     if (a.center) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        qc_part += float(v[e]) * a.center[h * kHeadDim + 32 * j + 8 * c + e];
+        qc_part += float(v[c][e]) * a.center[h * kHeadDim + 32 * j + 8 * c + e];
     }
   }
   // q . c of head row n: sum over the 4 channel quarters (lanes n, n+16, n+32, n+48)
   qc_part += __shfl_xor(qc_part, 16, kWave);
   qc_part += __shfl_xor(qc_part, 32, kWave);
-  // output lane holds heads 4 j + r: fetch their q . c from lanes 4 j + r
+  qc_part *= s_q;
+  // output lane holds heads 4 j + r: fetch their q . c and s_q from lanes 4 j + r
+  const float s_t = a.gscale[h];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     sq.qc[r] = __shfl(qc_part, 4 * j + r, kWave);
+    sq.sc[r] = s_t * __shfl(s_q, 4 * j + r, kWave);
     sq.head_ok[r] = 4 * j + r < G;
   }
-  sq.s_t = a.gscale[h];
 }
 
 // The score of one landed block with `valid` tokens (wave-uniform result).
@@ -144,7 +198,7 @@ __device__ __forceinline__ float scan_score(const ScanRec& r, const ScanQuery& s
   float best = -__builtin_inff();
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (sq.head_ok[q]) best = fmaxf(best, sq.s_t * m[q] + sq.qc[q]);
+    if (sq.head_ok[q]) best = fmaxf(best, sq.sc[q] * m[q] + sq.qc[q]);
   return sigma * wave_max_uniform(best);
 }
 
@@ -154,15 +208,20 @@ __device__ __forceinline__ float scan_score(const ScanRec& r, const ScanQuery& s
 // launch). PIPE: two blocks in flight (the next block's loads are issued
 // before the current block is scored), for launches whose register budget
 // allows it; the scores are the same either way.
-template <bool COHERENT, bool PIPE = false>
+//
+// Every wave of the work-group calls it for the same unit (with query_nvfp4 the
+// group stages the query together); ql: LDS for that query. Without PIPE the
+// query format is the template argument Q4 (the FP16 form keeps its registers).
+template <bool COHERENT, bool PIPE = false, bool Q4 = false>
 __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lane, int wave,
-                                                 int unit, int item) {
+                                                 int unit, int item, ScanQueryLds& ql) {
   const int b = unit / a.Hkv, h = unit % a.Hkv;
   const int L = clamp_len(a.seq_lens[b], a.Tmax);
   const int npages = ceil_div(L, kBlock);
   const int packed = npages - a.n_tail > 0 ? npages - a.n_tail : 0;
+  // a wave past the last block has nothing to load or score, but still takes
+  // part in the query stage
   const int blk_begin = (item * kScanWaves + wave) * a.bpw;
-  if (blk_begin >= a.NBmax) return;
   const int blk_end = min(blk_begin + a.bpw, a.NBmax);
   float* out = a.scores + int64_t(unit) * a.NBmax;
   // blocks past the packed pages (tail pages, beyond the sequence) score -inf
@@ -171,23 +230,39 @@ __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lan
     for (int blk = sc_end; blk < blk_end; ++blk) put_score<COHERENT>(out + blk, -__builtin_inff());
   auto valid_of = [&](int blk) { return min(kBlock, L - blk * kBlock); };
 
+  const ScanQueryLds* qp = a.query_nvfp4 ? &ql : nullptr;
+  // The first block's loads (the first two with PIPE) go out before the query
+  // is formed, so the query's own latency overlaps them.
   if constexpr (PIPE) {
     ScanRec r0, r1;
     if (blk_begin < sc_end) scan_load(r0, a, unit, blk_begin, lane);
-    ScanQuery sq;  // its loads overlap the first block's
-    scan_query(sq, a, b, h, lane);
+    if (blk_begin + 1 < sc_end) scan_load(r1, a, unit, blk_begin + 1, lane);
+    if (qp) stage_nvfp4_query(a, b, h, ql);
+    ScanQuery sq;
+    scan_query(sq, a, b, h, lane, qp);
     for (int blk = blk_begin; blk < sc_end; blk += 2) {
-      if (blk + 1 < sc_end) scan_load(r1, a, unit, blk + 1, lane);
       const float s0 = scan_score(r0, sq, valid_of(blk), a.sigma, lane);
       if (lane == 0) put_score<COHERENT>(out + blk, s0);
-      if (blk + 1 >= sc_end) break;
       if (blk + 2 < sc_end) scan_load(r0, a, unit, blk + 2, lane);
+      if (blk + 1 >= sc_end) break;
       const float s1 = scan_score(r1, sq, valid_of(blk + 1), a.sigma, lane);
       if (lane == 0) put_score<COHERENT>(out + blk + 1, s1);
+      if (blk + 3 < sc_end) scan_load(r1, a, unit, blk + 3, lane);
+    }
+  } else if constexpr (Q4) {
+    ScanRec r;
+    if (blk_begin < sc_end) scan_load(r, a, unit, blk_begin, lane);
+    stage_nvfp4_query(a, b, h, ql);
+    ScanQuery sq;
+    scan_query(sq, a, b, h, lane, &ql);
+    for (int blk = blk_begin; blk < sc_end; ++blk) {
+      if (blk > blk_begin) scan_load(r, a, unit, blk, lane);
+      const float s = scan_score(r, sq, valid_of(blk), a.sigma, lane);
+      if (lane == 0) put_score<COHERENT>(out + blk, s);
     }
   } else {
     ScanQuery sq;
-    scan_query(sq, a, b, h, lane);
+    scan_query(sq, a, b, h, lane, nullptr);
     for (int blk = blk_begin; blk < sc_end; ++blk) {
       ScanRec r;
       scan_load(r, a, unit, blk, lane);
@@ -201,7 +276,7 @@ __device__ __forceinline__ void scan_wave_blocks(const ScanBlockArgs& a, int lan
 ScanBlockArgs make_scan_args(const UnitGeom& g, int n_tail, float sigma, const _Float16* q,
                              const uint8_t* codes, const uint8_t* scales, const float* gscale,
                              const float* center, const int32_t* seq_lens, float* scores,
-                             dim3& grid, int max_bpw = 4) {
+                             dim3& grid, int max_bpw = 4, bool query_nvfp4 = false) {
   const int units = g.B * g.Hkv;
   // enough work-groups to fill 256 CUs several times over
   int bpw = max_bpw;
@@ -222,6 +297,7 @@ ScanBlockArgs make_scan_args(const UnitGeom& g, int n_tail, float sigma, const _
   a.Tmax = g.Tmax;
   a.n_tail = n_tail;
   a.bpw = bpw;
+  a.query_nvfp4 = query_nvfp4 ? 1 : 0;
   a.sigma = sigma;
   return a;
 }

@@ -102,6 +102,7 @@ template <int G, bool MAIN_BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 1))) void step_kernel(
     StepArgs s) {
   __shared__ AttnLds<G> lds;
+  __shared__ ScanQueryLds scan_ql;  // the NVFP4 query of a scan item
   __shared__ uint32_t ticket;
   const int cls = blockIdx.x % s.classes;
   const int n = (s.units - cls + s.classes - 1) / s.classes;  // units of this class
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   Item it = decode_ticket(int(ticket), n, s.scan_items, s.splits);
   it.unit = cls + s.classes * it.unit;
   if (it.scan) {
-    scan_wave_blocks<true, true>(s.scan, threadIdx.x & 63, threadIdx.x >> 6, it.unit, it.index);
+    scan_wave_blocks<true, true>(s.scan, threadIdx.x & 63, threadIdx.x >> 6, it.unit, it.index,
+                                 scan_ql);
     wait_all_memory();  // the scores have reached the coherence point
     __syncthreads();
     uint32_t* ctr = s.sync.scan_done + kLineWords * it.unit;
@@ -153,7 +155,8 @@ int step_counter_words(int units) {
   return units + kLineWords * units + kLineWords * kStepClasses + 1;
 }
 
-hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, const _Float16* q,
+hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, bool query_nvfp4,
+                       const _Float16* q,
                        const uint8_t* codes, const uint8_t* scales, const float* gscale,
                        const float* center, const void* k, const void* v,
                        const int32_t* seq_lens, const uint16_t* tail_k, const uint16_t* tail_v,
@@ -166,7 +169,7 @@ hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, c
   dim3 scan_grid;
   // up to 8 blocks per wave: each scan item ends with a wait for its stores
   s.scan = make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center, seq_lens, scores,
-                          scan_grid, 8);
+                          scan_grid, 8, query_nvfp4);
   AttnArgs& a = s.attn;
   a.q = q;
   a.k = static_cast<const uint16_t*>(k);

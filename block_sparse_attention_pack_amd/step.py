@@ -149,7 +149,7 @@ class DeviceStep:
         gran = "block" if self.block_mode else "token"
         cfg = bsa.select_cfg(self.cfg.granularity, budget, self.cfg.n_tail_pages,
                              self.cfg.proj_rank, self.cfg.softmax_scale,
-                             proj_dtype=self.cfg.proj_dtype)
+                             proj_dtype=self.cfg.proj_dtype, query_dtype=self.cfg.query_dtype)
         if splits is None:
             splits = default_splits(B * Hkv, budget, gran)
         dev = self.q.device
@@ -212,7 +212,8 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
     gran = bsa.BLOCK if s.granularity == "block" else bsa.TOKEN
     fp8 = gran == bsa.TOKEN and s.proj_fmt == "fp8"
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
-                         w.softmax_scale, proj_dtype=bsa.PROJ_FP8 if fp8 else bsa.PROJ_BF16)
+                         w.softmax_scale, proj_dtype=bsa.PROJ_FP8 if fp8 else bsa.PROJ_BF16,
+                         query_dtype=bsa.QUERY_NVFP4 if s.query_fmt == "nvfp4" else bsa.QUERY_F16)
     if splits is None:
         splits = default_splits(B * Hkv, s.budget, s.granularity, one_launch)
     nb = s.max_blocks

@@ -72,6 +72,7 @@ class Spec:
     ragged: bool = False  # lengths uniform in [max_tokens/2, max_tokens]
     rank: int = 0  # projection rank in token mode
     proj_fmt: str = "bf16"  # token mode: projected-key cache storage, "bf16" or "fp8"
+    query_fmt: str = "f16"  # block mode: the query the scan scores with, "f16" or "nvfp4"
     lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
@@ -102,9 +103,13 @@ SPECS: Dict[str, Spec] = {
     # the token workload's inputs (same seed) with an FP8 projected-key cache
     "token_fp8": Spec("token_fp8", 4, 8, 8, 32, 131072, "token", 2048, rank=32,
                       proj_fmt="fp8"),
+    # the Jet-QSparse decode shape's inputs (same seed), scanned with an NVFP4 query
+    "jetqsparse_q4": Spec("jetqsparse_q4", 2, 16, 4, 16, 131072, "block", 64,
+                          needle_count=20, needle_profile="zipf", needle_strength=3.0,
+                          key_offset_std=2.0, query_fmt="nvfp4"),
 }
 
-ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8"]
+ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,

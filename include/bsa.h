@@ -69,6 +69,15 @@ enum { BSA_GRANULARITY_BLOCK = 0, BSA_GRANULARITY_TOKEN = 1 };
  * both): BF16, or FP8 as OCP E4M3FN bytes. */
 enum { BSA_PROJ_BF16 = 0, BSA_PROJ_FP8 = 1 };
 
+/* The query the block scan scores with (Jet-QSparse abstract: the scan's
+ * query-key products run natively in FP4). F16: the step's query as given.
+ * NVFP4: each query head quantized as a key is packed (no centering; per-head
+ * FP32 scale s_q = amax / 2688, one E4M3 scale per 16 channels, E2M1 elements,
+ * each step one correctly rounded float32 operation; a head of zeros stays
+ * zero), and the dequantized query qtilde replaces q in both terms of the
+ * score. The attention always uses the FP16 query. */
+enum { BSA_QUERY_F16 = 0, BSA_QUERY_NVFP4 = 1 };
+
 /* Standard GQA KV cache: K and V are [batch][num_kv_heads][max_tokens][head_dim]
  * through the strides below (in elements, head_dim contiguous). Query head hq
  * belongs to KV head hq / (num_q_heads / num_kv_heads). */
@@ -94,6 +103,7 @@ typedef struct bsa_select_cfg {
   int32_t proj_rank;    /* TOKEN: r in {8, 16, 32, 64, 128} (16 .. 128 for FP8); BLOCK: ignored */
   float softmax_scale;  /* sigma, > 0 (1/sqrt(128) for the standard scale) */
   int32_t proj_dtype;   /* TOKEN: BSA_PROJ_BF16 or BSA_PROJ_FP8; BLOCK: must be BSA_PROJ_BF16 (0) */
+  int32_t query_dtype;  /* BLOCK: BSA_QUERY_F16 or BSA_QUERY_NVFP4; TOKEN: must be BSA_QUERY_F16 (0) */
 } bsa_select_cfg;
 
 /* ---------------------------------------------------------------------------

@@ -32,6 +32,11 @@ def q_group(w, b, h):
     return w.q[b, h * G:(h + 1) * G]
 
 
+def scan_q(w, b, h):
+    """The query the block scan scores with (the FP16 query, or its NVFP4 form)."""
+    return O.scan_query(q_group(w, b, h), w.spec.query_fmt)
+
+
 def check_pack_block(w, b, h, codes_gpu, scales_gpu):
     nb = w.spec.max_blocks
     rc, rs = O.pack_unit_blocks(w.k[b, h], w.key_center[h], w.global_scale[h], 0, nb)
@@ -55,7 +60,7 @@ def check_pack_token(w, b, h, kproj_gpu, tokens=None):
 def block_score_bound(w, b, h, rc, rs):
     """Per-block magnitude A of the estimated logits (see the module docstring)."""
     nb = w.spec.max_blocks
-    qg = np.abs(q_group(w, b, h).astype(np.float64))
+    qg = np.abs(scan_q(w, b, h))
     deq = np.abs(O.dequant_blocks(rc, rs)).reshape(nb, 128, 128)
     sigma = w.softmax_scale
     a = sigma * (float(w.global_scale[h]) * (deq @ qg.T) +
@@ -65,7 +70,7 @@ def block_score_bound(w, b, h, rc, rs):
 
 def check_block_scores(w, b, h, scores_gpu, rc, rs):
     s = w.spec
-    ref = O.scan_block_unit(q_group(w, b, h), rc, rs, w.global_scale[h], w.key_center[h],
+    ref = O.scan_block_unit(scan_q(w, b, h), rc, rs, w.global_scale[h], w.key_center[h],
                             int(w.seq_lens[b]), s.n_tail, w.softmax_scale, s.max_blocks)
     fin = np.isfinite(ref)
     assert np.array_equal(fin, np.isfinite(scores_gpu)), f"-inf pattern differs at {(b, h)}"

@@ -196,3 +196,13 @@ def test_append_checks_its_arguments(lib):
     assert app(tail, tail_k=FAKE + 8) == -1
     assert app(tok, codes=None) == -1 and "proj" in lib.bsa_last_error().decode()
     assert app(tok, codes=None, proj=FAKE) == -1
+
+
+def test_query_format_is_checked(lib):
+    L = _layout()
+    q4 = B.select_cfg(B.BLOCK, 8, query_dtype=B.QUERY_NVFP4)
+    assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(q4)) == 0  # a valid cfg
+    assert _scan(lib, L, B.select_cfg(B.BLOCK, 8, query_dtype=5)) == -2
+    assert "query_dtype" in lib.bsa_last_error().decode()
+    assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 32, query_dtype=B.QUERY_NVFP4)) == -1
+    assert "block mode only" in lib.bsa_last_error().decode()

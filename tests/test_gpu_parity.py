@@ -59,6 +59,7 @@ REDUCED = {
     "ragged": W.reduced("ragged", 16384, batch=3, budget=24),
     "token": W.reduced("token", 16384, batch=2),
     "token_fp8": W.reduced("token_fp8", 16384, batch=2),
+    "jetqsparse_q4": W.reduced("jetqsparse_q4", 8192, batch=2),
 }
 
 
@@ -423,3 +424,38 @@ def test_append_tokens_match_the_bulk_build(case):
     d.run()
     torch.cuda.synchronize()
     check_all(w2, d)
+
+
+def test_nvfp4_query_reads_back_every_element():
+    """The scan's NVFP4 query, element by element: block i of a unit holds the
+    one-hot key e_i (center 0), so block score i is a positive multiple of
+    qtilde_i. Head 0 puts elements on every E2M1 tie and spreads the group scales
+    over normal and subnormal E4M3 codes; head 1 is all zeros."""
+    T = 128 * 128
+    spec = dataclasses.replace(W.SPECS["jetqsparse_q4"], name="q4_elements", batch=1, kv_heads=2,
+                               q_heads=2, max_tokens=T, budget=8, needle_count=0,
+                               key_offset_std=0.0)
+    w = W.generate(spec)
+    k = np.zeros((1, 2, T, 128), np.float16)
+    for i in range(128):
+        k[0, :, i * 128:(i + 1) * 128, i] = 1.0
+    # head 0: s_q = 2^-12 (group 5 at scale 448 holds the largest 6); in units of
+    # its group's scale, every group holds a 6 and the E2M1 ties
+    x = np.array([6, -0.25, 0.75, -1.25, 1.75, 2.5, -3.5, 5, 0.375, 1, -1.5, 2, 3, 4.5, -6, 0])
+    scale_codes = [0x7D, 0x40, 0x31, 0x03, 0x09, 0x7E, 0x22, 0x58]
+    from oracle import nvfp4
+    q = np.zeros((1, 2, 128), np.float64)
+    for g, code in enumerate(scale_codes):
+        q[0, 0, 16 * g:16 * (g + 1)] = np.roll(x, g) * nvfp4.e4m3_value(code) * 2.0 ** -12
+    q16 = q.astype(np.float16)
+    assert np.array_equal(q16.astype(np.float64), q)  # exact in fp16
+    st = np.full(2, np.float32(1.0) / np.float32(2688.0), np.float32)
+    w2 = dataclasses.replace(w, k=k, q=q16, key_center=np.zeros((2, 128), np.float32),
+                             global_scale=st)
+    d = run_step(w2)
+    check_all(w2, d)
+    got = host(d.scores[0, 0]).astype(np.float64)
+    qt = PU.scan_q(w2, 0, 0)[0]
+    assert np.all(np.sign(got) == np.sign(qt))
+    assert np.allclose(got, got[np.argmax(qt)] / qt.max() * qt, rtol=1e-6, atol=0)
+    assert np.array_equal(host(d.scores[0, 1]), np.zeros(128, np.float32))
