@@ -301,7 +301,10 @@ struct AttnLds {
   // same LDS holds the waves' accumulators for the merge
   static constexpr int kScFloats = G * CHUNK, kAccFloats = G * kHeadDim;
   static constexpr int kShare = kScFloats > kAccFloats ? kScFloats : kAccFloats;
-  float sc[kAttnWaves * kShare];
+  union {
+    float sc[kAttnWaves * kShare];
+    ScanQueryLds scan_q;  // a decode-step scan item's query (no attention state then)
+  };
   float m[kAttnWaves][16], l[kAttnWaves][16];
   half8 qa[4 * kWave];       // q in the MFMA operand order
   bf16x8 qsplit[8 * kWave];  // q = q_hi + q_lo in the MFMA operand order

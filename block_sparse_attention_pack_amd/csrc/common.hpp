@@ -22,6 +22,14 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 
+// The block scan's NVFP4 query of one unit, staged in LDS by its work-group:
+// e2m1 * e4m3 of head n, channels 8 c .. 8 c + 7 at q[16 n + c]; the head's FP32
+// scale at s_q[n].
+struct ScanQueryLds {
+  half8 q[kMaxGroup * 16];
+  float s_q[kMaxGroup];
+};
+
 // --- number formats --------------------------------------------------------
 
 // OCP E4M3FN byte -> float (exact). 0x7F / 0xFF (NaN) never occur in a packed

@@ -97,12 +97,7 @@ struct ScanQuery {
 // scale of amax_g / (6 s_q), elements E2M1(q / (e4m3 * s_q)); every step one
 // correctly rounded float32 operation. The work-group does it once per item,
 // 16 threads per head with 8 channels each, and leaves e2m1 * e4m3 (exact in
-// f16) and s_q in LDS; s_q multiplies the dot products instead.
-struct ScanQueryLds {
-  half8 q[kMaxGroup * 16];  // head n, channels 8 c .. 8 c + 7 at q[16 n + c]
-  float s_q[kMaxGroup];
-};
-
+// f16) and s_q in LDS (ScanQueryLds); s_q multiplies the dot products instead.
 // Every thread of the work-group calls it (it ends with a barrier).
 __device__ __forceinline__ void stage_nvfp4_query(const ScanBlockArgs& a, int b, int h,
                                                   ScanQueryLds& ql) {

@@ -1,12 +1,16 @@
 // Top-k selection of one unit by one 256-thread work-group (block mode).
 //
-// Scores become order-preserving 32-bit keys. A radix select over 8-bit digits
-// (LDS histograms, at most four passes, stopping once the bucket that holds the
-// boundary is taken whole) finds the exact key kappa of the picks-th largest
-// candidate. Each thread owns a contiguous range of candidate indices, so
-// block-wide scans of the taken-by-key and tied counts place every chosen index: the
-// output is ascending, and of the candidates tied at kappa the lowest indices
-// are taken. The forced tail pages follow the scanned blocks.
+// Scores become order-preserving 32-bit keys. A radix select finds the exact
+// key kappa of the picks-th largest candidate: its first digit starts at the
+// highest bit in which the candidates' keys differ (the bits above are common
+// to all of them), digits are up to 8 bits wide, and the passes stop once the
+// bucket that holds the boundary is taken whole. A pass costs two barriers: the
+// histograms alternate between two LDS buffers (the next one is cleared while
+// the current one fills), and one wave scans the 256 bins and names the
+// boundary bucket. Each thread owns a contiguous range of candidate indices, so
+// one block-wide scan of the taken-by-key and tied counts places every chosen
+// index: the output is ascending, and of the candidates tied at kappa the lowest
+// indices are taken. The forced tail pages follow the scanned blocks.
 #pragma once
 
 #include "common.hpp"
@@ -18,9 +22,46 @@ constexpr int kSelectRegKeys = 8;  // rows up to 2048 candidates stay in registe
 
 struct SelectLds {
   uint32_t hist[256];
+  uint32_t hist2[256];  // the block select's second histogram (passes alternate)
   int wave_tot[kSelectThreads / kWave];
-  int beta, above;
+  int wave_tot2[kSelectThreads / kWave];
+  uint32_t wave_lo[kSelectThreads / kWave], wave_hi[kSelectThreads / kWave];
+  int beta, above, inb;
 };
+
+// Inclusive scans of two ints per thread over the work-group, with one pair of
+// barriers; tv, tw: the totals.
+__device__ __forceinline__ void select_block_scan2(int& v, int& w, SelectLds& s, int& tv,
+                                                   int& tw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int nv = __shfl_up(v, off, kWave), nw = __shfl_up(w, off, kWave);
+    if (lane >= off) {
+      v += nv;
+      w += nw;
+    }
+  }
+  if (lane == kWave - 1) {
+    s.wave_tot[wave] = v;
+    s.wave_tot2[wave] = w;
+  }
+  __syncthreads();
+  int bv = 0, bw = 0;
+  tv = 0;
+  tw = 0;
+#pragma unroll
+  for (int k = 0; k < kSelectThreads / kWave; ++k) {
+    const int xv = s.wave_tot[k], xw = s.wave_tot2[k];
+    bv += k < wave ? xv : 0;
+    bw += k < wave ? xw : 0;
+    tv += xv;
+    tw += xw;
+  }
+  __syncthreads();
+  v += bv;
+  w += bw;
+}
 
 // Inclusive scan of one int per thread over the 256-thread work-group.
 __device__ __forceinline__ int select_block_scan(int v, SelectLds& s, int& total) {
@@ -96,47 +137,93 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
   int r_eq = 0;
   bool take_ge = false;
   const bool take_all = picks == C;
+  const int lane = tid & 63, wave = tid >> 6;
   if (!take_all && picks > 0) {
-    uint32_t prefix = 0;
-    int bits = 0, r = picks;
-    while (true) {
-      const int shift = 24 - bits;
-      s.hist[tid] = 0;
-      __syncthreads();
-      for_each_key([&](int, uint32_t key) {
-        if (bits == 0 || (key >> (shift + 8)) == prefix)
-          atomicAdd(&s.hist[(key >> shift) & 0xFFu], 1u);
-      });
-      __syncthreads();
-      // thread t looks at bin d = 255 - t; the inclusive scan counts bins >= d
-      const int d = 255 - tid;
-      const int hd = int(s.hist[d]);
-      if (tid == 0) {  // defined results even if no bin qualifies (ordered by the scan's barriers)
-        s.beta = 0;
-        s.above = 0;
-      }
-      int total;
-      const int ge = select_block_scan(hd, s, total);
-      const int above = ge - hd;  // keys in bins above d
-      if (above < r && r <= ge) {
-        s.beta = d;
-        s.above = above;
-      }
-      __syncthreads();
-      const int beta = s.beta, above_beta = s.above;
-      const int in_bucket = int(s.hist[beta]);
-      __syncthreads();
-      r -= above_beta;
-      prefix = (prefix << 8) | uint32_t(beta);
-      bits += 8;
-      if (r == in_bucket) {  // the whole bucket is taken
-        take_ge = true;
-        kge = prefix << (32 - bits);
-        break;
-      }
-      if (bits == 32) {
+    // the candidates' key range
+    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+    for_each_key([&](int, uint32_t key) {
+      klo = key < klo ? key : klo;
+      khi = key > khi ? key : khi;
+    });
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t ol = uint32_t(__shfl_xor(int(klo), off, kWave));
+      const uint32_t oh = uint32_t(__shfl_xor(int(khi), off, kWave));
+      klo = ol < klo ? ol : klo;
+      khi = oh > khi ? oh : khi;
+    }
+    if (lane == 0) {
+      s.wave_lo[wave] = klo;
+      s.wave_hi[wave] = khi;
+    }
+    s.hist[tid] = 0;  // the first pass's histogram
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSelectThreads / kWave; ++k) {
+      klo = s.wave_lo[k] < klo ? s.wave_lo[k] : klo;
+      khi = s.wave_hi[k] > khi ? s.wave_hi[k] : khi;
+    }
+    // bits [hi, 32) are common to every candidate; prefix holds them
+    const uint32_t diff = klo ^ khi;
+    int hi = diff ? 32 - __builtin_clz(diff) : 0;
+    uint32_t prefix = hi < 32 ? khi >> hi : 0u;
+    int r = picks;
+    for (int pass = 0;; ++pass) {
+      if (hi == 0) {  // every bit resolved: kappa = prefix, r of its ties are taken
         kgt = keq = prefix;
         r_eq = r;
+        break;
+      }
+      const int width = hi < 8 ? hi : 8;
+      const int shift = hi - width;
+      uint32_t* cur = (pass & 1) ? s.hist2 : s.hist;
+      uint32_t* nxt = (pass & 1) ? s.hist : s.hist2;
+      nxt[tid] = 0;  // its last reader finished before the previous pass's last barrier
+      for_each_key([&](int, uint32_t key) {
+        if (hi == 32 || (key >> hi) == prefix)
+          atomicAdd(&cur[(key >> shift) & ((1u << width) - 1u)], 1u);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        // lane l takes bins 255 - 4 l .. 252 - 4 l (descending); ge counts the
+        // keys in bins >= d, above those in bins > d
+        if (lane == 0) {  // defined even if no bin qualified (the next writes win)
+          s.beta = 0;
+          s.above = 0;
+          s.inb = 0;
+        }
+        int c[4];
+        int run = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          run += int(cur[255 - 4 * lane - i]);
+          c[i] = run;
+        }
+        int incl = run;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int n = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += n;
+        }
+        const int P = incl - run;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int above = P + (i ? c[i - 1] : 0), ge = P + c[i];
+          if (above < r && r <= ge) {
+            s.beta = 255 - 4 * lane - i;
+            s.above = above;
+            s.inb = ge - above;
+          }
+        }
+      }
+      __syncthreads();
+      const int beta = s.beta, above_beta = s.above, in_bucket = s.inb;
+      r -= above_beta;
+      prefix = (prefix << width) | uint32_t(beta);
+      hi = shift;
+      if (r == in_bucket) {  // the whole bucket is taken
+        take_ge = true;
+        kge = prefix << hi;
         break;
       }
     }
@@ -152,9 +239,9 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
     ngt += taken_by_key(key);
     neq += tied(key);
   });
-  int tot_gt, tot_eq;
-  const int gt_before = select_block_scan(ngt, s, tot_gt) - ngt;
-  const int eq_before = select_block_scan(neq, s, tot_eq) - neq;
+  int sgt = ngt, seq = neq, tot_gt, tot_eq;
+  select_block_scan2(sgt, seq, s, tot_gt, tot_eq);
+  const int gt_before = sgt - ngt, eq_before = seq - neq;
   const int nsel = max(0, min(tot_gt + min(tot_eq, r_eq), budget));
   int pos = gt_before + min(eq_before, r_eq);
   int eq_seen = eq_before;

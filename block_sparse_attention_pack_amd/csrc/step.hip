@@ -102,7 +102,6 @@ template <int G, bool MAIN_BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 1))) void step_kernel(
     StepArgs s) {
   __shared__ AttnLds<G> lds;
-  __shared__ ScanQueryLds scan_ql;  // the NVFP4 query of a scan item
   __shared__ uint32_t ticket;
   const int cls = blockIdx.x % s.classes;
   const int n = (s.units - cls + s.classes - 1) / s.classes;  // units of this class
@@ -122,7 +121,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   it.unit = cls + s.classes * it.unit;
   if (it.scan) {
     scan_wave_blocks<true, true>(s.scan, threadIdx.x & 63, threadIdx.x >> 6, it.unit, it.index,
-                                 scan_ql);
+                                 lds.scan_q);
     wait_all_memory();  // the scores have reached the coherence point
     __syncthreads();
     uint32_t* ctr = s.sync.scan_done + kLineWords * it.unit;
