@@ -3,8 +3,9 @@
 A step is one pass of the whole path for one layer: score_scan (4-bit dense
 scan or projected-key scan), select_topk, sparse_decode_attn and combine, over a batch of
 synthetic inputs already resident in HBM. By default (--mode auto) a block-mode
-step with at least 16384 scanned blocks is one decode_step launch, every other
-step two calls, score_scan and select_attend_combine. Consecutive steps rotate
+step with at least 16384 scanned blocks and sequence lengths that differ is one
+decode_step launch, every other step two calls, score_scan and
+select_attend_combine. Consecutive steps rotate
 over --layers distinct copies of the KV cache, as consecutive layers of a model
 would, so no step finds the previous step's data in the 256 MB Infinity Cache.
 
@@ -43,6 +44,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_SOURCES = {  # kernel: (file name stem, sources)
     "scan_block_kernel": ("scan_block_kernel", ["scan.hip", "scan_core.hpp", "common.hpp"]),
     "scan_token_kernel<32>": ("scan_token_kernel_r32", ["scan.hip", "common.hpp"]),
+    "scan_token_kernel<32, fp8>": ("scan_token_kernel_r32_fp8", ["scan.hip", "common.hpp"]),
     "step_kernel": ("step_kernel", ["step.hip", "scan_core.hpp", "attn_core.hpp",
                                     "select_core.hpp", "combine_core.hpp", "common.hpp"]),
 }
@@ -73,7 +75,7 @@ def parse():
                          "record costs the GPU a marker packet)")
     ap.add_argument("--mode", default="auto", choices=["auto", "step", "fused", "three", "split"],
                     help="auto: step where the one-launch step pays off (block mode, "
-                         ">= 16384 scanned blocks), else fused; "
+                         ">= 16384 scanned blocks, ragged lengths), else fused; "
                          "step: decode_step (one launch in block mode); "
                          "fused: score_scan, select_attend_combine; "
                          "three: score_scan, select_topk, attend_combine; "
@@ -89,7 +91,7 @@ def measured_traffic(kernel: str, workload: str):
     stem, sources = TRAFFIC_SOURCES[kernel]
     try:
         with open(os.path.join(ROOT, "profiles", f"{stem}.{workload}.traffic.md")) as f:
-            fields = dict(re.findall(r"^(\w+): (\S+)$", f.read(), re.M))
+            fields = dict(re.findall(r"^(\w+): (.+)$", f.read(), re.M))
         h = hashlib.sha256()
         for name in sources:
             with open(os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", name), "rb") as f:
@@ -219,7 +221,9 @@ def main() -> int:
     w = W.generate(spec, threads=16)
     log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
     if a.mode == "auto":
-        a.mode = "step" if one_launch_pays(spec.units, spec.max_blocks, spec.granularity) else "fused"
+        ragged = len(set(int(x) for x in w.seq_lens)) > 1
+        a.mode = "step" if one_launch_pays(spec.units, spec.max_blocks, spec.granularity,
+                                           ragged) else "fused"
     d0 = upload(w, splits=a.splits, one_launch=a.mode == "step")
     d0.pack()
     torch.cuda.synchronize()

@@ -40,11 +40,13 @@ def default_splits(units: int, budget: int, granularity: str, one_launch: bool =
     return max(1, min(s, budget))
 
 
-def one_launch_pays(units: int, max_blocks: int, granularity: str) -> bool:
+def one_launch_pays(units: int, max_blocks: int, granularity: str, ragged: bool) -> bool:
     """Whether the one-launch decode step beats scan + select_attend_combine:
-    in block mode once the scan covers at least 16384 blocks (measured on
-    MI355X: +0.4% at 64 x 1024 blocks, +6% with ragged lengths, -23% at 8 x 256)."""
-    return granularity != "token" and units * max_blocks >= 16384
+    in block mode, when the scan covers at least 16384 blocks and the sequence
+    lengths differ. Measured on MI355X: +3% at 64 x 1024 blocks with lengths
+    in [64K, 128K], where the two-call attention launch is unevenly loaded;
+    -0.9% at 64 x 1024 blocks of equal length; -23% at 8 x 256."""
+    return granularity != "token" and units * max_blocks >= 16384 and ragged
 
 
 @dataclasses.dataclass

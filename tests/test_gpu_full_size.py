@@ -3,7 +3,8 @@
 Each workload is drawn at its full size (up to 128K tokens, batch 16), packed,
 and run through the same calls bench.py times by default, with its default split
 count: one decode_step launch where that pays off (block mode, at least 16384
-scanned blocks), else score_scan and select_attend_combine. Every stage of a few sampled units
+scanned blocks, sequence lengths that differ), else score_scan and
+select_attend_combine. Every stage of a few sampled units
 (the first, the last and one in between) is then checked against the oracle:
 pack bytes bit-exact, scores within the FP32 accumulation bound, the selection
 bit-exact on the GPU's own scores, outputs within 2e-3.
@@ -42,7 +43,8 @@ def test_full_size_sampled_units(name):
     spec = W.SPECS[name]
     print(f"[full] {name}: generating", flush=True)
     w = W.generate(spec, threads=16)
-    one = one_launch_pays(spec.units, spec.max_blocks, spec.granularity)
+    one = one_launch_pays(spec.units, spec.max_blocks, spec.granularity,
+                          len(set(int(x) for x in w.seq_lens)) > 1)
     d = upload(w, one_launch=one)  # the default split count, as bench.py uses
     d.pack()
     if one:
