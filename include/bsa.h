@@ -187,7 +187,9 @@ int bsa_append_token(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
  *       block n with t < L_b of  sigma * (s_t[h] * q_hq . (E2M1 * E4M3)(t)
  *                                           + q_hq . c[h])
  *   (the centering vector is added back so the estimate targets q . k;
- *   key_center NULL means c = 0); every other block scores -inf.
+ *   key_center NULL means c = 0); every other block scores -inf. With
+ *   query_dtype = BSA_QUERY_NVFP4, q_hq is replaced in both terms by its NVFP4
+ *   form qtilde_hq (defined at BSA_QUERY_NVFP4).
  *   codes, scales, global_scale required; kproj, proj unused.
  * TOKEN (JSSA Figure 1): qbar = mean of the group's query heads,
  *   p = P[h]^T qbar, scores[b][h][t] = sigma * p . kproj[b][h][t] for t < L_b,
@@ -263,7 +265,7 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
  * bsa_score_select = bsa_score_scan followed by bsa_select_topk, and
  * bsa_attend_combine = bsa_sparse_decode_attn followed by bsa_combine over the
  * num_splits partials of each (sequence, query head), with identical outputs.
- With at most 8 splits bsa_attend_combine merges in the last attention
+ * With at most 8 splits bsa_attend_combine merges in the last attention
  * work-group of each unit to finish, so the merge hides behind other units'
  * attention (with more it launches the merge separately). That group is found
  * with one arrival counter per unit in `counters` (device, bsa_counters_size
