@@ -459,3 +459,17 @@ def test_nvfp4_query_reads_back_every_element():
     assert np.all(np.sign(got) == np.sign(qt))
     assert np.allclose(got, got[np.argmax(qt)] / qt.max() * qt, rtol=1e-6, atol=0)
     assert np.array_equal(host(d.scores[0, 1]), np.zeros(128, np.float32))
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_nvfp4_query_group_sizes(G):
+    """The NVFP4 query staged by 16 threads per head, from 1 to 16 heads per KV
+    head (all 256 threads at 16): scores against the oracle's quantized query,
+    and the one-launch step and the two calls give the four calls' bits."""
+    spec = dataclasses.replace(W.SPECS["jetqsparse_q4"], name=f"q4group{G}", seed=120 + G, batch=2,
+                               kv_heads=2, q_heads=2 * G, max_tokens=4096, budget=6,
+                               needle_count=2)
+    w = W.generate(spec)
+    d = run_step(w)
+    check_all(w, d)
+    _two_calls_match(d)
