@@ -473,3 +473,17 @@ def test_nvfp4_query_group_sizes(G):
     d = run_step(w)
     check_all(w, d)
     _two_calls_match(d)
+
+
+@pytest.mark.parametrize("rank,fmt", [(8, "bf16"), (16, "bf16"), (64, "bf16"), (128, "bf16"),
+                                      (16, "fp8"), (64, "fp8"), (128, "fp8")])
+def test_token_mode_every_rank(rank, fmt):
+    """The projected-key pack, scan and attention at every supported rank (a row
+    of 16 to 256 bytes: 1 to 16 lanes per token), BF16 and FP8, ragged lengths."""
+    spec = dataclasses.replace(W.SPECS["token"], name=f"rank{rank}{fmt}", seed=140 + rank,
+                               batch=2, kv_heads=2, q_heads=8, max_tokens=8192, budget=160,
+                               rank=rank, proj_fmt=fmt, lengths=(8192, 5003))
+    w = W.generate(spec)
+    d = run_step(w)
+    check_all(w, d)
+    _two_calls_match(d)
