@@ -487,3 +487,28 @@ def test_token_mode_every_rank(rank, fmt):
     d = run_step(w)
     check_all(w, d)
     _two_calls_match(d)
+
+
+@pytest.mark.parametrize("name", ["ragged", "token"])
+def test_token_major_interleaved_kv_layout(name):
+    """K and V in one token-major buffer [B][T][2][Hkv][128] (head stride 128,
+    token stride 2 * Hkv * 128): every stage through the layout's strides."""
+    from block_sparse_attention_pack_amd import binding as bsa
+
+    spec = REDUCED[name]
+    w = W.generate(spec)
+    d = upload(w)
+    B, Hkv, T = spec.batch, spec.kv_heads, spec.max_tokens
+    buf = torch.empty((B, T, 2, Hkv, 128), dtype=d.k.dtype, device=d.k.device)
+    kview = buf[:, :, 0].permute(0, 2, 1, 3)  # [B, Hkv, T, 128]
+    vview = buf[:, :, 1].permute(0, 2, 1, 3)
+    kview.copy_(d.k)
+    vview.copy_(d.v)
+    layout = bsa.layout_for(kview, spec.q_heads)
+    assert (layout.kv_stride_h, layout.kv_stride_t) == (128, 2 * Hkv * 128)
+    d = dataclasses.replace(d, k=kview, v=vview, layout=layout)
+    d.pack()
+    d.run()
+    torch.cuda.synchronize()
+    check_all(w, d)
+    _two_calls_match(d)
