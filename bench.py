@@ -73,11 +73,13 @@ def parse():
     ap.add_argument("--event-stride", type=int, default=25,
                     help="record the per-kernel events on every n-th timed step (each event "
                          "record costs the GPU a marker packet)")
-    ap.add_argument("--mode", default="auto", choices=["auto", "step", "fused", "three", "split"],
+    ap.add_argument("--mode", default="auto",
+                    choices=["auto", "step", "fused", "scoresel", "three", "split"],
                     help="auto: step where the one-launch step pays off (block mode, "
                          ">= 16384 scanned blocks, ragged lengths), else fused; "
                          "step: decode_step (one launch in block mode); "
                          "fused: score_scan, select_attend_combine; "
+                         "scoresel: score_select, attend_combine; "
                          "three: score_scan, select_topk, attend_combine; "
                          "split: score_scan, select_topk, sparse_decode_attn, combine")
     return ap.parse_args()
@@ -246,6 +248,9 @@ def main() -> int:
     elif a.mode == "fused":
         stages = ["scan", "select_attend_combine"]
         calls = lambda d: [d.scan, d.select_attend_combine]
+    elif a.mode == "scoresel":
+        stages = ["score_select", "attend_combine"]
+        calls = lambda d: [d.score_select, d.attend_combine]
     elif a.mode == "three":
         stages = ["scan", "select", "attend_combine"]
         calls = lambda d: [d.scan, d.select, d.attend_combine]

@@ -189,10 +189,14 @@ int check_merge_args(const float* out, const uint32_t* counters) {
   return BSA_OK;
 }
 
+// select_ws (token mode, optional): the selection's workspace; the scan then
+// also fills its histograms, and the selection that follows is launched with
+// hist_ready.
 hipError_t launch_scan(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
                        const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                        const float* key_center, const void* kproj, const float* proj,
-                       const int32_t* seq_lens, float* scores, hipStream_t s) {
+                       const int32_t* seq_lens, float* scores, hipStream_t s,
+                       void* select_ws = nullptr) {
   const _Float16* qh = static_cast<const _Float16*>(q);
   if (cfg->granularity == BSA_GRANULARITY_BLOCK)
     return bsa::launch_scan_block(g, cfg->n_tail_pages, cfg->softmax_scale,
@@ -200,16 +204,18 @@ hipError_t launch_scan(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const 
                                   global_scale, key_center, seq_lens, scores, s);
   return bsa::launch_scan_token(g, cfg->softmax_scale, cfg->proj_rank,
                                 cfg->proj_dtype == BSA_PROJ_FP8, qh, kproj, proj, seq_lens,
-                                scores, s);
+                                scores, static_cast<uint32_t*>(select_ws),
+                                bsa::token_unit_words(g), cfg->budget, s);
 }
 
 hipError_t launch_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const float* scores,
                          const int32_t* seq_lens, void* workspace, int32_t* idx, int32_t* count,
-                         hipStream_t s) {
+                         hipStream_t s, bool hist_ready = false) {
   if (cfg->granularity == BSA_GRANULARITY_BLOCK)
     return bsa::launch_select_block(g, cfg->budget, cfg->n_tail_pages, scores, seq_lens, idx,
                                     count, s);
-  return bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx, count, s);
+  return bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx, count, s,
+                                  hist_ready);
 }
 
 #define BSA_CHECK(expr)   \
@@ -386,9 +392,12 @@ int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    // token mode: the scan fills the selection's histograms as it goes
+    const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
     hipError_t e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
-                               seq_lens, scores, s);
-    if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
+                               seq_lens, scores, s, tok ? workspace : nullptr);
+    if (e == hipSuccess)
+      e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
     return hip_status(e, "score_select");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
@@ -474,13 +483,17 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
     hipError_t e;
     if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
       e = bsa::launch_step(g, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
-                           cfg->query_dtype == BSA_QUERY_NVFP4, static_cast<const _Float16*>(q), codes, scales, global_scale,
-                           key_center, k, v, seq_lens, tail_k, tail_v, num_splits, scores, idx,
-                           count, part_o, part_lse, counters, out, out_lse, s);
+                           cfg->query_dtype == BSA_QUERY_NVFP4, static_cast<const _Float16*>(q),
+                           codes, scales, global_scale, key_center, k, v, seq_lens, tail_k,
+                           tail_v, num_splits, scores, idx, count, part_o, part_lse, counters,
+                           out, out_lse, s);
     } else {
+      // token mode: the scan fills the selection's histograms as it goes
+      const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
       e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
-                      scores, s);
-      if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
+                      scores, s, tok ? workspace : nullptr);
+      if (e == hipSuccess)
+        e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
       if (e == hipSuccess)
         e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
                              part_o, part_lse, counters, out, out_lse, nullptr, nullptr, nullptr,

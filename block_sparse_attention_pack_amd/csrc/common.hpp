@@ -30,6 +30,11 @@ struct ScanQueryLds {
   float s_q[kMaxGroup];
 };
 
+// Token selection's first radix digit: the top 12 bits of a score's key
+// (score_key), counted per unit in a 4096-bin histogram.
+constexpr int kTokHistShift = 20;
+constexpr int kTokHistBins = 4096;
+
 // --- number formats --------------------------------------------------------
 
 // OCP E4M3FN byte -> float (exact). 0x7F / 0xFF (NaN) never occur in a packed
@@ -235,16 +240,21 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, bool qu
                              const _Float16* q, const uint8_t* codes, const uint8_t* scales,
                              const float* gscale, const float* center, const int32_t* seq_lens,
                              float* scores, hipStream_t s);
+// hist0 (optional): the token selection's workspace, whose per-unit
+// histograms (hist_stride words apart) the scan fills as tok_hist would.
 hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
                              const _Float16* q, const void* kproj, const float* proj,
-                             const int32_t* seq_lens, float* scores, hipStream_t s);
+                             const int32_t* seq_lens, float* scores, uint32_t* hist0,
+                             int64_t hist_stride, int budget, hipStream_t s);
 size_t token_select_workspace(const UnitGeom& g);
+int64_t token_unit_words(const UnitGeom& g);  // words per unit of that workspace
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
                                const int32_t* seq_lens, int32_t* idx, int32_t* count,
                                hipStream_t s);
+// hist_ready: the histograms were filled by launch_scan_token (tok_hist is skipped).
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
-                               hipStream_t s);
+                               hipStream_t s, bool hist_ready = false);
 // Largest budget for which the attention launch selects the blocks itself.
 constexpr int kFusedSelectMax = 1024;
 // The attention launch merges the splits in its last group up to this many

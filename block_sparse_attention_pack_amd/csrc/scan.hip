@@ -39,11 +39,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 constexpr int kTokPerWg = 16384;
 constexpr int kTokStagger = 13;  // steps between the starting points of consecutive waves
 
+//
+// With hist0 set, the work-group also counts its candidates' first select
+// digits (the top 12 key bits of scores of tokens < L) as the token
+// selection's tok_hist does: 16-bit counters, two per LDS word, filled while
+// the scores are stored, then added to the unit's histogram at hist0 + unit *
+// hist_stride. Units where the selection takes nothing or everything (picks 0
+// or L) are not counted, as there.
 template <int R, bool FP8>
 __global__ __launch_bounds__(256) void scan_token_kernel(
     const _Float16* __restrict__ q, const void* __restrict__ kproj,
     const float* __restrict__ proj, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma) {
+    float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma,
+    uint32_t* __restrict__ hist0, int64_t hist_stride, int budget) {
   constexpr int kRowBytes = FP8 ? R : 2 * R;
   constexpr int kPer = FP8 ? 16 : 8;      // entries of a row per 16-byte piece
   static_assert(kRowBytes % 16 == 0 && kRowBytes <= 256, "rank");
@@ -55,10 +63,15 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   __shared__ float part[256];
   __shared__ float p_lds[R];
   __shared__ __attribute__((aligned(16))) float keep[4][kPerWave];  // the scores, until the end
+  __shared__ uint32_t h16[kTokHistBins / 2];  // bin d at half d & 1 of word d / 2
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit % Hkv;
   const int L = clamp_len(seq_lens[b], Tmax);
+  const int picks = min(budget, L);
+  const bool do_hist = hist0 != nullptr && picks > 0 && picks < L;  // uniform
+  if (do_hist)
+    for (int w = threadIdx.x; w < kTokHistBins / 2; w += 256) h16[w] = 0u;  // before the barriers below
   const int t_wave = blockIdx.x * kTokPerWg + wave * kPerWave;
   const int t_end = min(t_wave + kPerWave, Tmax);
   const uint8_t* base = static_cast<const uint8_t*>(kproj) + int64_t(unit) * Tmax * kRowBytes;
@@ -166,12 +179,36 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   // the wave's scores, 1 KiB per store instruction (its own LDS rows: no barrier)
   wave_lds_sync();
   const int n = t_end > t_wave ? t_end - t_wave : 0;
+  auto count_key = [&](float sc, int t) {
+    if (t < L) {
+      const uint32_t d = score_key(sc) >> kTokHistShift;
+      atomicAdd(&h16[d >> 1], (d & 1u) ? 0x10000u : 1u);  // a count stays below 2^16
+    }
+  };
   for (int i = 4 * lane; i < n; i += 4 * kWave) {
     if (i + 4 <= n) {
-      __builtin_nontemporal_store(*reinterpret_cast<const float4v*>(&keep[wave][i]),
-                                  reinterpret_cast<float4v*>(out + t_wave + i));
+      const float4v x = *reinterpret_cast<const float4v*>(&keep[wave][i]);
+      __builtin_nontemporal_store(x, reinterpret_cast<float4v*>(out + t_wave + i));
+      if (do_hist) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) count_key(x[k], t_wave + i + k);
+      }
     } else {
-      for (int k = i; k < n; ++k) out[t_wave + k] = keep[wave][k];
+      for (int k = i; k < n; ++k) {
+        out[t_wave + k] = keep[wave][k];
+        if (do_hist) count_key(keep[wave][k], t_wave + k);
+      }
+    }
+  }
+  if (do_hist) {
+    __syncthreads();
+    uint32_t* hist = hist0 + int64_t(unit) * hist_stride;
+    for (int w = threadIdx.x; w < kTokHistBins / 2; w += 256) {
+      const uint32_t x = h16[w];
+      if (x & 0xFFFFu)
+        __hip_atomic_fetch_add(&hist[2 * w], x & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (x >> 16)
+        __hip_atomic_fetch_add(&hist[2 * w + 1], x >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -192,11 +229,12 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, bool qu
 
 hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
                              const _Float16* q, const void* kproj, const float* proj,
-                             const int32_t* seq_lens, float* scores, hipStream_t s) {
+                             const int32_t* seq_lens, float* scores, uint32_t* hist0,
+                             int64_t hist_stride, int budget, hipStream_t s) {
   dim3 grid(ceil_div(g.Tmax, kTokPerWg), g.B * g.Hkv);
 #define BSA_SCAN_TOKEN(RK, F8)                                                                  \
   hipLaunchKernelGGL((scan_token_kernel<RK, F8>), grid, dim3(256), 0, s, q, kproj, proj,         \
-                     seq_lens, scores, g.Hkv, g.Hq, g.G, g.Tmax, sigma)
+                     seq_lens, scores, g.Hkv, g.Hq, g.G, g.Tmax, sigma, hist0, hist_stride, budget)
   if (fp8) {
     switch (rank) {
       case 16: BSA_SCAN_TOKEN(16, true); break;

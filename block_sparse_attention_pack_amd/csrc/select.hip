@@ -44,8 +44,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_block_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kTokChunk = 16384;  // keys per work-group in hist and filter
 constexpr int kTokBatch = 32;     // loads in flight per thread (hist)
-constexpr int kTokBins = 4096;    // first digit: top 12 bits
-constexpr int kTokShift = 20;
+constexpr int kTokBins = kTokHistBins;    // first digit: top 12 bits
+constexpr int kTokShift = kTokHistShift;
 constexpr int kTokSlot = 64;      // words of the state slot
 constexpr int kTokWin = 4096;     // bitmap words per finish window
 constexpr int kTokWpt = kTokWin / kSelectThreads;  // 16 words per thread and window
@@ -530,14 +530,17 @@ size_t token_select_workspace(const UnitGeom& g) {
   return size_t(tok_geom(g.Tmax).unit_words) * 4 * size_t(g.B) * size_t(g.Hkv);
 }
 
+int64_t token_unit_words(const UnitGeom& g) { return tok_geom(g.Tmax).unit_words; }
+
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
-                               hipStream_t s) {
+                               hipStream_t s, bool hist_ready) {
   const TokGeom tg = tok_geom(g.Tmax);
   const int units = g.B * g.Hkv;
   const dim3 grid(ceil_div(g.Tmax, kTokChunk), units), block(kSelectThreads);
-  hipLaunchKernelGGL(tok_hist_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
-                     tg, ws);
+  if (!hist_ready)
+    hipLaunchKernelGGL(tok_hist_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
+                       tg, ws);
   hipLaunchKernelGGL(tok_filter_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
                      tg, ws);
   hipLaunchKernelGGL(tok_finish_kernel, dim3(units), block, 0, s, scores, g.Tmax, seq_lens, g.Hkv,

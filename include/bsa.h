@@ -280,7 +280,9 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
  * layout). */
 size_t bsa_counters_size(const bsa_kv_layout* layout);
 
-/* bsa_score_scan then bsa_select_topk; arguments as there. */
+/* bsa_score_scan then bsa_select_topk; arguments as there. In token mode the
+ * scan also counts the selection's first radix digits into the workspace as it
+ * stores the scores, so the selection skips its own pass over them. */
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                      const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                      const float* key_center, const void* kproj, const float* proj,
