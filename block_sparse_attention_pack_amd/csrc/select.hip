@@ -10,7 +10,8 @@
 //   hist    every group adds the histogram of its keys' top 12 bits (of the
 //           order-preserving key) to its unit's, with device-scope atomics
 //           (the histogram is zero on entry: the finish of the previous call
-//           leaves it so);
+//           leaves it so); skipped when the token scan has already counted
+//           them (bsa_score_select, bsa_decode_step);
 //   filter  every group finds from that histogram the top digit beta that
 //           holds the picks-th largest key and writes two bitmaps of its keys:
 //           those with a larger top digit (taken), and those with top digit
