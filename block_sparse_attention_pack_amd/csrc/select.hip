@@ -16,11 +16,12 @@
 //           holds the picks-th largest key and writes two bitmaps of its keys:
 //           those with a larger top digit (taken), and those with top digit
 //           beta (the bucket: usually about 1% of the keys);
-//   finish  one group per unit lists the bucket's keys in token order, finds
-//           the exact boundary key among them (radix select over the remaining
-//           20 bits), compacts the taken tokens in index order (those above
-//           the boundary key, and of its ties the lowest indices), and returns
-//           the unit's histogram to zero.
+//   finish  one group per chunk lists the bucket's keys, finds the exact
+//           boundary key among them (radix select over the remaining 20 bits)
+//           and writes its chunk's taken tokens in index order (those above
+//           the boundary key, and of its ties the lowest indices) at offsets
+//           counted from the bitmaps below the chunk; the groups share
+//           returning the unit's histogram to zero.
 #include "common.hpp"
 #include "select_core.hpp"
 
@@ -48,14 +49,9 @@ constexpr int kTokBatch = 32;     // loads in flight per thread (hist)
 constexpr int kTokBins = kTokHistBins;    // first digit: top 12 bits
 constexpr int kTokShift = kTokHistShift;
 constexpr int kTokSlot = 64;      // words of the state slot
-constexpr int kTokWin = 4096;     // bitmap words per finish window
-constexpr int kTokWpt = kTokWin / kSelectThreads;  // 16 words per thread and window
-constexpr int kTokWinPad = kTokWin + kTokWin / 16;
-constexpr int kTokStage = 8192;   // buckets up to this size are listed in LDS
-
-// LDS index of window word k: one pad word per 16 keeps a thread's 16
-// consecutive words in distinct banks from its neighbours'
-__device__ __forceinline__ int tok_pad(int k) { return k + (k >> 4); }
+constexpr int kTokChunkWords = kTokChunk / 32;
+constexpr int kTokWin = 4096;     // bitmap words per finish window: 16 per thread
+constexpr int kTokList = 4096;    // buckets up to this size are listed in LDS by the finish
 
 // What the unit's state says is taken.
 enum TokMode : uint32_t {
@@ -109,15 +105,15 @@ __device__ __forceinline__ void tok_counts(const int32_t* seq_lens, int unit, in
 }
 
 // Histogram of the top 12 key bits of the unit's candidates.
-// grid (ceil(Tmax / kTokChunk), B * Hkv), 256 threads.
+// grid (B * Hkv, ceil(Tmax / kTokChunk)), 256 threads.
 __global__ __launch_bounds__(kSelectThreads) void tok_hist_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
     int budget, TokGeom tg, void* ws) {
   __shared__ uint32_t hist[kTokBins];
-  const int unit = blockIdx.y, tid = threadIdx.x;
+  const int unit = blockIdx.x, tid = threadIdx.x;
   int C, picks;
   tok_counts(seq_lens, unit, Hkv, Tmax, budget, C, picks);
-  const int base = blockIdx.x * kTokChunk;
+  const int base = blockIdx.y * kTokChunk;
   if (picks == 0 || picks == C || base >= C) return;  // nothing to rank here
   for (int d = tid; d < kTokBins; d += kSelectThreads) hist[d] = 0u;
   __syncthreads();
@@ -181,8 +177,8 @@ __device__ __forceinline__ void tok_boundary(const uint32_t* ghist, int picks, S
 }
 
 // Bitmaps of the keys taken by their top digit and of the bucket (keys whose
-// top digit is the boundary digit). grid (ceil(Tmax / kTokChunk), B * Hkv),
-// 256 threads; wave w owns the 4096 keys from blockIdx.x * kTokChunk + 4096 w,
+// top digit is the boundary digit). grid (B * Hkv, ceil(Tmax / kTokChunk)),
+// 256 threads; wave w owns the 4096 keys from blockIdx.y * kTokChunk + 4096 w,
 // as 64 rows of 64; lane j keeps row j's two words of each bitmap, so each
 // bitmap is written with one 8-byte store per lane.
 __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
@@ -191,14 +187,14 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
   constexpr int kRows = kTokChunk / kSelectThreads;
   static_assert(kRows == kWave, "one 64-key row per lane");
   __shared__ SelectLds lds;
-  const int unit = blockIdx.y, tid = threadIdx.x;
+  const int unit = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const TokUnit u = tok_unit(ws, tg, unit);
   int C, picks;
   tok_counts(seq_lens, unit, Hkv, Tmax, budget, C, picks);
   uint32_t mode = picks == 0 ? kTokNone : (picks == C ? kTokAll : kTokBucket);
   const float* row = scores + int64_t(unit) * Tmax;
-  const int wbase = blockIdx.x * kTokChunk + wave * kRows * 64;
+  const int wbase = blockIdx.y * kTokChunk + wave * kRows * 64;
   // the keys are loaded before the boundary is known, so their latency
   // overlaps the histogram reads
   float v[kRows];
@@ -212,7 +208,7 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
     tok_boundary(u.hist, picks, lds, beta, above, in);
     if (picks - above == in) mode = kTokGe;
   }
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.y == 0 && tid == 0) {
     TokState s;
     s.mode = mode;
     s.beta = uint32_t(beta);
@@ -249,272 +245,304 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
   }
 }
 
+// Sums of N ints over the work-group (red: N ints per wave of LDS, used once).
+template <int N>
+__device__ __forceinline__ void tok_block_sum(int (&v)[N], int (*red)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off, kWave);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) red[wave][k] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kSelectThreads / kWave; ++w) t += red[w][k];
+    v[k] = t;
+  }
+}
+
+// A window of kTokWin bitmap words from word w0: thread t holds the 16 words
+// tok_word(w0, j) (four aligned groups of 4, the groups of a wave adjacent in
+// memory); words >= Wc read as 0. Every load is issued (at an address clamped
+// to the last 4-word group holding a word < Wc, which lies inside the bitmap)
+// and masked afterwards, so the loads of a window are all in flight together.
+__device__ __forceinline__ int tok_word(int w0, int j) {
+  return w0 + (j >> 2) * (kTokWin / 4) + 4 * int(threadIdx.x) + (j & 3);
+}
+__device__ __forceinline__ void tok_window(const uint32_t* src, int w0, int Wc,
+                                           uint32_t (&m)[16]) {
+  const int last = (Wc - 1) & ~3;  // Wc >= 1 here
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int w = tok_word(w0, 4 * q);
+    const uint4 x = *reinterpret_cast<const uint4*>(src + min(w, last));
+    m[4 * q] = w < Wc ? x.x : 0u;
+    m[4 * q + 1] = w + 1 < Wc ? x.y : 0u;
+    m[4 * q + 2] = w + 2 < Wc ? x.z : 0u;
+    m[4 * q + 3] = w + 3 < Wc ? x.w : 0u;
+  }
+}
+
+// The bin of a histogram of nb bins (nb / 256 per thread, highest first) that
+// holds the r-th largest entry: d, and the count above it. Defined (0, 0) when
+// no bin does. Synchronises the group.
+__device__ __forceinline__ void tok_bin_of_rank(const uint32_t* hist, int nb, int r,
+                                                SelectLds& lds, int& d_out, int& above_out) {
+  const int tid = threadIdx.x;
+  const int per = nb / kSelectThreads;
+  int mine = 0;
+  for (int j = 0; j < per; ++j) mine += int(hist[nb - 1 - (tid * per + j)]);
+  if (tid == 0) {  // ordered before the writes below by the scan's barriers
+    lds.beta = 0;
+    lds.above = 0;
+  }
+  int total;
+  int ab = select_block_scan(mine, lds, total) - mine;
+  for (int j = 0; j < per; ++j) {
+    const int d = nb - 1 - (tid * per + j);
+    const int hd = int(hist[d]);
+    if (ab < r && r <= ab + hd) {
+      lds.beta = d;
+      lds.above = ab;
+    }
+    ab += hd;
+  }
+  __syncthreads();
+  d_out = lds.beta;
+  above_out = lds.above;
+}
+
 // Resolve the bucket and compact the taken tokens in index order.
-// grid (B * Hkv), 256 threads. The bitmaps are read in windows of kTokWin
-// words (thread t owns window words 16 t .. 16 t + 15).
+// grid (B * Hkv, chunks), 256 threads: work-group c writes the output entries
+// of chunk c's tokens (thread t owns the chunk's bitmap words 2t, 2t + 1).
+// Every group of a unit first lists the bucket (keys and token indices) in LDS
+// when it holds at most kTokList keys, and finds the boundary key kb by a
+// radix select over the bucket's keys (their low 20 bits: a 12-bit digit, then
+// an 8-bit one); a larger bucket is walked in the bitmap, with its scores read
+// from memory, each time it is needed. A token is taken by key if its top
+// digit is above the boundary digit (the taken bitmap), or it is in the bucket
+// with a key above kb (>= kb when the 12-bit sub-bucket is taken whole); of the
+// tokens tied at kb the first r_eq in index order are taken. Its output
+// position is the number of tokens taken by key before it plus min(ties before
+// it, r_eq); the counts before the chunk come from the taken bitmap's words
+// below it and the bucket's keys below it. Group 0 also pads the output and
+// writes the count; the groups share returning the histogram to zero.
 __global__ __launch_bounds__(kSelectThreads) void tok_finish_kernel(
     const float* __restrict__ scores, int Tmax, const int32_t* __restrict__ seq_lens, int Hkv,
     int budget, TokGeom tg, void* ws, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-  __shared__ uint32_t wgt[kTokWinPad];
-  __shared__ uint32_t wbk[kTokWinPad];
-  __shared__ uint32_t hist[kTokBins];
-  __shared__ uint32_t skey[kTokStage];
-  __shared__ int32_t stok[kTokStage];
+  __shared__ uint32_t skey[kTokList];
+  __shared__ int32_t stok[kTokList];
+  __shared__ uint32_t hist[kTokBins];   // the 12-bit digit below beta
+  __shared__ uint32_t hist2[256];       // the last 8 bits
+  __shared__ uint32_t wtk[kTokChunkWords], wte[kTokChunkWords];
+  __shared__ int red[kSelectThreads / kWave][6];
   __shared__ SelectLds lds;
-  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int unit = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
   const TokUnit u = tok_unit(ws, tg, unit);
-  const TokState st = *u.st;
   int C, picks;
   tok_counts(seq_lens, unit, Hkv, Tmax, budget, C, picks);
+  const int cs = chunk * kTokChunk;  // the chunk's first token
+  // the histogram is not read here (the filter has read it): clear it now
+  for (int d = chunk * kSelectThreads + tid; d < kTokBins; d += int(gridDim.y) * kSelectThreads)
+    u.hist[d] = 0u;
+  if (chunk > 0 && cs >= C) return;  // no tokens here; group 0 always continues
   const float* row = scores + int64_t(unit) * Tmax;
   const int Wc = ceil_div(C, 32);
+  const int w0 = chunk * kTokChunkWords + 2 * tid;  // this thread's two chunk words
+  uint32_t tk[2], cb[2];  // their taken and bucket bits
+  {
+    const int wl = Wc > 0 ? min(w0, (Wc - 1) & ~1) : 0;  // even; a valid pair of words
+    const uint2 x = *reinterpret_cast<const uint2*>(u.gt + wl);
+    const uint2 y = *reinterpret_cast<const uint2*>(u.bk + wl);
+    tk[0] = w0 < Wc ? x.x : 0u;
+    tk[1] = w0 + 1 < Wc ? x.y : 0u;
+    cb[0] = w0 < Wc ? y.x : 0u;
+    cb[1] = w0 + 1 < Wc ? y.y : 0u;
+  }
+  const TokState st = *u.st;
+  for (int d = tid; d < kTokBins; d += kSelectThreads) hist[d] = 0u;
+  hist2[tid] = 0u;
+  wtk[2 * tid] = wtk[2 * tid + 1] = 0u;
+  wte[2 * tid] = wte[2 * tid + 1] = 0u;
   const bool bucket = st.mode == kTokBucket;
   const int n = bucket ? int(st.n) : 0;
-  const bool staged = n <= kTokStage;
-  const bool one_window = Wc <= kTokWin;
+  const bool listed = bucket && n <= kTokList;
+  const uint32_t beta = st.beta;
+  __syncthreads();
 
-  // window words [w0, w0 + kTokWin) of a bitmap into LDS; words >= Wc read as 0
-  auto load_window = [&](const uint32_t* src, uint32_t* dst, int w0) {
+  // ---- taken-by-digit counts (before the chunk, all); the bucket listed ----
+  // sums: 0, 1: taken by top digit (before the chunk, in all); 2, 3: bucket
+  // keys taken by key (likewise); 4, 5: ties at kb (likewise)
+  int sums[6] = {0, 0, 0, 0, 0, 0};
+  int nlist = 0;  // bucket entries listed so far (in token order)
+  for (int v0 = 0; v0 < Wc; v0 += kTokWin) {
+    uint32_t g[16], m[16];
+    tok_window(u.gt, v0, Wc, g);
+    tok_window(u.bk, v0, Wc, m);
+    int mine = 0;
 #pragma unroll
-    for (int m = 0; m < kTokWin / 4 / kSelectThreads; ++m) {
-      const int k = (m * kSelectThreads + tid) * 4;
-      const int w = w0 + k;
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      // w < Wc <= W: the 4 words are inside the bitmap (its size is a multiple of 64)
-      if (w < Wc) x = *reinterpret_cast<const uint4*>(src + w);
-      dst[tok_pad(k)] = x.x;
-      dst[tok_pad(k + 1)] = w + 1 < Wc ? x.y : 0u;
-      dst[tok_pad(k + 2)] = w + 2 < Wc ? x.z : 0u;
-      dst[tok_pad(k + 3)] = w + 3 < Wc ? x.w : 0u;
+    for (int j = 0; j < 16; ++j) {
+      const int x = __popc(g[j]);
+      sums[1] += x;
+      sums[0] += tok_word(v0, j) < chunk * kTokChunkWords ? x : 0;
+      mine += __popc(m[j]);
     }
-  };
-  // this thread's bucket bits of the window in wbk, and their number
-  auto my_bucket_words = [&](uint32_t (&m)[kTokWpt]) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < kTokWpt; ++j) {
-      m[j] = wbk[tok_pad(tid * kTokWpt + j)];
-      c += __popc(m[j]);
-    }
-    return c;
-  };
-
-  // ---- list the bucket in token order (when it fits in LDS) ----------------
-  int listed = 0;
-  if (bucket && staged) {
-    for (int w0 = 0; w0 < Wc; w0 += kTokWin) {
-      load_window(u.bk, wbk, w0);
-      __syncthreads();
-      uint32_t m[kTokWpt];
-      const int c = my_bucket_words(m);
+    if (listed) {  // uniform: every thread takes part in the scan
       int tot;
-      int off = listed + select_block_scan(c, lds, tot) - c;
+      int k = nlist + select_block_scan(mine, lds, tot) - mine;
 #pragma unroll
-      for (int j = 0; j < kTokWpt; ++j) {
+      for (int j = 0; j < 16; ++j) {
         uint32_t b = m[j];
         while (b) {
           const int bit = __builtin_ctz(b);
           b &= b - 1;
-          if (off < kTokStage) stok[off] = (w0 + tid * kTokWpt + j) * 32 + bit;
-          ++off;
+          if (k < kTokList) stok[k] = tok_word(v0, j) * 32 + bit;
+          ++k;
         }
       }
-      listed += tot;
-      if (!one_window) __syncthreads();  // the window buffer is reused
+      nlist += tot;
     }
-    listed = min(listed, kTokStage);
-    __syncthreads();
-#pragma unroll 4
-    for (int k = tid; k < listed; k += kSelectThreads) {
-      const int t = stok[k];
-      skey[k] = t < C ? score_key(row[t]) : 0u;  // t < C always
-    }
-    __syncthreads();
   }
-  // calls f(key, token) for every bucket key; every thread must call it
+  // calls f(key, token) for every bucket key (no barriers)
+  int nl = 0;
   auto for_each = [&](auto&& f) {
-    if (staged) {
-      for (int k = tid; k < listed; k += kSelectThreads) f(skey[k], stok[k]);
+    if (listed) {
+      for (int k = tid; k < nl; k += kSelectThreads) f(skey[k], stok[k]);
     } else {
-      for (int w0 = 0; w0 < Wc; w0 += kTokWin) {
-        __syncthreads();
-        load_window(u.bk, wbk, w0);
-        __syncthreads();
-        uint32_t m[kTokWpt];
-        my_bucket_words(m);
-        for (int j = 0; j < kTokWpt; ++j) {
+      for (int v0 = 0; v0 < Wc; v0 += kTokWin) {
+        uint32_t m[16];
+        tok_window(u.bk, v0, Wc, m);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
           uint32_t b = m[j];
           while (b) {
             const int bit = __builtin_ctz(b);
             b &= b - 1;
-            const int t = (w0 + tid * kTokWpt + j) * 32 + bit;
+            const int t = tok_word(v0, j) * 32 + bit;
             if (t < C) f(score_key(row[t]), t);
           }
         }
       }
-      __syncthreads();
     }
   };
+  auto count1 = [&](uint32_t key) { atomicAdd(&hist[(key >> 8) & uint32_t(kTokBins - 1)], 1u); };
+
+  // ---- the bucket's keys (listed: gathered), counted by their next 12 bits ----
+  if (listed) {
+    __syncthreads();
+    nl = min(nlist, kTokList);
+#pragma unroll 4
+    for (int k = tid; k < nl; k += kSelectThreads) {
+      const int t = stok[k];
+      const uint32_t key = uint32_t(t) < uint32_t(C) ? score_key(row[t]) : 0u;  // always inside
+      skey[k] = key;
+      count1(key);
+    }
+  } else if (bucket) {
+    for_each([&](uint32_t key, int) { count1(key); });
+  }
 
   // ---- radix select of the r-th largest bucket key over its low 20 bits ----
-  // (a 12-bit digit, then an 8-bit one)
   bool ge = false;
   uint32_t kb = 0;
   int r_eq = 0;
   if (bucket) {
-    int r = int(st.r);
-    uint32_t prefix = st.beta;
-    int bits = 12;
-    for (int level = 0; level < 2; ++level) {
-      const int w = level == 0 ? 12 : 8;
-      const int nb = 1 << w;
-      const int shift = 32 - bits - w;
-      for (int d = tid; d < nb; d += kSelectThreads) hist[d] = 0u;
-      __syncthreads();
+    __syncthreads();
+    int r = int(st.r), d1, ab1;
+    tok_bin_of_rank(hist, kTokBins, r, lds, d1, ab1);
+    r -= ab1;
+    const uint32_t p1 = (beta << 12) | uint32_t(d1);  // the key's top 24 bits
+    if (r == int(hist[d1])) {  // the sub-bucket is taken whole
+      ge = true;
+      kb = p1 << 8;
+    } else {
       for_each([&](uint32_t key, int) {
-        if ((key >> (32 - bits)) == prefix) atomicAdd(&hist[(key >> shift) & uint32_t(nb - 1)], 1u);
+        if ((key >> 8) == p1) atomicAdd(&hist2[key & 255u], 1u);
       });
       __syncthreads();
-      const int per = nb / kSelectThreads;  // 16 or 1 bins per thread, highest first
-      int mine = 0;
-      for (int j = 0; j < per; ++j) mine += int(hist[nb - 1 - (tid * per + j)]);
-      if (tid == 0) {  // defined results even if no bin qualifies
-        lds.beta = 0;
-        lds.above = 0;
-      }
-      int total;
-      int ab = select_block_scan(mine, lds, total) - mine;
-      for (int j = 0; j < per; ++j) {
-        const int d = nb - 1 - (tid * per + j);
-        const int hd = int(hist[d]);
-        if (ab < r && r <= ab + hd) {
-          lds.beta = d;
-          lds.above = ab;
-        }
-        ab += hd;
-      }
-      __syncthreads();
-      const int beta = lds.beta;
-      const int in_bucket = int(hist[beta]);
-      r -= lds.above;
-      prefix = (prefix << w) | uint32_t(beta);
-      bits += w;
-      __syncthreads();
-      if (r == in_bucket) {  // the sub-bucket is taken whole
-        ge = true;
-        kb = bits == 32 ? prefix : prefix << (32 - bits);
-        break;
-      }
+      int d2, ab2;
+      tok_bin_of_rank(hist2, 256, r, lds, d2, ab2);
+      kb = (p1 << 8) | uint32_t(d2);  // the exact boundary key; r of its ties are taken
+      r_eq = max(0, min(r - ab2, n));
     }
-    if (!ge) {
-      kb = prefix;  // the exact boundary key; r of its ties are taken
-      r_eq = max(0, min(r, n));
+  }
+  auto by_key = [&](uint32_t key) { return ge ? key >= kb : key > kb; };
+  auto tied = [&](uint32_t key) { return !ge && key == kb; };
+
+  // ---- bucket counts before the chunk, and the chunk's bucket bits ----------
+  if (bucket) {
+    for_each([&](uint32_t key, int t) {
+      const bool bk = by_key(key), te = tied(key);
+      sums[2] += bk && t < cs ? 1 : 0;
+      sums[3] += bk ? 1 : 0;
+      sums[4] += te && t < cs ? 1 : 0;
+      sums[5] += te ? 1 : 0;
+      if (listed && t >= cs && t < cs + kTokChunk && (bk || te)) {
+        const int wl = (t - cs) >> 5;
+        atomicOr(bk ? &wtk[wl] : &wte[wl], 1u << (t & 31));
+      }
+    });
+  }
+  tok_block_sum(sums, red);  // also orders the bit marks above before the reads below
+  int32_t* out = idx + int64_t(unit) * budget;
+  if (chunk == 0) {
+    const int nsel = max(0, min(sums[1] + sums[3] + min(sums[5], r_eq), budget));
+    for (int k = nsel + tid; k < budget; k += kSelectThreads) out[k] = -1;
+    if (tid == 0) count[unit] = nsel;
+  }
+  uint32_t te[2] = {0u, 0u};
+  if (listed) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      tk[j] |= wtk[2 * tid + j];
+      te[j] = wte[2 * tid + j];
+    }
+  } else if (bucket) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t b = cb[j];
+      while (b) {
+        const int bit = __builtin_ctz(b);
+        b &= b - 1;
+        const int t = (w0 + j) * 32 + bit;
+        if (t >= C) continue;
+        const uint32_t key = score_key(row[t]);
+        if (by_key(key)) tk[j] |= 1u << bit;
+        else if (tied(key)) te[j] |= 1u << bit;
+      }
     }
   }
 
-  // ---- compaction, window by window ---------------------------------------
-  // A token is taken by key if its top digit is above the boundary digit, or
-  // it is in the bucket with a key above kb (>= kb when ge); of the tokens tied
-  // at kb the first r_eq in index order are taken. Its output position is the
-  // number of tokens taken by key before it plus min(ties before it, r_eq).
-  // With the bucket listed in LDS (in token order), each window's bucket
-  // entries are one contiguous range of the list; its threads classify them
-  // in parallel into the window's taken bitmap (wgt) and a tie bitmap (wbk,
-  // free once the list is built). Otherwise each thread walks its own words'
-  // bucket bits and reads their scores.
-  int32_t* out = idx + int64_t(unit) * budget;
-  int gt_run = 0, eq_run = 0;
-  auto lower_bound = [&](int tok) {  // first list entry with token >= tok
-    int lo = 0, hi = listed;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (stok[mid] < tok) lo = mid + 1;
-      else hi = mid;
-    }
-    return lo;
-  };
-  for (int w0 = 0; w0 < Wc; w0 += kTokWin) {
-    __syncthreads();
-    load_window(u.gt, wgt, w0);
-    if (bucket) {
-      if (staged) {
-        for (int k = tid; k < kTokWinPad; k += kSelectThreads) wbk[k] = 0u;
-      } else {
-        load_window(u.bk, wbk, w0);
-      }
-    }
-    __syncthreads();
-    if (bucket && staged) {
-      const int lo = lower_bound(w0 * 32), hi = lower_bound((w0 + kTokWin) * 32);
-      for (int k = lo + tid; k < hi; k += kSelectThreads) {
-        const uint32_t key = skey[k];
-        const int t = stok[k];
-        const int wl = (t >> 5) - w0;  // in [0, kTokWin): t lies in this window
-        const uint32_t bit = 1u << (t & 31);
-        if (ge ? key >= kb : key > kb) atomicOr(&wgt[tok_pad(wl)], bit);
-        else if (!ge && key == kb) atomicOr(&wbk[tok_pad(wl)], bit);
-      }
-      __syncthreads();
-    }
-    uint32_t tk[kTokWpt], te[kTokWpt];
-    int ngt = 0, neq = 0;
-    if (bucket && !staged) {
-      uint32_t m[kTokWpt];
-      my_bucket_words(m);
+  // ---- positions and writes --------------------------------------------------
+  const int own_gt = __popc(tk[0]) + __popc(tk[1]), own_eq = __popc(te[0]) + __popc(te[1]);
+  int ngt = own_gt, neq = own_eq, tot_gt, tot_eq;
+  select_block_scan2(ngt, neq, lds, tot_gt, tot_eq);  // inclusive
+  int eq_seen = sums[4] + neq - own_eq;
+  int pos = sums[0] + sums[2] + ngt - own_gt + min(eq_seen, r_eq);
 #pragma unroll
-      for (int j = 0; j < kTokWpt; ++j) {
-        uint32_t taken = wgt[tok_pad(tid * kTokWpt + j)], tie = 0u, b = m[j];
-        while (b) {
-          const int bit = __builtin_ctz(b);
-          b &= b - 1;
-          const int t = (w0 + tid * kTokWpt + j) * 32 + bit;
-          const uint32_t key = t < C ? score_key(row[t]) : 0u;
-          if (ge ? key >= kb : key > kb) taken |= 1u << bit;
-          else if (!ge && key == kb) tie |= 1u << bit;
-        }
-        tk[j] = taken;
-        te[j] = tie;
-        ngt += __popc(taken);
-        neq += __popc(tie);
+  for (int j = 0; j < 2; ++j) {
+    uint32_t mm = tk[j] | te[j];
+    while (mm) {
+      const int bit = __builtin_ctz(mm);
+      mm &= mm - 1;
+      bool take = (tk[j] >> bit) & 1u;
+      if (!take) {  // tied at kb
+        take = eq_seen < r_eq;
+        ++eq_seen;
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kTokWpt; ++j) {
-        tk[j] = wgt[tok_pad(tid * kTokWpt + j)];
-        te[j] = bucket ? wbk[tok_pad(tid * kTokWpt + j)] : 0u;
-        ngt += __popc(tk[j]);
-        neq += __popc(te[j]);
+      if (take) {
+        if (pos >= 0 && pos < budget) out[pos] = (w0 + j) * 32 + bit;
+        ++pos;
       }
     }
-    int win_gt, win_eq;
-    const int gt_before = gt_run + select_block_scan(ngt, lds, win_gt) - ngt;
-    int eq_seen = eq_run + select_block_scan(neq, lds, win_eq) - neq;
-    int pos = gt_before + min(eq_seen, r_eq);
-#pragma unroll
-    for (int j = 0; j < kTokWpt; ++j) {
-      uint32_t mm = tk[j] | te[j];
-      while (mm) {
-        const int bit = __builtin_ctz(mm);
-        mm &= mm - 1;
-        bool take = (tk[j] >> bit) & 1u;
-        if (!take) {  // tied at kb
-          take = eq_seen < r_eq;
-          ++eq_seen;
-        }
-        if (take) {
-          if (pos >= 0 && pos < budget) out[pos] = (w0 + tid * kTokWpt + j) * 32 + bit;
-          ++pos;
-        }
-      }
-    }
-    gt_run += win_gt;
-    eq_run += win_eq;
   }
-  const int nsel = max(0, min(gt_run + min(eq_run, r_eq), budget));
-  for (int k = nsel + tid; k < budget; k += kSelectThreads) out[k] = -1;
-  if (tid == 0) count[unit] = nsel;
-  // the unit's histogram back to zero for the next call (saves a launch)
-  for (int d = tid; d < kTokBins; d += kSelectThreads) u.hist[d] = 0u;
 }
 
 }  // namespace
@@ -538,13 +566,16 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                hipStream_t s, bool hist_ready) {
   const TokGeom tg = tok_geom(g.Tmax);
   const int units = g.B * g.Hkv;
-  const dim3 grid(ceil_div(g.Tmax, kTokChunk), units), block(kSelectThreads);
+  // the chunks of a unit share their unit's reads (histogram, bitmaps,
+  // bucket scores): consecutive work-group ids are spread over the XCDs, so a
+  // unit's groups are kept units apart to land on one XCD and its L2
+  const dim3 grid(units, ceil_div(g.Tmax, kTokChunk)), block(kSelectThreads);
   if (!hist_ready)
     hipLaunchKernelGGL(tok_hist_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
                        tg, ws);
   hipLaunchKernelGGL(tok_filter_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
                      tg, ws);
-  hipLaunchKernelGGL(tok_finish_kernel, dim3(units), block, 0, s, scores, g.Tmax, seq_lens, g.Hkv,
+  hipLaunchKernelGGL(tok_finish_kernel, grid, block, 0, s, scores, g.Tmax, seq_lens, g.Hkv,
                      budget, tg, ws, idx, count);
   return hipGetLastError();
 }
