@@ -292,6 +292,59 @@ def select_tokens_unit(scores: np.ndarray, seq_len: int, budget: int) -> Tuple[n
 
 
 # --------------------------------------------------------------------------
+# A8p: an adaptive token budget. The RaBitQCache abstract (second page) takes
+# top-p retrieval in place of a fixed top-k: the number of tokens follows how
+# concentrated the estimated attention is. Reading on this path: the token
+# scores are the estimated logits (score_t = sigma p . kproj_t, A1t); a
+# candidate's share is its softmax weight over all candidates t < L; the
+# selection is the shortest prefix of the ranking (score descending, lower
+# index first) whose shares reach top_p, cut at the budget. Non-finite scores:
+# NaN and -inf weigh nothing; if any score is +inf, the +inf candidates share
+# the whole mass equally (the softmax's limit). With top_p = 0, or when no
+# candidate has weight, the fixed budget applies.
+# --------------------------------------------------------------------------
+
+def token_weights(s: np.ndarray) -> np.ndarray:
+    """Unnormalized softmax weights exp(s_t - max s) under the reading above (float64)."""
+    s = np.asarray(s, dtype=np.float64)
+    ok = ~np.isnan(s)
+    if not ok.any():
+        return np.zeros_like(s)
+    m = s[ok].max()
+    if m == np.inf:
+        return (s == np.inf).astype(np.float64)
+    if m == -np.inf:
+        return np.zeros_like(s)
+    w = np.exp(np.where(ok, s, -np.inf) - m)
+    return w
+
+
+def select_tokens_top_p(scores: np.ndarray, seq_len: int, budget: int, top_p: float
+                        ) -> Tuple[np.ndarray, int]:
+    """The fewest top-ranked candidates whose softmax shares reach top_p, at most budget.
+
+    Returns (idx [budget] int32 ascending, padded with -1; count).
+    """
+    n = min(int(seq_len), scores.shape[0])
+    s = np.asarray(scores[:n], dtype=np.float64)
+    cand = np.arange(n)
+    order = np.lexsort((cand, -s))  # score descending (NaN last), then index ascending
+    picks = max(0, min(int(budget), n))
+    m = picks
+    w = token_weights(s)
+    z = float(w.sum())
+    if top_p > 0 and z > 0 and math.isfinite(z) and picks > 0:
+        cum = np.cumsum(w[order[:picks]])
+        hit = np.nonzero(cum >= top_p * z)[0]
+        if len(hit):
+            m = int(hit[0]) + 1
+    sel = np.sort(cand[order[:m]])
+    out = np.full(int(budget), -1, dtype=np.int32)
+    out[:m] = sel
+    return out, m
+
+
+# --------------------------------------------------------------------------
 # A3 / A9: sparse attention over the selected rows, split into partials
 # (Jet-QSparse abstract: sparse value aggregation with FP32 accumulation over
 # the selected blocks; JSSA Figure 1: the query heads share the index set and
