@@ -183,7 +183,10 @@ def cpu_baseline(w, budget_s: float):
             rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
         else:
             sc = O.scan_token_unit(qg, rec, w.proj[h], L, sigma, s.proj_fmt)
-            idx, _ = O.select_tokens_unit(sc, L, s.budget)
+            if s.top_p > 0:
+                idx, _ = O.select_tokens_top_p(sc, L, s.budget, s.top_p)
+            else:
+                idx, _ = O.select_tokens_unit(sc, L, s.budget)
             rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L])
         po, pl = O.attend_splits(qg, idx, 1, rows, sigma)
         O.combine(po, pl)
@@ -261,6 +264,14 @@ def main() -> int:
         for c in calls(layers[i % len(layers)]):
             c()
     torch.cuda.synchronize()
+    kept = None
+    if spec.top_p > 0:  # the adaptive budget: the attention reads the tokens kept
+        if a.warmup == 0:
+            for c in calls(d0):
+                c()
+            torch.cuda.synchronize()
+        kept = int(layers[max(a.warmup - 1, 0) % len(layers)].count.sum())
+        nbytes = W.algorithmic_bytes(w, kept_tokens=kept)
 
     ns = len(stages)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(a.steps)]
@@ -328,6 +339,8 @@ def main() -> int:
                    "granularity": spec.granularity, "budget": spec.budget,
                    "tail_pages": spec.n_tail, "splits": d0.splits, "layers_rotated": a.layers,
                    "calls": a.mode,
+                   **({"top_p": spec.top_p, "kept_tokens_per_step": kept} if kept is not None
+                      else {}),
                    "scan": ("%s query, e2m1*e4m3 keys -> f16 MFMA, f32 acc" % spec.query_fmt)
                    if d0.block_mode
                    else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank)},

@@ -54,6 +54,7 @@ class SelectCfg(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("proj_dtype", ctypes.c_int32),
         ("query_dtype", ctypes.c_int32),
+        ("top_p", ctypes.c_float),
     ]
 
 
@@ -148,11 +149,12 @@ def layout_for(k, num_q_heads: int, dtype: Optional[int] = None) -> KvLayout:
 
 def select_cfg(granularity: int, budget: int, n_tail_pages: int = 0, proj_rank: int = 0,
                softmax_scale: Optional[float] = None, head_dim: int = 128,
-               proj_dtype: int = PROJ_BF16, query_dtype: int = QUERY_F16) -> SelectCfg:
+               proj_dtype: int = PROJ_BF16, query_dtype: int = QUERY_F16,
+               top_p: float = 0.0) -> SelectCfg:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale, proj_dtype,
-                     query_dtype)
+                     query_dtype, top_p)
 
 
 def version() -> str:

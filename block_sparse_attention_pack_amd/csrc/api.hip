@@ -93,9 +93,15 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
                 "proj_dtype applies to token mode only (must be 0 in block mode)");
     BSA_REQUIRE(c->query_dtype == BSA_QUERY_F16 || c->query_dtype == BSA_QUERY_NVFP4,
                 BSA_ERR_UNSUPPORTED, "query_dtype %d", c->query_dtype);
+    BSA_REQUIRE(c->top_p == 0.0f, BSA_ERR_INVALID_ARG,
+                "top_p applies to token mode only (must be 0 in block mode)");
   } else {
     BSA_REQUIRE(c->query_dtype == BSA_QUERY_F16, BSA_ERR_INVALID_ARG,
                 "query_dtype applies to block mode only (must be 0 in token mode)");
+    BSA_REQUIRE(std::isfinite(c->top_p) && c->top_p >= 0.0f && c->top_p <= 1.0f,
+                BSA_ERR_INVALID_ARG, "top_p %g must lie in [0, 1]", double(c->top_p));
+    BSA_REQUIRE(c->top_p == 0.0f || c->budget <= bsa::kTopPMaxBudget, BSA_ERR_UNSUPPORTED,
+                "top_p needs a token budget <= %d (got %d)", bsa::kTopPMaxBudget, c->budget);
   }
   g->B = L->batch;
   g->Hkv = L->num_kv_heads;
@@ -215,7 +221,7 @@ hipError_t launch_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, cons
     return bsa::launch_select_block(g, cfg->budget, cfg->n_tail_pages, scores, seq_lens, idx,
                                     count, s);
   return bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx, count, s,
-                                  hist_ready);
+                                  hist_ready, cfg->top_p);
 }
 
 #define BSA_CHECK(expr)   \

@@ -252,9 +252,13 @@ hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const 
                                const int32_t* seq_lens, int32_t* idx, int32_t* count,
                                hipStream_t s);
 // hist_ready: the histograms were filled by launch_scan_token (tok_hist is skipped).
+// top_p > 0: the selection is then cut to the adaptive budget (tok_topp);
+// budget <= kTopPMaxBudget.
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
-                               hipStream_t s, bool hist_ready = false);
+                               hipStream_t s, bool hist_ready = false, float top_p = 0.0f);
+// Largest token budget the adaptive (top-p) budget sorts in one work-group's LDS.
+constexpr int kTopPMaxBudget = 4096;
 // Largest budget for which the attention launch selects the blocks itself.
 constexpr int kFusedSelectMax = 1024;
 // The attention launch merges the splits in its last group up to this many

@@ -48,7 +48,6 @@ constexpr int kTokChunk = 16384;  // keys per work-group in hist and filter
 constexpr int kTokBatch = 32;     // loads in flight per thread (hist)
 constexpr int kTokBins = kTokHistBins;    // first digit: top 12 bits
 constexpr int kTokShift = kTokHistShift;
-constexpr int kTokSlot = 64;      // words of the state slot
 constexpr int kTokChunkWords = kTokChunk / 32;
 constexpr int kTokWin = 4096;     // bitmap words per finish window: 16 per thread
 constexpr int kTokList = 4096;    // buckets up to this size are listed in LDS by the finish
@@ -65,10 +64,16 @@ struct TokState {
   uint32_t mode, beta, r, n;
 };
 
-// Per-unit workspace: histogram, state and two bitmaps (taken by top digit;
-// in the bucket), each on its own 256-byte boundary.
+// Per-unit workspace: histogram, state slot and two bitmaps, each on its own
+// 256-byte boundary. The slot holds TokState and, from word kTokLseWord, three
+// words per chunk that the filter leaves for the adaptive budget (the chunk's
+// score maximum, its sum of exp(s - maximum), its count of +inf scores).
+constexpr int kTokLseWord = 8;
+
 struct TokGeom {
   int W;               // 32-bit bitmap words per unit (a multiple of 2)
+  int chunks;          // kTokChunk-key chunks per unit
+  int slot;            // words of the state slot
   int64_t w_bitmap;    // words reserved per bitmap
   int64_t unit_words;  // workspace words per unit
 };
@@ -76,16 +81,19 @@ struct TokGeom {
 __host__ __device__ inline TokGeom tok_geom(int Tmax) {
   TokGeom t;
   t.W = ceil_div(Tmax, 64) * 2;
+  t.chunks = ceil_div(Tmax, kTokChunk);
+  t.slot = (kTokLseWord + 3 * t.chunks + 63) / 64 * 64;
   t.w_bitmap = (int64_t(t.W) + 63) / 64 * 64;
-  t.unit_words = kTokBins + kTokSlot + 2 * t.w_bitmap;
+  t.unit_words = kTokBins + t.slot + 2 * t.w_bitmap;
   return t;
 }
 
 struct TokUnit {
   uint32_t* hist;
   TokState* st;
-  uint32_t* gt;  // bit t: token t taken by its top digit
-  uint32_t* bk;  // bit t: token t in the bucket
+  uint32_t* lse;  // [chunks][3]: maximum (float bits), sum (float bits), +inf count
+  uint32_t* gt;   // bit t: token t taken by its top digit
+  uint32_t* bk;   // bit t: token t in the bucket
 };
 
 __device__ __forceinline__ TokUnit tok_unit(void* ws, const TokGeom& t, int unit) {
@@ -93,7 +101,8 @@ __device__ __forceinline__ TokUnit tok_unit(void* ws, const TokGeom& t, int unit
   TokUnit u;
   u.hist = base;
   u.st = reinterpret_cast<TokState*>(base + kTokBins);
-  u.gt = base + kTokBins + kTokSlot;
+  u.lse = base + kTokBins + kTokLseWord;
+  u.gt = base + kTokBins + t.slot;
   u.bk = u.gt + t.w_bitmap;
   return u;
 }
@@ -176,11 +185,25 @@ __device__ __forceinline__ void tok_boundary(const uint32_t* ghist, int picks, S
   __syncthreads();
 }
 
+// Merges a (maximum, sum of exp(x - maximum)) pair into another.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -__builtin_inff()) {
+    m = mx;
+    s = 0.0f;
+    return;
+  }
+  s = s * expf(m - mx) + s2 * expf(m2 - mx);
+  m = mx;
+}
+
 // Bitmaps of the keys taken by their top digit and of the bucket (keys whose
 // top digit is the boundary digit). grid (B * Hkv, ceil(Tmax / kTokChunk)),
 // 256 threads; wave w owns the 4096 keys from blockIdx.y * kTokChunk + 4096 w,
 // as 64 rows of 64; lane j keeps row j's two words of each bitmap, so each
 // bitmap is written with one 8-byte store per lane.
+// LSE: also store the chunk's softmax partial (for the adaptive budget).
+template <bool LSE>
 __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
     int budget, TokGeom tg, void* ws) {
@@ -201,7 +224,7 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
 #pragma unroll
   for (int j = 0; j < kRows; ++j) {
     const int i = wbase + j * 64 + lane;
-    v[j] = (mode == kTokBucket && i < C) ? row[i] : 0.0f;
+    v[j] = ((mode == kTokBucket || LSE) && i < C) ? row[i] : 0.0f;
   }
   int beta = 0, above = 0, in = 0;
   if (mode == kTokBucket) {
@@ -242,6 +265,49 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
   if (word < tg.W) {
     *reinterpret_cast<uint2*>(u.gt + word) = make_uint2(g0, g1);
     *reinterpret_cast<uint2*>(u.bk + word) = make_uint2(k0, k1);
+  }
+  if constexpr (LSE) {  // the chunk's softmax partial for the adaptive budget
+    float m = -__builtin_inff(), sm = 0.0f;
+    int ninf = 0;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const float x = v[j];
+      if (wbase + j * 64 + lane >= C || x != x || x == -__builtin_inff()) continue;
+      if (x == __builtin_inff()) {
+        ++ninf;
+      } else if (x > m) {
+        sm = sm * expf(m - x) + 1.0f;
+        m = x;
+      } else {
+        sm += expf(x - m);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(sm, off, kWave);
+      lse_merge(m, sm, m2, s2);
+      ninf += __shfl_xor(ninf, off, kWave);
+    }
+    if (lane == 0) {
+      lds.wave_lo[wave] = __builtin_bit_cast(uint32_t, m);
+      lds.wave_hi[wave] = __builtin_bit_cast(uint32_t, sm);
+      lds.wave_tot[wave] = ninf;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float M = __builtin_bit_cast(float, lds.wave_lo[0]);
+      float S = __builtin_bit_cast(float, lds.wave_hi[0]);
+      int NI = lds.wave_tot[0];
+      for (int w = 1; w < kSelectThreads / kWave; ++w) {
+        lse_merge(M, S, __builtin_bit_cast(float, lds.wave_lo[w]),
+                  __builtin_bit_cast(float, lds.wave_hi[w]));
+        NI += lds.wave_tot[w];
+      }
+      uint32_t* p = u.lse + 3 * blockIdx.y;
+      p[0] = __builtin_bit_cast(uint32_t, M);
+      p[1] = __builtin_bit_cast(uint32_t, S);
+      p[2] = uint32_t(NI);
+    }
   }
 }
 
@@ -545,6 +611,182 @@ __global__ __launch_bounds__(kSelectThreads) void tok_finish_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Adaptive budget (top-p retrieval, RaBitQCache abstract): of the unit's
+// selection (its `budget` best tokens, ascending), keep the fewest top-ranked
+// ones whose softmax shares over all candidates t < L reach top_p. A share is
+// exp(s_t - max) / sum_u exp(s_u - max); NaN and -inf weigh nothing; if any
+// score is +inf, the +inf candidates share the whole mass. With no weight at
+// all the selection stays whole.
+// grid (B * Hkv), kTopPThreads threads: the group merges the unit's total
+// weight from the filter's per-chunk partials (maximum, rescaled sum, +inf
+// count), sorts the selection by (key, lower index first) with a bitonic sort
+// in LDS, finds the cut from the prefix sums of the sorted weights, and
+// rewrites idx (ascending, padded with -1) and count.
+// ---------------------------------------------------------------------------
+constexpr int kTopPThreads = 1024;
+constexpr int kTopPPer = kTopPMaxBudget / kTopPThreads;  // sorted entries per thread
+
+
+__global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
+    int budget, float top_p, TokGeom tg, void* ws, int32_t* __restrict__ idx,
+    int32_t* __restrict__ count) {
+  __shared__ unsigned long long ent[kTopPMaxBudget];  // (key << 32) | ~position
+  __shared__ float sc[kTopPMaxBudget];                // score by position
+  __shared__ int32_t tok[kTopPMaxBudget];             // token by position
+  __shared__ uint8_t keep[kTopPMaxBudget];
+  __shared__ float red_m[kTopPThreads / kWave], red_s[kTopPThreads / kWave];
+  __shared__ int red_i[kTopPThreads / kWave];
+  __shared__ int cut;
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kTopPThreads / kWave;
+  const int C = clamp_len(seq_lens[unit / Hkv], Tmax);
+  const float* row = scores + int64_t(unit) * Tmax;
+  int32_t* out = idx + int64_t(unit) * budget;
+  const int n = min(max(count[unit], 0), min(budget, kTopPMaxBudget));
+  if (n == 0 || C <= 0) return;  // the group exits as one (n > 0 implies C > 0)
+
+  // ---- the unit's total weight: the filter's per-chunk partials, merged ----
+  const TokUnit u = tok_unit(ws, tg, unit);
+  float m = -__builtin_inff(), s = 0.0f;
+  int ninf = 0;
+  for (int c = tid; c < tg.chunks; c += kTopPThreads) {
+    const uint32_t* p = u.lse + 3 * c;
+    lse_merge(m, s, __builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1]));
+    ninf += int(p[2]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(s, off, kWave);
+    lse_merge(m, s, m2, s2);
+    ninf += __shfl_xor(ninf, off, kWave);
+  }
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_s[wave] = s;
+    red_i[wave] = ninf;
+  }
+  // ---- the selection into LDS ------------------------------------------------
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int k = tid; k < n2; k += kTopPThreads) {
+    if (k < n) {
+      const int t = out[k];
+      const float x = uint32_t(t) < uint32_t(C) ? row[t] : __builtin_nanf("");
+      tok[k] = t;
+      sc[k] = x;
+      keep[k] = 0;
+      ent[k] = (static_cast<unsigned long long>(score_key(x)) << 32) | (0xFFFFFFFFu - uint32_t(k));
+    } else {
+      ent[k] = 0ull;  // below every real entry (their low word is nonzero)
+    }
+  }
+  if (tid == 0) cut = n;
+  __syncthreads();
+  m = red_m[0];
+  s = red_s[0];
+  ninf = red_i[0];
+  for (int w = 1; w < kWaves; ++w) {
+    lse_merge(m, s, red_m[w], red_s[w]);
+    ninf += red_i[w];
+  }
+  __syncthreads();  // red_s and red_i are reused below
+  // weight of a score under the total's reading; z: the total
+  const bool inf_mode = ninf > 0;
+  const float z = inf_mode ? float(ninf) : s;
+  auto weight = [&](float x) {
+    if (inf_mode) return x == __builtin_inff() ? 1.0f : 0.0f;
+    return (x == x && x > -__builtin_inff()) ? expf(x - m) : 0.0f;
+  };
+
+  // ---- bitonic sort, descending ------------------------------------------------
+  // Pair i of a stage compares entries lo = 2i - (i mod stride) and lo + stride.
+  // A wave's 64 consecutive pairs then lie in one 128-entry segment whenever
+  // stride <= 64, so such a stage needs only the wave's own ordering before and
+  // after it; a stage with a longer stride (or the sort's end) needs the group's.
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n2 / 2; i += kTopPThreads) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const unsigned long long a = ent[lo], b = ent[hi];
+        const bool desc = (lo & size) == 0;
+        if (desc ? a < b : a > b) {
+          ent[lo] = b;
+          ent[hi] = a;
+        }
+      }
+      // the next stage's stride; after the last stage, the group reads the result
+      const int next = stride > 1 ? stride >> 1 : ((size << 1) <= n2 ? size : 1 << 30);
+      if (stride > 64 || next > 64) __syncthreads();
+      else wave_lds_sync();
+    }
+  }
+
+  // ---- the cut: the first sorted entry whose running weight reaches top_p z ----
+  if (z > 0.0f && z < __builtin_inff()) {
+    const float thr = top_p * z;
+    float w[kTopPPer], run = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopPPer; ++j) {
+      const int i = tid * kTopPPer + j;
+      w[j] = i < n ? weight(sc[0xFFFFFFFFu - uint32_t(ent[i])]) : 0.0f;
+      run += w[j];
+    }
+    // exclusive prefix of the per-thread sums, in a fixed order
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) red_s[wave] = incl;
+    __syncthreads();
+    float before = incl - run;
+    for (int w2 = 0; w2 < wave; ++w2) before += red_s[w2];
+    float cum = before;
+#pragma unroll
+    for (int j = 0; j < kTopPPer; ++j) {
+      const int i = tid * kTopPPer + j;
+      cum += w[j];
+      if (i < n && cum >= thr) {
+        atomicMin(&cut, i + 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int mcut = cut;
+  for (int i = tid; i < mcut; i += kTopPThreads) keep[0xFFFFFFFFu - uint32_t(ent[i])] = 1;
+  __syncthreads();
+
+  // ---- compaction in token order -----------------------------------------------
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < kTopPPer; ++j) {
+    const int k = tid * kTopPPer + j;
+    mine += k < n ? int(keep[k]) : 0;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) red_i[wave] = incl;
+  __syncthreads();
+  int pos = incl - mine;
+  for (int w2 = 0; w2 < wave; ++w2) pos += red_i[w2];
+#pragma unroll
+  for (int j = 0; j < kTopPPer; ++j) {
+    const int k = tid * kTopPPer + j;
+    if (k < n && keep[k]) out[pos++] = tok[k];
+  }
+  for (int k = mcut + tid; k < n; k += kTopPThreads) out[k] = -1;
+  if (tid == 0) count[unit] = mcut;
+}
 }  // namespace
 
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
@@ -563,7 +805,7 @@ int64_t token_unit_words(const UnitGeom& g) { return tok_geom(g.Tmax).unit_words
 
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
-                               hipStream_t s, bool hist_ready) {
+                               hipStream_t s, bool hist_ready, float top_p) {
   const TokGeom tg = tok_geom(g.Tmax);
   const int units = g.B * g.Hkv;
   // the chunks of a unit share their unit's reads (histogram, bitmaps,
@@ -573,10 +815,17 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
   if (!hist_ready)
     hipLaunchKernelGGL(tok_hist_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
                        tg, ws);
-  hipLaunchKernelGGL(tok_filter_kernel, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax, budget,
-                     tg, ws);
+  if (top_p > 0.0f)
+    hipLaunchKernelGGL(tok_filter_kernel<true>, grid, block, 0, s, scores, seq_lens, g.Hkv, g.Tmax,
+                       budget, tg, ws);
+  else
+    hipLaunchKernelGGL(tok_filter_kernel<false>, grid, block, 0, s, scores, seq_lens, g.Hkv,
+                       g.Tmax, budget, tg, ws);
   hipLaunchKernelGGL(tok_finish_kernel, grid, block, 0, s, scores, g.Tmax, seq_lens, g.Hkv,
                      budget, tg, ws, idx, count);
+  if (top_p > 0.0f)
+    hipLaunchKernelGGL(tok_topp_kernel, dim3(units), dim3(kTopPThreads), 0, s, scores, seq_lens,
+                       g.Hkv, g.Tmax, budget, top_p, tg, ws, idx, count);
   return hipGetLastError();
 }
 

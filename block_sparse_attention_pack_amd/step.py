@@ -215,7 +215,8 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
     fp8 = gran == bsa.TOKEN and s.proj_fmt == "fp8"
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
                          w.softmax_scale, proj_dtype=bsa.PROJ_FP8 if fp8 else bsa.PROJ_BF16,
-                         query_dtype=bsa.QUERY_NVFP4 if s.query_fmt == "nvfp4" else bsa.QUERY_F16)
+                         query_dtype=bsa.QUERY_NVFP4 if s.query_fmt == "nvfp4" else bsa.QUERY_F16,
+                         top_p=s.top_p)
     if splits is None:
         splits = default_splits(B * Hkv, s.budget, s.granularity, one_launch)
     nb = s.max_blocks

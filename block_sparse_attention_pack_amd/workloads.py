@@ -17,6 +17,9 @@ Five workloads follow the sparse-decode setting the pages evaluate:
 * ``token``       B8 Hkv8 Hq32 T131072, rank-32 projected keys from a seeded
                   orthonormal P, top-2048 tokens (JSSA abstract and Figure 1;
                   1.5625% density of JSSA Figure 3: 2048 of 131072)
+* ``token_topp``  the token shape with 8 strong needle blocks per unit and the
+                  adaptive budget at top_p 0.9 (RaBitQCache abstract), at most
+                  2048 tokens
 
 Every workload also exists at reduced size (``scale_tokens`` / ``batch``) so the
 oracle finishes in seconds while still spanning many tiles and a ragged tail.
@@ -73,6 +76,7 @@ class Spec:
     rank: int = 0  # projection rank in token mode
     proj_fmt: str = "bf16"  # token mode: projected-key cache storage, "bf16" or "fp8"
     query_fmt: str = "f16"  # block mode: the query the scan scores with, "f16" or "nvfp4"
+    top_p: float = 0.0  # token mode: 0 keeps the budget; else the adaptive (top-p) budget
     lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
@@ -107,9 +111,16 @@ SPECS: Dict[str, Spec] = {
     "jetqsparse_q4": Spec("jetqsparse_q4", 2, 16, 4, 16, 131072, "block", 64,
                           needle_count=20, needle_profile="zipf", needle_strength=3.0,
                           key_offset_std=2.0, query_fmt="nvfp4"),
+    # the token shape with the adaptive budget (top-p retrieval, RaBitQCache
+    # abstract): 8 strong needle blocks per unit hold most of the softmax mass,
+    # so keeping 90% of it takes fewer than the 2048 tokens
+    "token_topp": Spec("token_topp", 4, 8, 8, 32, 131072, "token", 2048, rank=32,
+                       needle_count=8, needle_profile="const", needle_strength=48.0,
+                       top_p=0.9),
 }
 
-ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4"]
+ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4",
+         "token_topp"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
@@ -321,13 +332,15 @@ def calibrate_scale(spec: Spec, k: np.ndarray, seq_lens: np.ndarray,
     return s
 
 
-def algorithmic_bytes(w: Workload) -> Dict[str, int]:
+def algorithmic_bytes(w: Workload, kept_tokens: Optional[int] = None) -> Dict[str, int]:
     """Bytes the method must move per decode step (scan + selected K,V), per stage.
 
     Block mode: 72 B per scanned token (64 B of E2M1 codes + 8 B of E4M3 scales)
     and 2 x 256 B per attended token (FP16 K and V rows; BF16 tail rows also
     count 512 B). Token mode: 2r B (BF16) or r B (FP8) per scanned token (the
-    projected key) and 512 B per selected token.
+    projected key) and 512 B per selected token. With the adaptive budget the
+    number of selected tokens depends on the scores: pass it as kept_tokens
+    (the sum of the step's counts over all units).
     """
     s = w.spec
     scan = attn = 0
@@ -349,5 +362,7 @@ def algorithmic_bytes(w: Workload) -> Dict[str, int]:
         else:
             scan += s.kv_heads * (1 if s.proj_fmt == "fp8" else 2) * s.rank * L
             attn += s.kv_heads * 512 * min(s.budget, L)
+    if kept_tokens is not None:
+        attn = 512 * int(kept_tokens)
     q_bytes = s.batch * s.q_heads * HEAD_DIM * 2
     return {"scan": scan, "attn": attn, "q": q_bytes, "total": scan + attn}

@@ -104,6 +104,12 @@ typedef struct bsa_select_cfg {
   float softmax_scale;  /* sigma, > 0 (1/sqrt(128) for the standard scale) */
   int32_t proj_dtype;   /* TOKEN: BSA_PROJ_BF16 or BSA_PROJ_FP8; BLOCK: must be BSA_PROJ_BF16 (0) */
   int32_t query_dtype;  /* BLOCK: BSA_QUERY_F16 or BSA_QUERY_NVFP4; TOKEN: must be BSA_QUERY_F16 (0) */
+  float top_p;          /* TOKEN: 0 keeps the fixed budget; in (0, 1] the budget adapts (top-p
+                           retrieval, RaBitQCache abstract): of the budget best tokens, the
+                           fewest top-ranked ones whose softmax shares of the unit's scores
+                           (over all t < L_b) reach top_p are kept; NaN and -inf weigh
+                           nothing, +inf scores share the whole mass, and with no weight at
+                           all the budget stays. Needs budget <= 4096. BLOCK: must be 0. */
 } bsa_select_cfg;
 
 /* ---------------------------------------------------------------------------

@@ -106,6 +106,8 @@ def check_selection(w, b, h, idx_gpu, count_gpu, scores_gpu, scores_ref):
                                                     s.budget)
         ref_idx, ref_cnt = O.select_blocks_unit(scores_ref, L, s.n_tail, s.budget)
         picks = s.budget - s.n_tail
+    elif s.top_p > 0:
+        return check_top_p_selection(scores_gpu, L, s.budget, s.top_p, idx_gpu, count_gpu)
     else:
         exact_idx, exact_cnt = O.select_tokens_unit(scores_gpu.astype(np.float64), L, s.budget)
         ref_idx, ref_cnt = O.select_tokens_unit(scores_ref, L, s.budget)
@@ -122,6 +124,38 @@ def check_selection(w, b, h, idx_gpu, count_gpu, scores_gpu, scores_ref):
             assert abs(scores_ref[x] - tau) <= BOUNDARY_REL * abs(tau), \
                 f"selection differs beyond the boundary band at {(b, h)}: entry {x}"
     return len(diff)
+
+
+# The adaptive budget's cut is a count decided by float sums (float32 on the
+# GPU, float64 in the oracle): a count is accepted when the oracle's shares of
+# its prefix lie within TOP_P_REL of top_p on the right sides; the set must then
+# be exactly the oracle's top-count set.
+TOP_P_REL = 1e-4
+
+
+def check_top_p_selection(scores_gpu, L, budget, top_p, idx_gpu, count_gpu):
+    """Adaptive-budget selection on the GPU's own scores (one unit)."""
+    s = np.asarray(scores_gpu, dtype=np.float64)
+    n = min(int(L), s.shape[0])
+    picks = max(0, min(int(budget), n))
+    m = int(count_gpu)
+    assert 0 <= m <= picks, (m, picks)
+    top_idx, top_cnt = O.select_tokens_unit(s, L, m) if m > 0 else (np.zeros(0, np.int32), 0)
+    assert top_cnt == m
+    assert np.array_equal(idx_gpu[:m], top_idx[:m]), "the kept tokens are not the top-ranked ones"
+    assert np.all(idx_gpu[m:] == -1), "padding"
+    ref_idx, ref_m = O.select_tokens_top_p(s, L, budget, top_p)
+    if m == ref_m:
+        assert np.array_equal(idx_gpu, ref_idx)
+        return 0
+    w = O.token_weights(s[:n])
+    z = w.sum()
+    assert z > 0 and np.isfinite(z), "the fixed budget applies when nothing has weight"
+    order = np.lexsort((np.arange(n), -s[:n]))
+    cum = np.cumsum(w[order[:picks]]) / z
+    assert m == picks or cum[m - 1] >= top_p * (1 - TOP_P_REL), (m, ref_m, cum[m - 1], top_p)
+    assert m == 1 or cum[m - 2] < top_p * (1 + TOP_P_REL), (m, ref_m, cum[m - 2], top_p)
+    return abs(m - ref_m)
 
 
 def oracle_partials(w, b, h, idx, splits):

@@ -206,3 +206,19 @@ def test_query_format_is_checked(lib):
     assert "query_dtype" in lib.bsa_last_error().decode()
     assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 32, query_dtype=B.QUERY_NVFP4)) == -1
     assert "block mode only" in lib.bsa_last_error().decode()
+
+
+def test_top_p_is_checked(lib):
+    L = _layout()
+    ok = B.select_cfg(B.TOKEN, 64, 0, 32, top_p=0.9)
+    assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(ok)) > 0  # a valid cfg
+    assert _scan(lib, L, B.select_cfg(B.BLOCK, 8, top_p=0.5)) == -1
+    assert "token mode only" in lib.bsa_last_error().decode()
+    for bad in (-0.1, 1.5, float("nan"), float("inf")):
+        assert _scan(lib, L, B.select_cfg(B.TOKEN, 64, 0, 32, top_p=bad)) == -1, bad
+        assert "top_p" in lib.bsa_last_error().decode()
+    big = _layout(max_tokens=16384, kv_stride_b=16384 * 128, kv_stride_h=16384 * 128)
+    assert _scan(lib, big, B.select_cfg(B.TOKEN, 8192, 0, 32, top_p=0.5)) == -2
+    assert "4096" in lib.bsa_last_error().decode()
+    fixed = B.select_cfg(B.TOKEN, 8192, 0, 32)  # the fixed budget has no such limit
+    assert lib.bsa_workspace_size(ctypes.byref(big), ctypes.byref(fixed)) > 0

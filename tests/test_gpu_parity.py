@@ -60,6 +60,7 @@ REDUCED = {
     "token": W.reduced("token", 16384, batch=2),
     "token_fp8": W.reduced("token_fp8", 16384, batch=2),
     "jetqsparse_q4": W.reduced("jetqsparse_q4", 8192, batch=2),
+    "token_topp": W.reduced("token_topp", 16384, batch=2),
 }
 
 

@@ -19,6 +19,8 @@ from block_sparse_attention_pack_amd import binding as bsa
 
 from oracle import decode as O
 
+import parity_util as PU
+
 pytestmark = pytest.mark.gpu
 
 
@@ -46,6 +48,8 @@ def _rows(pattern, n, rng):
         return pool[rng.integers(0, len(pool), n)]
     if pattern == "all_equal":
         return np.full(n, 0.25, dtype=np.float32)
+    if pattern == "peaked":  # logits spread over ~40: the softmax mass sits in a few hundred keys
+        return (rng.standard_normal(n) * 5.0).astype(np.float32)
     raise ValueError(pattern)
 
 
@@ -56,11 +60,13 @@ def _say(*a):
 
 def _histograms_back_at_zero(ws, units, T):
     """After a call each unit's histogram in the token workspace is zero again
-    (per unit: 4096 histogram words, a 64-word slot, two bitmaps of
-    ceil(T/64)*2 words rounded up to 64)."""
+    (per unit: 4096 histogram words; a slot of 8 + 3 words per 16384-key chunk,
+    rounded up to 64; two bitmaps of ceil(T/64)*2 words rounded up to 64)."""
     w = ws.view(torch.int32).cpu().numpy()
     W = -(-T // 64) * 2
-    per = 4096 + 64 + 2 * (-(-W // 64) * 64)
+    slot = -(-(8 + 3 * -(-T // 16384)) // 64) * 64
+    per = 4096 + slot + 2 * (-(-W // 64) * 64)
+    assert w.size == units * per, (w.size, units, per)
     for u in range(units):
         assert not w[u * per:u * per + 4096].any(), f"histogram of unit {u}"
 
@@ -150,3 +156,35 @@ def test_token_select_over_several_bitmap_windows(pattern):
             ri, rc = O.select_tokens_unit(scores[b, h].astype(np.float64), lengths[b], budget)
             assert int(gc[b, h]) == rc, (pattern, b, h)
             assert np.array_equal(gi[b, h], ri), (pattern, b, h)
+
+
+@pytest.mark.parametrize("pattern", ["random", "peaked", "few_values", "specials", "all_equal"])
+@pytest.mark.parametrize("budget", [1, 300, 4096])
+@pytest.mark.parametrize("top_p", [0.05, 0.5, 0.9, 1.0])
+def test_token_top_p_matches_oracle(pattern, budget, top_p):
+    """The adaptive budget: the kept tokens are the top-ranked ones, the count
+    is a valid cut of the softmax shares, and the workspace is left reusable."""
+    T = 40960
+    lengths = [T, 40001, 8193, 8192, 8191, 2049, 1, 0]
+    B, Hkv = len(lengths), 2
+    rng = np.random.default_rng([11, budget, len(pattern), int(top_p * 100)])
+    scores = np.stack([_rows(pattern, T, rng) for _ in range(B * Hkv)]).reshape(B, Hkv, T)
+    _say(f"[select] top-p pattern={pattern} budget={budget} p={top_p}")
+    layout = _layout(B, Hkv, T)
+    cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1, top_p=top_p)
+    ws_bytes = bsa.workspace_size(layout, cfg)
+    dev = torch.device("cuda")
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
+    sc = torch.from_numpy(scores).to(dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
+    count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
+    for rep in range(2):
+        bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
+        torch.cuda.synchronize()
+        _histograms_back_at_zero(ws, B * Hkv, T)
+        gi, gc = idx.cpu().numpy(), count.cpu().numpy()
+        for b in range(B):
+            for h in range(Hkv):
+                PU.check_top_p_selection(scores[b, h], lengths[b], budget, top_p, gi[b, h],
+                                         gc[b, h])
