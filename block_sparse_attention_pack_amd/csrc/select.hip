@@ -267,20 +267,22 @@ __global__ __launch_bounds__(kSelectThreads) void tok_filter_kernel(
     *reinterpret_cast<uint2*>(u.bk + word) = make_uint2(k0, k1);
   }
   if constexpr (LSE) {  // the chunk's softmax partial for the adaptive budget
+    // branch-free: the lane's maximum over its finite scores, then its sum
     float m = -__builtin_inff(), sm = 0.0f;
     int ninf = 0;
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
       const float x = v[j];
-      if (wbase + j * 64 + lane >= C || x != x || x == -__builtin_inff()) continue;
-      if (x == __builtin_inff()) {
-        ++ninf;
-      } else if (x > m) {
-        sm = sm * expf(m - x) + 1.0f;
-        m = x;
-      } else {
-        sm += expf(x - m);
-      }
+      const bool in = wbase + j * 64 + lane < C;
+      ninf += (in && x == __builtin_inff()) ? 1 : 0;
+      m = (in && x < __builtin_inff()) ? fmaxf(m, x) : m;  // fmaxf drops NaN
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const float x = v[j];
+      const bool fin = wbase + j * 64 + lane < C && x > -__builtin_inff() && x < __builtin_inff();
+      const float e = expf(x - m);
+      sm += fin ? e : 0.0f;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -619,27 +621,32 @@ __global__ __launch_bounds__(kSelectThreads) void tok_finish_kernel(
 // exp(s_t - max) / sum_u exp(s_u - max); NaN and -inf weigh nothing; if any
 // score is +inf, the +inf candidates share the whole mass. With no weight at
 // all the selection stays whole.
-// grid (B * Hkv), kTopPThreads threads: the group merges the unit's total
+// grid (B * Hkv), kTopPThreads threads. The group merges the unit's total
 // weight from the filter's per-chunk partials (maximum, rescaled sum, +inf
-// count), sorts the selection by (key, lower index first) with a bitonic sort
-// in LDS, finds the cut from the prefix sums of the sorted weights, and
-// rewrites idx (ascending, padded with -1) and count.
+// count). Each selected token's weight is taken in fixed point (2^40 units,
+// so every sum below is an exact integer, whatever its order), and the cut is
+// found without sorting: a radix search over the 32-bit score keys, 8 bits a
+// level, keeps the bin whose running weight (from the top) first reaches
+// top_p times the total; at the boundary key, whose ties weigh the same,
+// as many ties as needed are kept in index order.
 // ---------------------------------------------------------------------------
 constexpr int kTopPThreads = 1024;
-constexpr int kTopPPer = kTopPMaxBudget / kTopPThreads;  // sorted entries per thread
-
+constexpr int kTopPPer = kTopPMaxBudget / kTopPThreads;  // entries per thread (contiguous)
+constexpr double kTopPFix = 1099511627776.0;               // 2^40
 
 __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
     int budget, float top_p, TokGeom tg, void* ws, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
-  __shared__ unsigned long long ent[kTopPMaxBudget];  // (key << 32) | ~position
-  __shared__ float sc[kTopPMaxBudget];                // score by position
-  __shared__ int32_t tok[kTopPMaxBudget];             // token by position
-  __shared__ uint8_t keep[kTopPMaxBudget];
+  __shared__ unsigned long long ew[kTopPMaxBudget];  // fixed-point weight by position
+  __shared__ uint32_t ekey[kTopPMaxBudget];          // score key by position
+  __shared__ int32_t tok[kTopPMaxBudget];            // token by position
+  __shared__ unsigned long long hsum[256];
+  __shared__ unsigned long long wtot[kTopPThreads / kWave];
   __shared__ float red_m[kTopPThreads / kWave], red_s[kTopPThreads / kWave];
   __shared__ int red_i[kTopPThreads / kWave];
-  __shared__ int cut;
+  __shared__ unsigned long long sel_above, tie_w;
+  __shared__ int sel_d, n_above, n_tie;
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   constexpr int kWaves = kTopPThreads / kWave;
@@ -669,22 +676,26 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     red_s[wave] = s;
     red_i[wave] = ninf;
   }
-  // ---- the selection into LDS ------------------------------------------------
-  int n2 = 1;
-  while (n2 < n) n2 <<= 1;
-  for (int k = tid; k < n2; k += kTopPThreads) {
+  // ---- the selection into LDS (its scores kept in registers) ----------------
+  float x[kTopPPer];
+#pragma unroll
+  for (int j = 0; j < kTopPPer; ++j) {
+    const int k = tid * kTopPPer + j;
+    x[j] = __builtin_nanf("");
     if (k < n) {
       const int t = out[k];
-      const float x = uint32_t(t) < uint32_t(C) ? row[t] : __builtin_nanf("");
+      if (uint32_t(t) < uint32_t(C)) x[j] = row[t];
       tok[k] = t;
-      sc[k] = x;
-      keep[k] = 0;
-      ent[k] = (static_cast<unsigned long long>(score_key(x)) << 32) | (0xFFFFFFFFu - uint32_t(k));
-    } else {
-      ent[k] = 0ull;  // below every real entry (their low word is nonzero)
+      ekey[k] = score_key(x[j]);
     }
   }
-  if (tid == 0) cut = n;
+  if (tid < 256) hsum[tid] = 0ull;
+  if (tid == 0) {
+    n_above = 0;
+    n_tie = 0;
+    tie_w = 0ull;
+    sel_d = -1;
+  }
   __syncthreads();
   m = red_m[0];
   s = red_s[0];
@@ -693,81 +704,130 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     lse_merge(m, s, red_m[w], red_s[w]);
     ninf += red_i[w];
   }
-  __syncthreads();  // red_s and red_i are reused below
-  // weight of a score under the total's reading; z: the total
+  __syncthreads();  // red_i is reused below
   const bool inf_mode = ninf > 0;
   const float z = inf_mode ? float(ninf) : s;
-  auto weight = [&](float x) {
-    if (inf_mode) return x == __builtin_inff() ? 1.0f : 0.0f;
-    return (x == x && x > -__builtin_inff()) ? expf(x - m) : 0.0f;
-  };
-
-  // ---- bitonic sort, descending ------------------------------------------------
-  // Pair i of a stage compares entries lo = 2i - (i mod stride) and lo + stride.
-  // A wave's 64 consecutive pairs then lie in one 128-entry segment whenever
-  // stride <= 64, so such a stage needs only the wave's own ordering before and
-  // after it; a stage with a longer stride (or the sort's end) needs the group's.
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kTopPThreads) {
-        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-        const unsigned long long a = ent[lo], b = ent[hi];
-        const bool desc = (lo & size) == 0;
-        if (desc ? a < b : a > b) {
-          ent[lo] = b;
-          ent[hi] = a;
+  int mcut = n;
+  uint32_t kappa = 0;  // the boundary key
+  int j_tie = 0;       // ties at kappa kept
+  if (z > 0.0f && z < __builtin_inff()) {  // uniform
+    const unsigned long long thr =
+        static_cast<unsigned long long>(ceil(double(top_p) * double(z) * kTopPFix));
+#pragma unroll
+    for (int j = 0; j < kTopPPer; ++j) {
+      const int k = tid * kTopPPer + j;
+      if (k < n) {
+        const float w = inf_mode ? (x[j] == __builtin_inff() ? 1.0f : 0.0f)
+                                 : ((x[j] == x[j] && x[j] > -__builtin_inff()) ? expf(x[j] - m)
+                                                                               : 0.0f);
+        ew[k] = static_cast<unsigned long long>(double(w) * kTopPFix);
+      }
+    }
+    // ---- radix search for the boundary key, 8 bits a level ------------------
+    uint32_t prefix = 0;
+    unsigned long long above = 0ull;
+    bool found = true;
+    for (int level = 0; level < 4 && found; ++level) {
+      const int shift = 24 - 8 * level;
+      if (level > 0) {
+        if (tid < 256) hsum[tid] = 0ull;
+        __syncthreads();
+      }
+#pragma unroll
+      for (int j = 0; j < kTopPPer; ++j) {
+        const int k = tid * kTopPPer + j;
+        if (k < n) {
+          const uint32_t key = ekey[k];
+          if (level == 0 || (key >> (shift + 8)) == prefix)
+            atomicAdd(&hsum[(key >> shift) & 255u], ew[k]);
         }
       }
-      // the next stage's stride; after the last stage, the group reads the result
-      const int next = stride > 1 ? stride >> 1 : ((size << 1) <= n2 ? size : 1 << 30);
-      if (stride > 64 || next > 64) __syncthreads();
-      else wave_lds_sync();
-    }
-  }
-
-  // ---- the cut: the first sorted entry whose running weight reaches top_p z ----
-  if (z > 0.0f && z < __builtin_inff()) {
-    const float thr = top_p * z;
-    float w[kTopPPer], run = 0.0f;
+      __syncthreads();
+      // bins from the highest: the one where the running weight reaches thr
+      unsigned long long v = 0ull, incl = 0ull;
+      if (tid < 256) {
+        v = hsum[255 - tid];
+        incl = v;
 #pragma unroll
-    for (int j = 0; j < kTopPPer; ++j) {
-      const int i = tid * kTopPPer + j;
-      w[j] = i < n ? weight(sc[0xFFFFFFFFu - uint32_t(ent[i])]) : 0.0f;
-      run += w[j];
-    }
-    // exclusive prefix of the per-thread sums, in a fixed order
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    if (lane == kWave - 1) red_s[wave] = incl;
-    __syncthreads();
-    float before = incl - run;
-    for (int w2 = 0; w2 < wave; ++w2) before += red_s[w2];
-    float cum = before;
-#pragma unroll
-    for (int j = 0; j < kTopPPer; ++j) {
-      const int i = tid * kTopPPer + j;
-      cum += w[j];
-      if (i < n && cum >= thr) {
-        atomicMin(&cut, i + 1);
-        break;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const unsigned long long y = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += y;
+        }
+        if (lane == kWave - 1) wtot[wave] = incl;
       }
+      __syncthreads();
+      if (tid < 256) {
+        unsigned long long before = incl - v;
+        for (int w2 = 0; w2 < wave; ++w2) before += wtot[w2];
+        if (above + before < thr && thr <= above + before + v) {
+          sel_d = 255 - tid;
+          sel_above = above + before;
+        }
+      }
+      __syncthreads();
+      found = sel_d >= 0;  // uniform; none at level 0: the selection's weight stays below thr
+      if (found) {
+        prefix = (prefix << 8) | uint32_t(sel_d);
+        above = sel_above;
+      }
+      __syncthreads();  // every thread has read sel_d before it is reset
+      if (tid == 0) sel_d = -1;
+    }
+    if (found) {
+      kappa = prefix;
+      // entries above kappa, and the ties at kappa (equal weights)
+#pragma unroll
+      for (int j = 0; j < kTopPPer; ++j) {
+        const int k = tid * kTopPPer + j;
+        if (k < n) {
+          if (ekey[k] > kappa) atomicAdd(&n_above, 1);
+          else if (ekey[k] == kappa) {
+            atomicAdd(&n_tie, 1);
+            tie_w = ew[k];  // every tie writes the same value
+          }
+        }
+      }
+      __syncthreads();
+      const unsigned long long need = thr - above, wk = tie_w;  // need > 0
+      int jt = wk > 0 ? int(min((need + wk - 1) / wk, (unsigned long long)n_tie)) : n_tie;
+      j_tie = max(jt, 1);
+      mcut = min(n_above + j_tie, n);
     }
   }
-  __syncthreads();
-  const int mcut = cut;
-  for (int i = tid; i < mcut; i += kTopPThreads) keep[0xFFFFFFFFu - uint32_t(ent[i])] = 1;
-  __syncthreads();
 
-  // ---- compaction in token order -----------------------------------------------
+  // ---- keep the top mcut, compacted in token order ---------------------------
+  // kept: keys above kappa, and the first j_tie ties at kappa by position
+  // (everything when no cut was made)
+  const bool cutting = mcut < n || j_tie > 0;
+  int tie_mine = 0;
+#pragma unroll
+  for (int j = 0; j < kTopPPer; ++j) {
+    const int k = tid * kTopPPer + j;
+    tie_mine += (cutting && k < n && ekey[k] == kappa) ? 1 : 0;
+  }
+  int tincl = tie_mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(tincl, off, kWave);
+    if (lane >= off) tincl += y;
+  }
+  if (lane == kWave - 1) red_i[wave] = tincl;
+  __syncthreads();
+  int tie_rank = tincl - tie_mine;
+  for (int w2 = 0; w2 < wave; ++w2) tie_rank += red_i[w2];
+  bool keep[kTopPPer];
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < kTopPPer; ++j) {
     const int k = tid * kTopPPer + j;
-    mine += k < n ? int(keep[k]) : 0;
+    bool kp = k < n;
+    if (cutting && kp) {
+      const uint32_t key = ekey[k];
+      if (key == kappa) kp = tie_rank++ < j_tie;
+      else kp = key > kappa;
+    }
+    keep[j] = kp;
+    mine += kp ? 1 : 0;
   }
   int incl = mine;
 #pragma unroll
@@ -775,6 +835,7 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     const int y = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += y;
   }
+  __syncthreads();  // red_i is reused
   if (lane == kWave - 1) red_i[wave] = incl;
   __syncthreads();
   int pos = incl - mine;
@@ -782,11 +843,14 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
 #pragma unroll
   for (int j = 0; j < kTopPPer; ++j) {
     const int k = tid * kTopPPer + j;
-    if (k < n && keep[k]) out[pos++] = tok[k];
+    if (keep[j]) out[pos++] = tok[k];
   }
-  for (int k = mcut + tid; k < n; k += kTopPThreads) out[k] = -1;
-  if (tid == 0) count[unit] = mcut;
+  int total = 0;
+  for (int w2 = 0; w2 < kWaves; ++w2) total += red_i[w2];
+  for (int k = total + tid; k < n; k += kTopPThreads) out[k] = -1;
+  if (tid == 0) count[unit] = total;
 }
+
 }  // namespace
 
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
