@@ -6,7 +6,8 @@
 //
 // Token mode: a unit has up to max_tokens candidates (131072 at 128K context),
 // too many for one work-group to read fast, so the selection is spread over
-// kTokChunk-key chunks, one work-group each, in three launches:
+// kTokChunk-key chunks, one work-group each, in three launches (four with the
+// adaptive budget):
 //   hist    every group adds the histogram of its keys' top 12 bits (of the
 //           order-preserving key) to its unit's, with device-scope atomics
 //           (the histogram is zero on entry: the finish of the previous call
@@ -21,7 +22,11 @@
 //           and writes its chunk's taken tokens in index order (those above
 //           the boundary key, and of its ties the lowest indices) at offsets
 //           counted from the bitmaps below the chunk; the groups share
-//           returning the unit's histogram to zero.
+//           returning the unit's histogram to zero;
+//   topp    (only with top_p > 0, the adaptive budget) one group per unit
+//           keeps the shortest top-ranked prefix of that selection whose
+//           softmax shares reach top_p, from per-chunk partials the filter
+//           then also stores.
 #include "common.hpp"
 #include "select_core.hpp"
 
