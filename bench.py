@@ -1,23 +1,21 @@
 """Decode-step throughput of the sparse attention hot path on one MI355X.
 
 A step is one pass of the whole path for one layer: score_scan (4-bit dense
-scan or projected-key scan), select_topk, sparse_decode_attn and combine, over a batch of
-synthetic inputs already resident in HBM. By default (--mode auto) a block-mode
-step with at least 16384 scanned blocks and sequence lengths that differ is one
-decode_step launch, every other step two calls, score_scan and
-select_attend_combine. Consecutive steps rotate
-over --layers distinct copies of the KV cache, as consecutive layers of a model
-would, so no step finds the previous step's data in the 256 MB Infinity Cache.
+scan or projected-key scan), select_topk, sparse_decode_attn and combine, over a
+batch of synthetic inputs already resident in HBM. By default (--mode auto) a
+step is two calls, score_scan and select_attend_combine (the selection, then
+the attention with its merge). Consecutive steps rotate over --layers
+distinct copies of the KV cache, as consecutive layers of a model would, so no
+step finds the previous step's data in the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is (batch x KV heads) decode steps per second;
 `pct_hbm_peak` is the step's algorithmic bytes per second over 8 TB/s;
 `dense_same_gpu` is dense FP16 attention (every block selected) on the same
 cache and kernels, with the sparse step's speedup over it. `roofline` is the
-dominant kernel (the one-launch step kernel, which is the whole step, or else the
-scan) measured with HIP events on the
-launch stream over the timed region (recorded on every --event-stride-th step,
-since each event record costs the GPU a marker); `cpu_baseline` is the CPU oracle timed on
-a bounded sample of the same workload.
+dominant kernel, the scan, measured with HIP events on the launch stream over
+the timed region (recorded on about 8 sampled steps, since each event record
+costs the GPU a marker); `cpu_baseline` is the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -42,11 +40,10 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # calibrated on a copy of known size) in profiles/<kernel>.<workload>.traffic.md,
 # valid while the kernel's sources (listed here) are unchanged
 TRAFFIC_SOURCES = {  # kernel: (file name stem, sources)
-    "scan_block_kernel": ("scan_block_kernel", ["scan.hip", "scan_core.hpp", "common.hpp"]),
+    "scan_block_kernel": ("scan_block_kernel", ["scan.hip", "scan_core.hpp", "select_core.hpp",
+                                                "common.hpp"]),
     "scan_token_kernel<32>": ("scan_token_kernel_r32", ["scan.hip", "common.hpp"]),
     "scan_token_kernel<32, fp8>": ("scan_token_kernel_r32_fp8", ["scan.hip", "common.hpp"]),
-    "step_kernel": ("step_kernel", ["step.hip", "scan_core.hpp", "attn_core.hpp",
-                                    "select_core.hpp", "combine_core.hpp", "common.hpp"]),
 }
 
 
@@ -70,18 +67,21 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time only the whole step, without per-kernel events")
-    ap.add_argument("--event-stride", type=int, default=25,
+    ap.add_argument("--event-stride", type=int, default=0,
                     help="record the per-kernel events on every n-th timed step (each event "
-                         "record costs the GPU a marker packet)")
+                         "record costs the GPU a marker packet); 0: about 8 samples, with a "
+                         "stride coprime with --layers")
+    ap.add_argument("--warmup-ms", type=float, default=1500.0,
+                    help="after the --warmup steps, keep warming up (untimed) until this much "
+                         "wall time has passed, so clocks and address translations settle")
     ap.add_argument("--mode", default="auto",
-                    choices=["auto", "step", "fused", "scoresel", "three", "split"],
-                    help="auto: step where the one-launch step pays off (block mode, "
-                         ">= 16384 scanned blocks, ragged lengths), else fused; "
-                         "step: decode_step (one launch in block mode); "
-                         "fused: score_scan, select_attend_combine; "
+                    choices=["auto", "scoresel", "fused", "three", "split", "step"],
+                    help="auto: fused; "
                          "scoresel: score_select, attend_combine; "
+                         "fused: score_scan, select_attend_combine; "
                          "three: score_scan, select_topk, attend_combine; "
-                         "split: score_scan, select_topk, sparse_decode_attn, combine")
+                         "split: score_scan, select_topk, sparse_decode_attn, combine; "
+                         "step: decode_step")
     return ap.parse_args()
 
 
@@ -205,6 +205,42 @@ def cpu_baseline(w, budget_s: float):
                       f"(scan, select, attention, combine; NumPy float64) in {spent:.1f} s"}
 
 
+def event_stride(steps: int, layers: int, requested: int) -> int:
+    """Stride of the sampled steps: the requested one, else about 8 samples
+    whatever the step count, coprime with the layer rotation so that every
+    layer copy is sampled."""
+    if requested > 0:
+        return requested
+    s = max(1, steps // 8)
+    while math.gcd(s, layers) != 1:
+        s += 1
+    return s
+
+
+def percentiles(xs):
+    import numpy as np
+
+    return [round(float(np.percentile(xs, q)), 2) for q in (10, 50, 90)]
+
+
+def check_after_timing(layers, calls, steps: int) -> None:
+    """The timed steps completed as they should: every counter word is back at
+    zero (a bounded wait that gave up leaves the fault word set), and one
+    layer's output is reproduced bit for bit by an untimed step."""
+    import torch
+
+    for d in layers:
+        bad = int(torch.count_nonzero(d.counters))
+        assert bad == 0, f"{bad} counter words are not zero after the timed steps"
+    d = layers[(steps - 1) % len(layers)]
+    out, lse = d.out.clone(), d.out_lse.clone()
+    for c in calls(d):
+        c()
+    torch.cuda.synchronize()
+    assert torch.equal(out, d.out) and torch.equal(torch.nan_to_num(lse), torch.nan_to_num(d.out_lse)), \
+        "an untimed step did not reproduce the timed step's output"
+
+
 def main() -> int:
     a = parse()
     if a.gpus != 1:
@@ -216,7 +252,7 @@ def main() -> int:
     import torch
 
     from block_sparse_attention_pack_amd import binding, workloads as W
-    from block_sparse_attention_pack_amd.step import one_launch_pays, upload
+    from block_sparse_attention_pack_amd.step import STEP_FORMS, default_form, step_calls, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
@@ -226,10 +262,8 @@ def main() -> int:
     w = W.generate(spec, threads=16)
     log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
     if a.mode == "auto":
-        ragged = len(set(int(x) for x in w.seq_lens)) > 1
-        a.mode = "step" if one_launch_pays(spec.units, spec.max_blocks, spec.granularity,
-                                           ragged) else "fused"
-    d0 = upload(w, splits=a.splits, one_launch=a.mode == "step")
+        a.mode = default_form(spec.granularity)
+    d0 = upload(w, splits=a.splits)
     d0.pack()
     torch.cuda.synchronize()
     layers = [d0]
@@ -245,25 +279,23 @@ def main() -> int:
     nbytes = W.algorithmic_bytes(w)
     stream = torch.cuda.current_stream()
 
-    if a.mode == "step":
-        stages = ["decode_step"]
-        calls = lambda d: [d.decode_step]
-    elif a.mode == "fused":
-        stages = ["scan", "select_attend_combine"]
-        calls = lambda d: [d.scan, d.select_attend_combine]
-    elif a.mode == "scoresel":
-        stages = ["score_select", "attend_combine"]
-        calls = lambda d: [d.score_select, d.attend_combine]
-    elif a.mode == "three":
-        stages = ["scan", "select", "attend_combine"]
-        calls = lambda d: [d.scan, d.select, d.attend_combine]
-    else:
-        stages = ["scan", "select", "attend", "combine"]
-        calls = lambda d: [d.scan, d.select, d.attend, d.combine]
-    for i in range(a.warmup):
-        for c in calls(layers[i % len(layers)]):
-            c()
-    torch.cuda.synchronize()
+    stages = STEP_FORMS[a.mode]
+    calls = lambda d: step_calls(d, a.mode)
+    # untimed warm-up: the --warmup steps, then more in batches of 16 until
+    # --warmup-ms of wall time has passed (the driver's short runs otherwise
+    # time a GPU whose clocks have not settled)
+    t_warm = time.perf_counter()
+    warm_steps = 0
+    while True:
+        n_batch = max(a.warmup - warm_steps, 0) if warm_steps < a.warmup else 16
+        for _ in range(n_batch):
+            for c in calls(layers[warm_steps % len(layers)]):
+                c()
+            warm_steps += 1
+        torch.cuda.synchronize()
+        if warm_steps >= a.warmup and (time.perf_counter() - t_warm) * 1e3 >= a.warmup_ms:
+            break
+    warm_ms = (time.perf_counter() - t_warm) * 1e3
     kept = None
     if spec.top_p > 0:  # the adaptive budget: the attention reads the tokens kept
         if a.warmup == 0:
@@ -275,9 +307,9 @@ def main() -> int:
 
     ns = len(stages)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(a.steps)]
+    stride = event_stride(a.steps, a.layers, a.event_stride)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    stride = max(1, a.event_stride)
     for i in range(a.steps):
         cs = calls(layers[i % len(layers)])
         if a.no_stage_events or i % stride:
@@ -294,32 +326,33 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / a.steps
     units = spec.batch * spec.kv_heads
     value = units * a.steps / elapsed
-    stage_us = {}
-    if not a.no_stage_events:
-        sampled = range(0, a.steps, stride)
+    stage_us, stage_pct = {}, {}
+    sampled = [] if a.no_stage_events else list(range(0, a.steps, stride))
+    if sampled:
         for j, name in enumerate(stages):
             ts = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in sampled]
             stage_us[name] = float(np.mean(ts))
+            stage_pct[name] = percentiles(ts)
         step_us = [ev[i][0].elapsed_time(ev[i][ns]) * 1e3 for i in sampled]
-        stage_us["step_events_p50"] = float(np.median(step_us))
-    log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms; stages (us): {stage_us}")
+        stage_pct["step"] = percentiles(step_us)
+    log(f"[bench] {a.steps} steps in {elapsed * 1e3:.2f} ms after {warm_steps} warm-up steps "
+        f"({warm_ms:.0f} ms); stages (us): {stage_pct}")
+    check_after_timing(layers, calls, a.steps)
 
-    # the dominant kernel: the whole step when it is one launch, else the scan
-    one_launch = a.mode == "step" and d0.block_mode
-    kern_us = stage_us.get("decode_step" if one_launch else "scan")
-    kbytes = nbytes["total" if one_launch else "scan"]
+    # the dominant kernel: the scan (timed where it is a call of its own)
+    scan_stage = "scan"
+    kern_us = stage_us.get(scan_stage)
+    kbytes = nbytes["scan"]
     roofline = None
     if kern_us:
         achieved = kbytes / (kern_us * 1e-6) / 1e9
-        if one_launch:
-            kname = "step_kernel"
-        else:
-            kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"
-                     % (spec.rank, ", fp8" if spec.proj_fmt == "fp8" else ""))
+        kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"
+                 % (spec.rank, ", fp8" if spec.proj_fmt == "fp8" else ""))
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(kname, spec.name),
-                    "bytes_per_launch": kbytes}
+                    "bytes_per_launch": kbytes,
+                    "events": f"{scan_stage} stage, {len(sampled)} sampled steps, mean"}
     step_gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -347,7 +380,10 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": nbytes["total"],
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "stage_events": None if a.no_stage_events else f"every {stride}th timed step",
+        "stages_us_p10_p50_p90": stage_pct,
+        "stage_events": None if not sampled else
+        f"{len(sampled)} of {a.steps} timed steps (every {stride}th)",
+        "warmup_run": {"steps": warm_steps, "ms": round(warm_ms, 1)},
         "roofline": roofline,
     }
     if a.dense:

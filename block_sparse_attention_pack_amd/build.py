@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
-SOURCES = ["api.hip", "pack.hip", "scan.hip", "select.hip", "attn.hip", "combine.hip", "step.hip"]
+SOURCES = ["api.hip", "pack.hip", "scan.hip", "select.hip", "attn.hip", "combine.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

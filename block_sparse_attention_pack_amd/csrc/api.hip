@@ -123,20 +123,19 @@ namespace {
 // Attention, then the merge: in the attention launch's last group of each unit
 // up to bsa::kFusedMergeMaxSplits splits, in the row-parallel merge launch
 // beyond. With sel_scores the attention launch also selects the blocks (block
-// mode).
+// mode) into idx and count.
 hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
                             const void* k, const void* v, const int32_t* seq_lens,
-                            const int32_t* idx, const int32_t* count, const uint16_t* tail_k,
+                            int32_t* idx, int32_t* count, const uint16_t* tail_k,
                             const uint16_t* tail_v, int32_t num_splits, float* part_o,
                             float* part_lse, uint32_t* counters, float* out, float* out_lse,
-                            const float* sel_scores, int32_t* sel_idx, int32_t* sel_count,
-                            hipStream_t s) {
+                            hipStream_t s, const float* sel_scores = nullptr) {
   const bool merge_in_last_group = num_splits <= bsa::kFusedMergeMaxSplits;
   hipError_t e = bsa::launch_attention(
       g, cfg->granularity, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
       static_cast<const _Float16*>(q), k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
       part_o, part_lse, merge_in_last_group ? counters : nullptr, out, out_lse, sel_scores,
-      sel_idx, sel_count, s);
+      sel_scores ? idx : nullptr, sel_scores ? count : nullptr, s);
   if (e == hipSuccess && !merge_in_last_group)
     e = bsa::launch_combine(g.B * g.Hq, num_splits, part_o, part_lse, out, out_lse, s);
   return e;
@@ -222,6 +221,22 @@ hipError_t launch_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, cons
                                     count, s);
   return bsa::launch_select_token(g, cfg->budget, scores, seq_lens, workspace, idx, count, s,
                                   hist_ready, cfg->top_p);
+}
+
+// The scan and the selection. Token mode: the scan fills the selection's
+// first-digit histograms as it stores the scores, so the selection skips that
+// pass.
+hipError_t score_and_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
+                            const uint8_t* codes, const uint8_t* scales,
+                            const float* global_scale, const float* key_center,
+                            const void* kproj, const float* proj, const int32_t* seq_lens,
+                            float* scores, void* workspace, int32_t* idx, int32_t* count,
+                            hipStream_t s) {
+  const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
+  hipError_t e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                             seq_lens, scores, s, tok ? workspace : nullptr);
+  if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
+  return e;
 }
 
 #define BSA_CHECK(expr)   \
@@ -383,7 +398,7 @@ size_t bsa_counters_size(const bsa_kv_layout* layout) {
   if (!layout || layout->batch < 1 || layout->num_kv_heads < 1) return 0;
   const int64_t units = int64_t(layout->batch) * layout->num_kv_heads;
   if (units > 65535) return 0;  // no call accepts such a layout
-  return sizeof(uint32_t) * size_t(bsa::step_counter_words(int(units)));
+  return sizeof(uint32_t) * size_t(units);
 }
 
 int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
@@ -398,13 +413,9 @@ int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    // token mode: the scan fills the selection's histograms as it goes
-    const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
-    hipError_t e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
-                               seq_lens, scores, s, tok ? workspace : nullptr);
-    if (e == hipSuccess)
-      e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
-    return hip_status(e, "score_select");
+    return hip_status(score_and_select(g, cfg, q, codes, scales, global_scale, key_center, kproj,
+                                       proj, seq_lens, scores, workspace, idx, count, s),
+                      "score_select");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }
@@ -423,9 +434,9 @@ int bsa_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, c
                                 part_o, part_lse));
     BSA_CHECK(check_merge_args(out, counters));
     (void)hipGetLastError();
-    return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v,
-                                       num_splits, part_o, part_lse, counters, out, out_lse,
-                                       nullptr, nullptr, nullptr,
+    return hip_status(attend_and_merge(g, cfg, q, k, v, seq_lens, const_cast<int32_t*>(idx),
+                                       const_cast<int32_t*>(count), tail_k, tail_v, num_splits,
+                                       part_o, part_lse, counters, out, out_lse,
                                        static_cast<hipStream_t>(stream)),
                       "attend_combine");
   } catch (...) {
@@ -449,18 +460,15 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
     BSA_CHECK(check_merge_args(out, counters));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const bool in_attention =
-        cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax;
     hipError_t e;
-    if (in_attention) {
+    if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
       e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-                           part_o, part_lse, counters, out, out_lse, scores, idx, count, s);
+                           part_o, part_lse, counters, out, out_lse, s, scores);
     } else {
       e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s);
       if (e == hipSuccess)
         e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-                             part_o, part_lse, counters, out, out_lse, nullptr, nullptr, nullptr,
-                             s);
+                             part_o, part_lse, counters, out, out_lse, s);
     }
     return hip_status(e, "select_attend_combine");
   } catch (...) {
@@ -488,22 +496,18 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
     (void)hipGetLastError();
     hipError_t e;
     if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
-      e = bsa::launch_step(g, cfg->budget, cfg->n_tail_pages, cfg->softmax_scale,
-                           cfg->query_dtype == BSA_QUERY_NVFP4, static_cast<const _Float16*>(q),
-                           codes, scales, global_scale, key_center, k, v, seq_lens, tail_k,
-                           tail_v, num_splits, scores, idx, count, part_o, part_lse, counters,
-                           out, out_lse, s);
-    } else {
-      // token mode: the scan fills the selection's histograms as it goes
-      const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
+      // two launches: the scan, then the attention with the selection in its prologue
       e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
-                      scores, s, tok ? workspace : nullptr);
-      if (e == hipSuccess)
-        e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
+                      scores, s);
       if (e == hipSuccess)
         e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-                             part_o, part_lse, counters, out, out_lse, nullptr, nullptr, nullptr,
-                             s);
+                             part_o, part_lse, counters, out, out_lse, s, scores);
+    } else {
+      e = score_and_select(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                           seq_lens, scores, workspace, idx, count, s);
+      if (e == hipSuccess)
+        e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                             part_o, part_lse, counters, out, out_lse, s);
     }
     return hip_status(e, "decode_step");
   } catch (...) {

@@ -1,21 +1,29 @@
-// Sparse decode attention kernel (split partials, optional in-kernel selection
-// and merge) and its host launcher. The device code is in attn_core.hpp.
+// Sparse decode attention kernel (split partials, optional in-kernel merge)
+// and its host launcher. The device code is in attn_core.hpp.
 #include "attn_core.hpp"
 
 namespace bsa {
 namespace {
 
-// grid (splits, B * Hkv), 256 threads.
-template <int G, bool MAIN_BF16>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int block_mode_i) {
+// grid (splits, B * Hkv), 256 threads; two work-groups per CU (the pipeline's
+// rings need up to 256 VGPRs).
+template <int G, bool MAIN_BF16, bool BLOCK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(
+    AttnArgs a) {
   __shared__ AttnLds<G> lds;
-  attn_item<G, MAIN_BF16, false>(a, block_mode_i != 0, blockIdx.x, blockIdx.y, lds, StepSync{});
+  attn_item<G, MAIN_BF16, BLOCK>(a, blockIdx.x, blockIdx.y, lds);
+}
+
+template <int G, bool BLOCK>
+void launch_gb(dim3 grid, hipStream_t s, const AttnArgs& a, bool bf16) {
+  if (bf16) hipLaunchKernelGGL((attn_kernel<G, true, BLOCK>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_kernel<G, false, BLOCK>), grid, dim3(256), 0, s, a);
 }
 
 template <int G>
 void launch_g(dim3 grid, hipStream_t s, const AttnArgs& a, int block_mode, bool bf16) {
-  if (bf16) hipLaunchKernelGGL((attn_kernel<G, true>), grid, dim3(256), 0, s, a, block_mode);
-  else hipLaunchKernelGGL((attn_kernel<G, false>), grid, dim3(256), 0, s, a, block_mode);
+  if (block_mode) launch_gb<G, true>(grid, s, a, bf16);
+  else launch_gb<G, false>(grid, s, a, bf16);
 }
 
 }  // namespace

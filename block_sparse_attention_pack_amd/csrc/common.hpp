@@ -22,12 +22,14 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 
-// The block scan's NVFP4 query of one unit, staged in LDS by its work-group:
-// e2m1 * e4m3 of head n, channels 8 c .. 8 c + 7 at q[16 n + c]; the head's FP32
-// scale at s_q[n].
+// The block scan's query side of one unit, staged in LDS by its work-group:
+// with an NVFP4 query, e2m1 * e4m3 of head n, channels 8 c .. 8 c + 7 at
+// q[16 n + c] and the head's FP32 scale at s_q[n]; for every query, the head's
+// q . c (times s_q) at qc[n].
 struct ScanQueryLds {
   half8 q[kMaxGroup * 16];
   float s_q[kMaxGroup];
+  float qc[kMaxGroup];
 };
 
 // Token selection's first radix digit: the top 12 bits of a score's key
@@ -259,12 +261,16 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                hipStream_t s, bool hist_ready = false, float top_p = 0.0f);
 // Largest token budget the adaptive (top-p) budget sorts in one work-group's LDS.
 constexpr int kTopPMaxBudget = 4096;
-// Largest budget for which the attention launch selects the blocks itself.
-constexpr int kFusedSelectMax = 1024;
 // The attention launch merges the splits in its last group up to this many
 // (more, up to 32, measured slower than the separate merge launch).
 constexpr int kFusedMergeMaxSplits = 8;
 
+// Largest budget for which the attention launch selects the blocks itself.
+constexpr int kFusedSelectMax = 1024;
+
+// sel_scores (block mode, budget <= kFusedSelectMax, optional): the launch
+// also selects each unit's blocks from these scores, as select_topk would,
+// and writes the selection to sel_idx / sel_count; idx and count are unused.
 hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int n_tail,
                             float sigma, const _Float16* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* idx, const int32_t* count,
@@ -274,16 +280,6 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
                             int32_t* sel_count, hipStream_t s);
 hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
                           float* out, float* out_lse, hipStream_t s);
-// The block-mode decode step in one launch (scan, selection, attention, merge).
-// Its counters: step_counter_words(units) 32-bit words, zero before the launch.
-int step_counter_words(int units);
-hipError_t launch_step(const UnitGeom& g, int budget, int n_tail, float sigma, bool query_nvfp4,
-                       const _Float16* q,
-                       const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                       const float* center, const void* k, const void* v,
-                       const int32_t* seq_lens, const uint16_t* tail_k, const uint16_t* tail_v,
-                       int splits, float* scores, int32_t* idx, int32_t* count, float* part_o,
-                       float* part_lse, uint32_t* counters, float* out, float* out_lse,
-                       hipStream_t st);
+
 
 }  // namespace bsa

@@ -11,13 +11,15 @@
 namespace bsa {
 namespace {
 
+// Blocks per wave of the block scan (fewer when the grid would not fill the GPU).
+constexpr int kScanBlocksPerWave = 4;
+
 // grid (ceil(NBmax / (kScanWaves * bpw)), B * Hkv), 256 threads. Q4: the
 // NVFP4 query (a.query_nvfp4).
 template <bool Q4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void scan_block_kernel(ScanBlockArgs a) {
   __shared__ ScanQueryLds ql;
-  scan_wave_blocks<false, false, Q4>(a, threadIdx.x & 63, threadIdx.x >> 6, blockIdx.y,
-                                     blockIdx.x, ql);
+  scan_wave_blocks<Q4>(a, threadIdx.x & 63, threadIdx.x >> 6, blockIdx.y, blockIdx.x, ql);
 }
 
 // Token mode. grid (ceil(Tmax / kTokPerWg), B * Hkv), 256 threads; each wave
@@ -221,7 +223,7 @@ hipError_t launch_scan_block(const UnitGeom& g, int n_tail, float sigma, bool qu
                              float* scores, hipStream_t s) {
   dim3 grid;
   const ScanBlockArgs a = make_scan_args(g, n_tail, sigma, q, codes, scales, gscale, center,
-                                         seq_lens, scores, grid, 4, query_nvfp4);
+                                         seq_lens, scores, grid, kScanBlocksPerWave, query_nvfp4);
   if (query_nvfp4) hipLaunchKernelGGL(scan_block_kernel<true>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(scan_block_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -16,22 +16,12 @@ from . import binding as bsa
 from .workloads import BLOCK, HEAD_DIM, Workload
 
 
-def default_splits(units: int, budget: int, granularity: str, one_launch: bool = False) -> int:
-    """Split count of the attention.
-
-    Separate attention launch: about 512 work-groups. The kernel runs three
-    waves per SIMD, so 512 four-wave groups are resident on 256 CUs at once;
-    more, smaller splits only add merge work (and, with the selection in the
-    attention prologue, more copies of it). A split keeps at least two blocks
-    (block mode, from 8 units up; fewer units are latency-bound and gain from
-    one block per split) or 64 tokens (token mode).
-
-    One-launch decode step (block mode): four blocks per split. The selection
-    is made once per unit there, and short attention items shorten the end of
-    the launch, when the last units' attention runs after their scan.
-    """
-    if one_launch and granularity != "token":
-        return max(1, min(budget // 4, 1024))
+def default_splits(units: int, budget: int, granularity: str) -> int:
+    """Split count of the attention: about 512 work-groups, two per CU (the
+    kernel's pipeline runs two waves per SIMD), so every CU streams from the
+    first group on. A split keeps at least two blocks (block mode, from 8 units
+    up; fewer units are latency-bound and gain from one block per split) or 64
+    tokens (token mode)."""
     s = max(1, math.ceil(512 / max(units, 1)))
     if granularity == "token":
         s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
@@ -40,13 +30,26 @@ def default_splits(units: int, budget: int, granularity: str, one_launch: bool =
     return max(1, min(s, budget))
 
 
-def one_launch_pays(units: int, max_blocks: int, granularity: str, ragged: bool) -> bool:
-    """Whether the one-launch decode step beats scan + select_attend_combine:
-    in block mode, when the scan covers at least 16384 blocks and the sequence
-    lengths differ. Measured on MI355X: +3% at 64 x 1024 blocks with lengths
-    in [64K, 128K], where the two-call attention launch is unevenly loaded;
-    -0.9% at 64 x 1024 blocks of equal length; -23% at 8 x 256."""
-    return granularity != "token" and units * max_blocks >= 16384 and ragged
+# Forms of the step as calls of the C ABI (bench.py times one of them).
+STEP_FORMS = {
+    "scoresel": ["score_select", "attend_combine"],
+    "fused": ["scan", "select_attend_combine"],
+    "three": ["scan", "select", "attend_combine"],
+    "split": ["scan", "select", "attend", "combine"],
+    "step": ["decode_step"],
+}
+
+
+def default_form(granularity: str) -> str:
+    """The form bench.py times by default: score_scan, then
+    select_attend_combine (the selection, the attention and its merge), so
+    that the scan is a launch of its own whose rate is timed alone."""
+    return "fused"
+
+
+def step_calls(d: "DeviceStep", form: str):
+    """The bound methods of one step in the given form."""
+    return [getattr(d, name) for name in STEP_FORMS[form]]
 
 
 @dataclasses.dataclass
@@ -78,7 +81,7 @@ class DeviceStep:
     part_lse: "torch.Tensor"
     out: "torch.Tensor"
     out_lse: "torch.Tensor"
-    counters: "torch.Tensor"  # counters of attend_combine / decode_step (zero between calls)
+    counters: "torch.Tensor"  # arrival counters of the in-kernel merge (zero between calls)
 
     @property
     def block_mode(self) -> bool:
@@ -182,7 +185,7 @@ class DeviceStep:
 
     # -- the whole step as one call -------------------------------------------
     def decode_step(self, stream=None) -> None:
-        """bsa_decode_step: one launch in block mode."""
+        """bsa_decode_step: the whole step in one call."""
         bsa.decode_step(self.layout, self.cfg, self.q, self.codes, self.scales,
                         self.global_scale, self.key_center, self.kproj, self.proj, self.k,
                         self.v, self.seq_lens, self.tail_k, self.tail_v, self.splits,
@@ -192,12 +195,11 @@ class DeviceStep:
 
 
 def upload(w: Workload, device="cuda", splits: Optional[int] = None,
-           kv_dtype: str = "f16", one_launch: bool = False) -> DeviceStep:
+           kv_dtype: str = "f16") -> DeviceStep:
     """Copy a workload to the GPU and allocate every buffer of the step.
 
     ``kv_dtype="bf16"`` stores K and V as bfloat16 instead (values rounded from
-    the fp16 draws), for the BF16-cache variant. ``one_launch`` picks the
-    default split count for decode_step's single launch.
+    the fp16 draws), for the BF16-cache variant.
     """
     import torch
 
@@ -218,7 +220,7 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
                          query_dtype=bsa.QUERY_NVFP4 if s.query_fmt == "nvfp4" else bsa.QUERY_F16,
                          top_p=s.top_p)
     if splits is None:
-        splits = default_splits(B * Hkv, s.budget, s.granularity, one_launch)
+        splits = default_splits(B * Hkv, s.budget, s.granularity)
     nb = s.max_blocks
     codes = scales = kproj = proj = None
     if gran == bsa.BLOCK:

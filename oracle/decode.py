@@ -427,20 +427,27 @@ def attend(q_group: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, sigma: f
     return out, lse
 
 
-def split_ranges(budget: int, num_splits: int):
-    """Split s covers entries [s*per, min((s+1)*per, budget)) of the index list."""
-    per = -(-budget // num_splits)
-    return [(s * per, min((s + 1) * per, budget)) for s in range(num_splits)]
+def split_ranges(n: int, num_splits: int):
+    """Split s covers entries [s*per, min((s+1)*per, n)) of the n selected
+    entries, per = ceil(n / S): the splits share the entries actually selected,
+    so an adaptive budget that keeps fewer rows still spreads them evenly."""
+    per = -(-n // num_splits)
+    return [(min(s * per, n), min((s + 1) * per, n)) for s in range(num_splits)]
 
 
 def attend_splits(q_group, idx: np.ndarray, num_splits: int, rows_fn, sigma: float):
     """Per-split partials (O_s [S, G, 128], lse_s [S, G]) over the index list.
 
-    ``rows_fn(list_of_indices)`` returns the (K, V) rows of those entries.
+    idx holds the selection's entries followed by -1 padding; its count is the
+    number of entries before the padding. ``rows_fn(list_of_indices)`` returns
+    the (K, V) rows of those entries.
     """
+    idx = np.asarray(idx)
+    n = int(np.count_nonzero(idx >= 0))
+    assert np.all(idx[:n] >= 0) and np.all(idx[n:] < 0), "padding must follow the entries"
     parts_o, parts_l = [], []
-    for lo, hi in split_ranges(idx.shape[0], num_splits):
-        sel = [int(x) for x in idx[lo:hi] if x >= 0]
+    for lo, hi in split_ranges(n, num_splits):
+        sel = [int(x) for x in idx[lo:hi]]
         kr, vr = rows_fn(sel)
         o, l = attend(q_group, kr, vr, sigma)
         parts_o.append(o)

@@ -23,7 +23,8 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(ROOT, "include", h)).read()
+                   for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(bsa_[a-z_]+)\(", text, re.M)))
 
 
@@ -126,7 +127,7 @@ def test_combined_calls_check_their_arguments(lib):
     rc = lib.bsa_attend_combine(ctypes.byref(L), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, None, None, 2, FAKE, FAKE, None, FAKE, None, None)
     assert rc == -4
-    # select_attend_combine (block mode, selection in the attention launch)
+    # select_attend_combine (block mode: the selection, then the attention)
     args = lambda scores, splits, counters: (
         ctypes.byref(L), ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, scores, None, 0, None, None,
         splits, FAKE, FAKE, FAKE, FAKE, counters, FAKE, None, None)
@@ -139,10 +140,9 @@ def test_combined_calls_check_their_arguments(lib):
                                        FAKE, None, 0, None, None, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        FAKE, None, None)
     assert rc == -4
-    # per unit: a merge arrival word and a 128-byte scan-done line; 8 ticket
-    # lines; the fault flag
-    assert lib.bsa_counters_size(ctypes.byref(L)) == 4 * (33 + 257)
-    assert lib.bsa_counters_size(ctypes.byref(_layout(batch=3, num_kv_heads=2))) == 4 * (198 + 257)
+    # one merge arrival word per unit
+    assert lib.bsa_counters_size(ctypes.byref(L)) == 4
+    assert lib.bsa_counters_size(ctypes.byref(_layout(batch=3, num_kv_heads=2))) == 4 * 6
 
 
 def test_decode_step_checks_every_stage_first(lib):
@@ -150,10 +150,10 @@ def test_decode_step_checks_every_stage_first(lib):
     tok = B.select_cfg(B.TOKEN, 64, 0, 32)
 
     def step(c, codes=FAKE, kproj=None, splits=2, scores=FAKE, ws_bytes=0, counters=FAKE,
-             out=FAKE, k=FAKE):
+             out=FAKE, k=FAKE, ws=None):
         return lib.bsa_decode_step(
             ctypes.byref(L), ctypes.byref(c), FAKE, codes, FAKE, FAKE, None, kproj, FAKE, k,
-            FAKE, FAKE, None, None, splits, scores, None, ws_bytes, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, None, None, splits, scores, ws, ws_bytes, FAKE, FAKE, FAKE, FAKE,
             counters, out, None, None)
 
     assert step(cfg, codes=None) == -1  # the scan's key copy

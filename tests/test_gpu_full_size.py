@@ -2,10 +2,8 @@
 
 Each workload is drawn at its full size (up to 128K tokens, batch 16), packed,
 and run through the same calls bench.py times by default, with its default split
-count: one decode_step launch where that pays off (block mode, at least 16384
-scanned blocks, sequence lengths that differ), else score_scan and
-select_attend_combine. Every stage of a few sampled units
-(the first, the last and one in between) is then checked against the oracle:
+count (step.default_form). Every stage of sampled units (the first, the last
+and others spread between them) is then checked against the oracle:
 pack bytes bit-exact, scores within the FP32 accumulation bound, the selection
 bit-exact on the GPU's own scores, outputs within 2e-3.
 """
@@ -17,7 +15,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from block_sparse_attention_pack_amd import workloads as W
-from block_sparse_attention_pack_amd.step import one_launch_pays, upload
+from block_sparse_attention_pack_amd.step import default_form, step_calls, upload
 
 import parity_util as PU
 
@@ -32,10 +30,11 @@ def _gpu():
     binding.load()
 
 
-def _sampled_units(spec):
-    units = [(0, 0), (spec.batch - 1, spec.kv_heads - 1),
-             (spec.batch // 2, spec.kv_heads // 2)]
-    return sorted(set(units))
+def _sampled_units(spec, n=6):
+    """n units spread over the batch and the KV heads, the first and last included."""
+    U = spec.batch * spec.kv_heads
+    picks = sorted(set([0, U - 1] + [(U * i) // (n - 1) + i % spec.kv_heads for i in range(1, n - 1)]))
+    return [(u // spec.kv_heads, u % spec.kv_heads) for u in picks if u < U]
 
 
 @pytest.mark.parametrize("name", W.ORDER)
@@ -43,20 +42,15 @@ def test_full_size_sampled_units(name):
     spec = W.SPECS[name]
     print(f"[full] {name}: generating", flush=True)
     w = W.generate(spec, threads=16)
-    one = one_launch_pays(spec.units, spec.max_blocks, spec.granularity,
-                          len(set(int(x) for x in w.seq_lens)) > 1)
-    d = upload(w, one_launch=one)  # the default split count, as bench.py uses
+    form = default_form(spec.granularity)
+    d = upload(w)  # the default split count, as bench.py uses
     d.pack()
-    if one:
-        d.decode_step()
-    else:
-        d.scan()
-        d.select_attend_combine()
+    for call in step_calls(d, form):
+        call()
     torch.cuda.synchronize()
     assert int(d.counters.abs().sum()) == 0
     units = _sampled_units(spec)
-    print(f"[full] {name}: {'decode_step' if one else 'two calls'}, splits {d.splits}, "
-          f"checking units {units}", flush=True)
+    print(f"[full] {name}: {form}, splits {d.splits}, checking units {units}", flush=True)
     sys.stdout.flush()
     PU.check_units(w, d, units)
     del d

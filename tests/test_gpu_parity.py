@@ -101,10 +101,11 @@ STEP_OUT = ("scores", "idx", "count", "part_o", "part_lse", "out", "out_lse")
 
 
 def _two_calls_match(d):
-    """score_scan + select_attend_combine, and decode_step, reproduce the four
-    calls' bits (and leave every counter at zero)."""
+    """score_select + attend_combine, score_scan + select_attend_combine, and
+    decode_step reproduce the four calls' bits (and leave every counter at
+    zero)."""
     ref = [host(getattr(d, n)).copy() for n in STEP_OUT]
-    for run in (d.run_two, d.decode_step):
+    for run in (d.run_fused, d.run_two, d.decode_step):
         for n in STEP_OUT:
             getattr(d, n).fill_(7)
         run()
@@ -115,7 +116,8 @@ def _two_calls_match(d):
 
 
 def test_select_attend_combine_above_the_in_kernel_budget():
-    """Budgets above 1024 blocks select in their own launch; same results."""
+    """Budgets above 1024 blocks (more than 4 candidates per selecting thread
+    re-read from memory): same results in every form."""
     spec = dataclasses.replace(W.SPECS["jetqsparse"], name="big_budget", seed=90, batch=1,
                                kv_heads=1, q_heads=4, max_tokens=1280 * 128, budget=1100,
                                needle_count=5, key_offset_std=0.0)
@@ -285,8 +287,8 @@ def test_attend_combine_on_both_sides_of_the_merge_limit(splits):
 
 
 def test_decode_step_with_short_sequences_tails_and_many_splits():
-    """One launch: empty, sub-block and ragged sequences, 0-2 tail pages, and
-    split counts on both sides of the merge's fast path, call after call."""
+    """The whole step: empty, sub-block and ragged sequences, 0-2 tail pages, and
+    split counts on both sides of the in-kernel merge, call after call."""
     lengths = (0, 1, 129, 300, 2000, 4096)
     for n_tail in (0, 2):
         spec = dataclasses.replace(W.SPECS["ragged"], name=f"step_short{n_tail}", seed=85 + n_tail,
@@ -314,8 +316,8 @@ def test_decode_step_bf16_cache_and_large_group():
 
 @pytest.mark.parametrize("splits", [16, 32, 64])
 def test_decode_step_merges_many_splits(splits):
-    """The one-launch step merges up to 16 and 32 splits in one pass, more in
-    two: the four calls' bits either way."""
+    """More splits than the attention launch merges itself: the merge launch
+    gives the four calls' bits."""
     spec = W.reduced("jetqsparse", 16384, batch=2, budget=64)
     w = W.generate(spec)
     d = run_step(w, splits=splits)
@@ -466,7 +468,7 @@ def test_nvfp4_query_reads_back_every_element():
 def test_nvfp4_query_group_sizes(G):
     """The NVFP4 query staged by 16 threads per head, from 1 to 16 heads per KV
     head (all 256 threads at 16): scores against the oracle's quantized query,
-    and the one-launch step and the two calls give the four calls' bits."""
+    and the combined calls give the four calls' bits."""
     spec = dataclasses.replace(W.SPECS["jetqsparse_q4"], name=f"q4group{G}", seed=120 + G, batch=2,
                                kv_heads=2, q_heads=2 * G, max_tokens=4096, budget=6,
                                needle_count=2)

@@ -118,6 +118,22 @@ def test_combine_independent_of_split_count(splits):
         assert np.array_equal(po[0], o1)
 
 
+@pytest.mark.parametrize("n,splits", [(0, 3), (1, 8), (5, 2), (62, 8), (64, 8), (2048, 8), (7, 16)])
+def test_split_ranges_share_the_selected_entries(n, splits):
+    """The splits tile [0, n) in order, each at most ceil(n / S) entries, and
+    the empty ones come last."""
+    r = O.split_ranges(n, splits)
+    assert len(r) == splits
+    per = -(-n // splits)
+    cover = []
+    for lo, hi in r:
+        assert 0 <= lo <= hi <= n and hi - lo <= per
+        cover.extend(range(lo, hi))
+    assert cover == list(range(n))
+    sizes = [hi - lo for lo, hi in r]
+    assert sizes == sorted(sizes, reverse=True)
+
+
 def test_empty_selection_gives_zero_and_minus_inf():
     q = np.ones((4, 128), np.float16)
     po, pl = O.attend_splits(q, np.full(4, -1, np.int32), 2,
