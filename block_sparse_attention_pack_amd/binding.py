@@ -95,6 +95,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "bsa_decode_step": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
                             ctypes.c_size_t, _P, _P, _P, _P, _P, _P, _P, _P],
         "bsa_append_token": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "bsa_decode_step_noalloc": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                    _P, _P, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -257,3 +259,14 @@ def append_token(layout, cfg, k_new, v_new, seq_lens, k, v, key_center, global_s
         ctypes.byref(layout), ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
         _ptr(k), _ptr(v), _ptr(key_center), _ptr(global_scale), _ptr(proj), _ptr(codes),
         _ptr(scales), _ptr(kproj), _ptr(tail_k), _ptr(tail_v), _stream(stream)))
+
+
+def decode_step_noalloc(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj, k,
+                        v, seq_lens, tail_k, tail_v, num_splits, out, out_lse,
+                        stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_decode_step_noalloc(
+        ctypes.byref(layout), ctypes.byref(cfg), _ptr(q), _ptr(codes), _ptr(scales),
+        _ptr(global_scale), _ptr(key_center), _ptr(kproj), _ptr(proj), _ptr(k), _ptr(v),
+        _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), num_splits, _ptr(out), _ptr(out_lse),
+        _stream(stream)))

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -237,6 +238,108 @@ hipError_t score_and_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
                              seq_lens, scores, s, tok ? workspace : nullptr);
   if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
   return e;
+}
+
+// The whole step: block mode (budget <= kFusedSelectMax) as the scan and the
+// attention launch with the selection in its prologue; otherwise the scan, the
+// selection and the attention.
+hipError_t decode_step_launches(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const void* q,
+                                const uint8_t* codes, const uint8_t* scales,
+                                const float* global_scale, const float* key_center,
+                                const void* kproj, const float* proj, const void* k,
+                                const void* v, const int32_t* seq_lens, const uint16_t* tail_k,
+                                const uint16_t* tail_v, int32_t num_splits, float* scores,
+                                void* workspace, int32_t* idx, int32_t* count, float* part_o,
+                                float* part_lse, uint32_t* counters, float* out, float* out_lse,
+                                hipStream_t s) {
+  hipError_t e;
+  if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
+    e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
+                    scores, s);
+    if (e == hipSuccess)
+      e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                           part_o, part_lse, counters, out, out_lse, s, scores);
+  } else {
+    e = score_and_select(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                         seq_lens, scores, workspace, idx, count, s);
+    if (e == hipSuccess)
+      e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                           part_o, part_lse, counters, out, out_lse, s);
+  }
+  return e;
+}
+
+// --- the allocation-free step's scratch --------------------------------------
+// One array per GPU, in device memory the library owns for the life of the
+// process: the step's intermediates (scores, selection, split partials, merge
+// counters, token selection workspace) for callers that cannot allocate. Host
+// code never uses the array's name as an address: each device's address comes
+// from hipGetSymbolAddress on the first call there.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_of_current_device(uint8_t** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  BSA_REQUIRE(dev >= 0 && dev < kMaxScratchDevices, BSA_ERR_UNSUPPORTED,
+              "device %d: the scratch covers devices 0..%d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || !p)
+      return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(es));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+// Byte offsets of the step's buffers in the scratch (256-byte aligned); the
+// arrival counters and the workspace are adjacent, so one fill clears both.
+struct ScratchPlan {
+  size_t counters, workspace, workspace_bytes, scores, idx, count, part_o, part_lse, total;
+};
+
+int plan_scratch(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, int num_splits,
+                 ScratchPlan* p) {
+  const size_t U = size_t(g.B) * size_t(g.Hkv);
+  const size_t rows = size_t(g.B) * size_t(g.Hq);
+  const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  size_t off = 0;
+  p->counters = off;
+  off = up(off + U * 4);
+  p->workspace = off;
+  p->workspace_bytes = tok ? bsa::token_select_workspace(g) : 0;
+  off = up(off + p->workspace_bytes);
+  p->scores = off;
+  off = up(off + U * size_t(tok ? g.Tmax : g.NBmax) * 4);
+  p->idx = off;
+  off = up(off + U * size_t(cfg->budget) * 4);
+  p->count = off;
+  off = up(off + U * 4);
+  p->part_o = off;
+  off = up(off + rows * size_t(num_splits) * bsa::kHeadDim * 4);
+  p->part_lse = off;
+  off = up(off + rows * size_t(num_splits) * 4);
+  p->total = off;
+  BSA_REQUIRE(off <= kScratchBytes, BSA_ERR_WORKSPACE,
+              "this step needs %zu bytes of intermediates; the allocation-free step's scratch "
+              "holds %zu",
+              off, kScratchBytes);
+  return BSA_OK;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
 }
 
 #define BSA_CHECK(expr)   \
@@ -494,22 +597,59 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
     BSA_CHECK(check_merge_args(out, counters));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    hipError_t e;
-    if (cfg->granularity == BSA_GRANULARITY_BLOCK && cfg->budget <= bsa::kFusedSelectMax) {
-      // two launches: the scan, then the attention with the selection in its prologue
-      e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,
-                      scores, s);
-      if (e == hipSuccess)
-        e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-                             part_o, part_lse, counters, out, out_lse, s, scores);
-    } else {
-      e = score_and_select(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
-                           seq_lens, scores, workspace, idx, count, s);
-      if (e == hipSuccess)
-        e = attend_and_merge(g, cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
-                             part_o, part_lse, counters, out, out_lse, s);
-    }
-    return hip_status(e, "decode_step");
+    return hip_status(decode_step_launches(g, cfg, q, codes, scales, global_scale, key_center,
+                                           kproj, proj, k, v, seq_lens, tail_k, tail_v,
+                                           num_splits, scores, workspace, idx, count, part_o,
+                                           part_lse, counters, out, out_lse, s),
+                      "decode_step");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_decode_step_noalloc(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                            const void* q, const uint8_t* codes, const uint8_t* scales,
+                            const float* global_scale, const float* key_center,
+                            const void* kproj, const float* proj, const void* k, const void* v,
+                            const int32_t* seq_lens, const uint16_t* tail_k,
+                            const uint16_t* tail_v, int32_t num_splits, float* out,
+                            float* out_lse, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
+                BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
+                num_splits);
+    ScratchPlan plan;
+    BSA_CHECK(plan_scratch(g, cfg, num_splits, &plan));
+    uint8_t* base = nullptr;
+    BSA_CHECK(scratch_of_current_device(&base));
+    float* scores = reinterpret_cast<float*>(base + plan.scores);
+    int32_t* idx = reinterpret_cast<int32_t*>(base + plan.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(base + plan.count);
+    float* part_o = reinterpret_cast<float*>(base + plan.part_o);
+    float* part_lse = reinterpret_cast<float*>(base + plan.part_lse);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(base + plan.counters);
+    void* workspace = plan.workspace_bytes ? base + plan.workspace : nullptr;
+    BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
+    BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, plan.workspace_bytes, idx,
+                                count));
+    BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
+                                part_o, part_lse));
+    BSA_CHECK(check_merge_args(out, counters));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    // the arrival counters and the selection's workspace start at zero: the
+    // scratch keeps whatever the last call on this GPU left there
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(base + plan.counters),
+                       int64_t((plan.workspace + plan.workspace_bytes - plan.counters) / 4));
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess)
+      e = decode_step_launches(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
+                               k, v, seq_lens, tail_k, tail_v, num_splits, scores, workspace,
+                               idx, count, part_o, part_lse, counters, out, out_lse, s);
+    return hip_status(e, "decode_step_noalloc");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

@@ -29,7 +29,8 @@
  * Conventions for every entry point
  *   - Pointers named as device pointers are device memory of the current HIP
  *     device; the caller owns every buffer; the library allocates nothing,
- *     frees nothing and keeps no state between calls.
+ *     frees nothing and keeps no state between calls (apart from the scratch
+ *     that bsa_decode_step_noalloc keeps on each GPU, described there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and returns without waiting for it. Inputs must stay valid and outputs
  *     unread until the stream reaches the work.
@@ -234,8 +235,9 @@ int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  * abstract: FP16 aggregation with FP32 accumulation over contiguous block
  * tiles; JSSA Figure 1: gather-free reads of the selected rows).
  *
- * For query head hq of KV head h and split s, with per = ceil(budget/S), the
- * rows are those of idx entries [s*per, min((s+1)*per, budget)) that are not -1:
+ * For query head hq of KV head h and split s, with n = count (clamped to
+ * [0, budget]) and per = ceil(n/S), the rows are those of idx entries
+ * [s*per, min((s+1)*per, n)) (entries that are -1 are skipped):
  *   BLOCK: the tokens t of each selected block with t < L_b; a block that is one
  *     of the n_tail_pages newest pages (n >= N_b - n_tail_pages) is read from
  *     the BF16 tail store, slot n - (N_b - n_tail_pages), else from k, v.
@@ -245,8 +247,9 @@ int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  *   (an empty split writes 0 and -inf).
  * q: device fp16 [B][Hq][128]. k, v: device, kv_dtype, the layout above.
  * tail_k, tail_v: device bfloat16 bits [B][Hkv][n_tail_pages][128][128], or
- * NULL when n_tail_pages is 0. idx, count: as written by bsa_select_topk
- * (count is read only to skip the work of unused entries).
+ * NULL when n_tail_pages is 0. idx, count: as written by bsa_select_topk (the
+ * selection's entries first, then -1 padding); the splits share the count's
+ * entries evenly.
  * part_o: device float [B][Hq][S][128]; part_lse: device float [B][Hq][S];
  * 1 <= num_splits <= budget. */
 int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
@@ -275,15 +278,12 @@ int bsa_combine(int32_t rows, int32_t num_splits, int32_t head_dim, const float*
  * work-group of each unit to finish, so the merge hides behind other units'
  * attention (with more it launches the merge separately). That group is found
  * with one arrival counter per unit in `counters` (device, bsa_counters_size
- * bytes, of which these calls use the first 4 * batch * num_kv_heads): it must
- * be zero-filled before its first use, every call that completes leaves it
- * zero, and calls that share it must not run concurrently. In these calls no
- * work-group ever waits for another; bsa_decode_step's waits are described
- * there.
+ * bytes): it must be zero-filled before its first use, every call that
+ * completes leaves it zero, and calls that share it must not run
+ * concurrently. No work-group ever waits for another.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of the counters: 4 * (33 * batch * num_kv_heads + 257) (0 for a bad
- * layout). */
+/* Bytes of the counters: 4 * batch * num_kv_heads (0 for a bad layout). */
 size_t bsa_counters_size(const bsa_kv_layout* layout);
 
 /* bsa_score_scan then bsa_select_topk; arguments as there. In token mode the
@@ -327,19 +327,13 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
  * granularity needs. counters: bsa_counters_size bytes, zero-filled before the
  * first use.
  *
- * In block mode with budget <= 1024 this is one launch (Jet-QSparse abstract:
- * a dense scan of the 4-bit keys, a per-KV-head block selection, then sparse
- * aggregation of the chosen blocks). Its work-groups take work items in the
- * order of a ticket counter, the scan items ahead of the attention items; a
- * unit's attention items poll until the unit's scan items have stored their
- * scores. Those scan items hold earlier tickets, so they are already running
- * and never wait themselves: every wait ends. A wait is also bounded (about a
- * second, far beyond any correct run); past the bound the launch still ends,
- * its outputs are undefined, and the last counter word is set and stays set
- * (all other words return to zero). Calls sharing counters
- * must not run concurrently. Otherwise (token mode, larger budgets) it runs
- * the three calls in turn; workspace is bsa_select_topk's (unused in block
- * mode). */
+ * In block mode with budget <= 1024 this is two launches (Jet-QSparse
+ * abstract: a dense scan of the 4-bit keys, then a per-KV-head block selection
+ * and sparse aggregation of the chosen blocks): the scan, then the attention
+ * launch with the selection in its prologue, as bsa_select_attend_combine.
+ * Otherwise (token mode, larger budgets) it runs the scan, the selection and
+ * the attention in turn; workspace is bsa_select_topk's (unused in block
+ * mode). Calls sharing counters or a workspace must not run concurrently. */
 int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
                     const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                     const float* key_center, const void* kproj, const float* proj,
@@ -348,6 +342,30 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
                     float* scores, void* workspace, size_t workspace_bytes, int32_t* idx,
                     int32_t* count, float* part_o, float* part_lse, uint32_t* counters,
                     float* out, float* out_lse, void* stream);
+
+/* bsa_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Inputs and out / out_lse as in bsa_decode_step; the intermediates that call
+ * takes from the caller (scores, idx, count, part_o, part_lse, the arrival
+ * counters and the token selection's workspace) live instead in a scratch
+ * array of 64 MiB that the library holds on each GPU it runs on until the
+ * process ends. No call allocates or frees memory.
+ *
+ * The scratch of the current HIP device is used (its address is looked up on
+ * the first call on that device; stream must belong to it). A step whose
+ * intermediates exceed 64 MiB returns BSA_ERR_WORKSPACE with the size needed
+ * (token mode at 128K context reaches that near 128 units of 128K tokens).
+ * Each call first clears the counters and the workspace in the scratch, so no
+ * set-up is needed, but all calls on one GPU share the one scratch: calls that
+ * overlap on one GPU (other streams, other host threads) race and must not be
+ * made. The intermediates are not readable by the caller. */
+int bsa_decode_step_noalloc(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                            const void* q, const uint8_t* codes, const uint8_t* scales,
+                            const float* global_scale, const float* key_center,
+                            const void* kproj, const float* proj, const void* k, const void* v,
+                            const int32_t* seq_lens, const uint16_t* tail_k,
+                            const uint16_t* tail_v, int32_t num_splits, float* out,
+                            float* out_lse, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* bsa_last_error(void);

@@ -222,3 +222,24 @@ def test_top_p_is_checked(lib):
     assert "4096" in lib.bsa_last_error().decode()
     fixed = B.select_cfg(B.TOKEN, 8192, 0, 32)  # the fixed budget has no such limit
     assert lib.bsa_workspace_size(ctypes.byref(big), ctypes.byref(fixed)) > 0
+
+
+def test_noalloc_step_rejects_steps_beyond_its_scratch(lib):
+    """The allocation-free step keeps its intermediates in a 64 MiB scratch per
+    GPU: a token step whose scores alone need 128 MiB is refused before any
+    device call."""
+    big = _layout(batch=16, num_kv_heads=16, num_q_heads=64, max_tokens=131072,
+                  kv_stride_b=16 * 131072 * 128, kv_stride_h=131072 * 128)
+    tok = B.select_cfg(B.TOKEN, 2048, 0, 32)
+    rc = lib.bsa_decode_step_noalloc(ctypes.byref(big), ctypes.byref(tok), FAKE, None, None,
+                                     None, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 8,
+                                     FAKE, None, None)
+    assert rc == -4
+    msg = lib.bsa_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg
+    # a bad split count is an argument error
+    blk = B.select_cfg(B.BLOCK, 8)
+    rc = lib.bsa_decode_step_noalloc(ctypes.byref(_layout()), ctypes.byref(blk), FAKE, FAKE, FAKE,
+                                     FAKE, None, None, None, FAKE, FAKE, FAKE, None, None, 9, FAKE,
+                                     None, None)
+    assert rc == -1 and "num_splits" in lib.bsa_last_error().decode()
