@@ -258,7 +258,12 @@ int bsa_sparse_decode_attn(const bsa_kv_layout* layout, const bsa_select_cfg* cf
                            const uint16_t* tail_k, const uint16_t* tail_v, int32_t num_splits,
                            float* part_o, float* part_lse, void* stream);
 
-/* Log-sum-exp merge of split partials, per row r (a (sequence, query head)):
+/* Log-sum-exp merge of split partials (the pages aggregate each KV head's
+ * chosen rows into one softmax-weighted sum with FP32 accumulation,
+ * Jet-QSparse abstract; JSSA Figure 1: one attention over the selected rows
+ * per query head; split into S parts for parallelism, that sum is recovered
+ * exactly by this identity, the reading this library uses), per row r (a
+ * (sequence, query head)):
  *   lse[r] = log sum_s exp(part_lse[r][s]),
  *   out[r] = sum_s exp(part_lse[r][s] - lse[r]) * part_o[r][s][:];
  * rows whose splits are all empty get out = 0 and lse = -inf.

@@ -100,11 +100,18 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bfloat16, nearest-even, via torch's CPU conversion."""
-    import torch
+    """Round float32 to bfloat16 bits, to nearest with ties to even.
 
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=F32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16)
+    bfloat16 is the upper half of a binary32. Adding 0x7FFF plus the kept
+    half's last bit to the 32-bit pattern carries into the upper half exactly
+    when the dropped half is above 0x8000, or equal to it with an odd last
+    bit; a carry out of the mantissa moves to the next binade or to infinity,
+    as rounding does. NaN is kept a NaN, with the quiet bit set."""
+    u = np.ascontiguousarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x, dtype=F32))
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    quiet = (u >> 16) | 0x0040
+    return np.where(nan, quiet, rounded).astype(np.uint16)
 
 
 def n_pages(seq_len: int) -> int:

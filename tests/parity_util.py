@@ -107,7 +107,9 @@ def check_selection(w, b, h, idx_gpu, count_gpu, scores_gpu, scores_ref):
         ref_idx, ref_cnt = O.select_blocks_unit(scores_ref, L, s.n_tail, s.budget)
         picks = s.budget - s.n_tail
     elif s.top_p > 0:
-        return check_top_p_selection(scores_gpu, L, s.budget, s.top_p, idx_gpu, count_gpu)
+        n = check_top_p_selection(scores_gpu, L, s.budget, s.top_p, idx_gpu, count_gpu)
+        check_top_p_against_oracle(scores_ref, L, s.budget, s.top_p, idx_gpu, count_gpu)
+        return n
     else:
         exact_idx, exact_cnt = O.select_tokens_unit(scores_gpu.astype(np.float64), L, s.budget)
         ref_idx, ref_cnt = O.select_tokens_unit(scores_ref, L, s.budget)
@@ -156,6 +158,36 @@ def check_top_p_selection(scores_gpu, L, budget, top_p, idx_gpu, count_gpu):
     assert m == picks or cum[m - 1] >= top_p * (1 - TOP_P_REL), (m, ref_m, cum[m - 1], top_p)
     assert m == 1 or cum[m - 2] < top_p * (1 + TOP_P_REL), (m, ref_m, cum[m - 2], top_p)
     return abs(m - ref_m)
+
+
+def check_top_p_against_oracle(scores_ref, L, budget, top_p, idx_gpu, count_gpu):
+    """Adaptive-budget selection against the oracle's float64 scores (one unit).
+
+    The kept count m is accepted when the oracle's shares (softmax weights of
+    its own scores, ranked by them) of the top m reach top_p within TOP_P_REL
+    and those of the top m - 1 do not; the kept set may differ from the
+    oracle's top-m set only on tokens whose oracle score lies within
+    BOUNDARY_REL of the oracle's m-th score, as for a fixed budget."""
+    s = np.asarray(scores_ref, dtype=np.float64)
+    n = min(int(L), s.shape[0])
+    picks = max(0, min(int(budget), n))
+    m = int(count_gpu)
+    w = O.token_weights(s[:n])
+    z = w.sum()
+    if not (z > 0 and np.isfinite(z)):
+        assert m == picks, "the fixed budget applies when nothing has weight"
+        return
+    order = np.lexsort((np.arange(n), -s[:n]))
+    cum = np.cumsum(w[order[:picks]]) / z
+    assert 1 <= m <= picks, (m, picks)
+    assert m == picks or cum[m - 1] >= top_p * (1 - TOP_P_REL), (m, cum[m - 1], top_p)
+    assert m == 1 or cum[m - 2] < top_p * (1 + TOP_P_REL), (m, cum[m - 2], top_p)
+    got = set(int(x) for x in idx_gpu[:m])
+    exp = set(int(x) for x in order[:m])
+    tau = s[order[m - 1]]
+    for x in got ^ exp:
+        assert abs(s[x] - tau) <= BOUNDARY_REL * abs(tau), \
+            f"adaptive selection differs beyond the boundary band: token {x}"
 
 
 def oracle_partials(w, b, h, idx, splits):

@@ -2,6 +2,8 @@
 
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -279,17 +281,76 @@ def test_fp8_token_scores_exact_for_representable_keys():
     assert np.abs(s[:250] - exact[:250]).max() < 1e-12 and np.all(s[250:] == -np.inf)
 
 
+BF16_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "bf16_rne_points.txt")
+
+
+def _bf16_golden():
+    pts = []
+    for line in open(BF16_GOLDEN):
+        line = line.split("#")[0].split()
+        if len(line) >= 2:
+            pts.append((int(line[0], 16), int(line[1], 16)))
+    return pts
+
+
+def test_bf16_rounding_matches_hand_derived_points():
+    pts = _bf16_golden()
+    f = np.array([p[0] for p in pts], dtype=np.uint32).view(np.float32)
+    got = O.f32_to_bf16_bits(f)
+    for (fb, want), g in zip(pts, got):
+        if want & 0x7F80 == 0x7F80 and want & 0x7F:  # NaN: any quiet NaN of that sign
+            assert g & 0x7FC0 == 0x7FC0 and (g >> 15) == (want >> 15), hex(fb)
+        else:
+            assert int(g) == want, (hex(fb), hex(int(g)), hex(want))
+
+
+def test_bf16_rounding_is_the_nearest_value_ties_to_even():
+    """Brute force by value on random and crafted patterns: the result is the
+    nearer of the two bfloat16 values around x (exact in float64), the even one
+    on a tie, and infinity past the largest finite one's midpoint."""
+    rng = np.random.default_rng(12)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    edges = np.array([0x7F7F8000, 0x7F7FFFFF, 0x7F7F7FFF, 0xFF7F8000, 0x00008000, 0x80018000],
+                     dtype=np.uint32)
+    bits = np.concatenate([bits, (bits & 0xFFFF0000) | 0x8000, bits & 0xFFFF0000, edges])
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    got = O.f32_to_bf16_bits(x)
+    lo = (x.view(np.uint32) >> 16).astype(np.uint32)  # truncation toward zero
+    hi = lo + 1
+
+    def val(b):
+        # the pattern one step past the largest finite value stands for 2^128,
+        # as if the exponent range went on: rounding there gives infinity
+        v = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        past = (b & 0x7FFF) == 0x7F80
+        return np.where(past, np.where(b & 0x8000, -2.0**128, 2.0**128), v)
+
+    xv = x.astype(np.float64)
+    dlo, dhi = np.abs(xv - val(lo)), np.abs(val(hi) - xv)
+    with np.errstate(invalid="ignore"):
+        pick_hi = (dhi < dlo) | ((dhi == dlo) & (lo % 2 == 1))
+    want = np.where(pick_hi, hi, lo).astype(np.uint16)
+    assert np.array_equal(got, want)
+
+
 def test_tail_store_from_cache_worked_example():
     # 130 tokens, two tail pages: slot 0 is page 0 (rows 0..127), slot 1 page 1
-    # (rows 128, 129, then zeros); one tail page at 128 tokens is page 0 whole
-    rows = (np.arange(300 * 128).reshape(300, 128) % 97 - 48).astype(np.float16)
+    # (rows 128, 129, then zeros); one tail page at 128 tokens is page 0 whole.
+    # Rows hold float16 values whose bfloat16 roundings are hand-derived points:
+    # 1 + 4/1024 (a tie, to 1.0), 1 + 12/1024 (a tie, up), 1 + 9/1024 (down),
+    # 65504 (up to 65536), and small integers (exact).
+    vals = np.array([1 + 4 / 1024, 1 + 12 / 1024, 1 + 9 / 1024, 65504.0, -3.0, 7.0], np.float16)
+    want = {1 + 4 / 1024: 0x3F80, 1 + 12 / 1024: 0x3F82, 1 + 9 / 1024: 0x3F81, 65504.0: 0x4780,
+            -3.0: 0xC040, 7.0: 0x40E0}
+    rows = vals[np.arange(300 * 128).reshape(300, 128) % len(vals)]
+    bf = np.vectorize(lambda v: want[float(v)])(rows).astype(np.uint16)
     t = O.tail_store_from_cache(rows, 130, 2)
-    bf = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(t[0], bf(rows[:128]))
-    assert np.array_equal(t[1, :2], bf(rows[128:130])) and not t[1, 2:].any()
+    assert np.array_equal(t[0], bf[:128])
+    assert np.array_equal(t[1, :2], bf[128:130]) and not t[1, 2:].any()
     t1 = O.tail_store_from_cache(rows, 128, 1)
-    assert np.array_equal(t1[0], bf(rows[:128]))
+    assert np.array_equal(t1[0], bf[:128])
     # fewer pages than slots: the leading slots stay zero
     t3 = O.tail_store_from_cache(rows, 5, 2)
-    assert not t3[0].any() and np.array_equal(t3[1, :5], bf(rows[:5])) and not t3[1, 5:].any()
+    assert not t3[0].any() and np.array_equal(t3[1, :5], bf[:5]) and not t3[1, 5:].any()
 
