@@ -178,6 +178,44 @@ def dequant_blocks(code_rec: np.ndarray, scale_rec: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# A0v (option): NVFP4 value store (Jet-QSparse abstract: the persistent cache is
+# NVFP4 -- its KV pools hold 2.58-2.76x BF16's tokens, more than a 4-bit copy of
+# the keys alone can give -- while the chosen values are aggregated in FP16 with
+# FP32 accumulation)
+#
+# Reading: a value row is quantized as a key row is (A0), without centering,
+# with one FP32 scale s_v per KV head (s_v = fl32(amax |v|) / 2688 over the
+# head's packed rows, as for keys). Row t of a unit stores 64 code bytes
+# (channel 2i in the low nibble of byte i) and 8 scale bytes (byte g: the E4M3
+# scale of channels 16g .. 16g + 15). The aggregation uses the value
+# s_v * e2m1 * e4m3, of which e2m1 * e4m3 is exact in FP16 (at most 6
+# significant bits, within [2^-10, 2688]).
+# --------------------------------------------------------------------------
+
+def value_scale(v_rows: np.ndarray) -> np.float32:
+    """s_v of one KV head's packed value rows (any leading shape, last axis 128)."""
+    amax = F32(np.abs(np.asarray(v_rows, dtype=F32)).max()) if np.size(v_rows) else F32(0)
+    return F32(amax / F32(6.0 * 448.0)) if amax > 0 else F32(1.0)
+
+
+def pack_values(v_rows: np.ndarray, s_v: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Value rows [T, 128] -> (code bytes [T, 64], scale bytes [T, 8]) uint8."""
+    codes, sb = pack_nvfp4(v_rows, np.zeros(HEAD_DIM, dtype=F32), s_v)
+    c = codes.astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8), sb.astype(np.uint8)
+
+
+def dequant_values(code_bytes: np.ndarray, scale_bytes: np.ndarray, s_v: float) -> np.ndarray:
+    """(code bytes [T, 64], scale bytes [T, 8], s_v) -> value rows [T, 128] float64."""
+    cb = np.asarray(code_bytes, dtype=np.uint8)
+    codes = np.empty(cb.shape[:-1] + (HEAD_DIM,), dtype=np.uint8)
+    codes[..., 0::2] = cb & 0xF
+    codes[..., 1::2] = cb >> 4
+    scale = np.repeat(nvfp4.e4m3_decode(np.asarray(scale_bytes, dtype=np.uint8)), GROUP, axis=-1)
+    return float(np.float64(s_v)) * (nvfp4.e2m1_decode(codes) * scale)
+
+
+# --------------------------------------------------------------------------
 # A1: dense block scan (Jet-QSparse abstract: every decode step scores all cached
 # keys from the 4-bit copy, and the scores pick blocks of 128 tokens)
 #
@@ -359,12 +397,17 @@ def select_tokens_top_p(scores: np.ndarray, seq_len: int, budget: int, top_p: fl
 # --------------------------------------------------------------------------
 
 def gather_rows_block(k_unit, v_unit, blocks: Sequence[int], seq_len: int, n_tail: int,
-                      tail_k_unit=None, tail_v_unit=None) -> Tuple[np.ndarray, np.ndarray]:
+                      tail_k_unit=None, tail_v_unit=None, v_store=None
+                      ) -> Tuple[np.ndarray, np.ndarray]:
     """float64 K and V rows [n, 128] of the selected blocks, in block order.
 
     Tail pages (the n_tail newest) come from the BF16 tail store, slot
-    page - (n_pages - n_tail); tokens at or beyond seq_len are left out.
+    page - (n_pages - n_tail); tokens at or beyond seq_len are left out. With
+    v_store = (code bytes [T, 64], scale bytes [T, 8], s_v) the values of the
+    other pages are the NVFP4 store's (A0v).
     """
+    if v_store is not None:
+        v_unit = dequant_values(*v_store)
     npg = n_pages(seq_len)
     ks, vs = [], []
     for blk in blocks:
@@ -409,8 +452,15 @@ def tail_store_from_cache(rows: np.ndarray, seq_len: int, n_tail: int) -> np.nda
     return out
 
 
-def gather_rows_token(k_unit, v_unit, tokens: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+def gather_rows_token(k_unit, v_unit, tokens: Sequence[int], v_store=None
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """float64 K and V rows of the selected tokens (values from the NVFP4 store
+    (A0v) when v_store = (code bytes, scale bytes, s_v) is given)."""
     t = np.asarray(tokens, dtype=np.int64)
+    if v_store is not None:
+        cb, sb, s_v = v_store
+        return (np.asarray(k_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM),
+                dequant_values(cb[t], sb[t], s_v).reshape(-1, HEAD_DIM))
     return (np.asarray(k_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM),
             np.asarray(v_unit[t], dtype=np.float64).reshape(-1, HEAD_DIM))
 
