@@ -308,11 +308,14 @@ def main() -> int:
     ns = len(stages)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(a.steps)]
     stride = event_stride(a.steps, a.layers, a.event_stride)
+    # sampled steps start at the second one: the first follows a synchronize
+    # with an empty queue, so its events would also time the launch latency
+    sample0 = 1 if a.steps > 1 else 0
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(a.steps):
         cs = calls(layers[i % len(layers)])
-        if a.no_stage_events or i % stride:
+        if a.no_stage_events or i < sample0 or (i - sample0) % stride:
             for c in cs:
                 c()
             continue
@@ -327,7 +330,7 @@ def main() -> int:
     units = spec.batch * spec.kv_heads
     value = units * a.steps / elapsed
     stage_us, stage_pct = {}, {}
-    sampled = [] if a.no_stage_events else list(range(0, a.steps, stride))
+    sampled = [] if a.no_stage_events else list(range(sample0, a.steps, stride))
     if sampled:
         for j, name in enumerate(stages):
             ts = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in sampled]
@@ -382,7 +385,7 @@ def main() -> int:
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "stages_us_p10_p50_p90": stage_pct,
         "stage_events": None if not sampled else
-        f"{len(sampled)} of {a.steps} timed steps (every {stride}th)",
+        f"{len(sampled)} of {a.steps} timed steps (every {stride}th from step {sample0})",
         "warmup_run": {"steps": warm_steps, "ms": round(warm_ms, 1)},
         "roofline": roofline,
     }
