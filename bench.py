@@ -126,7 +126,8 @@ def dense_same_gpu(d0, sparse_ms: float, steps: int = 10):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    dense_bytes = s.kv_heads * 512 * int(d0.w.seq_lens.astype("int64").sum())  # every K, V row
+    row = 256 + (72 if s.value_fmt == "nvfp4" else 256)  # a K row and a V row
+    dense_bytes = s.kv_heads * row * int(d0.w.seq_lens.astype("int64").sum())
     del dd
     return {"ms_per_step": round(ms, 4), "steps": steps, "budget": full,
             "bytes_per_step": dense_bytes,
@@ -167,10 +168,14 @@ def cpu_baseline(w, budget_s: float):
                                      s.max_blocks)
         else:
             rec = O.project_keys(w.k[b, h], w.proj[h], s.proj_fmt)
-        packed.append((b, h, rec))
+        vst = None
+        if s.value_fmt == "nvfp4":
+            s_v = np.float32(w.value_scale[h])
+            vst = (*O.pack_values(w.v[b, h], s_v), s_v)
+        packed.append((b, h, rec, vst))
     log(f"[cpu] {len(packed)} units packed in {time.perf_counter() - t_start:.1f} s")
 
-    def step(b, h, rec):
+    def step(b, h, rec, vst):
         L = int(w.seq_lens[b])
         qg = w.q[b, h * G:(h + 1) * G]
         if s.granularity == "block":
@@ -180,22 +185,24 @@ def cpu_baseline(w, budget_s: float):
             sc = O.scan_block_unit(O.scan_query(qg, s.query_fmt), rc, rs, w.global_scale[h],
                                    w.key_center[h], L, s.n_tail, sigma, s.max_blocks)
             idx, _ = O.select_blocks_unit(sc, L, s.n_tail, s.budget)
-            rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
+            rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv,
+                                                   v_store=vst)
         else:
             sc = O.scan_token_unit(qg, rec, w.proj[h], L, sigma, s.proj_fmt)
             if s.top_p > 0:
                 idx, _ = O.select_tokens_top_p(sc, L, s.budget, s.top_p)
             else:
                 idx, _ = O.select_tokens_unit(sc, L, s.budget)
-            rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L])
+            rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L],
+                                                   v_store=vst)
         po, pl = O.attend_splits(qg, idx, 1, rows, sigma)
         O.combine(po, pl)
 
     done, spent = 0, 0.0
     while spent < budget_s / 2 or done == 0:
-        for b, h, rec in packed:
+        for b, h, rec, vst in packed:
             t0 = time.perf_counter()
-            step(b, h, rec)
+            step(b, h, rec, vst)
             spent += time.perf_counter() - t0
             done += 1
     log(f"[cpu] {done} unit steps in {spent:.1f} s")
@@ -379,7 +386,9 @@ def main() -> int:
                       else {}),
                    "scan": ("%s query, e2m1*e4m3 keys -> f16 MFMA, f32 acc" % spec.query_fmt)
                    if d0.block_mode
-                   else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank)},
+                   else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank),
+                   "values": ("nvfp4 store (e2m1 * e4m3 * s_v), f32 acc"
+                              if spec.value_fmt == "nvfp4" else "f16 cache, f32 acc")},
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": nbytes["total"],
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},

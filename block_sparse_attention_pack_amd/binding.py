@@ -20,6 +20,7 @@ DTYPE_F16, DTYPE_BF16 = 0, 1
 BLOCK, TOKEN = 0, 1
 PROJ_BF16, PROJ_FP8 = 0, 1
 QUERY_F16, QUERY_NVFP4 = 0, 1
+VALUE_CACHE, VALUE_NVFP4 = 0, 1
 
 ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "WORKSPACE"}
 
@@ -42,6 +43,7 @@ class KvLayout(ctypes.Structure):
         ("kv_stride_h", ctypes.c_int64),
         ("kv_stride_t", ctypes.c_int64),
         ("kv_dtype", ctypes.c_int32),
+        ("value_dtype", ctypes.c_int32),
     ]
 
 
@@ -82,6 +84,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     LP, CP = ctypes.POINTER(KvLayout), ctypes.POINTER(SelectCfg)
     sig = {
         "bsa_pack_kv_cache": [LP, CP, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P],
+        "bsa_pack_values": [LP, _P, _P, _I32, _I32, _P, _P],
         "bsa_score_scan": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "bsa_select_topk": [LP, CP, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
         "bsa_sparse_decode_attn": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
@@ -106,6 +109,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bsa_workspace_size.restype = ctypes.c_size_t
     lib.bsa_counters_size.argtypes = [LP]
     lib.bsa_counters_size.restype = ctypes.c_size_t
+    lib.bsa_value_store_size.argtypes = [LP]
+    lib.bsa_value_store_size.restype = ctypes.c_size_t
     lib.bsa_last_error.argtypes = []
     lib.bsa_last_error.restype = ctypes.c_char_p
     lib.bsa_version.argtypes = []
@@ -137,8 +142,10 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def layout_for(k, num_q_heads: int, dtype: Optional[int] = None) -> KvLayout:
-    """Layout of a [B, Hkv, T, 128] K (or V) tensor (any strides with channel stride 1)."""
+def layout_for(k, num_q_heads: int, dtype: Optional[int] = None,
+               value_dtype: int = VALUE_CACHE) -> KvLayout:
+    """Layout of a [B, Hkv, T, 128] K (or V) tensor (any strides with channel stride 1);
+    value_dtype VALUE_NVFP4 says that the steps read V from a 4-bit value store."""
     import torch
 
     B, Hkv, T, D = k.shape
@@ -146,7 +153,8 @@ def layout_for(k, num_q_heads: int, dtype: Optional[int] = None) -> KvLayout:
         raise ValueError("head_dim must be contiguous")
     if dtype is None:
         dtype = {torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}[k.dtype]
-    return KvLayout(B, Hkv, num_q_heads, D, 128, T, k.stride(0), k.stride(1), k.stride(2), dtype)
+    return KvLayout(B, Hkv, num_q_heads, D, 128, T, k.stride(0), k.stride(1), k.stride(2), dtype,
+                    value_dtype)
 
 
 def select_cfg(granularity: int, budget: int, n_tail_pages: int = 0, proj_rank: int = 0,
@@ -170,6 +178,16 @@ def pack_kv_cache(layout, cfg, k, key_center, global_scale, proj, block_begin, b
                                  _ptr(key_center), _ptr(global_scale), _ptr(proj), block_begin,
                                  block_end, _ptr(codes), _ptr(scales), _ptr(kproj),
                                  _stream(stream)))
+
+
+def value_store_size(layout) -> int:
+    return int(load().bsa_value_store_size(ctypes.byref(layout)))
+
+
+def pack_values(layout, v, value_scale, block_begin, block_end, store, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_pack_values(ctypes.byref(layout), _ptr(v), _ptr(value_scale), block_begin,
+                               block_end, _ptr(store), _stream(stream)))
 
 
 def score_scan(layout, cfg, q, codes, scales, global_scale, key_center, kproj, proj, seq_lens,

@@ -66,6 +66,8 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
               (long long)L->kv_stride_b, (long long)L->kv_stride_h, (long long)L->kv_stride_t);
   BSA_REQUIRE(L->kv_dtype == BSA_DTYPE_F16 || L->kv_dtype == BSA_DTYPE_BF16, BSA_ERR_UNSUPPORTED,
               "kv_dtype %d", L->kv_dtype);
+  BSA_REQUIRE(L->value_dtype == BSA_VALUE_CACHE || L->value_dtype == BSA_VALUE_NVFP4,
+              BSA_ERR_UNSUPPORTED, "value_dtype %d", L->value_dtype);
   BSA_REQUIRE(c->granularity == BSA_GRANULARITY_BLOCK || c->granularity == BSA_GRANULARITY_TOKEN,
               BSA_ERR_INVALID_ARG, "granularity %d", c->granularity);
   BSA_REQUIRE(std::isfinite(c->softmax_scale) && c->softmax_scale > 0.0f, BSA_ERR_INVALID_ARG,
@@ -114,6 +116,7 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
   g->sh = L->kv_stride_h;
   g->st = L->kv_stride_t;
   g->dtype = L->kv_dtype;
+  g->vq = L->value_dtype == BSA_VALUE_NVFP4;
   return BSA_OK;
 }
 
@@ -378,6 +381,42 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, co
                                             cfg->proj_dtype == BSA_PROJ_FP8, block_begin,
                                             block_end, kproj, s),
                       "pack_proj");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+size_t bsa_value_store_size(const bsa_kv_layout* layout) {
+  if (!layout || layout->batch < 1 || layout->num_kv_heads < 1 || layout->max_tokens < 1)
+    return 0;
+  bsa::UnitGeom g;
+  g.B = layout->batch;
+  g.Hkv = layout->num_kv_heads;
+  g.Tmax = layout->max_tokens;
+  return bsa::value_store_bytes(g);
+}
+
+int bsa_pack_values(const bsa_kv_layout* layout, const void* v, const float* value_scale,
+                    int32_t block_begin, int32_t block_end, void* store, void* stream) {
+  try {
+    BSA_REQUIRE(layout, BSA_ERR_INVALID_ARG, "layout must not be NULL");
+    // the layout checks of every call (the selection rule plays no part here)
+    bsa_select_cfg cfg{};
+    cfg.granularity = BSA_GRANULARITY_BLOCK;
+    cfg.budget = 1;
+    cfg.softmax_scale = 1.0f;
+    bsa::UnitGeom g;
+    BSA_CHECK(check_common(layout, &cfg, &g));
+    BSA_REQUIRE(v && aligned16(v) && value_scale && store && aligned16(store),
+                BSA_ERR_INVALID_ARG,
+                "v and store (16-byte aligned device pointers) and value_scale are required");
+    BSA_REQUIRE(0 <= block_begin && block_begin <= block_end && block_end <= g.NBmax,
+                BSA_ERR_INVALID_ARG, "block range [%d, %d) outside [0, %d]", block_begin,
+                block_end, g.NBmax);
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_pack_values(g, v, value_scale, block_begin, block_end, store,
+                                              static_cast<hipStream_t>(stream)),
+                      "pack_values");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

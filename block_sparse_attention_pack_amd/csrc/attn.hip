@@ -6,24 +6,31 @@ namespace bsa {
 namespace {
 
 // grid (splits, B * Hkv), 256 threads; two work-groups per CU (the pipeline's
-// rings need up to 256 VGPRs).
-template <int G, bool MAIN_BF16, bool BLOCK>
+// rings need up to 256 VGPRs). VM: where the values are read (kValCache,
+// kValStore, kValStoreTail).
+template <int G, bool MAIN_BF16, bool BLOCK, int VM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(
     AttnArgs a) {
   __shared__ AttnLds<G> lds;
-  attn_item<G, MAIN_BF16, BLOCK>(a, blockIdx.x, blockIdx.y, lds);
+  attn_item<G, MAIN_BF16, BLOCK, VM>(a, blockIdx.x, blockIdx.y, lds);
 }
 
-template <int G, bool BLOCK>
-void launch_gb(dim3 grid, hipStream_t s, const AttnArgs& a, bool bf16) {
-  if (bf16) hipLaunchKernelGGL((attn_kernel<G, true, BLOCK>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_kernel<G, false, BLOCK>), grid, dim3(256), 0, s, a);
+template <int G, bool BLOCK, int VM>
+void launch_gbv(dim3 grid, hipStream_t s, const AttnArgs& a, bool bf16) {
+  if (bf16) hipLaunchKernelGGL((attn_kernel<G, true, BLOCK, VM>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_kernel<G, false, BLOCK, VM>), grid, dim3(256), 0, s, a);
 }
 
 template <int G>
-void launch_g(dim3 grid, hipStream_t s, const AttnArgs& a, int block_mode, bool bf16) {
-  if (block_mode) launch_gb<G, true>(grid, s, a, bf16);
-  else launch_gb<G, false>(grid, s, a, bf16);
+void launch_g(dim3 grid, hipStream_t s, const AttnArgs& a, int block_mode, bool bf16, bool vq) {
+  if (block_mode) {
+    if (!vq) launch_gbv<G, true, kValCache>(grid, s, a, bf16);
+    else if (a.n_tail > 0) launch_gbv<G, true, kValStoreTail>(grid, s, a, bf16);
+    else launch_gbv<G, true, kValStore>(grid, s, a, bf16);
+  } else {
+    if (!vq) launch_gbv<G, false, kValCache>(grid, s, a, bf16);
+    else launch_gbv<G, false, kValStore>(grid, s, a, bf16);
+  }
 }
 
 }  // namespace
@@ -44,6 +51,7 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
   a.q = q;
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
+  a.vs = g.vq ? value_store(g, v) : ValueStore{nullptr, nullptr, nullptr};
   a.seq_lens = seq_lens;
   a.idx = idx;
   a.count = count;
@@ -68,11 +76,11 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
   const bool bf16 = g.dtype == BSA_DTYPE_BF16;
   dim3 grid(splits, g.B * g.Hkv);
   switch (g.G) {
-    case 1: launch_g<1>(grid, s, a, block_mode, bf16); break;
-    case 2: launch_g<2>(grid, s, a, block_mode, bf16); break;
-    case 4: launch_g<4>(grid, s, a, block_mode, bf16); break;
-    case 8: launch_g<8>(grid, s, a, block_mode, bf16); break;
-    case 16: launch_g<16>(grid, s, a, block_mode, bf16); break;
+    case 1: launch_g<1>(grid, s, a, block_mode, bf16, g.vq); break;
+    case 2: launch_g<2>(grid, s, a, block_mode, bf16, g.vq); break;
+    case 4: launch_g<4>(grid, s, a, block_mode, bf16, g.vq); break;
+    case 8: launch_g<8>(grid, s, a, block_mode, bf16, g.vq); break;
+    case 16: launch_g<16>(grid, s, a, block_mode, bf16, g.vq); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

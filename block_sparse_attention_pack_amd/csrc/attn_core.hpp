@@ -26,6 +26,12 @@
 //   3. PV as FP32 VALU FMAs, a lane owning DPL consecutive channels of a subset
 //      of the rows, so one wave load covers whole 256-byte value rows. The
 //      accumulators are rescaled only when some head's maximum grew.
+//      From the 4-bit value store a lane loads the DPL / 2 code bytes of its
+//      channels and the one E4M3 scale byte they share; the codes become
+//      floats by the hardware FP4 convert, and the row's scale times the KV
+//      head's FP32 scale multiplies either the probabilities or the values,
+//      whichever are fewer per lane (e2m1 * S is the value the packer rounded
+//      to, S = fl32(e4m3 * s_v)).
 // With block scores given (block mode), every work-group of a unit first makes
 // the unit's selection itself (select_unit_rows, the selection select_topk
 // makes) into LDS, and the split-0 group also writes idx / count: the
@@ -53,6 +59,16 @@ constexpr int kAttnWaves = 4;
 // served first finish far ahead of the rest, and measured slower (C3: 52.3 us
 // with one group ahead, 54.2 with two, 56.8 with three).
 constexpr int kRing = 1;
+// The same with values from the 4-bit store (a group is 5 KiB instead of 8).
+constexpr int kRingV4 = 1;
+
+// Where a kernel reads the values: the 16-bit cache (BF16 tail pages too), the
+// 4-bit store with no tail pages, or the 4-bit store with BF16 tail pages. In
+// the last form every group issues the loads of both forms, the unused ones at
+// one fixed line of the unit's store, so that no load sits behind a branch: a
+// branch around loads makes the compiler copy the loaded registers at the loop
+// end, which waits for every load in flight.
+constexpr int kValCache = 0, kValStore = 1, kValStoreTail = 2;
 constexpr int kWindow = 32;  // groups whose row indices a wave stages at a time
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -80,6 +96,7 @@ struct AttnArgs {
   const _Float16* q;
   const uint16_t* k;
   const uint16_t* v;
+  ValueStore vs;  // the 4-bit value store (VM != kValCache), else unused
   const int32_t* seq_lens;
   const int32_t* idx;
   const int32_t* count;
@@ -102,6 +119,9 @@ struct AttnArgs {
 struct UnitCtx {
   const uint16_t* kunit;  // K and V of this (sequence, KV head)
   const uint16_t* vunit;
+  const uint8_t* vcunit;  // its rows of the value store (VM != kValCache)
+  const uint8_t* vsunit;
+  float s_v;              // the value store's FP32 scale of this KV head
   const int32_t* uidx;
   const int* nulltoks;  // 16 entries of -1 in LDS (a null group's tokens)
   int e0, e1, L, npg, tail0, unit;
@@ -112,10 +132,13 @@ struct UnitCtx {
 struct GroupRef {
   const uint16_t* kb;
   const uint16_t* vb;
+  const uint8_t* vc;  // v4: row rho's value codes at vc + 64 row_index(rho),
+  const uint8_t* vsb; // its scales at vsb + 8 row_index(rho)
   int64_t rs;       // elements between rows (block mode)
   int nvalid;       // block mode: rows 0 .. nvalid-1 are valid
   const int* toks;  // token mode: the group's 16 staged token indices (-1 = masked)
   bool bf16;
+  bool v4;          // the values come from the 4-bit store (else vb, 16-bit)
 };
 
 // stage: the wave's staged window; tl: the group's index in it.
@@ -124,34 +147,41 @@ struct GroupRef {
 // live == false gives a null group: every row masked (token mode: its tokens
 // are the 16 -1 entries at nulltoks), addresses inside the unit (the same few
 // lines every time, so its loads are served from cache).
-template <bool MAIN_BF16, bool BLOCK>
+template <bool MAIN_BF16, bool BLOCK, int VM>
 __device__ __forceinline__ GroupRef describe(const AttnArgs& a, const UnitCtx& u, int q,
                                              const int* stage, int tl, bool live) {
   GroupRef r;
   r.toks = u.nulltoks;
   r.kb = u.kunit;
   r.vb = u.vunit;
+  r.vc = u.vcunit;
+  r.vsb = u.vsunit;
   r.rs = a.st;
   r.nvalid = 0;
   r.bf16 = MAIN_BF16;
+  r.v4 = VM != kValCache;
   if (!live) return r;
   if constexpr (BLOCK) {
-    const int blk = stage[tl];
+    // one block per group: its id (and so the branch below) is wave-uniform
+    const int blk = __builtin_amdgcn_readfirstlane(stage[tl]);
     const int part = q & 7;
     const bool ok = blk >= 0 && blk < u.npg;
     const int b0 = ok ? blk : 0;
     r.nvalid = ok ? max(0, min(16, u.L - b0 * kBlock - 16 * part)) : 0;
-    if (a.n_tail > 0 && ok && blk >= u.tail0) {
+    if (VM != kValStore && a.n_tail > 0 && ok && blk >= u.tail0) {
       const int64_t off =
           ((int64_t(u.unit) * a.n_tail + (blk - u.tail0)) * kBlock + 16 * part) * kHeadDim;
       r.kb = a.tail_k + off;
       r.vb = a.tail_v + off;
       r.rs = kHeadDim;
       r.bf16 = true;
+      r.v4 = false;
     } else {
-      const int64_t off = (int64_t(b0) * kBlock + 16 * part) * a.st;
-      r.kb = u.kunit + off;
-      r.vb = u.vunit + off;
+      const int64_t row0 = int64_t(b0) * kBlock + 16 * part;
+      r.kb = u.kunit + row0 * a.st;
+      r.vb = u.vunit + row0 * a.st;
+      r.vc = u.vcunit + row0 * kValueCodeRow;
+      r.vsb = u.vsunit + row0 * kValueScaleRow;
     }
   } else {
     r.nvalid = 16;
@@ -167,17 +197,23 @@ __device__ __forceinline__ bool row_valid(const GroupRef& r, int rho) {
   else return r.toks[rho] >= 0;
 }
 
-// Element offset of group row rho from kb / vb; masked rows read row 0 of the
-// group (block mode: a row of a selected block, or of the unit for a null
-// group; token mode: row 0 of the unit), which is always inside the cache.
+// Row of group row rho counted from kb / vb / vc / vsb; masked rows read row 0
+// of the group (block mode: a row of a selected block, or of the unit for a
+// null group; token mode: row 0 of the unit), which is always inside the cache.
 template <bool BLOCK>
-__device__ __forceinline__ int64_t row_offset(const GroupRef& r, int rho) {
+__device__ __forceinline__ int row_index(const GroupRef& r, int rho) {
   if constexpr (BLOCK) {
-    return rho < r.nvalid ? int64_t(rho) * r.rs : 0;
+    return rho < r.nvalid ? rho : 0;
   } else {
     const int tok = r.toks[rho];
-    return tok >= 0 ? int64_t(tok) * r.rs : 0;
+    return tok >= 0 ? tok : 0;
   }
+}
+
+// Element offset of group row rho from kb / vb.
+template <bool BLOCK>
+__device__ __forceinline__ int64_t row_offset(const GroupRef& r, int rho) {
+  return int64_t(row_index<BLOCK>(r, rho)) * r.rs;
 }
 
 // Key registers of one group: lane l holds row l % 16, channels 8 (l/16 + 4 c) .. +7
@@ -186,10 +222,10 @@ struct KeySlot {
   uint4v w[4];
 };
 
-template <bool MAIN_BF16, bool BLOCK>
+template <bool MAIN_BF16, bool BLOCK, int VM>
 __device__ __forceinline__ void issue_keys(KeySlot& ks, const AttnArgs& a, const UnitCtx& u,
                                            int q, const int* stage, int tl, int lane, bool live) {
-  const GroupRef r = describe<MAIN_BF16, BLOCK>(a, u, q, stage, tl, live);
+  const GroupRef r = describe<MAIN_BF16, BLOCK, VM>(a, u, q, stage, tl, live);
   const int64_t off = row_offset<BLOCK>(r, lane & 15);
   // plain loads: each 128-byte line is read by two of the wave's loads, and a
   // streaming (non-temporal) hint can evict it in between
@@ -199,30 +235,66 @@ __device__ __forceinline__ void issue_keys(KeySlot& ks, const AttnArgs& a, const
 }
 
 // Value registers of one group: lane l holds channels (l % LPR) * DPL .. of rows
-// l / LPR + NQ k.
-template <int G>
+// l / LPR + NQ k: 16-bit values in w[k][..], or from the 4-bit store the
+// channels' codes in c4[k] and their scale byte in sc[k].
+template <int G, int VM>
 struct ValSlot {
-  uint32_t w[PvShape<G>::RPL][PvShape<G>::VDW];
+  static constexpr int R16 = VM == kValStore ? 1 : PvShape<G>::RPL;
+  static constexpr int R4 = VM == kValCache ? 1 : PvShape<G>::RPL;
+  uint32_t w[R16][PvShape<G>::VDW];
+  uint32_t c4[R4];
+  uint32_t sc[R4];
 };
 
-template <int G, bool MAIN_BF16, bool BLOCK>
-__device__ __forceinline__ void issue_values(ValSlot<G>& vs, const AttnArgs& a, const UnitCtx& u,
-                                             int q, const int* stage, int tl, int lane,
-                                             bool live) {
+template <int G, bool MAIN_BF16, bool BLOCK, int VM>
+__device__ __forceinline__ void issue_values(ValSlot<G, VM>& vs, const AttnArgs& a,
+                                             const UnitCtx& u, int q, const int* stage, int tl,
+                                             int lane, bool live) {
   using PV = PvShape<G>;
-  const GroupRef r = describe<MAIN_BF16, BLOCK>(a, u, q, stage, tl, live);
+  const GroupRef r = describe<MAIN_BF16, BLOCK, VM>(a, u, q, stage, tl, live);
   const int dc = lane % PV::LPR, qsub = lane / PV::LPR;
+  if constexpr (VM != kValCache) {
+    // a tail group (kValStoreTail) reads row 0 of the unit's store instead
+    const uint8_t* cb = r.v4 ? r.vc : u.vcunit;
+    const uint8_t* sb = r.v4 ? r.vsb : u.vsunit;
 #pragma unroll
-  for (int k = 0; k < PV::RPL; ++k) {
-    const int64_t off = row_offset<BLOCK>(r, qsub + PV::NQ * k);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(r.vb + off + dc * PV::DPL);
-    if constexpr (PV::VDW == 4) {
-      const uint4v x = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(vp));
+    for (int k = 0; k < PV::RPL; ++k) {
+      const int64_t row = r.v4 ? row_index<BLOCK>(r, qsub + PV::NQ * k) : 0;
+      const uint8_t* cp = cb + row * kValueCodeRow + dc * (PV::DPL / 2);
+      if constexpr (PV::DPL == 8)
+        vs.c4[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cp));
+      else if constexpr (PV::DPL == 4)
+        vs.c4[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(cp));
+      else
+        vs.c4[k] = __builtin_nontemporal_load(cp);
+      vs.sc[k] = __builtin_nontemporal_load(sb + row * kValueScaleRow + (dc * PV::DPL) / 16);
+    }
+  }
+  if constexpr (VM == kValStoreTail) {
+    // the BF16 tail rows; a 4-bit group reads the first 256 bytes of the
+    // unit's store codes instead (always cached, never used)
+    const uint16_t* vb = r.v4 ? reinterpret_cast<const uint16_t*>(u.vcunit) : r.vb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vs.w[k][e] = x[e];
-    } else {
+    for (int k = 0; k < PV::RPL; ++k) {
+      const int64_t off = r.v4 ? 0 : row_offset<BLOCK>(r, qsub + PV::NQ * k);
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(vb + off + dc * PV::DPL);
 #pragma unroll
-      for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = __builtin_nontemporal_load(vp + e);
+      for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = vp[e];
+    }
+  }
+  if constexpr (VM == kValCache) {
+#pragma unroll
+    for (int k = 0; k < PV::RPL; ++k) {
+      const int64_t off = row_offset<BLOCK>(r, qsub + PV::NQ * k);
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(r.vb + off + dc * PV::DPL);
+      if constexpr (PV::VDW == 4) {
+        const uint4v x = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(vp));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vs.w[k][e] = x[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = __builtin_nontemporal_load(vp + e);
+      }
     }
   }
 }
@@ -250,14 +322,37 @@ struct SoftState {
   float m[4], l[4];
 };
 
+// The E2M1 codes of channels 0 .. N-1 (channel e in bits 4 e .. 4 e + 3) as
+// floats, two per hardware convert (the byte to convert is an immediate).
+template <int N>
+__device__ __forceinline__ void fp4_to_floats(uint32_t x, float (&vv)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "channels per lane");
+  float2v c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
+  vv[0] = c[0];
+  vv[1] = c[1];
+  if constexpr (N >= 4) {
+    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
+    vv[2] = c[0];
+    vv[3] = c[1];
+  }
+  if constexpr (N == 8) {
+    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
+    vv[4] = c[0];
+    vv[5] = c[1];
+    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
+    vv[6] = c[0];
+    vv[7] = c[1];
+  }
+}
+
 // One landed group: QK^T, the online softmax update, PV. Returns nothing; the
 // state and accumulators are updated in place. ptab / atab: this wave's
 // tables for the group's buffer.
-template <int G, bool BLOCK>
-__device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G>& vs,
+template <int G, bool BLOCK, int VM>
+__device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G, VM>& vs,
                                              const GroupRef& r,
                                              const half8 (&qa)[4], const bf16x8* qsplit,
-                                             float scale_log2, SoftState& st,
+                                             float scale_log2, float s_v, SoftState& st,
                                              float (&acc)[G][PvShape<G>::DPL],
                                              float (&ptab)[16][G], float (&atab)[G], int lane) {
   using PV = PvShape<G>;
@@ -337,15 +432,30 @@ __device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G>
     // a masked row has p = 0; its value bits are not data, so they are dropped
     const bool vok = full || row_valid<BLOCK>(r, row);
     float vv[DPL];
+    if (VM != kValCache && r.v4) {
+      // E2M1 code of channel e in bits 4 e .. 4 e + 3; a dropped row's scale is
+      // zero (its byte could be a NaN code)
+      fp4_to_floats<DPL>(vs.c4[k], vv);
+      const float f =
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vok ? vs.sc[k] : 0u, 1.0f, false)[0] * s_v;
+      if constexpr (G <= DPL) {
 #pragma unroll
-    for (int e = 0; e < PV::VDW; ++e) {
-      const uint32_t x = vok ? vs.w[k][e] : 0u;
-      if (r.bf16) {
-        vv[2 * e] = bf16_bits_to_float(x & 0xFFFFu);
-        vv[2 * e + 1] = bf16_bits_to_float(x >> 16);
+        for (int hh = 0; hh < G; ++hh) pr[hh] *= f;
       } else {
-        vv[2 * e] = half_bits_to_float(uint16_t(x & 0xFFFFu));
-        vv[2 * e + 1] = half_bits_to_float(uint16_t(x >> 16));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vv[e] *= f;
+      }
+    } else if constexpr (VM != kValStore) {
+#pragma unroll
+      for (int e = 0; e < PV::VDW; ++e) {
+        const uint32_t x = vok ? vs.w[k][e] : 0u;
+        if (r.bf16) {
+          vv[2 * e] = bf16_bits_to_float(x & 0xFFFFu);
+          vv[2 * e + 1] = bf16_bits_to_float(x >> 16);
+        } else {
+          vv[2 * e] = half_bits_to_float(uint16_t(x & 0xFFFFu));
+          vv[2 * e + 1] = half_bits_to_float(uint16_t(x >> 16));
+        }
       }
     }
 #pragma unroll
@@ -360,11 +470,13 @@ __device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G>
 
 // The attention of (split, unit): its rows' partial (O, lse) per head, and the
 // merge when a.counters is set.
-template <int G, bool MAIN_BF16, bool BLOCK>
+template <int G, bool MAIN_BF16, bool BLOCK, int VM>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit,
                                           AttnLds<G>& lds) {
   using PV = PvShape<G>;
   constexpr int DPL = PV::DPL, LPR = PV::LPR;
+  constexpr int RING = VM != kValCache ? kRingV4 : kRing;
+  constexpr bool VQ = VM != kValCache;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = unit / a.Hkv, h = unit % a.Hkv;
   UnitCtx u;
@@ -374,6 +486,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
   u.tail0 = u.npg - a.n_tail;  // first page held in the tail store
   u.kunit = a.k + b * a.sb + h * a.sh;
   u.vunit = a.v + b * a.sb + h * a.sh;
+  u.vcunit = VQ ? a.vs.codes + int64_t(unit) * a.Tmax * kValueCodeRow : nullptr;
+  u.vsunit = VQ ? a.vs.scales + int64_t(unit) * a.Tmax * kValueScaleRow : nullptr;
+  u.s_v = VQ ? a.vs.s_v[h] : 1.0f;
   u.nulltoks = lds.nulltoks;
 
   // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
@@ -466,31 +581,33 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
     }
     wave_lds_sync();
     auto qof = [&](int t) { return wave + kAttnWaves * t; };
-    KeySlot kr[kRing];
-    ValSlot<G> vr[kRing];
+    KeySlot kr[RING];
+    ValSlot<G, VM> vr[RING];
     // every slot is always issued (groups past the window are null groups), so
     // the ring registers are defined on every path
 #pragma unroll
-    for (int k = 0; k < kRing; ++k) {
+    for (int k = 0; k < RING; ++k) {
       const int t = w0 + k;
-      issue_keys<MAIN_BF16, BLOCK>(kr[k], a, u, qof(t), stage, t - w0, lane, t < wend);
-      issue_values<G, MAIN_BF16, BLOCK>(vr[k], a, u, qof(t), stage, t - w0, lane, t < wend);
+      issue_keys<MAIN_BF16, BLOCK, VM>(kr[k], a, u, qof(t), stage, t - w0, lane, t < wend);
+      issue_values<G, MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(t), stage, t - w0, lane,
+                                            t < wend);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-    for (int t0 = w0; t0 < wend; t0 += kRing) {
+    for (int t0 = w0; t0 < wend; t0 += RING) {
 #pragma unroll
-      for (int k = 0; k < kRing; ++k) {
+      for (int k = 0; k < RING; ++k) {
         const int t = t0 + k;
-        const int tn = t + kRing;  // the group this slot takes next
+        const int tn = t + RING;  // the group this slot takes next
         if (t < wend) {
-          const GroupRef r = describe<MAIN_BF16, BLOCK>(a, u, qof(t), stage, t - w0, true);
-          attend_group<G, BLOCK>(kr[k], vr[k], r, qa, lds.qsplit, a.scale_log2, st, acc,
-                                 lds.ptab[wave][t & 1], lds.atab[wave][t & 1], lane);
+          const GroupRef r = describe<MAIN_BF16, BLOCK, VM>(a, u, qof(t), stage, t - w0, true);
+          attend_group<G, BLOCK, VM>(kr[k], vr[k], r, qa, lds.qsplit, a.scale_log2, u.s_v, st,
+                                     acc, lds.ptab[wave][t & 1], lds.atab[wave][t & 1], lane);
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue_keys<MAIN_BF16, BLOCK>(kr[k], a, u, qof(tn), stage, tn - w0, lane, tn < wend);
-        issue_values<G, MAIN_BF16, BLOCK>(vr[k], a, u, qof(tn), stage, tn - w0, lane, tn < wend);
+        issue_keys<MAIN_BF16, BLOCK, VM>(kr[k], a, u, qof(tn), stage, tn - w0, lane, tn < wend);
+        issue_values<G, MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(tn), stage, tn - w0, lane,
+                                              tn < wend);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -226,11 +226,34 @@ struct UnitGeom {
   int B, Hkv, Hq, G, Tmax, NBmax;
   int64_t sb, sh, st;  // K/V strides in elements
   int dtype;
+  bool vq;  // V is the 4-bit value store (BSA_VALUE_NVFP4)
 };
+
+// The 4-bit value store in one buffer: E2M1 codes [B][Hkv][Tmax][64], then
+// E4M3 scales [B][Hkv][Tmax][8], then the FP32 scale per KV head.
+constexpr int kValueCodeRow = 64;
+constexpr int kValueScaleRow = 8;
+struct ValueStore {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* s_v;
+};
+inline size_t value_store_bytes(const UnitGeom& g) {
+  const size_t rows = size_t(g.B) * size_t(g.Hkv) * size_t(g.Tmax);
+  return rows * (kValueCodeRow + kValueScaleRow) + sizeof(float) * size_t(g.Hkv);
+}
+inline ValueStore value_store(const UnitGeom& g, const void* base) {
+  uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(base));
+  const size_t rows = size_t(g.B) * size_t(g.Hkv) * size_t(g.Tmax);
+  return ValueStore{p, p + rows * kValueCodeRow,
+                    reinterpret_cast<float*>(p + rows * (kValueCodeRow + kValueScaleRow))};
+}
 
 hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* center,
                              const float* gscale, int blk0, int blk1, uint8_t* codes,
                              uint8_t* scales, hipStream_t s);
+hipError_t launch_pack_values(const UnitGeom& g, const void* v, const float* vscale, int blk0,
+                              int blk1, void* store, hipStream_t s);
 hipError_t launch_pack_proj(const UnitGeom& g, const void* k, const float* proj, int rank,
                             bool fp8, int blk0, int blk1, void* kproj, hipStream_t s);
 hipError_t launch_append(const UnitGeom& g, int n_tail, int rank, bool fp8, const void* k_new,

@@ -5,6 +5,9 @@
 // calibrated key centering, packed straight from the 16-bit activations).
 // Token mode: projected keys kproj = P^T k, stored as BF16 or as E4M3FN bytes
 // (JSSA Figure 1 and Figure 10).
+// The 4-bit value store: value rows in NVFP4 like uncentred keys, one FP32
+// scale per KV head (the NVFP4 cache of the Jet-QSparse abstract with its
+// values compressed too).
 //
 // Every rounding step is a single IEEE float32 operation (no contraction into
 // fused multiply-adds), so the bytes are reproducible bit for bit.
@@ -32,6 +35,26 @@ __device__ __forceinline__ void load16(const uint16_t* p, float* out) {
   }
 }
 
+// One 16-channel group in NVFP4 under the FP32 scale s: the E4M3 scale byte is
+// returned, the 16 E2M1 codes are packed into lo (channels 0..7) and hi (8..15),
+// channel u in bits 4 (u % 8) .. +3. y holds the group's (centred) values.
+__device__ __forceinline__ uint32_t nvfp4_group(const float (&y)[16], float s, uint32_t& lo,
+                                                uint32_t& hi) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) amax = fmaxf(amax, __builtin_fabsf(y[u]));
+  const uint32_t sbyte = e4m3_from_float(amax / (6.0f * s));
+  const float S = e4m3_to_float(sbyte) * s;
+  lo = hi = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const uint32_t c = S > 0.0f ? e2m1_from_float(y[u] / S) : 0u;
+    if (u < 8) lo |= c << (4 * u);
+    else hi |= c << (4 * (u - 8));
+  }
+  return sbyte;
+}
+
 // One work-group packs one (unit, block): 1024 (token, 16-channel group) items,
 // four per thread. Consecutive threads take consecutive groups of one token.
 template <int DT>
@@ -43,7 +66,6 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(
   const int unit = blockIdx.y;
   const int b = unit / Hkv, h = unit % Hkv;
   const float s_t = gscale[h];
-  const float six_st = 6.0f * s_t;
   uint8_t* crec = codes + (int64_t(unit) * NBmax + blk) * kCodeRecord;
   uint8_t* srec = scales + (int64_t(unit) * NBmax + blk) * kScaleRecord;
   const uint16_t* kb = k + b * sb + h * sh + int64_t(blk) * kBlock * st;
@@ -53,27 +75,46 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(
     const int tau = item >> 3, g = item & 7;
     float y[16];
     load16<DT>(kb + tau * st + 16 * g, y);
-    float amax = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float c = center ? center[h * kHeadDim + 16 * g + u] : 0.0f;
-      y[u] = y[u] - c;
-      amax = fmaxf(amax, __builtin_fabsf(y[u]));
-    }
-    const uint32_t sbyte = e4m3_from_float(amax / six_st);
-    const float S = e4m3_to_float(sbyte) * s_t;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t c = S > 0.0f ? e2m1_from_float(y[u] / S) : 0u;
-      if (u < 8) lo |= c << (4 * u);
-      else hi |= c << (4 * (u - 8));
-    }
+    for (int u = 0; u < 16; ++u) y[u] = y[u] - (center ? center[h * kHeadDim + 16 * g + u] : 0.0f);
+    uint32_t lo, hi;
+    const uint32_t sbyte = nvfp4_group(y, s_t, lo, hi);
     const int i = tau >> 4, n = tau & 15, j = g >> 1, s = g & 1;
     uint32_t* dst = reinterpret_cast<uint32_t*>(crec + ((i * 4 + j) * 16 + n) * 16 + 8 * s);
     dst[0] = lo;
     dst[1] = hi;
     srec[((j * 16 + n) * 8 + i) * 2 + s] = uint8_t(sbyte);
+  }
+}
+
+// The value store: one work-group packs the 128 rows of one (unit, block),
+// four (row, 16-channel group) items per thread; work-group (0, 0) also copies
+// the per-KV-head scales into the store.
+template <int DT>
+__global__ __launch_bounds__(256) void pack_values_kernel(
+    const uint16_t* __restrict__ v, const float* __restrict__ vscale, int Hkv, int Tmax,
+    int64_t sb, int64_t sh, int64_t st, int blk0, int blk1, ValueStore vs) {
+  const int unit = blockIdx.y;
+  if (blockIdx.x == 0 && unit == 0)
+    for (int h = threadIdx.x; h < Hkv; h += 256) vs.s_v[h] = vscale[h];
+  const int blk = blk0 + blockIdx.x;
+  if (blk >= blk1) return;
+  const int b = unit / Hkv, h = unit % Hkv;
+  const float s_v = vscale[h];
+  const uint16_t* vb = v + b * sb + h * sh + int64_t(blk) * kBlock * st;
+  const int64_t row0 = int64_t(unit) * Tmax + int64_t(blk) * kBlock;
+#pragma unroll 1
+  for (int r = 0; r < 4; ++r) {
+    const int item = threadIdx.x + 256 * r;
+    const int tau = item >> 3, g = item & 7;
+    float y[16];
+    load16<DT>(vb + tau * st + 16 * g, y);
+    uint32_t lo, hi;
+    const uint32_t sbyte = nvfp4_group(y, s_v, lo, hi);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vs.codes + (row0 + tau) * kValueCodeRow + 8 * g);
+    dst[0] = lo;
+    dst[1] = hi;
+    vs.scales[(row0 + tau) * kValueScaleRow + g] = uint8_t(sbyte);
   }
 }
 
@@ -135,6 +176,7 @@ struct AppendArgs {
   bool fp8;
   uint16_t* tail_k;  // n_tail > 0 (else null)
   uint16_t* tail_v;
+  ValueStore vs;     // codes non-null: v is the 4-bit value store
   int Hkv, Tmax, NBmax, rank, n_tail;
 };
 
@@ -154,7 +196,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   // the cache rows
   if (tid < kHeadDim) {
     a.k[b * a.sb + h * a.sh + int64_t(L) * a.st + tid] = kn[tid];
-    a.v[b * a.sb + h * a.sh + int64_t(L) * a.st + tid] = vn[tid];
+    if (!a.vs.codes) a.v[b * a.sb + h * a.sh + int64_t(L) * a.st + tid] = vn[tid];
+  }
+  // the value store: the token's row, as pack_values_kernel packs it
+  if (a.vs.codes && tid >= 64 && tid < 72) {
+    const int g = tid - 64;
+    float y[16];
+    load16<DT>(vn + 16 * g, y);
+    uint32_t lo, hi;
+    const uint32_t sbyte = nvfp4_group(y, a.vs.s_v[h], lo, hi);
+    const int64_t row = int64_t(unit) * a.Tmax + L;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.vs.codes + row * kValueCodeRow + 8 * g);
+    dst[0] = lo;
+    dst[1] = hi;
+    a.vs.scales[row * kValueScaleRow + g] = uint8_t(sbyte);
   }
   // block mode: the token's records, as pack_nvfp4_kernel writes them
   if (a.codes && tid < 8) {
@@ -162,22 +217,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const float s_t = a.gscale[h];
     float y[16];
     load16<DT>(kn + 16 * g, y);
-    float amax = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const float c = a.center ? a.center[h * kHeadDim + 16 * g + u] : 0.0f;
-      y[u] = y[u] - c;
-      amax = fmaxf(amax, __builtin_fabsf(y[u]));
-    }
-    const uint32_t sbyte = e4m3_from_float(amax / (6.0f * s_t));
-    const float S = e4m3_to_float(sbyte) * s_t;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t c = S > 0.0f ? e2m1_from_float(y[u] / S) : 0u;
-      if (u < 8) lo |= c << (4 * u);
-      else hi |= c << (4 * (u - 8));
-    }
+    for (int u = 0; u < 16; ++u)
+      y[u] = y[u] - (a.center ? a.center[h * kHeadDim + 16 * g + u] : 0.0f);
+    uint32_t lo, hi;
+    const uint32_t sbyte = nvfp4_group(y, s_t, lo, hi);
     uint8_t* crec = a.codes + (int64_t(unit) * a.NBmax + blk) * kCodeRecord;
     uint8_t* srec = a.scales + (int64_t(unit) * a.NBmax + blk) * kScaleRecord;
     const int i = tau >> 4, n = tau & 15, j = g >> 1, s = g & 1;
@@ -251,6 +295,7 @@ hipError_t launch_append(const UnitGeom& g, int n_tail, int rank, bool fp8, cons
                          uint8_t* scales, const float* proj, void* kproj, uint16_t* tail_k,
                          uint16_t* tail_v, hipStream_t s) {
   AppendArgs a;
+  a.vs = g.vq ? value_store(g, v) : ValueStore{nullptr, nullptr, nullptr};
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.seq_lens = seq_lens;
@@ -292,6 +337,21 @@ hipError_t launch_pack_block(const UnitGeom& g, const void* k, const float* cent
   else
     hipLaunchKernelGGL(pack_nvfp4_kernel<BSA_DTYPE_BF16>, grid, dim3(256), 0, s, kp, center,
                        gscale, g.Hkv, g.NBmax, g.sb, g.sh, g.st, blk0, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_values(const UnitGeom& g, const void* v, const float* vscale, int blk0,
+                              int blk1, void* store, hipStream_t s) {
+  // an empty range still sets the store's scales
+  dim3 grid(blk1 > blk0 ? blk1 - blk0 : 1, blk1 > blk0 ? g.B * g.Hkv : 1);
+  const uint16_t* vp = static_cast<const uint16_t*>(v);
+  const ValueStore vs = value_store(g, store);
+  if (g.dtype == BSA_DTYPE_F16)
+    hipLaunchKernelGGL(pack_values_kernel<BSA_DTYPE_F16>, grid, dim3(256), 0, s, vp, vscale,
+                       g.Hkv, g.Tmax, g.sb, g.sh, g.st, blk0, blk1, vs);
+  else
+    hipLaunchKernelGGL(pack_values_kernel<BSA_DTYPE_BF16>, grid, dim3(256), 0, s, vp, vscale,
+                       g.Hkv, g.Tmax, g.sb, g.sh, g.st, blk0, blk1, vs);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ class DeviceStep:
     splits: int
     q: "torch.Tensor"
     k: "torch.Tensor"
-    v: "torch.Tensor"
+    v: "torch.Tensor"  # the V cache, or the 4-bit value store (layout.value_dtype)
     seq_lens: "torch.Tensor"
     key_center: "torch.Tensor"
     global_scale: "torch.Tensor"
@@ -82,6 +82,12 @@ class DeviceStep:
     out: "torch.Tensor"
     out_lse: "torch.Tensor"
     counters: "torch.Tensor"  # arrival counters of the in-kernel merge (zero between calls)
+    v_src: Optional["torch.Tensor"] = None  # full-precision V the value store is packed from
+    value_scale: Optional["torch.Tensor"] = None  # the value store's FP32 scale per KV head
+
+    @property
+    def value_store(self) -> bool:
+        return self.layout.value_dtype == bsa.VALUE_NVFP4
 
     @property
     def block_mode(self) -> bool:
@@ -92,6 +98,8 @@ class DeviceStep:
         nb = self.w.spec.max_blocks
         bsa.pack_kv_cache(self.layout, self.cfg, self.k, self.key_center, self.global_scale,
                           self.proj, 0, nb, self.codes, self.scales, self.kproj, stream)
+        if self.value_store:
+            bsa.pack_values(self.layout, self.v_src, self.value_scale, 0, nb, self.v, stream)
 
     # -- the decode step ------------------------------------------------------
     def scan(self, stream=None) -> None:
@@ -212,7 +220,13 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
     if kv_dtype == "bf16":
         k = k.to(torch.bfloat16)
         v = v.to(torch.bfloat16)
-    layout = bsa.layout_for(k, Hq)
+    v4 = s.value_fmt == "nvfp4"
+    layout = bsa.layout_for(k, Hq, value_dtype=bsa.VALUE_NVFP4 if v4 else bsa.VALUE_CACHE)
+    v_src = value_scale = None
+    if v4:
+        v_src = v
+        value_scale = t(w.value_scale)
+        v = torch.zeros((bsa.value_store_size(layout),), dtype=torch.uint8, device=dev)
     gran = bsa.BLOCK if s.granularity == "block" else bsa.TOKEN
     fp8 = gran == bsa.TOKEN and s.proj_fmt == "fp8"
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
@@ -252,4 +266,5 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         out=torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev),
         out_lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
         counters=torch.zeros((bsa.counters_size(layout) // 4,), dtype=torch.int32, device=dev),
+        v_src=v_src, value_scale=value_scale,
     )

@@ -4,7 +4,7 @@ This module only draws inputs. It holds none of the decode-step arithmetic
 (no quantization, scoring, selection or attention); both the CPU oracle and
 the GPU path receive exactly the arrays built here.
 
-Five workloads follow the sparse-decode setting the pages evaluate:
+The workloads follow the sparse-decode settings the pages evaluate:
 
 * ``tiny``        B1  Hkv1 Hq4  T4096   block budget 8     (3 needle blocks, +2.0)
 * ``llama8b``     B1  Hkv8 Hq32 T32768  block budget 64    (1% needle blocks, norm 3)
@@ -22,6 +22,9 @@ Five workloads follow the sparse-decode setting the pages evaluate:
                   the softmax mass sits in about 1000 tokens) and the adaptive
                   budget at top_p 0.9 (RaBitQCache abstract): of at most 2048
                   tokens, about 860 are kept
+* ``jetqsparse_v4`` the jetqsparse inputs with the values held in a 4-bit
+                  NVFP4 store (the Jet-QSparse abstract's NVFP4 cache with values
+                  compressed too): 72 B per attended value row instead of 256
 
 Every workload also exists at reduced size (``scale_tokens`` / ``batch``) so the
 oracle finishes in seconds while still spanning many tiles and a ragged tail.
@@ -30,11 +33,12 @@ Random streams are drawn per (sequence, KV head) from
 ``numpy.random.default_rng([seed, stream, b, h])``, so any unit can be redrawn
 on its own (the full-size sampled checks rely on that).
 
-Calibration inputs (the key-centering vector and the per-KV-head FP32 scale)
+Calibration inputs (the key-centering vector and the per-KV-head FP32 scales)
 are produced here too: the centering vector is the per-channel mean of the
 keys over the packed region (the tiny workload states exactly that), and the
 per-KV-head scale maps the largest centered key magnitude onto the largest
-NVFP4 magnitude (6 x 448 = 2688), so that no block scale saturates.
+NVFP4 magnitude (6 x 448 = 2688), so that no block scale saturates; the value
+store's scale does the same for the largest |v| of the KV head.
 """
 
 from __future__ import annotations
@@ -79,6 +83,7 @@ class Spec:
     proj_fmt: str = "bf16"  # token mode: projected-key cache storage, "bf16" or "fp8"
     query_fmt: str = "f16"  # block mode: the query the scan scores with, "f16" or "nvfp4"
     top_p: float = 0.0  # token mode: 0 keeps the budget; else the adaptive (top-p) budget
+    value_fmt: str = "f16"  # "f16": V from the cache; "nvfp4": V from the 4-bit value store
     lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
@@ -119,10 +124,14 @@ SPECS: Dict[str, Spec] = {
     "token_topp": Spec("token_topp", 4, 8, 8, 32, 131072, "token", 2048, rank=32,
                        needle_count=8, needle_profile="const", needle_strength=96.0,
                        top_p=0.9),
+    # the Jet-QSparse decode shape's inputs (same seed), values in the 4-bit store
+    "jetqsparse_v4": Spec("jetqsparse_v4", 2, 16, 4, 16, 131072, "block", 64,
+                          needle_count=20, needle_profile="zipf", needle_strength=3.0,
+                          key_offset_std=2.0, value_fmt="nvfp4"),
 }
 
 ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4",
-         "token_topp"]
+         "token_topp", "jetqsparse_v4"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
@@ -161,6 +170,7 @@ class Workload:
     tail_v: Optional[np.ndarray]
     proj: Optional[np.ndarray]  # float32 [Hkv, D, r]
     needles: List[List[np.ndarray]]  # [b][h] -> block ids carrying needles
+    value_scale: Optional[np.ndarray] = None  # float32 [Hkv], the 4-bit value store's scale
 
     @property
     def softmax_scale(self) -> float:
@@ -309,8 +319,11 @@ def generate(spec: Spec, threads: int = 8) -> Workload:
         total = max(int(col_cnt.sum()), 1)
         key_center = (col_sum.sum(axis=0) / total).astype(np.float32)
         global_scale = calibrate_scale(spec, k, seq_lens, key_center, threads)
+    value_scale = None
+    if spec.value_fmt == "nvfp4":
+        value_scale = calibrate_value_scale(spec, v, seq_lens, threads)
     return Workload(spec, q, k, v, seq_lens, key_center, global_scale,
-                    tail_k, tail_v, proj, needles)
+                    tail_k, tail_v, proj, needles, value_scale)
 
 
 def calibrate_scale(spec: Spec, k: np.ndarray, seq_lens: np.ndarray,
@@ -334,12 +347,31 @@ def calibrate_scale(spec: Spec, k: np.ndarray, seq_lens: np.ndarray,
     return s
 
 
+def calibrate_value_scale(spec: Spec, v: np.ndarray, seq_lens: np.ndarray,
+                          threads: int = 8) -> np.ndarray:
+    """Per-KV-head FP32 scale of the value store: largest |v| over t < L_b / 2688."""
+    amax = np.zeros((spec.batch, spec.kv_heads), dtype=np.float32)
+
+    def work(bh):
+        b, h = bh
+        L = int(seq_lens[b])
+        if L:
+            amax[b, h] = np.abs(v[b, h, :L].astype(np.float32)).max()
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(work, [(b, h) for b in range(spec.batch) for h in range(spec.kv_heads)]))
+    s = (amax.max(axis=0) / np.float32(NVFP4_MAX)).astype(np.float32)
+    s[s == 0] = np.float32(1.0)
+    return s
+
+
 def algorithmic_bytes(w: Workload, kept_tokens: Optional[int] = None) -> Dict[str, int]:
     """Bytes the method must move per decode step (scan + selected K,V), per stage.
 
     Block mode: 72 B per scanned token (64 B of E2M1 codes + 8 B of E4M3 scales)
     and 2 x 256 B per attended token (FP16 K and V rows; BF16 tail rows also
-    count 512 B). Token mode: 2r B (BF16) or r B (FP8) per scanned token (the
+    count 512 B), or 256 + 72 B with the 4-bit value store (tail rows still
+    512 B). Token mode: 2r B (BF16) or r B (FP8) per scanned token (the
     projected key) and 512 B per selected token. With the adaptive budget the
     number of selected tokens depends on the scores: pass it as kept_tokens
     (the sum of the step's counts over all units).
@@ -356,15 +388,16 @@ def algorithmic_bytes(w: Workload, kept_tokens: Optional[int] = None) -> Dict[st
             forced = min(s.n_tail, n_pages)
             chosen = min(s.budget - s.n_tail, packed) + forced
             # every chosen page is a full 128-token tile except the newest one
-            tokens = 0
+            tail_tokens = 0
             for p in range(n_pages - forced, n_pages):
-                tokens += min(BLOCK, L - p * BLOCK)
-            tokens += (chosen - forced) * BLOCK if forced else min(chosen * BLOCK, L)
-            attn += s.kv_heads * 512 * tokens
+                tail_tokens += min(BLOCK, L - p * BLOCK)
+            main_tokens = (chosen - forced) * BLOCK if forced else min(chosen * BLOCK, L)
+            row = 256 + (72 if s.value_fmt == "nvfp4" else 256)
+            attn += s.kv_heads * (512 * tail_tokens + row * main_tokens)
         else:
             scan += s.kv_heads * (1 if s.proj_fmt == "fp8" else 2) * s.rank * L
-            attn += s.kv_heads * 512 * min(s.budget, L)
+            attn += s.kv_heads * (256 + (72 if s.value_fmt == "nvfp4" else 256)) * min(s.budget, L)
     if kept_tokens is not None:
-        attn = 512 * int(kept_tokens)
+        attn = (256 + (72 if s.value_fmt == "nvfp4" else 256)) * int(kept_tokens)
     q_bytes = s.batch * s.q_heads * HEAD_DIM * 2
     return {"scan": scan, "attn": attn, "q": q_bytes, "total": scan + attn}

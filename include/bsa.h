@@ -79,6 +79,13 @@ enum { BSA_PROJ_BF16 = 0, BSA_PROJ_FP8 = 1 };
  * score. The attention always uses the FP16 query. */
 enum { BSA_QUERY_F16 = 0, BSA_QUERY_NVFP4 = 1 };
 
+/* Where the attention reads the values (Jet-QSparse abstract: an NVFP4
+ * persistent cache, whose capacity gain needs 4-bit values as well as keys).
+ * CACHE: v is the standard cache below, in kv_dtype. NVFP4: v is a 4-bit value
+ * store (layout further below) in every entry point that reads or writes V,
+ * and the attention aggregates its dequantized values. */
+enum { BSA_VALUE_CACHE = 0, BSA_VALUE_NVFP4 = 1 };
+
 /* Standard GQA KV cache: K and V are [batch][num_kv_heads][max_tokens][head_dim]
  * through the strides below (in elements, head_dim contiguous). Query head hq
  * belongs to KV head hq / (num_q_heads / num_kv_heads). */
@@ -93,6 +100,7 @@ typedef struct bsa_kv_layout {
   int64_t kv_stride_h;  /* elements between KV heads */
   int64_t kv_stride_t;  /* elements between tokens, >= head_dim, multiple of 8 */
   int32_t kv_dtype;     /* BSA_DTYPE_F16 or BSA_DTYPE_BF16 (K and V alike) */
+  int32_t value_dtype;  /* BSA_VALUE_CACHE (V in this layout) or BSA_VALUE_NVFP4 */
 } bsa_kv_layout;
 
 /* Selection rule of the step. */
@@ -136,6 +144,38 @@ typedef struct bsa_select_cfg {
  * The dequantized key is s_t[h] * E2M1(code) * E4M3(sb) + c[h].
  * ------------------------------------------------------------------------- */
 
+/* ---------------------------------------------------------------------------
+ * Layout of the 4-bit value store (value_dtype = BSA_VALUE_NVFP4)
+ *
+ * One device buffer of bsa_value_store_size() bytes, 16-byte aligned; with
+ * R = B * Hkv * max_tokens rows, row (b, h, t) = (b * Hkv + h) * max_tokens + t:
+ *   codes  uint8 [R][64] at byte 0: E2M1 code of channel d at byte d/2 of the
+ *          row, low nibble for even d
+ *   scales uint8 [R][8] at byte 64 R: E4M3 scale of channels 16 g .. 16 g + 15
+ *          at byte g of the row
+ *   s_v    float [Hkv] at byte 72 R: the FP32 scale of each KV head
+ * A value row v is packed as a key row is, with no centering and s_v in place
+ * of s_t: sb = E4M3_rne_sat(fl32(max|v over the group| / fl32(6 * s_v))),
+ * S = fl32(E4M3(sb) * s_v), code = S > 0 ? E2M1_rne_sat(fl32(v / S)) : 0. The
+ * attention reads the value E2M1(code) * S (= s_v * E2M1 * E4M3 up to one
+ * float32 rounding of S). The tail store of BLOCK mode stays BF16.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the value store: 72 * B * Hkv * max_tokens + 4 * Hkv (0 for a bad
+ * layout). */
+size_t bsa_value_store_size(const bsa_kv_layout* layout);
+
+/* Pack values into the store for tokens [128*block_begin, 128*block_end) of
+ * every unit, and set the store's s_v from value_scale (device float [Hkv],
+ * finite > 0; the caller's calibration, e.g. the largest |v| of the KV head
+ * over 2688 = 6 * 448, so that no group scale saturates).
+ * v: device, kv_dtype, the K/V layout's strides (the full-precision values;
+ * value_dtype is not read). store: bsa_value_store_size() bytes. Requires
+ * 0 <= block_begin <= block_end <= max_tokens/128; an empty range only sets
+ * s_v. */
+int bsa_pack_values(const bsa_kv_layout* layout, const void* v, const float* value_scale,
+                    int32_t block_begin, int32_t block_end, void* store, void* stream);
+
 /* Build the key copy for blocks [block_begin, block_end) of every unit.
  *
  * BLOCK: k (device, kv_dtype, layout above), key_center (device float
@@ -166,7 +206,9 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  * For each sequence b with length L_b = seq_lens[b] before the append
  * (0 <= L_b < max_tokens; other sequences are left unchanged) and KV head h,
  * with k_new, v_new device [B][Hkv][128] in kv_dtype (16-byte aligned):
- *   k[b][h][L_b] = k_new[b][h], v[b][h][L_b] = v_new[b][h];
+ *   k[b][h][L_b] = k_new[b][h], v[b][h][L_b] = v_new[b][h] (with a 4-bit value
+ *     store: v_new[b][h] packed into its row (b, h, L_b), as bsa_pack_values
+ *     packs it, with the store's s_v);
  *   BLOCK: the token's E2M1 codes and E4M3 scales in codes, scales, exactly as
  *     bsa_pack_kv_cache packs that token (a token's records depend on its own
  *     row only), from key_center (or NULL) and global_scale;
@@ -245,7 +287,9 @@ int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
  *   part_o[b][hq][s][:]  = sum_t softmax_t(sigma q . k_t) v_t over the split's rows
  *   part_lse[b][hq][s]   = log sum_t exp(sigma q . k_t)
  *   (an empty split writes 0 and -inf).
- * q: device fp16 [B][Hq][128]. k, v: device, kv_dtype, the layout above.
+ * q: device fp16 [B][Hq][128]. k, v: device, kv_dtype, the layout above (v:
+ * the 4-bit value store when value_dtype = BSA_VALUE_NVFP4; its rows are then
+ * the dequantized values, the tail store's stay BF16).
  * tail_k, tail_v: device bfloat16 bits [B][Hkv][n_tail_pages][128][128], or
  * NULL when n_tail_pages is 0. idx, count: as written by bsa_select_topk (the
  * selection's entries first, then -1 padding); the splits share the count's

@@ -1,7 +1,7 @@
 """Stage-by-stage comparison of the HIP path with the oracle, one unit at a time.
 
 Tolerances (the oracle is float64):
-  pack           bit-exact bytes
+  pack           bit-exact bytes (key copy, projected keys, 4-bit value store)
   block scores   |gpu - oracle| <= 8e-6 * A + 1e-6, A = sigma * (s_t * sum|q| |dequant k|
                  + sum |q| |c|) maximised over the block: FP32 accumulation of at
                  most 130 exactly formed products (error <= 130 * 2^-24 * A)
@@ -55,6 +55,39 @@ def check_pack_token(w, b, h, kproj_gpu, tokens=None):
     assert np.array_equal(got, ref), \
         f"kproj differs at unit {(b, h)}: {int((got != ref).sum())} entries"
     return ref
+
+
+def store_views(d):
+    """The 4-bit value store of a DeviceStep as (codes [B, Hkv, T, 64], scales
+    [B, Hkv, T, 8], s_v [Hkv]) device views (the buffer layout of bsa_value_store_size)."""
+    s = d.w.spec
+    R = s.batch * s.kv_heads * s.max_tokens
+    codes = d.v[:64 * R].view(s.batch, s.kv_heads, s.max_tokens, 64)
+    scales = d.v[64 * R:72 * R].view(s.batch, s.kv_heads, s.max_tokens, 8)
+    s_v = d.v[72 * R:72 * R + 4 * s.kv_heads].view(torch_float32())
+    return codes, scales, s_v
+
+
+def torch_float32():
+    import torch
+
+    return torch.float32
+
+
+def oracle_value_store(w, b, h):
+    """(code bytes, scale bytes, s_v) of one unit's values, packed by the oracle."""
+    s_v = np.float32(w.value_scale[h])
+    cb, sb = O.pack_values(w.v[b, h], s_v)
+    return cb, sb, s_v
+
+
+def check_pack_values(w, b, h, codes_gpu, scales_gpu, s_v_gpu):
+    cb, sb, s_v = oracle_value_store(w, b, h)
+    assert np.float32(s_v_gpu) == s_v, f"value store scale differs at {(b, h)}"
+    assert np.array_equal(codes_gpu, cb), f"value code bytes differ at unit {(b, h)}: " \
+        f"{int((codes_gpu != cb).sum())} of {cb.size}"
+    assert np.array_equal(scales_gpu, sb), f"value scale bytes differ at unit {(b, h)}"
+    return cb, sb, s_v
 
 
 def block_score_bound(w, b, h, rc, rs):
@@ -190,23 +223,29 @@ def check_top_p_against_oracle(scores_ref, L, budget, top_p, idx_gpu, count_gpu)
             f"adaptive selection differs beyond the boundary band: token {x}"
 
 
-def oracle_partials(w, b, h, idx, splits):
+def oracle_partials(w, b, h, idx, splits, v_store=None):
+    """The oracle's split partials on the given selection; v_store = the unit's
+    (code bytes, scale bytes, s_v) when the values come from the 4-bit store."""
     s = w.spec
     L = int(w.seq_lens[b])
     qg = q_group(w, b, h)
+    if s.value_fmt == "nvfp4" and v_store is None:
+        v_store = oracle_value_store(w, b, h)
     if s.granularity == "block":
         tk = w.tail_k[b, h] if s.n_tail else None
         tv = w.tail_v[b, h] if s.n_tail else None
-        rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv)
+        rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv,
+                                               v_store=v_store)
     else:
         rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h],
-                                               [t for t in sel if t < L])
+                                               [t for t in sel if t < L], v_store=v_store)
     return O.attend_splits(qg, np.asarray(idx), splits, rows, w.softmax_scale)
 
 
-def check_attention(w, b, h, idx_gpu, splits, part_o_gpu, part_lse_gpu, out_gpu, lse_gpu):
+def check_attention(w, b, h, idx_gpu, splits, part_o_gpu, part_lse_gpu, out_gpu, lse_gpu,
+                    v_store=None):
     """part_o_gpu [G, S, D], part_lse_gpu [G, S], out_gpu [G, D], lse_gpu [G]."""
-    po, pl = oracle_partials(w, b, h, idx_gpu, splits)  # [S, G, D], [S, G]
+    po, pl = oracle_partials(w, b, h, idx_gpu, splits, v_store)  # [S, G, D], [S, G]
     o, lse = O.combine(po, pl)
     fin = np.isfinite(pl)
     assert np.array_equal(fin, np.isfinite(part_lse_gpu.T)), f"empty splits differ at {(b, h)}"
@@ -229,7 +268,12 @@ def check_units(w, d, units=None):
     if units is None:
         units = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
     host = lambda t: t.cpu().numpy()
+    store = store_views(d) if s.value_fmt == "nvfp4" else None
     for b, h in units:
+        v_store = None
+        if store is not None:
+            v_store = check_pack_values(w, b, h, host(store[0][b, h]), host(store[1][b, h]),
+                                        host(store[2])[h])
         scores = host(d.scores[b, h])
         if s.granularity == "block":
             rc, rs = check_pack_block(w, b, h, host(d.codes[b, h]), host(d.scales[b, h]))
@@ -240,4 +284,26 @@ def check_units(w, d, units=None):
         check_selection(w, b, h, host(d.idx[b, h]), host(d.count[b, h]), scores, ref)
         rows = slice(h * G, (h + 1) * G)
         check_attention(w, b, h, host(d.idx[b, h]), d.splits, host(d.part_o[b, rows]),
-                        host(d.part_lse[b, rows]), host(d.out[b, rows]), host(d.out_lse[b, rows]))
+                        host(d.part_lse[b, rows]), host(d.out[b, rows]), host(d.out_lse[b, rows]),
+                        v_store)
+
+
+STEP_OUT = ("scores", "idx", "count", "part_o", "part_lse", "out", "out_lse")
+
+
+def check_forms_match(d):
+    """score_select + attend_combine, score_scan + select_attend_combine, and
+    decode_step reproduce the four calls' bits (and leave every counter at
+    zero); d has just run the four calls."""
+    import torch
+
+    host = lambda t: t.cpu().numpy()
+    ref = [host(getattr(d, n)).copy() for n in STEP_OUT]
+    for run in (d.run_fused, d.run_two, d.decode_step):
+        for n in STEP_OUT:
+            getattr(d, n).fill_(7)
+        run()
+        torch.cuda.synchronize()
+        for n, a in zip(STEP_OUT, ref):
+            assert np.array_equal(a, host(getattr(d, n)), equal_nan=True), (run.__name__, n)
+        assert int(d.counters.abs().sum()) == 0

@@ -66,6 +66,7 @@ def _scan(lib, layout, cfg, q=FAKE):
     (dict(max_tokens=1000), -1),
     (dict(kv_stride_t=100), -1),
     (dict(kv_dtype=7), -2),
+    (dict(value_dtype=7), -2),
 ])
 def test_bad_layouts_are_rejected(lib, kw, code):
     cfg = B.select_cfg(B.BLOCK, 8)
@@ -104,6 +105,21 @@ def test_null_and_misaligned_pointers_are_rejected(lib):
     assert lib.bsa_combine(4, 2, 64, FAKE, FAKE, FAKE, None, None) == -2
     assert lib.bsa_combine(4, 0, 128, FAKE, FAKE, FAKE, None, None) == -1
     assert lib.bsa_combine(0, 1, 128, None, None, None, None, None) == 0  # nothing to do
+
+
+def test_value_store_size_and_pack_checks(lib):
+    L = _layout(batch=3, num_kv_heads=2, num_q_heads=8, value_dtype=B.VALUE_NVFP4)
+    assert lib.bsa_value_store_size(ctypes.byref(L)) == 72 * 3 * 2 * 4096 + 4 * 2
+    assert lib.bsa_value_store_size(ctypes.byref(_layout(batch=0))) == 0
+    assert lib.bsa_value_store_size(None) == 0
+    rc = lib.bsa_pack_values(ctypes.byref(L), FAKE, FAKE, 0, 33, FAKE, None)
+    assert rc == -1 and "block range" in lib.bsa_last_error().decode()
+    assert lib.bsa_pack_values(ctypes.byref(L), FAKE, FAKE, 0, 32, None, None) == -1
+    assert lib.bsa_pack_values(ctypes.byref(L), FAKE, None, 0, 32, FAKE, None) == -1
+    assert lib.bsa_pack_values(ctypes.byref(L), FAKE + 8, FAKE, 0, 32, FAKE, None) == -1
+    assert lib.bsa_pack_values(None, FAKE, FAKE, 0, 32, FAKE, None) == -1
+    assert lib.bsa_pack_values(ctypes.byref(_layout(head_dim=64)), FAKE, FAKE, 0, 1, FAKE,
+                               None) == -2
 
 
 def test_workspace_size(lib):

@@ -97,22 +97,8 @@ def test_query_group_sizes(G):
     _two_calls_match(d)
 
 
-STEP_OUT = ("scores", "idx", "count", "part_o", "part_lse", "out", "out_lse")
-
-
 def _two_calls_match(d):
-    """score_select + attend_combine, score_scan + select_attend_combine, and
-    decode_step reproduce the four calls' bits (and leave every counter at
-    zero)."""
-    ref = [host(getattr(d, n)).copy() for n in STEP_OUT]
-    for run in (d.run_fused, d.run_two, d.decode_step):
-        for n in STEP_OUT:
-            getattr(d, n).fill_(7)
-        run()
-        torch.cuda.synchronize()
-        for n, a in zip(STEP_OUT, ref):
-            assert np.array_equal(a, host(getattr(d, n)), equal_nan=True), (run.__name__, n)
-        assert int(d.counters.abs().sum()) == 0
+    PU.check_forms_match(d)
 
 
 def test_select_attend_combine_above_the_in_kernel_budget():
@@ -361,6 +347,16 @@ APPEND_CASES = {
     "token_fp8": (dataclasses.replace(W.SPECS["token_fp8"], name="append_fp8", seed=115, batch=3,
                                       kv_heads=2, q_heads=8, max_tokens=2048, budget=256,
                                       lengths=(0, 1000, 2000)), "f16"),
+    # the 4-bit value store: appended values packed into it (tail pages still BF16)
+    "block_tail2_v4": (dataclasses.replace(W.SPECS["ragged"], name="append_tail2_v4", seed=116,
+                                           batch=5, kv_heads=2, q_heads=8, max_tokens=2048,
+                                           budget=8, n_tail=2, needle_count=2,
+                                           lengths=(0, 127, 250, 1900, 2048),
+                                           value_fmt="nvfp4"), "f16"),
+    "token_v4_bf16": (dataclasses.replace(W.SPECS["token"], name="append_token_v4", seed=117,
+                                          batch=3, kv_heads=2, q_heads=8, max_tokens=2048,
+                                          budget=256, lengths=(0, 1000, 2000),
+                                          value_fmt="nvfp4"), "bf16"),
 }
 
 
@@ -380,7 +376,7 @@ def test_append_tokens_match_the_bulk_build(case):
     B, Hkv, T, nt = spec.batch, spec.kv_heads, spec.max_tokens, spec.n_tail
     lens = np.asarray(w.seq_lens, dtype=np.int64).copy()
     k_exp = d.k.cpu().clone()  # the cache dtype
-    v_exp = d.v.cpu().clone()
+    v_exp = (d.v_src if d.value_store else d.v).cpu().clone()
     if nt:  # the tail store the appends keep up: BF16 pages of the cache rows
         kf, vf = k_exp.float().numpy(), v_exp.float().numpy()
         for name, rows in (("tail_k", kf), ("tail_v", vf)):
@@ -404,10 +400,17 @@ def test_append_tokens_match_the_bulk_build(case):
         d.seq_lens.add_(1).clamp_(max=T)
     torch.cuda.synchronize()
     assert np.array_equal(host(d.seq_lens), lens)
-    assert torch.equal(d.k.cpu(), k_exp) and torch.equal(d.v.cpu(), v_exp)
+    assert torch.equal(d.k.cpu(), k_exp)
+    if not d.value_store:
+        assert torch.equal(d.v.cpu(), v_exp)
     kf, vf = k_exp.float().numpy(), v_exp.float().numpy()
+    store = PU.store_views(d) if d.value_store else None
     for b in range(B):
         for h in range(Hkv):
+            if store is not None:
+                # every row of the store: the appended ones and those the bulk pack wrote
+                PU.check_pack_values(dataclasses.replace(w, v=vf), b, h, host(store[0][b, h]),
+                                     host(store[1][b, h]), host(store[2])[h])
             if spec.granularity == "block":
                 # every token's records: the appended ones and those the bulk pack wrote
                 PU.check_pack_block(dataclasses.replace(w, k=kf), b, h, host(d.codes[b, h]),
