@@ -147,12 +147,19 @@ def cpu_baseline(w, budget_s: float):
 
     from oracle import decode as O
 
+    # threads it can use: the BLAS pool (NumPy's matrix products) within the
+    # process's CPU affinity; every other NumPy step runs on one core
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas = 1
+    cores = max(1, min(blas, affinity))
     s = w.spec
     G, sigma = s.group, w.softmax_scale
     order = [(b, h) for b in range(s.batch) for h in range(s.kv_heads)]
@@ -207,6 +214,8 @@ def cpu_baseline(w, budget_s: float):
             done += 1
     log(f"[cpu] {done} unit steps in {spent:.1f} s")
     return {"value": done / spent, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "threads": f"BLAS pool {blas} within an affinity of {affinity} cores; "
+                       "the non-BLAS steps run on one core",
             "sample": f"{len(packed)} of {len(order)} (sequence, KV head) units of the same "
                       f"workload, packed once (pack not timed), then stepped {done} times "
                       f"(scan, select, attention, combine; NumPy float64) in {spent:.1f} s"}

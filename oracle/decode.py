@@ -17,6 +17,10 @@ Sources (the only specification there is):
   fixes the density (2048 of 128K); Figure 10 evaluates BF16 and FP8
   projected-key caches; Table 15 shows per-KV-head selection beats a
   head-shared vote.
+* "Coarse Semantic Blocks for Efficient Training-Free Sparse Attention",
+  Abstract: keys are clustered into large blocks of tokens from noncontiguous
+  positions; a query picks blocks by scoring their centroids and attends the
+  original keys and values inside the picked blocks, under a token budget.
 
 Everything is per unit = one (sequence b, KV head h). Query head hq belongs to
 KV head hq // G. Arithmetic is float64 except the steps whose result is a
@@ -594,3 +598,79 @@ def scan_token_unit(q_group: np.ndarray, kproj: np.ndarray, proj: np.ndarray,
 
 def softmax_scale(head_dim: int = HEAD_DIM) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+# --------------------------------------------------------------------------
+# A10: coarse semantic blocks scored by their centroids (Coarse Semantic
+# Blocks abstract)
+#
+# Readings: the abstract leaves the clustering method open, so the index takes
+# a token -> block assignment as given (a block id per token, -1 for none);
+# block c holds the tokens t < L assigned to it, in ascending order, and its
+# centroid is the mean of their keys (a block with no token has none and is
+# never chosen). A KV head's query heads pick one block set together (the
+# token and block modes' sharing): a block's score is the largest over the
+# head's queries of sigma q . centroid. Blocks are ranked by score (descending,
+# the lower block id first among equal scores, NaN last); the chosen blocks are
+# the longest prefix of that ranking whose sizes add up to at most the token
+# budget (whole blocks only). The attention reads the chosen blocks' tokens,
+# block after block in ranking order, members ascending.
+# --------------------------------------------------------------------------
+
+def cluster_index(k_unit: np.ndarray, assign: np.ndarray, n_clusters: int, seq_len: int
+                  ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(centroids [C, 128] float64, offsets [C + 1], members [offsets[C]]) of
+    one unit: block c's tokens are members[offsets[c]:offsets[c + 1]]."""
+    L = int(seq_len)
+    a = np.asarray(assign[:L], dtype=np.int64)
+    members, offsets = [], [0]
+    cent = np.zeros((n_clusters, HEAD_DIM))
+    for c in range(n_clusters):
+        toks = np.nonzero(a == c)[0]
+        members.append(toks)
+        offsets.append(offsets[-1] + len(toks))
+        if len(toks):
+            cent[c] = np.asarray(k_unit[toks], dtype=np.float64).mean(axis=0)
+    return cent, np.asarray(offsets, dtype=np.int64), (
+        np.concatenate(members) if members else np.zeros(0, dtype=np.int64))
+
+
+def cluster_scores(q_group: np.ndarray, centroids: np.ndarray, sizes: np.ndarray,
+                   sigma: float) -> np.ndarray:
+    """score_c = max over the group's query heads of sigma q . centroid_c;
+    -inf for a block with no token."""
+    q = np.asarray(q_group, dtype=np.float64)
+    s = sigma * (np.asarray(centroids, dtype=np.float64) @ q.T).max(axis=1)
+    return np.where(np.asarray(sizes) > 0, s, -np.inf)
+
+
+def select_clusters(scores: np.ndarray, sizes: np.ndarray, budget: int
+                    ) -> Tuple[np.ndarray, int]:
+    """Chosen block ids in ranking order: the longest prefix of the ranking of
+    the non-empty blocks whose sizes sum to at most budget; and that sum."""
+    s = np.asarray(scores, dtype=np.float64)
+    ids = np.arange(len(s))
+    key = np.where(np.isnan(s), -np.inf, s)
+    nan_last = np.isnan(s).astype(np.int64)
+    order = np.lexsort((ids, -key, nan_last))  # NaN last, then score desc, then id
+    chosen, total = [], 0
+    for c in order:
+        if sizes[c] == 0:
+            continue
+        if total + int(sizes[c]) > budget:
+            break
+        chosen.append(int(c))
+        total += int(sizes[c])
+    return np.asarray(chosen, dtype=np.int64), total
+
+
+def cluster_tokens(chosen: np.ndarray, offsets: np.ndarray, members: np.ndarray,
+                   budget: int) -> Tuple[np.ndarray, int]:
+    """The tokens the attention reads (the chosen blocks' members, block after
+    block), padded with -1 to budget; and their count."""
+    toks = [members[offsets[c]:offsets[c + 1]] for c in chosen]
+    t = np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+    out = np.full(budget, -1, dtype=np.int32)
+    out[:len(t)] = t
+    return out, int(len(t))
+

@@ -62,6 +62,9 @@ def test_noalloc_matches_decode_step_twice_then_smaller(mode):
     _check(small)
 
 
-def test_noalloc_top_p_and_nvfp4_query():
+def test_noalloc_top_p_nvfp4_query_and_value_store():
     _check(W.reduced("token_topp", 16384, batch=2))
     _check(W.reduced("jetqsparse_q4", 8192, batch=2))
+    _check(W.reduced("jetqsparse_v4", 8192, batch=2))
+    _check(dataclasses.replace(W.reduced("ragged", 16384, batch=3, budget=24), name="na_v4_tail",
+                               value_fmt="nvfp4"))
