@@ -116,13 +116,17 @@ def dense_same_gpu(d0, sparse_ms: float, steps: int = 10):
     full = s.max_blocks if d0.block_mode else s.max_tokens
     dd = d0.with_budget(full)
     stream = torch.cuda.current_stream()
+    if d0.cluster_mode:  # every block fits: the choice, then the attention
+        dense_call = lambda: (dd.score_select_clusters(), dd.attend_combine())
+    else:
+        dense_call = dd.select_attend_combine
     for _ in range(2):
-        dd.select_attend_combine()
+        dense_call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(steps):
-        dd.select_attend_combine()
+        dense_call()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -173,6 +177,8 @@ def cpu_baseline(w, budget_s: float):
         if s.granularity == "block":
             rec = O.pack_unit_blocks(w.k[b, h], w.key_center[h], w.global_scale[h], 0,
                                      s.max_blocks)
+        elif s.granularity == "cluster":
+            rec = O.cluster_index(w.k[b, h], w.assign[b, h], s.n_clusters, int(w.seq_lens[b]))
         else:
             rec = O.project_keys(w.k[b, h], w.proj[h], s.proj_fmt)
         vst = None
@@ -193,6 +199,13 @@ def cpu_baseline(w, budget_s: float):
                                    w.key_center[h], L, s.n_tail, sigma, s.max_blocks)
             idx, _ = O.select_blocks_unit(sc, L, s.n_tail, s.budget)
             rows = lambda sel: O.gather_rows_block(w.k[b, h], w.v[b, h], sel, L, s.n_tail, tk, tv,
+                                                   v_store=vst)
+        elif s.granularity == "cluster":
+            cent, off, mem = rec
+            sc = O.cluster_scores(qg, cent, np.diff(off), sigma)
+            ch, _ = O.select_clusters(sc, np.diff(off), s.budget)
+            idx, _ = O.cluster_tokens(ch, off, mem, s.budget)
+            rows = lambda sel: O.gather_rows_token(w.k[b, h], w.v[b, h], [t for t in sel if t < L],
                                                    v_store=vst)
         else:
             sc = O.scan_token_unit(qg, rec, w.proj[h], L, sigma, s.proj_fmt)
@@ -268,7 +281,7 @@ def main() -> int:
     import torch
 
     from block_sparse_attention_pack_amd import binding, workloads as W
-    from block_sparse_attention_pack_amd.step import STEP_FORMS, default_form, step_calls, upload
+    from block_sparse_attention_pack_amd.step import default_form, forms_of, step_calls, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
@@ -287,6 +300,11 @@ def main() -> int:
         if d0.block_mode:
             layers.append(dataclasses.replace(d0, k=d0.k.clone(), v=d0.v.clone(),
                                               codes=d0.codes.clone(), scales=d0.scales.clone()))
+        elif d0.cluster_mode:
+            layers.append(dataclasses.replace(d0, k=d0.k.clone(), v=d0.v.clone(),
+                                              centroids=d0.centroids.clone(),
+                                              offsets=d0.offsets.clone(),
+                                              members=d0.members.clone()))
         else:
             layers.append(dataclasses.replace(d0, k=d0.k.clone(), v=d0.v.clone(),
                                               kproj=d0.kproj.clone()))
@@ -295,7 +313,7 @@ def main() -> int:
     nbytes = W.algorithmic_bytes(w)
     stream = torch.cuda.current_stream()
 
-    stages = STEP_FORMS[a.mode]
+    stages = forms_of(spec.granularity)[a.mode]
     calls = lambda d: step_calls(d, a.mode)
     # untimed warm-up: the --warmup steps, then more in batches of 16 until
     # --warmup-ms of wall time has passed (the driver's short runs otherwise
@@ -313,7 +331,7 @@ def main() -> int:
             break
     warm_ms = (time.perf_counter() - t_warm) * 1e3
     kept = None
-    if spec.top_p > 0:  # the adaptive budget: the attention reads the tokens kept
+    if spec.top_p > 0 or d0.cluster_mode:  # the attention reads the tokens kept
         if a.warmup == 0:
             for c in calls(d0):
                 c()
@@ -358,15 +376,19 @@ def main() -> int:
         f"({warm_ms:.0f} ms); stages (us): {stage_pct}")
     check_after_timing(layers, calls, a.steps)
 
-    # the dominant kernel: the scan (timed where it is a call of its own)
-    scan_stage = "scan"
+    # the dominant kernel: the scan (timed where it is a call of its own); in
+    # cluster mode the attention (the centroids are the smaller read)
+    if d0.cluster_mode:
+        scan_stage, kbytes = "attend_combine", nbytes["attn"]
+        kname = "attn_kernel<%d, false, false, %d>" % (spec.group, int(d0.value_store))
+    else:
+        scan_stage, kbytes = "scan", nbytes["scan"]
+        kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"
+                 % (spec.rank, ", fp8" if spec.proj_fmt == "fp8" else ""))
     kern_us = stage_us.get(scan_stage)
-    kbytes = nbytes["scan"]
     roofline = None
     if kern_us:
         achieved = kbytes / (kern_us * 1e-6) / 1e9
-        kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"
-                 % (spec.rank, ", fp8" if spec.proj_fmt == "fp8" else ""))
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(kname, spec.name),
@@ -395,7 +417,9 @@ def main() -> int:
                       else {}),
                    "scan": ("%s query, e2m1*e4m3 keys -> f16 MFMA, f32 acc" % spec.query_fmt)
                    if d0.block_mode
-                   else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank),
+                   else ("f32 centroids of %d coarse blocks" % spec.n_clusters
+                         if d0.cluster_mode
+                         else "%s rank-%d keys, f32" % (spec.proj_fmt, spec.rank)),
                    "values": ("nvfp4 store (e2m1 * e4m3 * s_v), f32 acc"
                               if spec.value_fmt == "nvfp4" else "f16 cache, f32 acc")},
         "pct_hbm_peak": round(100.0 * step_gbs / PEAK_HBM_GBS, 2),

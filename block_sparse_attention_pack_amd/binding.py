@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsa.so")
 
 DTYPE_F16, DTYPE_BF16 = 0, 1
-BLOCK, TOKEN = 0, 1
+BLOCK, TOKEN, CLUSTER = 0, 1, 2
 PROJ_BF16, PROJ_FP8 = 0, 1
 QUERY_F16, QUERY_NVFP4 = 0, 1
 VALUE_CACHE, VALUE_NVFP4 = 0, 1
@@ -57,6 +57,7 @@ class SelectCfg(ctypes.Structure):
         ("proj_dtype", ctypes.c_int32),
         ("query_dtype", ctypes.c_int32),
         ("top_p", ctypes.c_float),
+        ("num_clusters", ctypes.c_int32),
     ]
 
 
@@ -85,6 +86,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     sig = {
         "bsa_pack_kv_cache": [LP, CP, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P],
         "bsa_pack_values": [LP, _P, _P, _I32, _I32, _P, _P],
+        "bsa_build_cluster_index": [LP, CP, _P, _P, _P, _P, _P, _P, _P],
+        "bsa_score_clusters": [LP, CP, _P, _P, _P, _P, _P],
+        "bsa_select_clusters": [LP, CP, _P, _P, _P, _P, _P, _P],
+        "bsa_score_select_clusters": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P],
         "bsa_score_scan": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "bsa_select_topk": [LP, CP, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
         "bsa_sparse_decode_attn": [LP, CP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
@@ -160,11 +165,11 @@ def layout_for(k, num_q_heads: int, dtype: Optional[int] = None,
 def select_cfg(granularity: int, budget: int, n_tail_pages: int = 0, proj_rank: int = 0,
                softmax_scale: Optional[float] = None, head_dim: int = 128,
                proj_dtype: int = PROJ_BF16, query_dtype: int = QUERY_F16,
-               top_p: float = 0.0) -> SelectCfg:
+               top_p: float = 0.0, num_clusters: int = 0) -> SelectCfg:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     return SelectCfg(granularity, budget, n_tail_pages, proj_rank, softmax_scale, proj_dtype,
-                     query_dtype, top_p)
+                     query_dtype, top_p, num_clusters)
 
 
 def version() -> str:
@@ -288,3 +293,32 @@ def decode_step_noalloc(layout, cfg, q, codes, scales, global_scale, key_center,
         _ptr(global_scale), _ptr(key_center), _ptr(kproj), _ptr(proj), _ptr(k), _ptr(v),
         _ptr(seq_lens), _ptr(tail_k), _ptr(tail_v), num_splits, _ptr(out), _ptr(out_lse),
         _stream(stream)))
+
+
+def build_cluster_index(layout, cfg, k, assign, seq_lens, centroids, offsets, members,
+                        stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_build_cluster_index(ctypes.byref(layout), ctypes.byref(cfg), _ptr(k),
+                                       _ptr(assign), _ptr(seq_lens), _ptr(centroids),
+                                       _ptr(offsets), _ptr(members), _stream(stream)))
+
+
+def score_clusters(layout, cfg, q, centroids, offsets, scores, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_score_clusters(ctypes.byref(layout), ctypes.byref(cfg), _ptr(q),
+                                  _ptr(centroids), _ptr(offsets), _ptr(scores), _stream(stream)))
+
+
+def select_clusters(layout, cfg, scores, offsets, members, idx, count, stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_select_clusters(ctypes.byref(layout), ctypes.byref(cfg), _ptr(scores),
+                                   _ptr(offsets), _ptr(members), _ptr(idx), _ptr(count),
+                                   _stream(stream)))
+
+
+def score_select_clusters(layout, cfg, q, centroids, offsets, members, scores, idx, count,
+                          stream=None) -> None:
+    lib = load()
+    _check(lib.bsa_score_select_clusters(ctypes.byref(layout), ctypes.byref(cfg), _ptr(q),
+                                         _ptr(centroids), _ptr(offsets), _ptr(members),
+                                         _ptr(scores), _ptr(idx), _ptr(count), _stream(stream)))

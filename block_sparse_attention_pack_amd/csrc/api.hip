@@ -68,12 +68,22 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
               "kv_dtype %d", L->kv_dtype);
   BSA_REQUIRE(L->value_dtype == BSA_VALUE_CACHE || L->value_dtype == BSA_VALUE_NVFP4,
               BSA_ERR_UNSUPPORTED, "value_dtype %d", L->value_dtype);
-  BSA_REQUIRE(c->granularity == BSA_GRANULARITY_BLOCK || c->granularity == BSA_GRANULARITY_TOKEN,
+  BSA_REQUIRE(c->granularity == BSA_GRANULARITY_BLOCK || c->granularity == BSA_GRANULARITY_TOKEN ||
+                  c->granularity == BSA_GRANULARITY_CLUSTER,
               BSA_ERR_INVALID_ARG, "granularity %d", c->granularity);
   BSA_REQUIRE(std::isfinite(c->softmax_scale) && c->softmax_scale > 0.0f, BSA_ERR_INVALID_ARG,
               "softmax_scale must be finite and > 0");
   const int NB = L->max_tokens / bsa::kBlock;
-  if (c->granularity == BSA_GRANULARITY_BLOCK) {
+  if (c->granularity == BSA_GRANULARITY_CLUSTER) {
+    BSA_REQUIRE(c->num_clusters >= 1 && c->num_clusters <= bsa::kMaxClusters, BSA_ERR_UNSUPPORTED,
+                "num_clusters %d: supported 1 .. %d", c->num_clusters, bsa::kMaxClusters);
+    BSA_REQUIRE(c->budget >= 1 && c->budget <= L->max_tokens, BSA_ERR_INVALID_ARG,
+                "token budget %d must lie in [1, %d]", c->budget, L->max_tokens);
+    BSA_REQUIRE(c->n_tail_pages == 0 && c->proj_dtype == 0 && c->query_dtype == 0 &&
+                    c->top_p == 0.0f,
+                BSA_ERR_INVALID_ARG,
+                "cluster mode takes no tail pages, projection, query format or top_p");
+  } else if (c->granularity == BSA_GRANULARITY_BLOCK) {
     BSA_REQUIRE(c->n_tail_pages >= 0 && c->n_tail_pages <= 2, BSA_ERR_INVALID_ARG,
                 "n_tail_pages %d must be 0, 1 or 2", c->n_tail_pages);
     BSA_REQUIRE(c->budget >= 1 && c->budget >= c->n_tail_pages && c->budget <= NB,
@@ -91,7 +101,9 @@ int check_common(const bsa_kv_layout* L, const bsa_select_cfg* c, bsa::UnitGeom*
     BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16 || r >= 16, BSA_ERR_UNSUPPORTED,
                 "an FP8 projected cache needs proj_rank >= 16");
   }
-  if (c->granularity == BSA_GRANULARITY_BLOCK) {
+  if (c->granularity == BSA_GRANULARITY_CLUSTER) {
+    // checked above
+  } else if (c->granularity == BSA_GRANULARITY_BLOCK) {
     BSA_REQUIRE(c->proj_dtype == BSA_PROJ_BF16, BSA_ERR_INVALID_ARG,
                 "proj_dtype applies to token mode only (must be 0 in block mode)");
     BSA_REQUIRE(c->query_dtype == BSA_QUERY_F16 || c->query_dtype == BSA_QUERY_NVFP4,
@@ -143,6 +155,14 @@ hipError_t attend_and_merge(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
   if (e == hipSuccess && !merge_in_last_group)
     e = bsa::launch_combine(g.B * g.Hq, num_splits, part_o, part_lse, out, out_lse, s);
   return e;
+}
+
+// The calls that have no cluster-mode form.
+int reject_cluster(const bsa_select_cfg* cfg, const char* what) {
+  BSA_REQUIRE(cfg->granularity != BSA_GRANULARITY_CLUSTER, BSA_ERR_UNSUPPORTED,
+              "%s has no cluster mode: use bsa_score_select_clusters and bsa_attend_combine",
+              what);
+  return BSA_OK;
 }
 
 // Argument checks of each stage, run before anything is enqueued (the combined
@@ -363,6 +383,7 @@ int bsa_pack_kv_cache(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, co
     bsa::UnitGeom g;
     int rc = check_common(layout, cfg, &g);
     if (rc) return rc;
+    BSA_CHECK(reject_cluster(cfg, "bsa_pack_kv_cache"));
     BSA_REQUIRE(k && aligned16(k), BSA_ERR_INVALID_ARG, "k must be a 16-byte aligned device pointer");
     BSA_REQUIRE(0 <= block_begin && block_begin <= block_end && block_end <= g.NBmax,
                 BSA_ERR_INVALID_ARG, "block range [%d, %d) outside [0, %d]", block_begin,
@@ -430,6 +451,7 @@ int bsa_append_token(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_append_token"));
     BSA_REQUIRE(k_new && v_new && aligned16(k_new) && aligned16(v_new) && k && v && seq_lens,
                 BSA_ERR_INVALID_ARG,
                 "k_new, v_new (16-byte aligned), k, v and seq_lens are required");
@@ -464,6 +486,7 @@ int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_score_scan"));
     BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
     (void)hipGetLastError();
     return hip_status(launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
@@ -486,6 +509,7 @@ int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_select_topk"));
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     (void)hipGetLastError();
     return hip_status(launch_select(g, cfg, scores, seq_lens, workspace, idx, count,
@@ -551,6 +575,7 @@ int bsa_score_select(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, con
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_score_select"));
     BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -596,6 +621,7 @@ int bsa_select_attend_combine(const bsa_kv_layout* layout, const bsa_select_cfg*
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_select_attend_combine"));
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
                                 part_o, part_lse));
@@ -629,6 +655,7 @@ int bsa_decode_step(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, cons
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_decode_step"));
     BSA_CHECK(check_scan_args(cfg, q, codes, scales, global_scale, kproj, proj, seq_lens, scores));
     BSA_CHECK(check_select_args(g, cfg, scores, seq_lens, workspace, workspace_bytes, idx, count));
     BSA_CHECK(check_attend_args(cfg, q, k, v, seq_lens, idx, count, tail_k, tail_v, num_splits,
@@ -656,6 +683,7 @@ int bsa_decode_step_noalloc(const bsa_kv_layout* layout, const bsa_select_cfg* c
   try {
     bsa::UnitGeom g;
     BSA_CHECK(check_common(layout, cfg, &g));
+    BSA_CHECK(reject_cluster(cfg, "bsa_decode_step_noalloc"));
     BSA_REQUIRE(num_splits >= 1 && num_splits <= cfg->budget && num_splits <= 1024,
                 BSA_ERR_INVALID_ARG, "num_splits %d must lie in [1, min(budget, 1024)]",
                 num_splits);
@@ -689,6 +717,101 @@ int bsa_decode_step_noalloc(const bsa_kv_layout* layout, const bsa_select_cfg* c
                                k, v, seq_lens, tail_k, tail_v, num_splits, scores, workspace,
                                idx, count, part_o, part_lse, counters, out, out_lse, s);
     return hip_status(e, "decode_step_noalloc");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+namespace {
+int check_cluster_common(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                         bsa::UnitGeom* g) {
+  BSA_CHECK(check_common(layout, cfg, g));
+  BSA_REQUIRE(cfg->granularity == BSA_GRANULARITY_CLUSTER, BSA_ERR_INVALID_ARG,
+              "the cluster calls need granularity BSA_GRANULARITY_CLUSTER");
+  return BSA_OK;
+}
+}  // namespace
+
+int bsa_build_cluster_index(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                            const void* k, const int32_t* assign, const int32_t* seq_lens,
+                            float* centroids, int32_t* offsets, int32_t* members, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_cluster_common(layout, cfg, &g));
+    BSA_REQUIRE(k && aligned16(k) && assign && seq_lens && centroids && aligned16(centroids) &&
+                    offsets && members,
+                BSA_ERR_INVALID_ARG,
+                "k, centroids (16-byte aligned), assign, seq_lens, offsets and members are "
+                "required");
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_cluster_index(g, cfg->num_clusters, k, assign, seq_lens,
+                                                centroids, offsets, members,
+                                                static_cast<hipStream_t>(stream)),
+                      "build_cluster_index");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_score_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                       const float* centroids, const int32_t* offsets, float* scores,
+                       void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_cluster_common(layout, cfg, &g));
+    BSA_REQUIRE(q && aligned16(q) && centroids && aligned16(centroids) && offsets && scores,
+                BSA_ERR_INVALID_ARG,
+                "q, centroids (16-byte aligned), offsets and scores are required");
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_cluster_step(g, cfg->num_clusters, cfg->budget,
+                                               cfg->softmax_scale, true, false,
+                                               static_cast<const _Float16*>(q), centroids, offsets,
+                                               nullptr, nullptr, scores, nullptr, nullptr,
+                                               static_cast<hipStream_t>(stream)),
+                      "score_clusters");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_select_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                        const float* scores, const int32_t* offsets, const int32_t* members,
+                        int32_t* idx, int32_t* count, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_cluster_common(layout, cfg, &g));
+    BSA_REQUIRE(scores && offsets && members && idx && count, BSA_ERR_INVALID_ARG,
+                "scores, offsets, members, idx and count are required");
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_cluster_step(g, cfg->num_clusters, cfg->budget,
+                                               cfg->softmax_scale, false, true, nullptr, nullptr,
+                                               offsets, members, scores, nullptr, idx, count,
+                                               static_cast<hipStream_t>(stream)),
+                      "select_clusters");
+  } catch (...) {
+    return fail(BSA_ERR_HIP, "unexpected exception");
+  }
+}
+
+int bsa_score_select_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                              const void* q, const float* centroids, const int32_t* offsets,
+                              const int32_t* members, float* scores, int32_t* idx,
+                              int32_t* count, void* stream) {
+  try {
+    bsa::UnitGeom g;
+    BSA_CHECK(check_cluster_common(layout, cfg, &g));
+    BSA_REQUIRE(q && aligned16(q) && centroids && aligned16(centroids) && offsets && members &&
+                    scores && idx && count,
+                BSA_ERR_INVALID_ARG,
+                "q, centroids (16-byte aligned), offsets, members, scores, idx and count are "
+                "required");
+    (void)hipGetLastError();
+    return hip_status(bsa::launch_cluster_step(g, cfg->num_clusters, cfg->budget,
+                                               cfg->softmax_scale, true, true,
+                                               static_cast<const _Float16*>(q), centroids, offsets,
+                                               members, nullptr, scores, idx, count,
+                                               static_cast<hipStream_t>(stream)),
+                      "score_select_clusters");
   } catch (...) {
     return fail(BSA_ERR_HIP, "unexpected exception");
   }

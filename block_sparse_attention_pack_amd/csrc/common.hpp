@@ -304,5 +304,18 @@ hipError_t launch_attention(const UnitGeom& g, int granularity, int budget, int 
 hipError_t launch_combine(int rows, int splits, const float* part_o, const float* part_lse,
                           float* out, float* out_lse, hipStream_t s);
 
+// Coarse semantic blocks (BSA_GRANULARITY_CLUSTER): at most this many per unit.
+constexpr int kMaxClusters = 4096;
+hipError_t launch_cluster_index(const UnitGeom& g, int C, const void* k, const int32_t* assign,
+                                const int32_t* seq_lens, float* centroids, int32_t* offsets,
+                                int32_t* members, hipStream_t s);
+// score: score the centroids (into scores_out when set); else read scores_in.
+// select: write the chosen blocks' tokens to idx [units][budget] and count.
+hipError_t launch_cluster_step(const UnitGeom& g, int C, int budget, float sigma, bool score,
+                               bool select, const _Float16* q, const float* centroids,
+                               const int32_t* offsets, const int32_t* members,
+                               const float* scores_in, float* scores_out, int32_t* idx,
+                               int32_t* count, hipStream_t s);
+
 
 }  // namespace bsa

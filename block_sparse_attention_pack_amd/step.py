@@ -23,7 +23,7 @@ def default_splits(units: int, budget: int, granularity: str) -> int:
     up; fewer units are latency-bound and gain from one block per split) or 64
     tokens (token mode)."""
     s = max(1, math.ceil(512 / max(units, 1)))
-    if granularity == "token":
+    if granularity in ("token", "cluster"):
         s = min(s, max(1, budget // 64))  # at least one 16-row group per wave
     elif units >= 8:
         s = min(s, max(1, budget // 2))
@@ -40,16 +40,29 @@ STEP_FORMS = {
 }
 
 
+# The same for coarse semantic blocks (cluster mode).
+CLUSTER_FORMS = {
+    "fused": ["score_select_clusters", "attend_combine"],
+    "split": ["score_clusters", "select_clusters", "attend", "combine"],
+}
+
+
 def default_form(granularity: str) -> str:
     """The form bench.py times by default: score_scan, then
     select_attend_combine (the selection, the attention and its merge), so
-    that the scan is a launch of its own whose rate is timed alone."""
+    that the scan is a launch of its own whose rate is timed alone; in cluster
+    mode the centroid scoring with the choice, then the attention."""
     return "fused"
+
+
+def forms_of(granularity: str):
+    return CLUSTER_FORMS if granularity == "cluster" else STEP_FORMS
 
 
 def step_calls(d: "DeviceStep", form: str):
     """The bound methods of one step in the given form."""
-    return [getattr(d, name) for name in STEP_FORMS[form]]
+    forms = CLUSTER_FORMS if d.cluster_mode else STEP_FORMS
+    return [getattr(d, name) for name in forms[form]]
 
 
 @dataclasses.dataclass
@@ -84,6 +97,14 @@ class DeviceStep:
     counters: "torch.Tensor"  # arrival counters of the in-kernel merge (zero between calls)
     v_src: Optional["torch.Tensor"] = None  # full-precision V the value store is packed from
     value_scale: Optional["torch.Tensor"] = None  # the value store's FP32 scale per KV head
+    assign: Optional["torch.Tensor"] = None  # cluster mode: each token's block, and the index
+    centroids: Optional["torch.Tensor"] = None
+    offsets: Optional["torch.Tensor"] = None
+    members: Optional["torch.Tensor"] = None
+
+    @property
+    def cluster_mode(self) -> bool:
+        return self.cfg.granularity == bsa.CLUSTER
 
     @property
     def value_store(self) -> bool:
@@ -96,6 +117,10 @@ class DeviceStep:
     # -- the cache build (not part of the timed step) ------------------------
     def pack(self, stream=None) -> None:
         nb = self.w.spec.max_blocks
+        if self.cluster_mode:
+            bsa.build_cluster_index(self.layout, self.cfg, self.k, self.assign, self.seq_lens,
+                                    self.centroids, self.offsets, self.members, stream)
+            return
         bsa.pack_kv_cache(self.layout, self.cfg, self.k, self.key_center, self.global_scale,
                           self.proj, 0, nb, self.codes, self.scales, self.kproj, stream)
         if self.value_store:
@@ -106,6 +131,19 @@ class DeviceStep:
         bsa.score_scan(self.layout, self.cfg, self.q, self.codes, self.scales,
                        self.global_scale, self.key_center, self.kproj, self.proj,
                        self.seq_lens, self.scores, stream)
+
+    # -- cluster mode ---------------------------------------------------------
+    def score_clusters(self, stream=None) -> None:
+        bsa.score_clusters(self.layout, self.cfg, self.q, self.centroids, self.offsets,
+                           self.scores, stream)
+
+    def select_clusters(self, stream=None) -> None:
+        bsa.select_clusters(self.layout, self.cfg, self.scores, self.offsets, self.members,
+                            self.idx, self.count, stream)
+
+    def score_select_clusters(self, stream=None) -> None:
+        bsa.score_select_clusters(self.layout, self.cfg, self.q, self.centroids, self.offsets,
+                                  self.members, self.scores, self.idx, self.count, stream)
 
     def select(self, stream=None) -> None:
         bsa.select_topk(self.layout, self.cfg, self.scores, self.seq_lens, self.workspace,
@@ -123,8 +161,12 @@ class DeviceStep:
 
     def run(self, stream=None) -> None:
         """The step as four calls: scan, select, attention, combine."""
-        self.scan(stream)
-        self.select(stream)
+        if self.cluster_mode:
+            self.score_clusters(stream)
+            self.select_clusters(stream)
+        else:
+            self.scan(stream)
+            self.select(stream)
         self.attend(stream)
         self.combine(stream)
 
@@ -159,10 +201,11 @@ class DeviceStep:
 
         L = self.layout
         B, Hkv, Hq = L.batch, L.num_kv_heads, L.num_q_heads
-        gran = "block" if self.block_mode else "token"
+        gran = "block" if self.block_mode else ("cluster" if self.cluster_mode else "token")
         cfg = bsa.select_cfg(self.cfg.granularity, budget, self.cfg.n_tail_pages,
                              self.cfg.proj_rank, self.cfg.softmax_scale,
-                             proj_dtype=self.cfg.proj_dtype, query_dtype=self.cfg.query_dtype)
+                             proj_dtype=self.cfg.proj_dtype, query_dtype=self.cfg.query_dtype,
+                             num_clusters=self.cfg.num_clusters)
         if splits is None:
             splits = default_splits(B * Hkv, budget, gran)
         dev = self.q.device
@@ -227,17 +270,25 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         v_src = v
         value_scale = t(w.value_scale)
         v = torch.zeros((bsa.value_store_size(layout),), dtype=torch.uint8, device=dev)
-    gran = bsa.BLOCK if s.granularity == "block" else bsa.TOKEN
+    gran = {"block": bsa.BLOCK, "token": bsa.TOKEN, "cluster": bsa.CLUSTER}[s.granularity]
     fp8 = gran == bsa.TOKEN and s.proj_fmt == "fp8"
     cfg = bsa.select_cfg(gran, s.budget, s.n_tail, s.rank if gran == bsa.TOKEN else 0,
                          w.softmax_scale, proj_dtype=bsa.PROJ_FP8 if fp8 else bsa.PROJ_BF16,
                          query_dtype=bsa.QUERY_NVFP4 if s.query_fmt == "nvfp4" else bsa.QUERY_F16,
-                         top_p=s.top_p)
+                         top_p=s.top_p, num_clusters=s.n_clusters)
     if splits is None:
         splits = default_splits(B * Hkv, s.budget, s.granularity)
     nb = s.max_blocks
     codes = scales = kproj = proj = None
-    if gran == bsa.BLOCK:
+    assign = centroids = offsets = members = None
+    if gran == bsa.CLUSTER:
+        C = s.n_clusters
+        assign = t(w.assign)
+        centroids = torch.empty((B, Hkv, C, HEAD_DIM), dtype=torch.float32, device=dev)
+        offsets = torch.empty((B, Hkv, C + 1), dtype=torch.int32, device=dev)
+        members = torch.empty((B, Hkv, T), dtype=torch.int32, device=dev)
+        scores = torch.empty((B, Hkv, C), dtype=torch.float32, device=dev)
+    elif gran == bsa.BLOCK:
         codes = torch.empty((B, Hkv, nb, 8192), dtype=torch.uint8, device=dev)
         scales = torch.empty((B, Hkv, nb, 1024), dtype=torch.uint8, device=dev)
         scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
@@ -267,4 +318,5 @@ def upload(w: Workload, device="cuda", splits: Optional[int] = None,
         out_lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
         counters=torch.zeros((bsa.counters_size(layout) // 4,), dtype=torch.int32, device=dev),
         v_src=v_src, value_scale=value_scale,
+        assign=assign, centroids=centroids, offsets=offsets, members=members,
     )

@@ -25,6 +25,12 @@ The workloads follow the sparse-decode settings the pages evaluate:
 * ``jetqsparse_v4`` the jetqsparse inputs with the values held in a 4-bit
                   NVFP4 store (the Jet-QSparse abstract's NVFP4 cache with values
                   compressed too): 72 B per attended value row instead of 256
+* ``cluster``     B8 Hkv8 Hq32 T131072 in 1024 coarse blocks of noncontiguous
+                  tokens (each token's block drawn uniformly, about 128 tokens a
+                  block; keys = the block's center + unit noise), 4 needle blocks
+                  whose centers lean towards the group's mean query, a token
+                  budget of 2048 (Coarse Semantic Blocks abstract: blocks picked
+                  by their centroids under a token budget)
 
 Every workload also exists at reduced size (``scale_tokens`` / ``batch``) so the
 oracle finishes in seconds while still spanning many tiles and a ragged tail.
@@ -56,7 +62,7 @@ BLOCK = 128
 NVFP4_MAX = 2688.0
 
 # stream ids for default_rng([seed, stream, ...])
-_S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_OUTLIER, _S_LENS, _S_PROJ = range(1, 9)
+_S_Q, _S_K, _S_V, _S_NEEDLE, _S_OFFSET, _S_OUTLIER, _S_LENS, _S_PROJ, _S_ASSIGN = range(1, 10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -69,7 +75,7 @@ class Spec:
     kv_heads: int
     q_heads: int
     max_tokens: int
-    granularity: str  # "block" or "token"
+    granularity: str  # "block", "token" or "cluster"
     budget: int  # blocks (block mode) or tokens (token mode), forced pages included
     n_tail: int = 0  # BF16 tail pages per (sequence, KV head), always selected
     needle_count: int = 0  # needle blocks per unit
@@ -84,6 +90,7 @@ class Spec:
     query_fmt: str = "f16"  # block mode: the query the scan scores with, "f16" or "nvfp4"
     top_p: float = 0.0  # token mode: 0 keeps the budget; else the adaptive (top-p) budget
     value_fmt: str = "f16"  # "f16": V from the cache; "nvfp4": V from the 4-bit value store
+    n_clusters: int = 0  # cluster mode: coarse blocks per unit
     lengths: Optional[tuple] = None  # explicit sequence lengths (edge cases), one per sequence
 
     @property
@@ -128,10 +135,13 @@ SPECS: Dict[str, Spec] = {
     "jetqsparse_v4": Spec("jetqsparse_v4", 2, 16, 4, 16, 131072, "block", 64,
                           needle_count=20, needle_profile="zipf", needle_strength=3.0,
                           key_offset_std=2.0, value_fmt="nvfp4"),
+    # coarse semantic blocks picked by their centroids, at the token shape
+    "cluster": Spec("cluster", 5, 8, 8, 32, 131072, "cluster", 2048, n_clusters=1024,
+                    needle_count=4, needle_profile="const", needle_strength=8.0),
 }
 
 ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4",
-         "token_topp", "jetqsparse_v4"]
+         "token_topp", "jetqsparse_v4", "cluster"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
@@ -148,9 +158,11 @@ def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
         kw["batch"] = batch
     if s.needle_count:
         kw["needle_count"] = max(1, int(round(s.needle_count * frac)))
+    if s.n_clusters:
+        kw["n_clusters"] = max(4, int(round(s.n_clusters * frac)))
     if budget is not None:
         kw["budget"] = budget
-    elif s.granularity == "token":
+    elif s.granularity in ("token", "cluster"):
         kw["budget"] = max(1, int(round(s.budget * frac)))
     else:
         kw["budget"] = min(s.budget, max(s.n_tail + 1, max_tokens // BLOCK // 4))
@@ -171,6 +183,7 @@ class Workload:
     proj: Optional[np.ndarray]  # float32 [Hkv, D, r]
     needles: List[List[np.ndarray]]  # [b][h] -> block ids carrying needles
     value_scale: Optional[np.ndarray] = None  # float32 [Hkv], the 4-bit value store's scale
+    assign: Optional[np.ndarray] = None  # int32 [B, Hkv, T]: each token's coarse block (cluster)
 
     @property
     def softmax_scale(self) -> float:
@@ -244,6 +257,27 @@ def _unit_keys(spec: Spec, b: int, h: int, qdir: np.ndarray, offset: Optional[np
     return x
 
 
+def _cluster_keys(spec: Spec, b: int, h: int, qdir: np.ndarray):
+    """(keys float32 [T, D], assignment int32 [T]) of one unit in cluster mode:
+    each token's block uniform over the n_clusters, keys = the block's center
+    (N(0, 1) per channel) + N(0, 1) noise; needle blocks' centers gain
+    needle_strength along qdir."""
+    rng = np.random.default_rng([spec.seed, _S_ASSIGN, b, h])
+    C = spec.n_clusters
+    assign = rng.integers(0, C, size=spec.max_tokens).astype(np.int32)
+    centers = rng.standard_normal((C, HEAD_DIM), dtype=np.float32)
+    if spec.needle_count:
+        nrng = np.random.default_rng([spec.seed, _S_NEEDLE, b, h])
+        picks = nrng.choice(C, size=min(spec.needle_count, C), replace=False)
+        strengths = _needle_strengths(spec, len(picks), nrng)
+        for c, st in zip(picks, strengths):
+            centers[c] += (st * qdir).astype(np.float32)
+    krng = np.random.default_rng([spec.seed, _S_K, b, h])
+    x = krng.standard_normal((spec.max_tokens, HEAD_DIM), dtype=np.float32)
+    x += centers[assign]
+    return x, assign
+
+
 def _unit_values(spec: Spec, b: int, h: int) -> np.ndarray:
     rng = np.random.default_rng([spec.seed, _S_V, b, h])
     return rng.standard_normal((spec.max_tokens, HEAD_DIM), dtype=np.float32)
@@ -279,6 +313,7 @@ def generate(spec: Spec, threads: int = 8) -> Workload:
 
     k = np.empty((B, Hkv, T, D), dtype=np.float16)
     v = np.empty((B, Hkv, T, D), dtype=np.float16)
+    assign = np.empty((B, Hkv, T), dtype=np.int32) if spec.granularity == "cluster" else None
     tail_k = tail_v = None
     if spec.n_tail:
         tail_k = np.zeros((B, Hkv, spec.n_tail, BLOCK, D), dtype=np.uint16)
@@ -290,7 +325,10 @@ def generate(spec: Spec, threads: int = 8) -> Workload:
         b, h = bh
         qm = q[b, h * G:(h + 1) * G].astype(np.float64).mean(axis=0)
         qdir = qm / max(np.linalg.norm(qm), 1e-30)
-        xk = _unit_keys(spec, b, h, qdir, offset, outliers, needles[b][h])
+        if assign is not None:
+            xk, assign[b, h] = _cluster_keys(spec, b, h, qdir)
+        else:
+            xk = _unit_keys(spec, b, h, qdir, offset, outliers, needles[b][h])
         xv = _unit_values(spec, b, h)
         k[b, h] = xk.astype(np.float16)
         v[b, h] = xv.astype(np.float16)
@@ -311,10 +349,10 @@ def generate(spec: Spec, threads: int = 8) -> Workload:
         list(ex.map(work, units))
 
     proj = None
-    if spec.granularity == "token":
+    if spec.granularity != "block":
         key_center = np.zeros((Hkv, D), dtype=np.float32)
         global_scale = np.ones((Hkv,), dtype=np.float32)
-        proj = _proj(spec)
+        proj = _proj(spec) if spec.granularity == "token" else None
     else:
         total = max(int(col_cnt.sum()), 1)
         key_center = (col_sum.sum(axis=0) / total).astype(np.float32)
@@ -323,7 +361,7 @@ def generate(spec: Spec, threads: int = 8) -> Workload:
     if spec.value_fmt == "nvfp4":
         value_scale = calibrate_value_scale(spec, v, seq_lens, threads)
     return Workload(spec, q, k, v, seq_lens, key_center, global_scale,
-                    tail_k, tail_v, proj, needles, value_scale)
+                    tail_k, tail_v, proj, needles, value_scale, assign)
 
 
 def calibrate_scale(spec: Spec, k: np.ndarray, seq_lens: np.ndarray,
@@ -374,7 +412,9 @@ def algorithmic_bytes(w: Workload, kept_tokens: Optional[int] = None) -> Dict[st
     512 B). Token mode: 2r B (BF16) or r B (FP8) per scanned token (the
     projected key) and 512 B per selected token. With the adaptive budget the
     number of selected tokens depends on the scores: pass it as kept_tokens
-    (the sum of the step's counts over all units).
+    (the sum of the step's counts over all units); likewise in cluster mode
+    (512 B of FP32 centroid and 4 B of offset per block scanned, then the chosen
+    blocks' tokens, whose number depends on their sizes).
     """
     s = w.spec
     scan = attn = 0
@@ -394,8 +434,11 @@ def algorithmic_bytes(w: Workload, kept_tokens: Optional[int] = None) -> Dict[st
             main_tokens = (chosen - forced) * BLOCK if forced else min(chosen * BLOCK, L)
             row = 256 + (72 if s.value_fmt == "nvfp4" else 256)
             attn += s.kv_heads * (512 * tail_tokens + row * main_tokens)
-        else:
+        elif s.granularity == "token":
             scan += s.kv_heads * (1 if s.proj_fmt == "fp8" else 2) * s.rank * L
+            attn += s.kv_heads * (256 + (72 if s.value_fmt == "nvfp4" else 256)) * min(s.budget, L)
+        else:  # cluster: FP32 centroids and the offsets; the chosen tokens' K, V rows
+            scan += s.kv_heads * (512 * s.n_clusters + 4 * (s.n_clusters + 1))
             attn += s.kv_heads * (256 + (72 if s.value_fmt == "nvfp4" else 256)) * min(s.budget, L)
     if kept_tokens is not None:
         attn = (256 + (72 if s.value_fmt == "nvfp4" else 256)) * int(kept_tokens)

@@ -64,7 +64,11 @@ enum {
 };
 
 enum { BSA_DTYPE_F16 = 0, BSA_DTYPE_BF16 = 1 };
-enum { BSA_GRANULARITY_BLOCK = 0, BSA_GRANULARITY_TOKEN = 1 };
+/* BLOCK: 128-token blocks of a 4-bit key copy (Jet-QSparse); TOKEN: tokens
+ * of a projected-key copy (JSSA); CLUSTER: coarse semantic blocks of
+ * noncontiguous tokens, picked by their centroids (Coarse Semantic Blocks
+ * abstract; the calls at the end of this header). */
+enum { BSA_GRANULARITY_BLOCK = 0, BSA_GRANULARITY_TOKEN = 1, BSA_GRANULARITY_CLUSTER = 2 };
 
 /* Storage of the projected-key cache (TOKEN mode; JSSA Figure 10 evaluates
  * both): BF16, or FP8 as OCP E4M3FN bytes. */
@@ -106,7 +110,8 @@ typedef struct bsa_kv_layout {
 /* Selection rule of the step. */
 typedef struct bsa_select_cfg {
   int32_t granularity;  /* BSA_GRANULARITY_BLOCK or BSA_GRANULARITY_TOKEN */
-  int32_t budget;       /* per unit: blocks (forced tail pages included) or tokens */
+  int32_t budget;       /* per unit: blocks (forced tail pages included) or tokens (TOKEN,
+                           CLUSTER: the token budget the chosen blocks fit in) */
   int32_t n_tail_pages; /* BLOCK: 0..2 newest pages kept in a BF16 store and always
                            selected (Jet-QSparse abstract); TOKEN: must be 0 */
   int32_t proj_rank;    /* TOKEN: r in {8, 16, 32, 64, 128} (16 .. 128 for FP8); BLOCK: ignored */
@@ -119,6 +124,7 @@ typedef struct bsa_select_cfg {
                            (over all t < L_b) reach top_p are kept; NaN and -inf weigh
                            nothing, +inf scores share the whole mass, and with no weight at
                            all the budget stays. Needs budget <= 4096. BLOCK: must be 0. */
+  int32_t num_clusters; /* CLUSTER: C, coarse blocks per unit, 1..4096; else ignored */
 } bsa_select_cfg;
 
 /* ---------------------------------------------------------------------------
@@ -415,6 +421,61 @@ int bsa_decode_step_noalloc(const bsa_kv_layout* layout, const bsa_select_cfg* c
                             const int32_t* seq_lens, const uint16_t* tail_k,
                             const uint16_t* tail_v, int32_t num_splits, float* out,
                             float* out_lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Coarse semantic blocks (granularity BSA_GRANULARITY_CLUSTER)
+ *
+ * Coarse Semantic Blocks abstract: the keys are clustered into large blocks
+ * of noncontiguous tokens; a query picks blocks by scoring their centroids
+ * and attends the original keys and values of the picked blocks. The
+ * clustering itself is the caller's (the abstract names no method): the index
+ * is built from a token -> block assignment. Index of one unit:
+ *   centroids float [B][Hkv][C][128]: block c's centroid, the mean of its
+ *             tokens' keys (FP32 sum over the tokens in ascending order, then
+ *             one division); zero for a block with no token;
+ *   offsets   int32 [B][Hkv][C + 1]: block c's tokens are
+ *             members[offsets[c] .. offsets[c + 1]);
+ *   members   int32 [B][Hkv][max_tokens]: the tokens, block after block,
+ *             ascending within a block (the first offsets[C] entries).
+ * The step, per unit (reading of the abstract: the KV head's query heads pick
+ * one block set together, as in the other modes):
+ *   score_c = max over the group's query heads hq of sigma * q_hq . centroid_c
+ *             (-inf for a block with no token);
+ *   the blocks ranked by score (descending, the lower block id first among
+ *   equal scores, NaN last); the chosen blocks are the longest prefix of the
+ *   ranking whose sizes add up to at most the token budget (whole blocks);
+ *   idx = their tokens, block after block in ranking order, ascending within a
+ *   block, padded with -1 to budget; count = their number.
+ * The attention then reads those tokens in place, as in token mode:
+ * bsa_sparse_decode_attn and bsa_attend_combine accept CLUSTER with this idx
+ * and count. The other calls reject CLUSTER (BSA_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+
+/* Build the index from assign (device int32 [B][Hkv][max_tokens]: the block
+ * of each token, -1 or any value outside [0, C) for none; tokens t >= L_b are
+ * not indexed) and the keys k (kv_dtype, the layout above). Off the decode
+ * step. centroids, offsets, members: as above (device, 16-byte aligned). */
+int bsa_build_cluster_index(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                            const void* k, const int32_t* assign, const int32_t* seq_lens,
+                            float* centroids, int32_t* offsets, int32_t* members, void* stream);
+
+/* The centroids' scores: scores device float [B][Hkv][C]. q: device fp16
+ * [B][Hq][128]. */
+int bsa_score_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const void* q,
+                       const float* centroids, const int32_t* offsets, float* scores,
+                       void* stream);
+
+/* The choice from given scores: idx device int32 [B][Hkv][budget], count
+ * device int32 [B][Hkv]. */
+int bsa_select_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                        const float* scores, const int32_t* offsets, const int32_t* members,
+                        int32_t* idx, int32_t* count, void* stream);
+
+/* bsa_score_clusters then bsa_select_clusters, in one call. */
+int bsa_score_select_clusters(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
+                              const void* q, const float* centroids, const int32_t* offsets,
+                              const int32_t* members, float* scores, int32_t* idx,
+                              int32_t* count, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* bsa_last_error(void);

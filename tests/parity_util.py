@@ -12,6 +12,13 @@ Tolerances (the oracle is float64):
                  1e-4 relative of the boundary score
   attention      max |O_gpu - O_oracle| <= 2e-3 and |lse_gpu - lse_oracle| <= 2e-3,
                  both sides on the GPU's selection
+  cluster index  offsets and members bit-exact; centroids (FP32 sums of up to a few
+                 hundred FP16 keys) within 1e-5 of the max |key| plus 1e-5 relative
+  cluster scores |gpu - oracle| <= 2e-5 * A + 1e-6, A = sigma * max_h sum |q_h| |centroid|
+                 (the GPU scores its own FP32 centroids)
+  cluster choice bit-exact on the GPU's own scores; against the oracle's scores the
+                 rankings may part only between blocks whose scores lie within 1e-4
+                 relative of each other
 """
 
 from __future__ import annotations
@@ -259,6 +266,51 @@ def check_attention(w, b, h, idx_gpu, splits, part_o_gpu, part_lse_gpu, out_gpu,
     return err
 
 
+def check_cluster_index(w, b, h, cent_gpu, off_gpu, mem_gpu):
+    s = w.spec
+    cent, off, mem = O.cluster_index(w.k[b, h], w.assign[b, h], s.n_clusters, int(w.seq_lens[b]))
+    assert np.array_equal(off_gpu, off), f"cluster offsets differ at {(b, h)}"
+    assert np.array_equal(mem_gpu[:off[-1]], mem), f"cluster members differ at {(b, h)}"
+    kmax = float(np.abs(w.k[b, h].astype(np.float64)).max())
+    err = np.abs(cent_gpu.astype(np.float64) - cent)
+    assert np.all(err <= 1e-5 * kmax + 1e-5 * np.abs(cent)), \
+        f"centroids at {(b, h)}: max err {err.max():.3e}"
+    return cent, off, mem
+
+
+def check_cluster_scores(w, b, h, scores_gpu, cent, off):
+    sizes = np.diff(off)
+    ref = O.cluster_scores(q_group(w, b, h), cent, sizes, w.softmax_scale)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(scores_gpu)), f"-inf pattern differs at {(b, h)}"
+    A = w.softmax_scale * (np.abs(cent) @ np.abs(q_group(w, b, h).astype(np.float64)).T).max(axis=1)
+    err = np.abs(scores_gpu[fin].astype(np.float64) - ref[fin])
+    lim = 2e-5 * A[fin] + 1e-6
+    assert np.all(err <= lim), f"cluster scores at {(b, h)}: worst ratio {(err / lim).max():.2f}"
+    return ref
+
+
+def check_cluster_choice(w, b, h, idx_gpu, count_gpu, scores_gpu, scores_ref, off, mem):
+    s = w.spec
+    sizes = np.diff(off)
+    ch, tot = O.select_clusters(scores_gpu.astype(np.float64), sizes, s.budget)
+    toks, n = O.cluster_tokens(ch, off, mem, s.budget)
+    assert int(count_gpu) == n == tot, (b, h, int(count_gpu), n)
+    assert np.array_equal(idx_gpu, toks), f"cluster choice on the GPU's scores differs at {(b, h)}"
+    ch_ref, _ = O.select_clusters(scores_ref, sizes, s.budget)
+    if not np.array_equal(ch, ch_ref):
+        # the first rank where the two parts: its two blocks tie within 1e-4
+        k = next(i for i in range(min(len(ch), len(ch_ref)) + 1)
+                 if i >= len(ch) or i >= len(ch_ref) or ch[i] != ch_ref[i])
+        pair = [c for c in (ch[k] if k < len(ch) else None, ch_ref[k] if k < len(ch_ref) else None)
+                if c is not None]
+        if len(pair) == 2:
+            a, c = scores_ref[pair[0]], scores_ref[pair[1]]
+            assert abs(a - c) <= BOUNDARY_REL * max(abs(a), abs(c)), \
+                f"cluster ranking parts beyond the tie band at {(b, h)}"
+    return n
+
+
 def check_units(w, d, units=None):
     """Compare every stage of a DeviceStep with the oracle for the given units
     (all by default); w must hold the K and V the GPU holds. Device buffers are
@@ -275,6 +327,17 @@ def check_units(w, d, units=None):
             v_store = check_pack_values(w, b, h, host(store[0][b, h]), host(store[1][b, h]),
                                         host(store[2])[h])
         scores = host(d.scores[b, h])
+        if s.granularity == "cluster":
+            cent, off, mem = check_cluster_index(w, b, h, host(d.centroids[b, h]),
+                                                 host(d.offsets[b, h]), host(d.members[b, h]))
+            ref = check_cluster_scores(w, b, h, scores, cent, off)
+            check_cluster_choice(w, b, h, host(d.idx[b, h]), host(d.count[b, h]), scores, ref,
+                                 off, mem)
+            rows = slice(h * G, (h + 1) * G)
+            check_attention(w, b, h, host(d.idx[b, h]), d.splits, host(d.part_o[b, rows]),
+                            host(d.part_lse[b, rows]), host(d.out[b, rows]),
+                            host(d.out_lse[b, rows]), v_store)
+            continue
         if s.granularity == "block":
             rc, rs = check_pack_block(w, b, h, host(d.codes[b, h]), host(d.scales[b, h]))
             ref = check_block_scores(w, b, h, scores, rc, rs)
