@@ -5,9 +5,8 @@
 namespace bsa {
 namespace {
 
-// grid (splits, B * Hkv), 256 threads; two work-groups per CU (the pipeline's
-// rings need up to 256 VGPRs). VM: where the values are read (kValCache,
-// kValStore, kValStoreTail).
+// grid (splits, B * Hkv), 256 threads, at least two work-groups per CU. VM:
+// where the values are read (kValCache, kValStore, kValStoreTail).
 template <int G, bool MAIN_BF16, bool BLOCK, int VM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(
     AttnArgs a) {

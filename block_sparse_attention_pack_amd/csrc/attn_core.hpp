@@ -11,27 +11,44 @@
 // tokens), dealt round-robin to the 4 waves. Each wave streams its groups
 // through one software pipeline with no phases: the next group's keys and
 // values are in flight while a group is used, so the HBM sees a steady stream
-// from the first group to the last. Per group:
-//   1. QK^T on v_mfma_f32_16x16x32_f16 (A = the group's query heads, rows >= G
-//      zero; B = 16 key rows, lane l holding row l % 16 and, for MFMA step c,
-//      channels 8 (l/16 + 4 c) .. +7, so each wave load reads 64 contiguous
-//      bytes of every row). BF16 rows (tail pages or a BF16 cache) take two
-//      bf16 MFMAs with q split exactly into q_hi + q_lo (an fp16 value is the
-//      sum of two bf16 values).
-//   2. An online softmax in the log2 domain, still in the MFMA output layout
-//      (a 16-lane row holds four heads of the 16 rows): row maxima and sums by
-//      DPP, the running maximum and sum per head kept by every lane of the row.
-//      The probabilities and the heads' rescale factors go through a small
-//      double-buffered LDS table to the value layout.
-//   3. PV as FP32 VALU FMAs, a lane owning DPL consecutive channels of a subset
-//      of the rows, so one wave load covers whole 256-byte value rows. The
-//      accumulators are rescaled only when some head's maximum grew.
-//      From the 4-bit value store a lane loads the DPL / 2 code bytes of its
-//      channels and the one E4M3 scale byte they share; the codes become
-//      floats by the hardware FP4 convert, and the row's scale times the KV
-//      head's FP32 scale multiplies either the probabilities or the values,
-//      whichever are fewer per lane (e2m1 * S is the value the packer rounded
-//      to, S = fl32(e4m3 * s_v)).
+// from the first group to the last.
+//
+// Both products run on the matrix cores, in transposed form, so that the
+// scores land in each lane exactly where the second product takes them: no
+// LDS round trip and no lane exchange between the two. Lane l = (j, n),
+// j = l / 16, n = l % 16, stands for head n throughout. Per group:
+//   1. S^T = K Q^T on v_mfma_f32_16x16x32_f16. A = the group's 16 key rows,
+//      lane l holding row l % 16 and, for MFMA step c, channels 8 (l/16 + 4 c)
+//      .. +7, so each wave load reads 64 contiguous bytes of every row; B = the
+//      query heads (heads >= G zero). Lane (j, n) receives the scores of head
+//      n at rows 4 j .. 4 j + 3. BF16 rows (tail pages or a BF16 cache) take
+//      two bf16 MFMAs with q split exactly into q_hi + q_lo (an fp16 value is
+//      the sum of two bf16 values).
+//   2. An online softmax in the log2 domain: head n's maximum and sum over the
+//      16 rows are the lane's four values combined with those of the three
+//      other lanes of head n by two lane-swap steps (v_permlane16_swap,
+//      v_permlane32_swap), so those four lanes hold the same running maximum
+//      and sum, bit for bit.
+//   3. O^T += V^T P^T on v_mfma_f32_16x16x16. B = P^T is what step 2 left in
+//      the lane (rows 4 j .. 4 j + 3 of head n). A = V^T, with channel slot m
+//      of MFMA step c standing for channel 8 m + c: lane (j, n) loads the 16
+//      contiguous bytes of channels 8 n .. 8 n + 7 of its rows 4 j .. 4 j + 3
+//      (a wave load covers four whole 256-byte rows), and one byte permute per
+//      operand dword puts the rows in the MFMA's K order. The probabilities
+//      enter as two 16-bit parts p = p_hi + p_lo, each rounded to nearest, so
+//      the products carry 22 (fp16) or 17 (bf16) significant bits of p, and
+//      accumulate in FP32. Lane (j, n) accumulates head n, channels 32 j ..
+//      32 j + 31. The accumulators are rescaled only when some head's maximum
+//      grew.
+//      From the 4-bit value store a lane loads the four code bytes of its
+//      channels in each of its rows, and the one E4M3 scale byte they share.
+//      The hardware FP4 convert (run at scale 1: it honours only the exponent
+//      of its scale) and one packed f16 multiply by the E4M3 scale give
+//      e2m1 * e4m3 exactly in f16 (at most 6 significant bits, in [2^-10,
+//      2688]). Those rows accumulate apart from any BF16 tail rows, and the
+//      KV head's FP32 scale s_v multiplies their sum at the end: the result
+//      is the sum over e2m1 * fl32(e4m3 * s_v), the values the packer rounded
+//      to, up to one rounding of each product's scale.
 // With block scores given (block mode), every work-group of a unit first makes
 // the unit's selection itself (select_unit_rows, the selection select_topk
 // makes) into LDS, and the split-0 group also writes idx / count: the
@@ -56,8 +73,9 @@ constexpr int kAttnWaves = 4;
 // 16-row groups of keys, and of values, in flight per wave beyond the one being
 // used. One: with 2048 waves streaming that is 16 MiB in flight, enough for
 // the HBM; deeper rings (32 and 48 MiB) queue so deep that the work-groups
-// served first finish far ahead of the rest, and measured slower (C3: 52.3 us
-// with one group ahead, 54.2 with two, 56.8 with three).
+// served first finish far ahead of the rest, and measured slower (16 x 4
+// heads at 128K, 64 blocks: 52.3 us with one group ahead, 54.2 with two, 56.8
+// with three).
 constexpr int kRing = 1;
 // The same with values from the 4-bit store (a group is 5 KiB instead of 8).
 constexpr int kRingV4 = 1;
@@ -70,17 +88,13 @@ constexpr int kRingV4 = 1;
 // end, which waits for every load in flight.
 constexpr int kValCache = 0, kValStore = 1, kValStoreTail = 2;
 constexpr int kWindow = 32;  // groups whose row indices a wave stages at a time
+constexpr int kAccStride = kHeadDim + 4;  // floats per head in the merge table
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int G>
-struct PvShape {
-  static constexpr int DPL = G <= 4 ? 8 : (G == 8 ? 4 : 2);  // channels per lane
-  static constexpr int LPR = kHeadDim / DPL;                  // lanes per row
-  static constexpr int NQ = kWave / LPR;                      // rows per wave load
-  static constexpr int RPL = 16 / NQ;                         // value rows per lane per group
-  static constexpr int VDW = DPL / 2;                         // dwords of a row per lane
-};
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void split_bf16(const half8& q, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -90,6 +104,27 @@ __device__ __forceinline__ void split_bf16(const half8& q, bf16x8& hi, bf16x8& l
     hi[e] = h;
     lo[e] = __bf16(f - float(h));  // exact: f has 11 significant bits, h the top 8
   }
+}
+
+// v combined over lanes n, n + 16, n + 32, n + 48 (n = lane % 16), the same
+// bits in all four: permlane16_swap leaves rows (0, 0, 2, 2) in one register
+// and (1, 1, 3, 3) in the other, permlane32_swap the low and the high half.
+// (The two results are copied out as scalars first: a bit cast applied to an
+// element of the returned vector reads element 0.)
+template <bool MAX>
+__device__ __forceinline__ float heads_reduce(float v) {
+  auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                            __builtin_bit_cast(uint32_t, v), false, false);
+  uint32_t x0 = s[0], x1 = s[1];
+  float a = __builtin_bit_cast(float, x0), b = __builtin_bit_cast(float, x1);
+  v = MAX ? fmaxf(a, b) : a + b;
+  s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                       __builtin_bit_cast(uint32_t, v), false, false);
+  x0 = s[0];
+  x1 = s[1];
+  a = __builtin_bit_cast(float, x0);
+  b = __builtin_bit_cast(float, x1);
+  return MAX ? fmaxf(a, b) : a + b;
 }
 
 struct AttnArgs {
@@ -234,40 +269,35 @@ __device__ __forceinline__ void issue_keys(KeySlot& ks, const AttnArgs& a, const
   for (int c = 0; c < 4; ++c) ks.w[c] = kp[4 * c];
 }
 
-// Value registers of one group: lane l holds channels (l % LPR) * DPL .. of rows
-// l / LPR + NQ k: 16-bit values in w[k][..], or from the 4-bit store the
-// channels' codes in c4[k] and their scale byte in sc[k].
-template <int G, int VM>
+// Value registers of one group: lane (j, n) holds channels 8 n .. 8 n + 7 of
+// rows 4 j + i, i < 4: as 16-bit values in w[i][0..3] (dword e = channels
+// 8 n + 2 e, 8 n + 2 e + 1), or from the 4-bit store as their codes in c4[i]
+// and their shared scale byte in sc[i].
+template <int VM>
 struct ValSlot {
-  static constexpr int R16 = VM == kValStore ? 1 : PvShape<G>::RPL;
-  static constexpr int R4 = VM == kValCache ? 1 : PvShape<G>::RPL;
-  uint32_t w[R16][PvShape<G>::VDW];
+  static constexpr int R16 = VM == kValStore ? 1 : 4;
+  static constexpr int R4 = VM == kValCache ? 1 : 4;
+  uint32_t w[R16][4];
   uint32_t c4[R4];
   uint32_t sc[R4];
 };
 
-template <int G, bool MAIN_BF16, bool BLOCK, int VM>
-__device__ __forceinline__ void issue_values(ValSlot<G, VM>& vs, const AttnArgs& a,
+template <bool MAIN_BF16, bool BLOCK, int VM>
+__device__ __forceinline__ void issue_values(ValSlot<VM>& vs, const AttnArgs& a,
                                              const UnitCtx& u, int q, const int* stage, int tl,
                                              int lane, bool live) {
-  using PV = PvShape<G>;
   const GroupRef r = describe<MAIN_BF16, BLOCK, VM>(a, u, q, stage, tl, live);
-  const int dc = lane % PV::LPR, qsub = lane / PV::LPR;
+  const int n = lane & 15, j = lane >> 4;
   if constexpr (VM != kValCache) {
     // a tail group (kValStoreTail) reads row 0 of the unit's store instead
     const uint8_t* cb = r.v4 ? r.vc : u.vcunit;
     const uint8_t* sb = r.v4 ? r.vsb : u.vsunit;
 #pragma unroll
-    for (int k = 0; k < PV::RPL; ++k) {
-      const int64_t row = r.v4 ? row_index<BLOCK>(r, qsub + PV::NQ * k) : 0;
-      const uint8_t* cp = cb + row * kValueCodeRow + dc * (PV::DPL / 2);
-      if constexpr (PV::DPL == 8)
-        vs.c4[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cp));
-      else if constexpr (PV::DPL == 4)
-        vs.c4[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(cp));
-      else
-        vs.c4[k] = __builtin_nontemporal_load(cp);
-      vs.sc[k] = __builtin_nontemporal_load(sb + row * kValueScaleRow + (dc * PV::DPL) / 16);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = r.v4 ? row_index<BLOCK>(r, 4 * j + i) : 0;
+      vs.c4[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t*>(cb + row * kValueCodeRow + 4 * n));
+      vs.sc[i] = __builtin_nontemporal_load(sb + row * kValueScaleRow + (n >> 1));
     }
   }
   if constexpr (VM == kValStoreTail) {
@@ -275,26 +305,21 @@ __device__ __forceinline__ void issue_values(ValSlot<G, VM>& vs, const AttnArgs&
     // unit's store codes instead (always cached, never used)
     const uint16_t* vb = r.v4 ? reinterpret_cast<const uint16_t*>(u.vcunit) : r.vb;
 #pragma unroll
-    for (int k = 0; k < PV::RPL; ++k) {
-      const int64_t off = r.v4 ? 0 : row_offset<BLOCK>(r, qsub + PV::NQ * k);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(vb + off + dc * PV::DPL);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = r.v4 ? 0 : row_offset<BLOCK>(r, 4 * j + i);
+      const uint4v x = *reinterpret_cast<const uint4v*>(vb + off + 8 * n);
 #pragma unroll
-      for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = vp[e];
+      for (int e = 0; e < 4; ++e) vs.w[i][e] = x[e];
     }
   }
   if constexpr (VM == kValCache) {
 #pragma unroll
-    for (int k = 0; k < PV::RPL; ++k) {
-      const int64_t off = row_offset<BLOCK>(r, qsub + PV::NQ * k);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(r.vb + off + dc * PV::DPL);
-      if constexpr (PV::VDW == 4) {
-        const uint4v x = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(vp));
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = row_offset<BLOCK>(r, 4 * j + i);
+      const uint4v x =
+          __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(r.vb + off + 8 * n));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vs.w[k][e] = x[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < PV::VDW; ++e) vs.w[k][e] = __builtin_nontemporal_load(vp + e);
-      }
+      for (int e = 0; e < 4; ++e) vs.w[i][e] = x[e];
     }
   }
 }
@@ -302,11 +327,9 @@ __device__ __forceinline__ void issue_values(ValSlot<G, VM>& vs, const AttnArgs&
 // LDS of one attention work-group.
 template <int G>
 struct AttnLds {
-  int stage[kAttnWaves][16 * kWindow];  // each wave's staged row indices
-  float ptab[kAttnWaves][2][16][G];     // a group's probabilities [row][head] (double-buffered)
-  float atab[kAttnWaves][2][G];         // a group's rescale factor per head
-  bf16x8 qsplit[8 * kWave];             // q = q_hi + q_lo in the MFMA operand order
-  float acc[kAttnWaves][G * kHeadDim];  // the waves' accumulators for the merge
+  int stage[kAttnWaves][16 * kWindow];     // each wave's staged row indices
+  bf16x8 qsplit[8 * kWave];                // q = q_hi + q_lo in the MFMA operand order
+  float acc[kAttnWaves][G * kAccStride];   // the waves' accumulators for the merge
   float m[kAttnWaves][G], l[kAttnWaves][G];
   int nulltoks[16];  // token mode: a null group's tokens (all -1)
   int is_last;
@@ -316,155 +339,153 @@ struct AttnLds {
 };
 
 // The online-softmax state of one wave: lane (j, n) holds the running maximum
-// (log2 domain) and sum of heads 4 j + r, r < 4; every lane of a 16-lane row
-// holds the same maximum, and the row's lane 0 holds the sum that is kept.
+// (log2 domain) and sum of head n, the same in the four lanes of the head.
 struct SoftState {
-  float m[4], l[4];
+  float m, l;
 };
 
-// The E2M1 codes of channels 0 .. N-1 (channel e in bits 4 e .. 4 e + 3) as
-// floats, two per hardware convert (the byte to convert is an immediate).
-template <int N>
-__device__ __forceinline__ void fp4_to_floats(uint32_t x, float (&vv)[N]) {
-  static_assert(N == 2 || N == 4 || N == 8, "channels per lane");
-  float2v c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
-  vv[0] = c[0];
-  vv[1] = c[1];
-  if constexpr (N >= 4) {
-    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
-    vv[2] = c[0];
-    vv[3] = c[1];
-  }
-  if constexpr (N == 8) {
-    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
-    vv[4] = c[0];
-    vv[5] = c[1];
-    c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
-    vv[6] = c[0];
-    vv[7] = c[1];
+// The A operands of the PV product from 16-bit rows: rw[i][e] holds channels
+// 8 n + 2 e (low half) and 8 n + 2 e + 1 (high half) of row 4 j + i; MFMA step
+// c = 2 e + h takes channel 8 n + c of rows 4 j .. 4 j + 3, as two dwords.
+__device__ __forceinline__ void value_operands(const uint32_t (&rw)[4][4], uint2v (&av)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    av[2 * e][0] = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x05040100u);
+    av[2 * e][1] = __builtin_amdgcn_perm(rw[3][e], rw[2][e], 0x05040100u);
+    av[2 * e + 1][0] = __builtin_amdgcn_perm(rw[1][e], rw[0][e], 0x07060302u);
+    av[2 * e + 1][1] = __builtin_amdgcn_perm(rw[3][e], rw[2][e], 0x07060302u);
   }
 }
 
-// One landed group: QK^T, the online softmax update, PV. Returns nothing; the
-// state and accumulators are updated in place. ptab / atab: this wave's
-// tables for the group's buffer.
+// E2M1 codes x (channel 2 b + t in bits 8 b + 4 t .. +3) times the f16 scale
+// pair s2, as f16 pairs (channels 2 b, 2 b + 1) in out[b]; the byte to
+// convert is an immediate of the instruction.
+__device__ __forceinline__ void fp4_row_to_f16(uint32_t x, half2v s2, uint32_t (&out)[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2);
+}
+
+// acc[c] += A_c P^T over the group's 16 rows, P = hi + lo (16-bit parts).
+template <bool BF>
+__device__ __forceinline__ void pv_mfma(const uint2v (&av)[8], const float (&p)[4],
+                                        float4v (&acc)[8]) {
+  if constexpr (BF) {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h = __bf16(p[i]);
+      hi[i] = h;
+      lo[i] = __bf16(p[i] - float(h));
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x4 a = __builtin_bit_cast(bf16x4, av[c]);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[c], 0, 0, 0);
+    }
+  } else {
+    half4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 h = _Float16(p[i]);
+      hi[i] = h;
+      lo[i] = _Float16(p[i] - float(h));
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const half4 a = __builtin_bit_cast(half4, av[c]);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, hi, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, lo, acc[c], 0, 0, 0);
+    }
+  }
+}
+
+// One landed group: S^T, the online softmax update, O^T += V^T P^T. The state
+// and accumulators are updated in place: acc takes the 16-bit rows, or (VM !=
+// kValCache) the 4-bit rows before their factor s_v; acct (kValStoreTail
+// only) the BF16 tail rows.
 template <int G, bool BLOCK, int VM>
-__device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G, VM>& vs,
-                                             const GroupRef& r,
-                                             const half8 (&qa)[4], const bf16x8* qsplit,
-                                             float scale_log2, float s_v, SoftState& st,
-                                             float (&acc)[G][PvShape<G>::DPL],
-                                             float (&ptab)[16][G], float (&atab)[G], int lane) {
-  using PV = PvShape<G>;
-  constexpr int DPL = PV::DPL;
-  // ---- QK^T ----
+__device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<VM>& vs,
+                                             const GroupRef& r, const half8 (&qa)[4],
+                                             const bf16x8* qsplit, float scale_log2,
+                                             SoftState& st, float4v (&acc)[8],
+                                             float4v (&acct)[8], int lane) {
+  // ---- S^T = K Q^T (lane (j, n): rows 4 j + i of head n) ----
   float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
   if (!r.bf16) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       half8 kv;
       __builtin_memcpy(&kv, &ks.w[c], 16);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kv, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qa[c], d, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8 kv;
       __builtin_memcpy(&kv, &ks.w[c], 16);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qsplit[(2 * c) * kWave + lane], kv, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qsplit[(2 * c + 1) * kWave + lane], kv, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qsplit[(2 * c) * kWave + lane], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qsplit[(2 * c + 1) * kWave + lane], d, 0, 0,
+                                                  0);
     }
   }
-  // ---- online softmax (MFMA output layout: lane (j, n) = heads 4 j + r of row n) ----
-  const int n16 = lane & 15, j4 = lane >> 4;
-  const bool rok = row_valid<BLOCK>(r, n16);
-  bool grew = false;
-  float p[4], alpha[4];
+  // ---- online softmax ----
+  const int n = lane & 15, j = lane >> 4;
+  bool rv[4];
+  float s[4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const float s = rok ? d[q4] * scale_log2 : -__builtin_inff();
-    const float mx = row16_max(s);
-    const float mo = st.m[q4];
-    const float mn = fmaxf(mo, mx);
-    const bool live = mn > -__builtin_inff();
-    alpha[q4] = live ? __builtin_amdgcn_exp2f(mo - mn) : 1.0f;
-    p[q4] = live ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
-    grew = grew || (4 * j4 + q4 < G && mn > mo);
-    st.m[q4] = mn;
-    st.l[q4] = st.l[q4] * alpha[q4] + row16_sum(p[q4]);
+  for (int i = 0; i < 4; ++i) {
+    rv[i] = row_valid<BLOCK>(r, 4 * j + i);
+    s[i] = rv[i] ? d[i] * scale_log2 : -__builtin_inff();
   }
-  const bool rescale = __ballot(grew) != 0;  // wave-uniform
-  if (4 * j4 < G) {
-    if constexpr (G >= 4) {
-      float4v pv = {p[0], p[1], p[2], p[3]};
-      *reinterpret_cast<float4v*>(&ptab[n16][4 * j4]) = pv;
-      if (n16 == 0) {
-        float4v av = {alpha[0], alpha[1], alpha[2], alpha[3]};
-        *reinterpret_cast<float4v*>(&atab[4 * j4]) = av;
-      }
-    } else {
+  const float mx = heads_reduce<true>(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+  const float mo = st.m;
+  const float mn = fmaxf(mo, mx);
+  const bool live = mn > -__builtin_inff();
+  const float alpha = live ? __builtin_amdgcn_exp2f(mo - mn) : 1.0f;
+  float p[4];
 #pragma unroll
-      for (int q4 = 0; q4 < G; ++q4) {
-        ptab[n16][q4] = p[q4];
-        if (n16 == 0) atab[q4] = alpha[q4];
-      }
+  for (int i = 0; i < 4; ++i) p[i] = live ? __builtin_amdgcn_exp2f(s[i] - mn) : 0.0f;
+  st.m = mn;
+  st.l = st.l * alpha + heads_reduce<false>((p[0] + p[1]) + (p[2] + p[3]));
+  if (__ballot(n < G && mn > mo) != 0) {  // wave-uniform
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+    if constexpr (VM == kValStoreTail) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acct[c] *= alpha;
     }
   }
-  wave_lds_sync();
-  // ---- PV (value layout: lane (qsub, dc) = channels dc * DPL .. of rows qsub + NQ k) ----
-  const int qsub = lane / PV::LPR;
-  if (rescale) {
-    float al[G];
+  // ---- O^T += V^T P^T ----
+  // a masked row has p = 0; its value bits are not data, so they are dropped
+  // (zero bits, or a zero scale for a 4-bit row: E2M1 has no NaN code)
+  uint32_t rw[4][4];
+  uint2v av[8];
+  if constexpr (VM != kValCache) {
+    if (VM == kValStore || r.v4) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) al[hh] = atab[hh];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[hh][e] *= al[hh];
-  }
-  const bool full = BLOCK ? r.nvalid >= 16 : __ballot(rok) == ~0ull;  // all 16 rows valid
-#pragma unroll
-  for (int k = 0; k < PV::RPL; ++k) {
-    const int row = qsub + PV::NQ * k;
-    float pr[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) pr[hh] = ptab[row][hh];
-    // a masked row has p = 0; its value bits are not data, so they are dropped
-    const bool vok = full || row_valid<BLOCK>(r, row);
-    float vv[DPL];
-    if (VM != kValCache && r.v4) {
-      // E2M1 code of channel e in bits 4 e .. 4 e + 3; a dropped row's scale is
-      // zero (its byte could be a NaN code)
-      fp4_to_floats<DPL>(vs.c4[k], vv);
-      const float f =
-          __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vok ? vs.sc[k] : 0u, 1.0f, false)[0] * s_v;
-      if constexpr (G <= DPL) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) pr[hh] *= f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) vv[e] *= f;
+      for (int i = 0; i < 4; ++i) {
+        // the scale byte twice, so the convert gives the f16 pair (S, S)
+        const uint32_t sb = rv[i] ? vs.sc[i] : 0u;
+        fp4_row_to_f16(vs.c4[i], __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb * 0x101u, 1.0f, false),
+                       rw[i]);
       }
-    } else if constexpr (VM != kValStore) {
-#pragma unroll
-      for (int e = 0; e < PV::VDW; ++e) {
-        const uint32_t x = vok ? vs.w[k][e] : 0u;
-        if (r.bf16) {
-          vv[2 * e] = bf16_bits_to_float(x & 0xFFFFu);
-          vv[2 * e + 1] = bf16_bits_to_float(x >> 16);
-        } else {
-          vv[2 * e] = half_bits_to_float(uint16_t(x & 0xFFFFu));
-          vv[2 * e + 1] = half_bits_to_float(uint16_t(x >> 16));
-        }
-      }
+      value_operands(rw, av);
+      pv_mfma<false>(av, p, acc);
+      return;
     }
+  }
+  if constexpr (VM != kValStore) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[hh][e] = __builtin_fmaf(pr[hh], vv[e], acc[hh][e]);
-    // with 8 or 16 heads a row's G probabilities are read where they are used
-    // (hoisting every row's reads needs more registers than there are)
-    if constexpr (G >= 8) __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 4; ++e) rw[i][e] = rv[i] ? vs.w[i][e] : 0u;
+    value_operands(rw, av);
+    float4v (&dst)[8] = VM == kValStoreTail ? acct : acc;
+    if (r.bf16) pv_mfma<true>(av, p, dst);
+    else pv_mfma<false>(av, p, dst);
   }
 }
 
@@ -473,8 +494,6 @@ __device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<G,
 template <int G, bool MAIN_BF16, bool BLOCK, int VM>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit,
                                           AttnLds<G>& lds) {
-  using PV = PvShape<G>;
-  constexpr int DPL = PV::DPL, LPR = PV::LPR;
   constexpr int RING = VM != kValCache ? kRingV4 : kRing;
   constexpr bool VQ = VM != kValCache;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -491,7 +510,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
   u.s_v = VQ ? a.vs.s_v[h] : 1.0f;
   u.nulltoks = lds.nulltoks;
 
-  // query operands: lane l holds head row l % 16, channels 8 (l/16 + 4 c) .. + 8
+  // query operands: lane l holds head l % 16, channels 8 (l/16 + 4 c) .. + 8
   // for MFMA step c (the key layout above); every wave loads its own, before
   // the selection so that their latency overlaps it
   const int n16 = lane & 15, j4 = lane >> 4;
@@ -552,16 +571,14 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
   int* stage = lds.stage[wave];
 
   SoftState st;
+  st.m = -__builtin_inff();
+  st.l = 0.0f;
+  float4v acc[8], acct[8];  // acct: BF16 tail rows beside 4-bit rows (kValStoreTail)
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    st.m[q4] = -__builtin_inff();
-    st.l[q4] = 0.0f;
+  for (int c = 0; c < 8; ++c) {
+    acc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    acct[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  float acc[G][DPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
 
 #pragma unroll 1
   for (int w0 = 0; w0 < nmine; w0 += kWindow) {
@@ -582,15 +599,14 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
     wave_lds_sync();
     auto qof = [&](int t) { return wave + kAttnWaves * t; };
     KeySlot kr[RING];
-    ValSlot<G, VM> vr[RING];
+    ValSlot<VM> vr[RING];
     // every slot is always issued (groups past the window are null groups), so
     // the ring registers are defined on every path
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
       const int t = w0 + k;
       issue_keys<MAIN_BF16, BLOCK, VM>(kr[k], a, u, qof(t), stage, t - w0, lane, t < wend);
-      issue_values<G, MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(t), stage, t - w0, lane,
-                                            t < wend);
+      issue_values<MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(t), stage, t - w0, lane, t < wend);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
@@ -601,44 +617,38 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
         const int tn = t + RING;  // the group this slot takes next
         if (t < wend) {
           const GroupRef r = describe<MAIN_BF16, BLOCK, VM>(a, u, qof(t), stage, t - w0, true);
-          attend_group<G, BLOCK, VM>(kr[k], vr[k], r, qa, lds.qsplit, a.scale_log2, u.s_v, st,
-                                     acc, lds.ptab[wave][t & 1], lds.atab[wave][t & 1], lane);
+          attend_group<G, BLOCK, VM>(kr[k], vr[k], r, qa, lds.qsplit, a.scale_log2, st, acc,
+                                     acct, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
         issue_keys<MAIN_BF16, BLOCK, VM>(kr[k], a, u, qof(tn), stage, tn - w0, lane, tn < wend);
-        issue_values<G, MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(tn), stage, tn - w0, lane,
-                                              tn < wend);
+        issue_values<MAIN_BF16, BLOCK, VM>(vr[k], a, u, qof(tn), stage, tn - w0, lane,
+                                           tn < wend);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
   // ---- merge the waves' states -------------------------------------------
-  const int dc = lane % LPR, qsub = lane / LPR;
-  // rows of one channel chunk are spread over NQ lanes: sum them
+  // lane (j, n) holds head n, channels 32 j + 8 i + c in acc[c][i]
+  if constexpr (VQ) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      float x = acc[hh][e];
-#pragma unroll
-      for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
-      acc[hh][e] = x;
+    for (int c = 0; c < 8; ++c) {
+      acc[c] *= u.s_v;
+      if constexpr (VM == kValStoreTail) acc[c] += acct[c];
     }
-  if (qsub == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) lds.acc[wave][hh * kHeadDim + dc * DPL + e] = acc[hh][e];
   }
-  if (n16 == 0) {
+  if (n16 < G) {
+    float* dst = &lds.acc[wave][n16 * kAccStride + 32 * j4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int hh = 4 * j4 + q4;
-      if (hh < G) {
-        lds.m[wave][hh] = st.m[q4];
-        lds.l[wave][hh] = st.l[q4];
-      }
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4v*>(dst + 8 * i) = float4v{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *reinterpret_cast<float4v*>(dst + 8 * i + 4) =
+          float4v{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+    if (j4 == 0) {
+      lds.m[wave][n16] = st.m;
+      lds.l[wave][n16] = st.l;
     }
   }
   __syncthreads();
@@ -652,7 +662,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
         const float f = __builtin_amdgcn_exp2f(lds.m[w][hh] - M);
-        num += f * lds.acc[w][o];
+        num += f * lds.acc[w][hh * kAccStride + d];
         den += f * lds.l[w][hh];
       }
     }

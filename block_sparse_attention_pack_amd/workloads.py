@@ -25,6 +25,8 @@ The workloads follow the sparse-decode settings the pages evaluate:
 * ``jetqsparse_v4`` the jetqsparse inputs with the values held in a 4-bit
                   NVFP4 store (the Jet-QSparse abstract's NVFP4 cache with values
                   compressed too): 72 B per attended value row instead of 256
+* ``jetqsparse_g16`` the jetqsparse shape with 64 query heads (16 per KV head,
+                  the largest group the kernels take)
 * ``cluster``     B8 Hkv8 Hq32 T131072 in 1024 coarse blocks of noncontiguous
                   tokens (each token's block drawn uniformly, about 128 tokens a
                   block; keys = the block's center + unit noise), 4 needle blocks
@@ -135,13 +137,17 @@ SPECS: Dict[str, Spec] = {
     "jetqsparse_v4": Spec("jetqsparse_v4", 2, 16, 4, 16, 131072, "block", 64,
                           needle_count=20, needle_profile="zipf", needle_strength=3.0,
                           key_offset_std=2.0, value_fmt="nvfp4"),
+    # the Jet-QSparse decode shape with 16 query heads per KV head
+    "jetqsparse_g16": Spec("jetqsparse_g16", 2, 16, 4, 64, 131072, "block", 64,
+                           needle_count=20, needle_profile="zipf", needle_strength=3.0,
+                           key_offset_std=2.0),
     # coarse semantic blocks picked by their centroids, at the token shape
     "cluster": Spec("cluster", 5, 8, 8, 32, 131072, "cluster", 2048, n_clusters=1024,
                     needle_count=4, needle_profile="const", needle_strength=8.0),
 }
 
 ORDER = ["tiny", "llama8b", "jetqsparse", "ragged", "token", "token_fp8", "jetqsparse_q4",
-         "token_topp", "jetqsparse_v4", "cluster"]
+         "token_topp", "jetqsparse_v4", "cluster", "jetqsparse_g16"]
 
 
 def reduced(name: str, max_tokens: int, batch: Optional[int] = None,
