@@ -44,6 +44,9 @@ TRAFFIC_SOURCES = {  # kernel: (file name stem, sources)
                                                 "common.hpp"]),
     "scan_token_kernel<32>": ("scan_token_kernel_r32", ["scan.hip", "common.hpp"]),
     "scan_token_kernel<32, fp8>": ("scan_token_kernel_r32_fp8", ["scan.hip", "common.hpp"]),
+    "attn_kernel<4, false, false, 0, 1>": ("attn_kernel_g4_token",
+                                        ["attn.hip", "attn_core.hpp", "combine_core.hpp",
+                                         "select_core.hpp", "common.hpp"]),
 }
 
 
@@ -380,7 +383,7 @@ def main() -> int:
     # cluster mode the attention (the centroids are the smaller read)
     if d0.cluster_mode:
         scan_stage, kbytes = "attend_combine", nbytes["attn"]
-        kname = "attn_kernel<%d, false, false, %d>" % (spec.group, int(d0.value_store))
+        kname = "attn_kernel<%d, false, false, %d, 1>" % (spec.group, int(d0.value_store))
     else:
         scan_stage, kbytes = "scan", nbytes["scan"]
         kname = ("scan_block_kernel" if d0.block_mode else "scan_token_kernel<%d%s>"

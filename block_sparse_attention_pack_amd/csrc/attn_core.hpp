@@ -70,15 +70,15 @@ namespace bsa {
 namespace {
 
 constexpr int kAttnWaves = 4;
-// 16-row groups of keys, and of values, in flight per wave beyond the one being
-// used. One: with 2048 waves streaming that is 16 MiB in flight, enough for
-// the HBM; deeper rings (32 and 48 MiB) queue so deep that the work-groups
-// served first finish far ahead of the rest, and measured slower (16 x 4
-// heads at 128K, 64 blocks: 52.3 us with one group ahead, 54.2 with two, 56.8
-// with three).
-constexpr int kRing = 1;
-// The same with values from the 4-bit store (a group is 5 KiB instead of 8).
-constexpr int kRingV4 = 1;
+// RING (a template argument): 16-row groups of keys and values a wave has in
+// flight. One when the grid fills the CUs: with 2048 waves streaming that is
+// 16 MiB in flight, enough for the HBM; two groups per wave (32 MiB) queue so
+// deep that the work-groups served first finish far ahead of the rest, and
+// measured slower (16 x 4 heads at 128K, 64 blocks: 55.9 us with one group,
+// 56.8 with two; with 16 splits 65.1 and 61.4). Two when a 16-bit block-mode
+// grid leaves CUs with fewer than two work-groups (8 units, 32 splits: 18.8
+// against 18.0 us).
+constexpr int kRingSmallGrid = 2;
 
 // Where a kernel reads the values: the 16-bit cache (BF16 tail pages too), the
 // 4-bit store with no tail pages, or the 4-bit store with BF16 tail pages. In
@@ -491,10 +491,9 @@ __device__ __forceinline__ void attend_group(const KeySlot& ks, const ValSlot<VM
 
 // The attention of (split, unit): its rows' partial (O, lse) per head, and the
 // merge when a.counters is set.
-template <int G, bool MAIN_BF16, bool BLOCK, int VM>
+template <int G, bool MAIN_BF16, bool BLOCK, int VM, int RING>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int split, int unit,
                                           AttnLds<G>& lds) {
-  constexpr int RING = VM != kValCache ? kRingV4 : kRing;
   constexpr bool VQ = VM != kValCache;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = unit / a.Hkv, h = unit % a.Hkv;
