@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 SOURCES = ["api.hip", "pack.hip", "scan.hip", "select.hip", "attn.hip", "combine.hip",
-           "cluster.hip", "probe.hip"]
+           "cluster.hip", "probe.hip", "tokselect.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

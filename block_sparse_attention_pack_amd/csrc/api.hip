@@ -188,7 +188,7 @@ int check_select_args(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, const f
   BSA_REQUIRE(scores && seq_lens && idx && count, BSA_ERR_INVALID_ARG,
               "scores, seq_lens, idx and count are required");
   if (cfg->granularity == BSA_GRANULARITY_TOKEN) {
-    const size_t need = bsa::token_select_workspace(g);
+    const size_t need = bsa::token_select_workspace(g, cfg->budget, cfg->top_p);
     BSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), BSA_ERR_WORKSPACE,
                 "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   }
@@ -256,7 +256,9 @@ hipError_t score_and_select(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, c
                             const void* kproj, const float* proj, const int32_t* seq_lens,
                             float* scores, void* workspace, int32_t* idx, int32_t* count,
                             hipStream_t s) {
-  const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN;
+  // (the one-group token select reads no histogram)
+  const bool tok = cfg->granularity == BSA_GRANULARITY_TOKEN &&
+                   !bsa::token_select_one_group(g, cfg->budget, cfg->top_p);
   hipError_t e = launch_scan(g, cfg, q, codes, scales, global_scale, key_center, kproj, proj,
                              seq_lens, scores, s, tok ? workspace : nullptr);
   if (e == hipSuccess) e = launch_select(g, cfg, scores, seq_lens, workspace, idx, count, s, tok);
@@ -339,7 +341,7 @@ int plan_scratch(const bsa::UnitGeom& g, const bsa_select_cfg* cfg, int num_spli
   p->counters = off;
   off = up(off + U * 4);
   p->workspace = off;
-  p->workspace_bytes = tok ? bsa::token_select_workspace(g) : 0;
+  p->workspace_bytes = tok ? bsa::token_select_workspace(g, cfg->budget, cfg->top_p) : 0;
   off = up(off + p->workspace_bytes);
   p->scores = off;
   off = up(off + U * size_t(tok ? g.Tmax : g.NBmax) * 4);
@@ -500,7 +502,7 @@ int bsa_score_scan(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const
 size_t bsa_workspace_size(const bsa_kv_layout* layout, const bsa_select_cfg* cfg) {
   bsa::UnitGeom g;
   if (check_common(layout, cfg, &g)) return 0;
-  return cfg->granularity == BSA_GRANULARITY_TOKEN ? bsa::token_select_workspace(g) : 0;
+  return cfg->granularity == BSA_GRANULARITY_TOKEN ? bsa::token_select_workspace(g, cfg->budget, cfg->top_p) : 0;
 }
 
 int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg, const float* scores,

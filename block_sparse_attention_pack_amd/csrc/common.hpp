@@ -271,7 +271,7 @@ hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
                              const _Float16* q, const void* kproj, const float* proj,
                              const int32_t* seq_lens, float* scores, uint32_t* hist0,
                              int64_t hist_stride, int budget, hipStream_t s);
-size_t token_select_workspace(const UnitGeom& g);
+size_t token_select_workspace(const UnitGeom& g, int budget, float top_p);
 int64_t token_unit_words(const UnitGeom& g);  // words per unit of that workspace
 hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const float* scores,
                                const int32_t* seq_lens, int32_t* idx, int32_t* count,
@@ -279,6 +279,17 @@ hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const 
 // hist_ready: the histograms were filled by launch_scan_token (tok_hist is skipped).
 // top_p > 0: the selection is then cut to the adaptive budget (tok_topp);
 // budget <= kTopPMaxBudget.
+// Token select by one work-group per unit (tokselect.hip): its LDS bitmaps
+// hold up to kTokSelectMaxTokens tokens, and its threshold sample is sized for
+// budgets up to kTokSelectOneMaxBudget; the adaptive budget, longer rows and
+// larger budgets take the chunked launches (select.hip).
+constexpr int kTokSelectMaxTokens = 131072;
+constexpr int kTokSelectOneMaxBudget = 2048;
+bool token_select_one_group(const UnitGeom& g, int budget, float top_p);
+size_t token_select_one_workspace(const UnitGeom& g);  // its region, after the chunked one's
+hipError_t launch_select_token_one(const UnitGeom& g, int budget, const float* scores,
+                                   const int32_t* seq_lens, void* ws, int32_t* idx,
+                                   int32_t* count, hipStream_t s);
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
                                hipStream_t s, bool hist_ready = false, float top_p = 0.0f);

@@ -866,8 +866,11 @@ hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const 
   return hipGetLastError();
 }
 
-size_t token_select_workspace(const UnitGeom& g) {
-  return size_t(tok_geom(g.Tmax).unit_words) * 4 * size_t(g.B) * size_t(g.Hkv);
+// The chunked select's region (tok_geom words per unit), then, where the
+// one-group select applies, its region.
+size_t token_select_workspace(const UnitGeom& g, int budget, float top_p) {
+  return size_t(tok_geom(g.Tmax).unit_words) * 4 * size_t(g.B) * size_t(g.Hkv) +
+         (token_select_one_group(g, budget, top_p) ? token_select_one_workspace(g) : 0);
 }
 
 int64_t token_unit_words(const UnitGeom& g) { return tok_geom(g.Tmax).unit_words; }
@@ -876,6 +879,10 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
                                hipStream_t s, bool hist_ready, float top_p) {
   const TokGeom tg = tok_geom(g.Tmax);
+  if (!hist_ready && token_select_one_group(g, budget, top_p))
+    return launch_select_token_one(
+        g, budget, scores, seq_lens,
+        static_cast<uint32_t*>(ws) + tg.unit_words * int64_t(g.B) * g.Hkv, idx, count, s);
   const int units = g.B * g.Hkv;
   // the chunks of a unit share their unit's reads (histogram, bitmaps,
   // bucket scores): consecutive work-group ids are spread over the XCDs, so a

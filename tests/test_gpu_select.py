@@ -58,17 +58,23 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _histograms_back_at_zero(ws, units, T):
+def _histograms_back_at_zero(ws, units, T, one_group=False):
     """After a call each unit's histogram in the token workspace is zero again
     (per unit: 4096 histogram words; a slot of 8 + 3 words per 16384-key chunk,
-    rounded up to 64; two bitmaps of ceil(T/64)*2 words rounded up to 64)."""
+    rounded up to 64; two bitmaps of ceil(T/64)*2 words rounded up to 64).
+    With the one-launch select (budget <= 2048, no top_p, T <= 131072) a
+    second region follows, 64 + 2 * 8192 words per unit and 32768-token chunk:
+    its arrival counter (word 0) is zero again too."""
     w = ws.view(torch.int32).cpu().numpy()
     W = -(-T // 64) * 2
     slot = -(-(8 + 3 * -(-T // 16384)) // 64) * 64
     per = 4096 + slot + 2 * (-(-W // 64) * 64)
-    assert w.size == units * per, (w.size, units, per)
+    one = 64 + -(-T // 32768) * 2 * 8192 if one_group else 0
+    assert w.size == units * (per + one), (w.size, units, per, one)
     for u in range(units):
         assert not w[u * per:u * per + 4096].any(), f"histogram of unit {u}"
+        if one_group:
+            assert w[units * per + u * one] == 0, f"arrival counter of unit {u}"
 
 
 @pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
@@ -92,13 +98,62 @@ def test_token_select_matches_oracle(pattern, budget):
     for rep in range(2):  # a second call on the same workspace
         bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
         torch.cuda.synchronize()
-        _histograms_back_at_zero(ws, B * Hkv, T)
+        _histograms_back_at_zero(ws, B * Hkv, T, one_group=budget <= 2048)
         gi, gc = idx.cpu().numpy(), count.cpu().numpy()
         for b in range(B):
             for h in range(Hkv):
                 ri, rc = O.select_tokens_unit(scores[b, h].astype(np.float64), lengths[b], budget)
                 assert int(gc[b, h]) == rc, (pattern, budget, b, h, rep)
                 assert np.array_equal(gi[b, h], ri), (pattern, budget, b, h, rep)
+
+
+def _sample_positions(C):
+    """Tokens whose scores the one-launch token select samples for its
+    threshold (1024 evenly spaced ones when a row has more than 16384
+    candidates)."""
+    return (np.arange(1024, dtype=np.int64) * C) // 1024
+
+
+@pytest.mark.parametrize("case", ["sampled_high", "unsampled_high"])
+def test_token_select_when_the_sample_misleads(case):
+    """Rows built against the threshold sample: only the sampled tokens score
+    high (far fewer than the budget lie above the sampled threshold), or only
+    the unsampled ones do (far more candidates than the list holds). Both take
+    the selection over the scores in memory and must still be exact."""
+    T = 131072
+    lengths = [T, 65536, 16385, 16384]
+    B, Hkv, budget = len(lengths), 1, 2048
+    rng = np.random.default_rng([12, len(case)])
+    scores = np.zeros((B, Hkv, T), dtype=np.float32)
+    for b, C in enumerate(lengths):
+        pos = _sample_positions(C)
+        row = np.full(T, -5.0, dtype=np.float32)
+        if case == "sampled_high":
+            row[:C] = -1.0 - rng.random(C).astype(np.float32)
+            row[pos] = 1.0 + rng.random(len(pos)).astype(np.float32)
+        else:
+            row[:C] = 1.0 + rng.random(C).astype(np.float32)
+            row[pos] = -1.0 - rng.random(len(pos)).astype(np.float32)
+        scores[b, 0] = row
+    _say(f"[select] token sample case={case} T={T}")
+    layout = _layout(B, Hkv, T)
+    cfg = bsa.select_cfg(bsa.TOKEN, budget, 0, 32, 0.1)
+    ws_bytes = bsa.workspace_size(layout, cfg)
+    dev = torch.device("cuda")
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
+    sc = torch.from_numpy(scores).to(dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    idx = torch.full((B, Hkv, budget), 5, dtype=torch.int32, device=dev)
+    count = torch.full((B, Hkv), 5, dtype=torch.int32, device=dev)
+    for rep in range(2):  # the arrival counters are left at zero for the second
+        bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
+        torch.cuda.synchronize()
+        _histograms_back_at_zero(ws, B * Hkv, T, one_group=True)
+    gi, gc = idx.cpu().numpy(), count.cpu().numpy()
+    for b in range(B):
+        ri, rc = O.select_tokens_unit(scores[b, 0].astype(np.float64), lengths[b], budget)
+        assert int(gc[b, 0]) == rc, (case, b)
+        assert np.array_equal(gi[b, 0], ri), (case, b)
 
 
 @pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
