@@ -5,9 +5,10 @@
 // (select_core.hpp); a unit has at most max_tokens/128 candidates.
 //
 // Token mode: a unit has up to max_tokens candidates (131072 at 128K context),
-// too many for one work-group to read fast, so the selection is spread over
-// kTokChunk-key chunks, one work-group each, in three launches (four with the
-// adaptive budget):
+// too many for one work-group to read fast. Budgets up to 2048 without the
+// adaptive budget, at up to 131072 tokens, take the one-launch select of
+// tokselect.hip. Otherwise the selection is spread over kTokChunk-key chunks,
+// one work-group each, in three launches (four with the adaptive budget):
 //   hist    every group adds the histogram of its keys' top 12 bits (of the
 //           order-preserving key) to its unit's, with device-scope atomics
 //           (the histogram is zero on entry: the finish of the previous call
