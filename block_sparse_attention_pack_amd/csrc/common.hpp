@@ -279,17 +279,19 @@ hipError_t launch_select_block(const UnitGeom& g, int budget, int n_tail, const 
 // hist_ready: the histograms were filled by launch_scan_token (tok_hist is skipped).
 // top_p > 0: the selection is then cut to the adaptive budget (tok_topp);
 // budget <= kTopPMaxBudget.
-// Token select by one work-group per unit (tokselect.hip): its LDS bitmaps
-// hold up to kTokSelectMaxTokens tokens, and its threshold sample is sized for
-// budgets up to kTokSelectOneMaxBudget; the adaptive budget, longer rows and
-// larger budgets take the chunked launches (select.hip).
+// Token select in one launch (tokselect.hip): its LDS bitmaps hold up to
+// kTokSelectMaxTokens tokens, and its threshold sample is sized for budgets up
+// to kTokSelectOneMaxBudget; longer rows and larger budgets take the chunked
+// launches (select.hip). lse (the adaptive budget, else null): where it leaves
+// the softmax partials tok_topp reads.
 constexpr int kTokSelectMaxTokens = 131072;
 constexpr int kTokSelectOneMaxBudget = 2048;
 bool token_select_one_group(const UnitGeom& g, int budget, float top_p);
 size_t token_select_one_workspace(const UnitGeom& g);  // its region, after the chunked one's
 hipError_t launch_select_token_one(const UnitGeom& g, int budget, const float* scores,
                                    const int32_t* seq_lens, void* ws, int32_t* idx,
-                                   int32_t* count, hipStream_t s);
+                                   int32_t* count, uint32_t* lse, int64_t lse_stride,
+                                   hipStream_t s);
 hipError_t launch_select_token(const UnitGeom& g, int budget, const float* scores,
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
                                hipStream_t s, bool hist_ready = false, float top_p = 0.0f);

@@ -5,10 +5,11 @@
 // (select_core.hpp); a unit has at most max_tokens/128 candidates.
 //
 // Token mode: a unit has up to max_tokens candidates (131072 at 128K context),
-// too many for one work-group to read fast. Budgets up to 2048 without the
-// adaptive budget, at up to 131072 tokens, take the one-launch select of
-// tokselect.hip. Otherwise the selection is spread over kTokChunk-key chunks,
-// one work-group each, in three launches (four with the adaptive budget):
+// too many for one work-group to read fast. Budgets up to 2048 at up to 131072
+// tokens take the one-launch select of tokselect.hip (then topp below, with
+// the adaptive budget). Otherwise the selection is spread over kTokChunk-key
+// chunks, one work-group each, in three launches (four with the adaptive
+// budget):
 //   hist    every group adds the histogram of its keys' top 12 bits (of the
 //           order-preserving key) to its unit's, with device-scope atomics
 //           (the histogram is zero on entry: the finish of the previous call
@@ -880,11 +881,19 @@ hipError_t launch_select_token(const UnitGeom& g, int budget, const float* score
                                const int32_t* seq_lens, void* ws, int32_t* idx, int32_t* count,
                                hipStream_t s, bool hist_ready, float top_p) {
   const TokGeom tg = tok_geom(g.Tmax);
-  if (!hist_ready && token_select_one_group(g, budget, top_p))
-    return launch_select_token_one(
-        g, budget, scores, seq_lens,
-        static_cast<uint32_t*>(ws) + tg.unit_words * int64_t(g.B) * g.Hkv, idx, count, s);
   const int units = g.B * g.Hkv;
+  if (!hist_ready && token_select_one_group(g, budget, top_p)) {
+    // with the adaptive budget its softmax partials go where the filter leaves
+    // them (the chunked region's slots), and tok_topp follows
+    uint32_t* w32 = static_cast<uint32_t*>(ws);
+    const hipError_t e = launch_select_token_one(
+        g, budget, scores, seq_lens, w32 + tg.unit_words * int64_t(units), idx, count,
+        top_p > 0.0f ? w32 + kTokBins + kTokLseWord : nullptr, tg.unit_words, s);
+    if (e == hipSuccess && top_p > 0.0f)
+      hipLaunchKernelGGL(tok_topp_kernel, dim3(units), dim3(kTopPThreads), 0, s, scores, seq_lens,
+                         g.Hkv, g.Tmax, budget, top_p, tg, ws, idx, count);
+    return e == hipSuccess ? hipGetLastError() : e;
+  }
   // the chunks of a unit share their unit's reads (histogram, bitmaps,
   // bucket scores): consecutive work-group ids are spread over the XCDs, so a
   // unit's groups are kept units apart to land on one XCD and its L2

@@ -25,6 +25,8 @@
 //      listed key above kappa, one in a "tied" bitmap for each key equal to
 //      it, and writes the taken tokens and the lowest-index ties ascending in
 //      one pass over the bitmap words (two block scans).
+// With the adaptive budget, every group also leaves its two 16384-token
+// halves' softmax partials for tok_topp, which then cuts the selection.
 // If the lists hold fewer than picks or more than kTsCap candidates, or a chunk
 // more than kTsChunkCap (a sample far from the unit's distribution, or many
 // equal keys), steps 3 and 4 run over the unit's scores in memory instead: the
@@ -54,8 +56,27 @@ struct TsLds {
   uint32_t hist[2][256];
   uint32_t wlo[kTsWaves], whi[kTsWaves];
   int wtot[kTsWaves], wtot2[kTsWaves];
+  int32_t out[kTokSelectOneMaxBudget];     // the selection, in order
+  float pm[2][kTsWaves], ps[2][kTsWaves];  // the softmax partials' per-wave parts
+  int pi[2][kTsWaves];
   int ncand, beta, above, inb, req, is_last;
 };
+
+constexpr float kTsLog2e = 1.4426950408889634f;
+
+// (m, s) <- the log-sum-exp merge of (m, s) and (m2, s2): s a sum of exp(x - m)
+// (the exponentials by the hardware exp2: the shares they feed decide a count
+// within a tolerance of 1e-4, far above its few-ulp error)
+__device__ __forceinline__ void ts_lse_merge(float& m, float& s, float m2, float s2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -__builtin_inff()) {
+    m = mx;
+    s = 0.0f;
+    return;
+  }
+  s = s * __builtin_amdgcn_exp2f((m - mx) * kTsLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mx) * kTsLog2e);
+  m = mx;
+}
 
 // Inclusive scans of two ints per thread over the work-group; tv, tw: totals.
 __device__ __forceinline__ void ts_scan2(int& v, int& w, TsLds& s, int& tv, int& tw) {
@@ -216,11 +237,15 @@ __host__ __device__ constexpr int64_t ts_unit_words(int chunks) {
   return kTsListWord + int64_t(chunks) * 2 * kTsChunkCap;
 }
 
-// grid (B * Hkv, ceil(Tmax / kTsChunk)), kTsThreads threads.
+// grid (B * Hkv, ceil(Tmax / kTsChunk)), kTsThreads threads. lse (the adaptive
+// budget, else null): where each 16384-token half-chunk's softmax partial goes
+// (maximum over its finite scores, sum of exp(s - maximum), count of +inf), at
+// lse + unit * lse_stride + 3 * half-chunk, as the chunked select's filter
+// leaves them for tok_topp.
 __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv, int Tmax,
     int budget, uint32_t* __restrict__ ws, int32_t* __restrict__ idx,
-    int32_t* __restrict__ count) {
+    int32_t* __restrict__ count, uint32_t* __restrict__ lse, int64_t lse_stride) {
   __shared__ TsLds s;
   const int unit = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -269,6 +294,64 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
         for (int j = 0; j < kPer; ++j) f(sk[j]);
       }, s);
       T = c.ge ? c.kge : c.keq;  // the sample's rank-want key (its ties included)
+    }
+  }
+
+  if (lse) {  // the half-chunks' softmax partials (uniform branch)
+    static_assert(kQ % 2 == 0, "two halves");
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float m = -__builtin_inff(), sm = 0.0f;
+      int ninf = 0;
+#pragma unroll
+      for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
+        const int q = qb + tid + kTsThreads * b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = v[b][e];
+          const bool in = q < nq && 4 * q + e < C;
+          ninf += (in && x == __builtin_inff()) ? 1 : 0;
+          m = (in && x < __builtin_inff()) ? fmaxf(m, x) : m;  // fmaxf drops NaN
+        }
+      }
+#pragma unroll
+      for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
+        const int q = qb + tid + kTsThreads * b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = v[b][e];
+          const bool fin = q < nq && 4 * q + e < C && x > -__builtin_inff() && x < __builtin_inff();
+          const float ex = __builtin_amdgcn_exp2f((x - m) * kTsLog2e);
+          sm += fin ? ex : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(sm, off, kWave);
+        ts_lse_merge(m, sm, m2, s2);
+        ninf += __shfl_xor(ninf, off, kWave);
+      }
+      if (lane == 0) {
+        s.pm[hh][wave] = m;
+        s.ps[hh][wave] = sm;
+        s.pi[hh][wave] = ninf;
+      }
+    }
+    __syncthreads();
+    if (tid < 2) {
+      const int half = 2 * chunk + tid;  // the 16384-token chunk
+      if (half * (kTsChunk / 2) < Tmax) {
+        float M = s.pm[tid][0], S = s.ps[tid][0];
+        int NI = s.pi[tid][0];
+        for (int w = 1; w < kTsWaves; ++w) {
+          ts_lse_merge(M, S, s.pm[tid][w], s.ps[tid][w]);
+          NI += s.pi[tid][w];
+        }
+        uint32_t* p = lse + int64_t(unit) * lse_stride + 3 * half;
+        p[0] = __builtin_bit_cast(uint32_t, M);
+        p[1] = __builtin_bit_cast(uint32_t, S);
+        p[2] = uint32_t(NI);
+      }
     }
   }
 
@@ -411,6 +494,13 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
   const int r_eq = s.req;
 
   // ---- 4. output in token order ----
+  // Thread t owns bitmap words [t wpt, (t + 1) wpt) for the counts: its chosen
+  // bits (taken, plus the ties whose rank among all ties is below r_eq) replace
+  // its taken words and its words' first output positions its tied words. The
+  // tokens are then written word by word with the words dealt out at a stride
+  // of the group size, so a run of chosen tokens (a block of them) is spread
+  // over several threads, into LDS, and leave in dense stores.
+  constexpr int kMaxWpt = kTokSelectMaxTokens / 32 / kTsThreads;
   const int wpt = ceil_div(nwords, kTsThreads);
   const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
   int ngt = 0, neq = 0;
@@ -420,36 +510,59 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
   }
   int sgt = ngt, seq = neq, tot_gt, tot_eq;
   ts_scan2(sgt, seq, s, tot_gt, tot_eq);
-  const int eq_before = seq - neq;
   const int nsel = min(tot_gt + min(tot_eq, r_eq), budget);
-  int opos = (sgt - ngt) + min(eq_before, r_eq);
-  int eq_seen = eq_before;
-  for (int w = w0; w < w1; ++w) {
-    const uint32_t te = s.tied[w];
-    // of this word's ties, the lowest-index (r_eq - eq_seen) are taken
-    uint32_t keep = 0u, x = te;
-    for (int k = r_eq - eq_seen; k > 0 && x; --k) {
-      keep |= x & (0u - x);
-      x &= x - 1u;
+  int eq_seen = seq - neq, nmine = 0;
+  uint32_t selw[kMaxWpt];
+#pragma unroll
+  for (int i = 0; i < kMaxWpt; ++i) {
+    const int w = w0 + i;
+    selw[i] = 0u;
+    if (w < w1) {
+      const uint32_t te = s.tied[w];
+      // of this word's ties, the lowest-index (r_eq - eq_seen) are taken
+      uint32_t keep = 0u, x = te;
+      for (int k = r_eq - eq_seen; k > 0 && x; --k) {
+        keep |= x & (0u - x);
+        x &= x - 1u;
+      }
+      eq_seen += __builtin_popcount(te);
+      selw[i] = s.taken[w] | keep;
+      nmine += __builtin_popcount(selw[i]);
     }
-    eq_seen += __builtin_popcount(te);
-    uint32_t m = s.taken[w] | keep;
+  }
+  int before = nmine, dummy = 0, tot_sel, tot_dummy;
+  ts_scan2(before, dummy, s, tot_sel, tot_dummy);
+  before -= nmine;
+#pragma unroll
+  for (int i = 0; i < kMaxWpt; ++i) {
+    const int w = w0 + i;
+    if (w < w1) {  // only this thread reads or writes its own words here
+      s.taken[w] = selw[i];
+      s.tied[w] = uint32_t(before);
+      before += __builtin_popcount(selw[i]);
+    }
+  }
+  __syncthreads();
+  for (int w = tid; w < nwords; w += kTsThreads) {
+    uint32_t m = s.taken[w];
+    int p = int(s.tied[w]);
     while (m) {
       const int b = __builtin_ctz(m);
       m &= m - 1u;
-      if (opos < budget) out[opos] = 32 * w + b;
-      ++opos;
+      if (p < budget) s.out[p] = 32 * w + b;
+      ++p;
     }
   }
-  for (int k = nsel + tid; k < budget; k += kTsThreads) out[k] = -1;
+  __syncthreads();
+  for (int k = tid; k < budget; k += kTsThreads) out[k] = k < nsel ? s.out[k] : -1;
   if (tid == 0) count[unit] = nsel;
 }
 
 }  // namespace
 
 bool token_select_one_group(const UnitGeom& g, int budget, float top_p) {
-  return top_p <= 0.0f && g.Tmax <= kTokSelectMaxTokens && g.Tmax % 4 == 0 &&
-         budget <= kTokSelectOneMaxBudget;
+  (void)top_p;  // the adaptive budget's partials come with the listing
+  return g.Tmax <= kTokSelectMaxTokens && g.Tmax % 4 == 0 && budget <= kTokSelectOneMaxBudget;
 }
 
 size_t token_select_one_workspace(const UnitGeom& g) {
@@ -458,12 +571,13 @@ size_t token_select_one_workspace(const UnitGeom& g) {
 
 hipError_t launch_select_token_one(const UnitGeom& g, int budget, const float* scores,
                                    const int32_t* seq_lens, void* ws, int32_t* idx,
-                                   int32_t* count, hipStream_t s) {
+                                   int32_t* count, uint32_t* lse, int64_t lse_stride,
+                                   hipStream_t s) {
   // a unit's chunks are units apart in the dispatch order, so with a unit count
   // that is a multiple of 8 they land on one XCD and share its L2
   const dim3 grid(g.B * g.Hkv, ceil_div(g.Tmax, kTsChunk));
   hipLaunchKernelGGL(tok_select_kernel, grid, dim3(kTsThreads), 0, s, scores, seq_lens, g.Hkv,
-                     g.Tmax, budget, static_cast<uint32_t*>(ws), idx, count);
+                     g.Tmax, budget, static_cast<uint32_t*>(ws), idx, count, lse, lse_stride);
   return hipGetLastError();
 }
 

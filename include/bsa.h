@@ -274,10 +274,9 @@ size_t bsa_workspace_size(const bsa_kv_layout* layout, const bsa_select_cfg* cfg
  * when that is 0). TOKEN: zero-fill it before its first use; every call that
  * completes leaves the parts that must start at zero (histograms, arrival
  * counters) zeroed again, so it is reused as is; calls that share it must not
- * run concurrently. Its size depends on the cfg: with
- * top_p = 0, budget <= 2048 and max_tokens <= 131072 (a multiple of 4) the
- * selection runs in one launch and also needs room for a per-unit candidate
- * list. */
+ * run concurrently. Its size depends on the cfg: with budget <= 2048 and
+ * max_tokens <= 131072 (a multiple of 4) the selection runs in one launch
+ * and also needs room for per-unit candidate lists. */
 int bsa_select_topk(const bsa_kv_layout* layout, const bsa_select_cfg* cfg,
                     const float* scores, const int32_t* seq_lens, void* workspace,
                     size_t workspace_bytes, int32_t* idx, int32_t* count, void* stream);

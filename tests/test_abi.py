@@ -128,14 +128,14 @@ def test_workspace_size(lib):
     bad = B.select_cfg(B.BLOCK, 8)
     bad.budget = -1
     assert lib.bsa_workspace_size(ctypes.byref(L), ctypes.byref(bad)) == 0
-    # token mode: budgets up to 2048 without top_p select in one launch, which
+    # token mode: budgets up to 2048 (with or without top_p) select in one launch, which
     # adds a per-unit region (arrival counter, counts, an 8192-entry list per
     # 32768-token chunk)
     L2 = _layout(batch=2, num_kv_heads=3, num_q_heads=6)
     size = lambda budget, top_p=0.0: lib.bsa_workspace_size(
         ctypes.byref(L2), ctypes.byref(B.select_cfg(B.TOKEN, budget, 0, 32, top_p=top_p)))
     assert size(2048) - size(4096) == 6 * (64 + 2 * 8192) * 4
-    assert size(300, top_p=0.5) == size(4096)
+    assert size(300, top_p=0.5) == size(2048)
 
 
 def test_combined_calls_check_their_arguments(lib):

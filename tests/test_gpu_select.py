@@ -62,7 +62,7 @@ def _histograms_back_at_zero(ws, units, T, one_group=False):
     """After a call each unit's histogram in the token workspace is zero again
     (per unit: 4096 histogram words; a slot of 8 + 3 words per 16384-key chunk,
     rounded up to 64; two bitmaps of ceil(T/64)*2 words rounded up to 64).
-    With the one-launch select (budget <= 2048, no top_p, T <= 131072) a
+    With the one-launch select (budget <= 2048, T <= 131072) a
     second region follows, 64 + 2 * 8192 words per unit and 32768-token chunk:
     its arrival counter (word 0) is zero again too."""
     w = ws.view(torch.int32).cpu().numpy()
@@ -237,7 +237,7 @@ def test_token_top_p_matches_oracle(pattern, budget, top_p):
     for rep in range(2):
         bsa.select_topk(layout, cfg, sc, lens, ws, ws_bytes, idx, count)
         torch.cuda.synchronize()
-        _histograms_back_at_zero(ws, B * Hkv, T)
+        _histograms_back_at_zero(ws, B * Hkv, T, one_group=budget <= 2048)
         gi, gc = idx.cpu().numpy(), count.cpu().numpy()
         for b in range(B):
             for h in range(Hkv):
