@@ -14,24 +14,26 @@
 //      expected). With at most kTsCap candidates, T = 0 and every candidate
 //      is listed.
 //   2. Listing. The chunk's keys >= T go to the chunk's list in the workspace
-//      (key, token) with its count, staged in LDS and written with dense
-//      stores.
+//      (key, token) in token order, with its count, staged in LDS and written
+//      with dense stores.
 // The unit's last group to arrive (an arrival counter, as the attention's
 // merge uses) then:
 //   3. finds the exact key kappa of the picks-th largest listed key by a radix
 //      select over the list held in registers (the block select's procedure
 //      over a 1024-thread group), and how many of its ties are taken;
-//   4. sets a bit in an LDS "taken" bitmap of the unit's tokens for each
-//      listed key above kappa, one in a "tied" bitmap for each key equal to
-//      it, and writes the taken tokens and the lowest-index ties ascending in
-//      one pass over the bitmap words (two block scans).
+//   4. writes the listed tokens above kappa and the lowest-index ties in list
+//      order, which is token order: each chosen slot's output position comes
+//      from ballots over runs of 64 slots and one scan of the runs' counts.
 // With the adaptive budget, every group also leaves its two 16384-token
 // halves' softmax partials for tok_topp, which then cuts the selection.
 // If the lists hold fewer than picks or more than kTsCap candidates, or a chunk
 // more than kTsChunkCap (a sample far from the unit's distribution, or many
-// equal keys), steps 3 and 4 run over the unit's scores in memory instead: the
-// same result, with one read of the scores per radix pass. The last group
+// equal keys), steps 3 and 4 run over the unit's scores in memory instead, with
+// one read of the scores per radix pass, marks in LDS bitmaps of the unit's
+// tokens and the output from scans of the bitmap words: the same result. The last group
 // returns the counter to zero, so the workspace is ready for the next call.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace bsa {
@@ -55,14 +57,26 @@ struct TsLds {
   uint32_t tied[kTsStage + kWave];   // staging: their tokens
   uint32_t hist[2][256];
   uint32_t wlo[kTsWaves], whi[kTsWaves];
-  int wtot[kTsWaves], wtot2[kTsWaves];
+  int wtot[4][kTsWaves];
+  uint32_t slots[kTsPer * kTsWaves];  // per 64 list slots: chosen counts, then their bases
   int32_t out[kTokSelectOneMaxBudget];     // the selection, in order
   float pm[2][kTsWaves], ps[2][kTsWaves];  // the softmax partials' per-wave parts
   int pi[2][kTsWaves];
-  int ncand, beta, above, inb, req, is_last;
+  int ncand, beta, above, inb, is_last;
 };
 
 constexpr float kTsLog2e = 1.4426950408889634f;
+
+// For a key T > 0: the float f with key(x) >= T exactly when x >= f (x not
+// NaN; NaN has key 0 and fails every compare). Keys up to that of -inf admit
+// every number; above them a negative key is the complement of the float's
+// bits and a positive one the float's bits with the sign bit set, and a key
+// past +inf's gives a NaN, which admits nothing. The -0 and +0 share a key
+// and compare equal, so either bound serves for them.
+__device__ __forceinline__ float ts_key_floor(uint32_t T) {
+  if (T <= 0x007FFFFFu) return -__builtin_inff();
+  return __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
+}
 
 // (m, s) <- the log-sum-exp merge of (m, s) and (m2, s2): s a sum of exp(x - m)
 // (the exponentials by the hardware exp2: the shares they feed decide a count
@@ -78,36 +92,38 @@ __device__ __forceinline__ void ts_lse_merge(float& m, float& s, float m2, float
   m = mx;
 }
 
-// Inclusive scans of two ints per thread over the work-group; tv, tw: totals.
-__device__ __forceinline__ void ts_scan2(int& v, int& w, TsLds& s, int& tv, int& tw) {
+// Inclusive scans of N ints per thread over the work-group (thread order);
+// t: the totals.
+template <int N>
+__device__ __forceinline__ void ts_scan(int (&v)[N], int (&t)[N], TsLds& s) {
+  static_assert(N <= 4, "scan width");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const int nv = __shfl_up(v, off, kWave), nw = __shfl_up(w, off, kWave);
-    if (lane >= off) {
-      v += nv;
-      w += nw;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int x = __shfl_up(v[n], off, kWave);
+      if (lane >= off) v[n] += x;
     }
   }
-  if (lane == kWave - 1) {
-    s.wtot[wave] = v;
-    s.wtot2[wave] = w;
-  }
-  __syncthreads();
-  int bv = 0, bw = 0;
-  tv = 0;
-  tw = 0;
+  if (lane == kWave - 1)
 #pragma unroll
-  for (int k = 0; k < kTsWaves; ++k) {
-    const int xv = s.wtot[k], xw = s.wtot2[k];
-    bv += k < wave ? xv : 0;
-    bw += k < wave ? xw : 0;
-    tv += xv;
-    tw += xw;
+    for (int n = 0; n < N; ++n) s.wtot[n][wave] = v[n];
+  __syncthreads();
+  // lane k < kTsWaves takes wave k's total: a scan over those lanes
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    int x = lane < kTsWaves ? s.wtot[n][lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kTsWaves; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    t[n] = __shfl(x, kTsWaves - 1, kWave);
+    const int before = __shfl(x, wave > 0 ? wave - 1 : 0, kWave);
+    v[n] += wave > 0 ? before : 0;
   }
   __syncthreads();
-  v += bv;
-  w += bw;
 }
 
 // What a radix select decided: keys > kgt are taken, and r_eq of the keys
@@ -166,10 +182,23 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
     uint32_t* cur = s.hist[pass & 1];
     uint32_t* nxt = s.hist[(pass & 1) ^ 1];
     if (tid < 256) nxt[tid] = 0;  // its last reader finished before the last barrier
+    // a thread adds a run of its keys that share a bin with one atomic: where
+    // the keys crowd into few bins (candidates just above the threshold
+    // below a few far larger ones), same-address lanes of one LDS atomic are
+    // served one at a time
+    uint32_t run_bin = 0u, run_n = 0u;
     for_each_key([&](uint32_t key) {
-      if (hi == 32 || (key >> hi) == prefix)
-        atomicAdd(&cur[(key >> shift) & ((1u << width) - 1u)], 1u);
+      if (hi == 32 || (key >> hi) == prefix) {
+        const uint32_t bin = (key >> shift) & ((1u << width) - 1u);
+        if (run_n && bin != run_bin) {
+          atomicAdd(&cur[run_bin], run_n);
+          run_n = 0u;
+        }
+        run_bin = bin;
+        ++run_n;
+      }
     });
+    if (run_n) atomicAdd(&cur[run_bin], run_n);
     __syncthreads();
     if (wave == 0) {
       // lane l takes bins 255 - 4 l .. 252 - 4 l (descending)
@@ -281,6 +310,8 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     v[b] = *reinterpret_cast<const float4v*>(row + 4 * int64_t(q));
   }
 
+  const bool whole_chunk = (chunk + 1) * kTsChunk <= C;  // no token of the chunk at or past C
+
   // ---- 1. threshold ----
   uint32_t T = 0u;
   if (C > kTsCap) {
@@ -299,44 +330,49 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
 
   if (lse) {  // the half-chunks' softmax partials (uniform branch)
     static_assert(kQ % 2 == 0, "two halves");
+    auto partials = [&](auto whole) {  // whole: every token of the chunk is below C
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float m = -__builtin_inff(), sm = 0.0f;
-      int ninf = 0;
+      for (int hh = 0; hh < 2; ++hh) {
+        float m = -__builtin_inff(), sm = 0.0f;
+        int ninf = 0;
 #pragma unroll
-      for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
-        const int q = qb + tid + kTsThreads * b;
+        for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
+          const int q = qb + tid + kTsThreads * b;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = v[b][e];
-          const bool in = q < nq && 4 * q + e < C;
-          ninf += (in && x == __builtin_inff()) ? 1 : 0;
-          m = (in && x < __builtin_inff()) ? fmaxf(m, x) : m;  // fmaxf drops NaN
+          for (int e = 0; e < 4; ++e) {
+            const float x = v[b][e];
+            const bool in = decltype(whole)::value || (q < nq && 4 * q + e < C);
+            ninf += (in && x == __builtin_inff()) ? 1 : 0;
+            m = (in && x < __builtin_inff()) ? fmaxf(m, x) : m;  // fmaxf drops NaN
+          }
+        }
+#pragma unroll
+        for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
+          const int q = qb + tid + kTsThreads * b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = v[b][e];
+            const bool in = decltype(whole)::value || (q < nq && 4 * q + e < C);
+            const bool fin = in && x > -__builtin_inff() && x < __builtin_inff();
+            const float ex = __builtin_amdgcn_exp2f((x - m) * kTsLog2e);
+            sm += fin ? ex : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(sm, off, kWave);
+          ts_lse_merge(m, sm, m2, s2);
+          ninf += __shfl_xor(ninf, off, kWave);
+        }
+        if (lane == 0) {
+          s.pm[hh][wave] = m;
+          s.ps[hh][wave] = sm;
+          s.pi[hh][wave] = ninf;
         }
       }
-#pragma unroll
-      for (int b = hh * kQ / 2; b < (hh + 1) * kQ / 2; ++b) {
-        const int q = qb + tid + kTsThreads * b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = v[b][e];
-          const bool fin = q < nq && 4 * q + e < C && x > -__builtin_inff() && x < __builtin_inff();
-          const float ex = __builtin_amdgcn_exp2f((x - m) * kTsLog2e);
-          sm += fin ? ex : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(sm, off, kWave);
-        ts_lse_merge(m, sm, m2, s2);
-        ninf += __shfl_xor(ninf, off, kWave);
-      }
-      if (lane == 0) {
-        s.pm[hh][wave] = m;
-        s.ps[hh][wave] = sm;
-        s.pi[hh][wave] = ninf;
-      }
-    }
+    };
+    if (whole_chunk) partials(std::true_type{});
+    else partials(std::false_type{});
     __syncthreads();
     if (tid < 2) {
       const int half = 2 * chunk + tid;  // the 16384-token chunk
@@ -355,28 +391,50 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     }
   }
 
-  // ---- 2. listing: this chunk's keys >= T ----
-  int mine = 0;
+  // ---- 2. listing: this chunk's keys >= T, in token order ----
+  // Piece b of thread t holds tokens 4 (qb + t + kTsThreads b) .. + 3, so the
+  // list runs piece by piece, thread by thread. A thread's count per piece (at
+  // most 4) is scanned over the group two pieces to an int: a piece's total
+  // stays below 2^16.
+  static_assert(kQ * 4 == 32, "a candidate mask of 32 bits");
+  uint32_t cm = 0u;  // bit 4 b + e: value e of piece b is a candidate
+  // key(x) >= T as one float compare: x >= Tf for T > 0 (false for NaN)
+  const float Tf = ts_key_floor(T);
+  auto mark_candidates = [&](auto whole) {  // whole: every token of the chunk is below C
 #pragma unroll
-  for (int b = 0; b < kQ; ++b) {
-    const int q = qb + tid + kTsThreads * b;
+    for (int b = 0; b < kQ; ++b) {
+      const int q = qb + tid + kTsThreads * b;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) mine += (q < nq && 4 * q + e < C && score_key(v[b][e]) >= T);
+      for (int e = 0; e < 4; ++e) {
+        const bool in = decltype(whole)::value || (q < nq && 4 * q + e < C);
+        cm |= uint32_t(in && (T == 0u || v[b][e] >= Tf)) << (4 * b + e);
+      }
+    }
+  };
+  if (whole_chunk) mark_candidates(std::true_type{});
+  else mark_candidates(std::false_type{});
+  int pc[kQ / 2], incl[kQ / 2], tpc[kQ / 2];
+#pragma unroll
+  for (int hh = 0; hh < kQ / 2; ++hh)
+    pc[hh] = __builtin_popcount((cm >> (8 * hh)) & 0xFu) +
+             (__builtin_popcount((cm >> (8 * hh + 4)) & 0xFu) << 16);
+#pragma unroll
+  for (int hh = 0; hh < kQ / 2; ++hh) incl[hh] = pc[hh];
+  ts_scan(incl, tpc, s);
+  int tot = 0;
+#pragma unroll
+  for (int hh = 0; hh < kQ / 2; ++hh) {
+    incl[hh] -= pc[hh];  // exclusive: the thread's slots in pieces 2 hh, 2 hh + 1
+    tpc[hh] = __builtin_amdgcn_readfirstlane(tpc[hh]);
+    tot += (tpc[hh] & 0xFFFF) + (tpc[hh] >> 16);
   }
-  int incl = mine;
+  // this thread's first slot in piece b's run of the list
+  auto first_slot = [&](int b) {
+    int a = 0;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int n = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += n;
-  }
-  if (lane == kWave - 1) s.wtot[wave] = incl;
-  __syncthreads();
-  int tot = 0, lpos = incl - mine;  // the group's total; this lane's first slot in the group
-#pragma unroll
-  for (int k = 0; k < kTsWaves; ++k) {
-    tot += s.wtot[k];
-    lpos += k < wave ? s.wtot[k] : 0;
-  }
+    for (int k = 0; k < b; ++k) a += (tpc[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
+    return a + ((incl[b >> 1] >> (16 * (b & 1))) & 0xFFFF);
+  };
   uint32_t* lk = uw + kTsListWord + int64_t(chunk) * 2 * kTsChunkCap;  // keys, then tokens
   if (tid == 0) store_coherent(reinterpret_cast<int32_t*>(uw + kTsCountWord + chunk), tot);
   if (tot <= kTsStage) {  // the same in every thread
@@ -385,14 +443,15 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
 #pragma unroll
     for (int b = 0; b < kQ; ++b) {
       const int q = qb + tid + kTsThreads * b;
+      int at = first_slot(b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = score_key(v[b][e]);
-        const bool c = q < nq && 4 * q + e < C && key >= T;
-        const int at = c ? lpos : kTsStage + lane;
-        s.taken[at] = key;
-        s.tied[at] = uint32_t(4 * q + e);
-        lpos += c;
+        const bool c = (cm >> (4 * b + e)) & 1u;
+        const int a = c ? at : kTsStage + lane;
+        s.taken[a] = key;
+        s.tied[a] = uint32_t(4 * q + e);
+        at += c;
       }
     }
     __syncthreads();
@@ -404,45 +463,54 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
 #pragma unroll
     for (int b = 0; b < kQ; ++b) {
       const int q = qb + tid + kTsThreads * b;
+      int at = first_slot(b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = score_key(v[b][e]);
-        if (q < nq && 4 * q + e < C && key >= T) {
-          if (lpos < kTsChunkCap) {
-            store_coherent(reinterpret_cast<int32_t*>(lk + lpos), int32_t(key));
-            store_coherent(reinterpret_cast<int32_t*>(lk + kTsChunkCap + lpos), 4 * q + e);
+        if ((cm >> (4 * b + e)) & 1u) {
+          if (at < kTsChunkCap) {
+            store_coherent(reinterpret_cast<int32_t*>(lk + at), int32_t(key));
+            store_coherent(reinterpret_cast<int32_t*>(lk + kTsChunkCap + at), 4 * q + e);
           }
-          ++lpos;
+          ++at;
         }
       }
     }
   }
   if (!last_group_of_unit(uw + kTsCounterWord, 0, gridDim.y, &s.is_last)) return;
 
-  // ---- the unit's last group: 3. exact boundary, and the bitmaps ----
+  // ---- the unit's last group: 3. exact boundary ----
   // the chunks' counts; candidate i is in chunk k where pre[k] <= i < pre[k + 1]
   const int chunks = gridDim.y;
   int pre[kTsMaxChunks + 1];
   bool over = false;
   pre[0] = 0;
+  int cnt[kTsMaxChunks];  // every word of the counts' line is loaded at once
+#pragma unroll
+  for (int k = 0; k < kTsMaxChunks; ++k)
+    cnt[k] = load_coherent(reinterpret_cast<const int32_t*>(uw + kTsCountWord + k));
 #pragma unroll
   for (int k = 0; k < kTsMaxChunks; ++k) {
-    const int ck = k < chunks ? load_coherent(reinterpret_cast<const int32_t*>(uw + kTsCountWord + k))
-                              : 0;
+    const int ck = k < chunks ? cnt[k] : 0;
     over = over || ck > kTsChunkCap;
     pre[k + 1] = pre[k] + ck;
   }
   const int nc = pre[kTsMaxChunks];
-  const int nwords = ceil_div(C, 32);
-  for (int w = tid; w < nwords; w += kTsThreads) {
-    s.taken[w] = 0u;
-    s.tied[w] = 0u;
-  }
   if (!over && nc >= picks && nc <= kTsCap) {
+    // slot i = tid + kTsThreads j; from j = jn on no thread holds a candidate,
+    // and every loop over j stops there (the group is bound by issue: its
+    // per-slot instructions run once per wave)
+    const int jn = ceil_div(nc, kTsThreads);
     uint32_t ck[kTsPer];
     int ct[kTsPer];
 #pragma unroll
     for (int j = 0; j < kTsPer; ++j) {
+      ck[j] = 0u;
+      ct[j] = -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kTsPer; ++j) {
+      if (j >= jn) continue;
       const int i = tid + kTsThreads * j;
       int k = 0;
 #pragma unroll
@@ -452,46 +520,115 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
       ck[j] = uint32_t(load_coherent(reinterpret_cast<const int32_t*>(l + off)));
       ct[j] = load_coherent(reinterpret_cast<const int32_t*>(l + kTsChunkCap + off));
     }
-#pragma unroll
-    for (int j = 0; j < kTsPer; ++j)
-      if (tid + kTsThreads * j >= nc) ct[j] = -1;
-    __syncthreads();  // the bitmaps are clear
-    const TsCut cut = ts_radix(picks, [&](auto&& f) {
+    if (jn > 0) {  // only the last occupied j has slots past the list (all loads issued first)
 #pragma unroll
       for (int j = 0; j < kTsPer; ++j)
-        if (ct[j] >= 0) f(ck[j]);
-    }, s);
-#pragma unroll
-    for (int j = 0; j < kTsPer; ++j)
-      if (ct[j] >= 0) ts_mark(cut, ck[j], ct[j], s);
-    s.req = cut.r_eq;  // the same in every thread; read after the barrier below
-  } else {
-    __syncthreads();  // the bitmaps are clear
-    // the unit's scores in memory, 16-byte pieces, kTsBatch loads at a time
-    auto each_global = [&](auto&& f) {
-      for (int q0 = 0; q0 < nq; q0 += kTsThreads * kTsBatch) {
-        float4v x[kTsBatch];
-#pragma unroll
-        for (int b = 0; b < kTsBatch; ++b)
-          x[b] = *reinterpret_cast<const float4v*>(
-              row + 4 * int64_t(min(q0 + tid + kTsThreads * b, nq - 1)));
-#pragma unroll
-        for (int b = 0; b < kTsBatch; ++b) {
-          const int q = q0 + tid + kTsThreads * b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (q < nq && 4 * q + e < C) f(score_key(x[b][e]), 4 * q + e);
-        }
-      }
-    };
+        if (j == jn - 1 && tid + kTsThreads * j >= nc) ct[j] = -1;
+    }
     const TsCut cut = ts_radix(picks, [&](auto&& f) {
-      each_global([&](uint32_t key, int) { f(key); });
+#pragma unroll
+      for (int j = 0; j < kTsPer; ++j) {
+        if (j >= jn) continue;
+        if (ct[j] >= 0) f(ck[j]);
+      }
     }, s);
-    each_global([&](uint32_t key, int t) { ts_mark(cut, key, t, s); });
-    s.req = cut.r_eq;
+
+    // ---- 4. output: the chosen slots in slot order, which is token order ----
+    // Chosen: the keys above the cut, and the ties whose rank among the ties
+    // is below r_eq. Slot i = kTsThreads j + 64 wave + lane, so one ballot
+    // counts a run of 64 slots; wave 0 scans the runs' counts (taken and
+    // tied, two 16-bit fields) into their bases, and a chosen slot's output
+    // position is the taken slots before it plus min(ties before it, r_eq).
+    auto chosen = [&](int j, bool& gt, bool& eq) {
+      gt = ct[j] >= 0 && (cut.ge ? ck[j] >= cut.kge : ck[j] > cut.kgt);
+      eq = ct[j] >= 0 && !cut.ge && ck[j] == cut.keq;
+    };
+#pragma unroll
+    for (int j = 0; j < kTsPer; ++j) {
+      if (j >= jn) continue;
+      bool gt, eq;
+      chosen(j, gt, eq);
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      if (lane == 0) s.slots[j * kTsWaves + wave] = uint32_t(__popcll(mg)) | uint32_t(__popcll(me)) << 16;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      static_assert(kTsPer * kTsWaves == 4 * kWave, "four runs per lane");
+      uint32_t c[4], x = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = 4 * lane + i < kTsWaves * jn ? s.slots[4 * lane + i] : 0u;
+        x += c[i];  // each field stays below 2^16: at most kTsCap slots
+      }
+      uint32_t inc = x;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t n = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += n;
+      }
+      uint32_t base = inc - x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s.slots[4 * lane + i] = base;
+        base += c[i];
+      }
+      if (lane == kWave - 1) s.ncand = int(inc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTsPer; ++j) {
+      if (j >= jn) continue;
+      bool gt, eq;
+      chosen(j, gt, eq);
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t base = s.slots[j * kTsWaves + wave];
+      const int pg = int(base & 0xFFFFu) +
+                     int(__builtin_amdgcn_mbcnt_hi(uint32_t(mg >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(uint32_t(mg), 0u)));
+      const int pe = int(base >> 16) +
+                     int(__builtin_amdgcn_mbcnt_hi(uint32_t(me >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(uint32_t(me), 0u)));
+      const int p = gt ? pg + min(pe, cut.r_eq) : (eq && pe < cut.r_eq ? pg + pe : budget);
+      if (p < budget) s.out[p] = ct[j];
+    }
+    const uint32_t tsel = uint32_t(s.ncand);
+    const int nsel = min(int(tsel & 0xFFFFu) + min(int(tsel >> 16), cut.r_eq), budget);
+    __syncthreads();
+    for (int k = tid; k < budget; k += kTsThreads) out[k] = k < nsel ? s.out[k] : -1;
+    if (tid == 0) count[unit] = nsel;
+    return;
   }
+
+  // ---- the fallback: marks in bitmaps of the unit's tokens ----
+  const int nwords = ceil_div(C, 32);
+  for (int w = tid; w < nwords; w += kTsThreads) {
+    s.taken[w] = 0u;
+    s.tied[w] = 0u;
+  }
+  __syncthreads();  // the bitmaps are clear
+  // the unit's scores in memory, 16-byte pieces, kTsBatch loads at a time
+  auto each_global = [&](auto&& f) {
+    for (int q0 = 0; q0 < nq; q0 += kTsThreads * kTsBatch) {
+      float4v x[kTsBatch];
+#pragma unroll
+      for (int b = 0; b < kTsBatch; ++b)
+        x[b] = *reinterpret_cast<const float4v*>(
+            row + 4 * int64_t(min(q0 + tid + kTsThreads * b, nq - 1)));
+#pragma unroll
+      for (int b = 0; b < kTsBatch; ++b) {
+        const int q = q0 + tid + kTsThreads * b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (q < nq && 4 * q + e < C) f(score_key(x[b][e]), 4 * q + e);
+      }
+    }
+  };
+  const TsCut cut = ts_radix(picks, [&](auto&& f) {
+    each_global([&](uint32_t key, int) { f(key); });
+  }, s);
+  each_global([&](uint32_t key, int t) { ts_mark(cut, key, t, s); });
   __syncthreads();
-  const int r_eq = s.req;
+  const int r_eq = cut.r_eq;
 
   // ---- 4. output in token order ----
   // Thread t owns bitmap words [t wpt, (t + 1) wpt) for the counts: its chosen
@@ -508,10 +645,10 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     ngt += __builtin_popcount(s.taken[w]);
     neq += __builtin_popcount(s.tied[w]);
   }
-  int sgt = ngt, seq = neq, tot_gt, tot_eq;
-  ts_scan2(sgt, seq, s, tot_gt, tot_eq);
-  const int nsel = min(tot_gt + min(tot_eq, r_eq), budget);
-  int eq_seen = seq - neq, nmine = 0;
+  int sc[2] = {ngt, neq}, st[2];
+  ts_scan(sc, st, s);
+  const int nsel = min(st[0] + min(st[1], r_eq), budget);
+  int eq_seen = sc[1] - neq, nmine = 0;
   uint32_t selw[kMaxWpt];
 #pragma unroll
   for (int i = 0; i < kMaxWpt; ++i) {
@@ -530,9 +667,9 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
       nmine += __builtin_popcount(selw[i]);
     }
   }
-  int before = nmine, dummy = 0, tot_sel, tot_dummy;
-  ts_scan2(before, dummy, s, tot_sel, tot_dummy);
-  before -= nmine;
+  int sb[1] = {nmine}, stot[1];
+  ts_scan(sb, stot, s);
+  int before = sb[0] - nmine;
 #pragma unroll
   for (int i = 0; i < kMaxWpt; ++i) {
     const int w = w0 + i;
