@@ -14,8 +14,8 @@
 //      expected). With at most kTsCap candidates, T = 0 and every candidate
 //      is listed.
 //   2. Listing. The chunk's keys >= T go to the chunk's list in the workspace
-//      (key, token) in token order, with its count, staged in LDS and written
-//      with dense stores.
+//      (the score's bits, token) in token order, with its count, staged in
+//      LDS and written with dense stores.
 // The unit's last group to arrive (an arrival counter, as the attention's
 // merge uses) then:
 //   3. finds the exact key kappa of the picks-th largest listed key by a radix
@@ -47,13 +47,13 @@ constexpr int kTsPer = kTsCap / kTsThreads;
 constexpr int kTsBatch = 8;      // 16-byte loads in flight per thread (fallback passes)
 constexpr int kTsChunk = 32768;  // tokens listed per work-group
 
-// A group's listed keys and tokens are staged in the bitmaps' words (used only
+// A group's listed scores and tokens are staged in the bitmaps' words (used only
 // by the unit's last group, after every group has stored its list), so the
 // global list is written with dense stores.
 constexpr int kTsStage = kTokSelectMaxTokens / 32;
 
 struct TsLds {
-  uint32_t taken[kTsStage + kWave];  // staging: the keys (and a dropped slot per lane)
+  uint32_t taken[kTsStage + kWave];  // staging: the scores' bits (and a dropped slot per lane)
   uint32_t tied[kTsStage + kWave];   // staging: their tokens
   uint32_t hist[2][256];
   uint32_t wlo[kTsWaves], whi[kTsWaves];
@@ -78,6 +78,48 @@ __device__ __forceinline__ float ts_key_floor(uint32_t T) {
   return __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
 }
 
+// Wave-wide scans and reductions with DPP moves (ALU lane exchanges, no LDS
+// round trip): four row shifts combine the lanes of each 16-lane row, then
+// lane 15 of rows 0 and 2 is broadcast into rows 1 and 3, and lane 31 into
+// rows 2 and 3. A lane whose source lies outside its row keeps `old`.
+constexpr int kDppRowShr = 0x110;      // + n: lane i takes lane i - n of its row
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row into the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+template <int CTRL, int ROWS>
+using TsDpp = std::integral_constant<int, CTRL | ROWS << 16>;  // a step: control, rows written
+template <class Step>
+__device__ __forceinline__ int ts_dpp(int old, int x, Step) {
+  return __builtin_amdgcn_update_dpp(old, x, Step::value & 0xFFFF, Step::value >> 16, 0xF, false);
+}
+template <class Op>
+__device__ __forceinline__ void ts_wave_steps(Op&& op) {
+  op(TsDpp<kDppRowShr + 1, 0xF>{});
+  op(TsDpp<kDppRowShr + 2, 0xF>{});
+  op(TsDpp<kDppRowShr + 4, 0xF>{});
+  op(TsDpp<kDppRowShr + 8, 0xF>{});
+  op(TsDpp<kDppRowBcast15, 0xA>{});
+  op(TsDpp<kDppRowBcast31, 0xC>{});
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int ts_wave_scan(int x) {
+  ts_wave_steps([&](auto step) { x += ts_dpp(0, x, step); });
+  return x;
+}
+
+// The wave's minimum and maximum (the same in every lane).
+__device__ __forceinline__ void ts_wave_minmax(uint32_t& lo, uint32_t& hi) {
+  ts_wave_steps([&](auto step) {
+    const uint32_t l = uint32_t(ts_dpp(int(lo), int(lo), step));
+    const uint32_t h = uint32_t(ts_dpp(int(hi), int(hi), step));
+    lo = l < lo ? l : lo;
+    hi = h > hi ? h : hi;
+  });
+  lo = uint32_t(__builtin_amdgcn_readlane(int(lo), kWave - 1));
+  hi = uint32_t(__builtin_amdgcn_readlane(int(hi), kWave - 1));
+}
+
 // (m, s) <- the log-sum-exp merge of (m, s) and (m2, s2): s a sum of exp(x - m)
 // (the exponentials by the hardware exp2: the shares they feed decide a count
 // within a tolerance of 1e-4, far above its few-ulp error)
@@ -97,15 +139,10 @@ __device__ __forceinline__ void ts_lse_merge(float& m, float& s, float m2, float
 template <int N>
 __device__ __forceinline__ void ts_scan(int (&v)[N], int (&t)[N], TsLds& s) {
   static_assert(N <= 4, "scan width");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const int x = __shfl_up(v[n], off, kWave);
-      if (lane >= off) v[n] += x;
-    }
-  }
+  for (int n = 0; n < N; ++n) v[n] = ts_wave_scan(v[n]);
   if (lane == kWave - 1)
 #pragma unroll
     for (int n = 0; n < N; ++n) s.wtot[n][wave] = v[n];
@@ -113,15 +150,9 @@ __device__ __forceinline__ void ts_scan(int (&v)[N], int (&t)[N], TsLds& s) {
   // lane k < kTsWaves takes wave k's total: a scan over those lanes
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    int x = lane < kTsWaves ? s.wtot[n][lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kTsWaves; off <<= 1) {
-      const int y = __shfl_up(x, off, kWave);
-      if (lane >= off) x += y;
-    }
-    t[n] = __shfl(x, kTsWaves - 1, kWave);
-    const int before = __shfl(x, wave > 0 ? wave - 1 : 0, kWave);
-    v[n] += wave > 0 ? before : 0;
+    const int x = ts_wave_scan(lane < kTsWaves ? s.wtot[n][lane] : 0);
+    t[n] = __builtin_amdgcn_readlane(x, kTsWaves - 1);
+    v[n] += wave > 0 ? __builtin_amdgcn_readlane(x, wave > 0 ? wave - 1 : 0) : 0;
   }
   __syncthreads();
 }
@@ -146,24 +177,16 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
     klo = key < klo ? key : klo;
     khi = key > khi ? key : khi;
   });
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t ol = uint32_t(__shfl_xor(int(klo), off, kWave));
-    const uint32_t oh = uint32_t(__shfl_xor(int(khi), off, kWave));
-    klo = ol < klo ? ol : klo;
-    khi = oh > khi ? oh : khi;
-  }
+  ts_wave_minmax(klo, khi);
   if (lane == 0) {
     s.wlo[wave] = klo;
     s.whi[wave] = khi;
   }
   if (tid < 256) s.hist[0][tid] = 0;
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kTsWaves; ++k) {
-    klo = s.wlo[k] < klo ? s.wlo[k] : klo;
-    khi = s.whi[k] > khi ? s.whi[k] : khi;
-  }
+  klo = lane < kTsWaves ? s.wlo[lane] : 0xFFFFFFFFu;  // lane k: wave k's
+  khi = lane < kTsWaves ? s.whi[lane] : 0u;
+  ts_wave_minmax(klo, khi);
   const uint32_t diff = klo ^ khi;
   int hi = diff ? 32 - __builtin_clz(diff) : 0;  // bits [hi, 32) are common
   uint32_t prefix = hi < 32 ? khi >> hi : 0u;
@@ -214,13 +237,7 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
         run += int(cur[255 - 4 * lane - i]);
         c[i] = run;
       }
-      int incl = run;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int n = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += n;
-      }
-      const int P = incl - run;
+      const int P = ts_wave_scan(run) - run;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int above = P + (i ? c[i - 1] : 0), ge = P + c[i];
@@ -255,8 +272,8 @@ __device__ __forceinline__ void ts_mark(const TsCut& cut, uint32_t key, int t, T
 
 // The unit's words in the one-launch region of the token workspace: the
 // arrival counter, the chunks' candidate counts (each on its own 128-byte
-// line), then per chunk a list of up to kTsChunkCap candidates (keys, then
-// tokens).
+// line), then per chunk a list of up to kTsChunkCap candidates (score bits,
+// then tokens).
 constexpr int kTsChunkCap = 8192;
 constexpr int kTsCounterWord = 0, kTsCountWord = 32, kTsListWord = 64;
 constexpr int kTsMaxChunks = kTokSelectMaxTokens / kTsChunk;
@@ -358,13 +375,14 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
             sm += fin ? ex : 0.0f;
           }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(sm, off, kWave);
+        // the wave's merge in lane 63 (an empty partner is (-inf, 0))
+        ts_wave_steps([&](auto step) {
+          const float m2 = __int_as_float(ts_dpp(__float_as_int(-__builtin_inff()), __float_as_int(m), step));
+          const float s2 = __int_as_float(ts_dpp(0, __float_as_int(sm), step));
           ts_lse_merge(m, sm, m2, s2);
-          ninf += __shfl_xor(ninf, off, kWave);
-        }
-        if (lane == 0) {
+          ninf += ts_dpp(0, ninf, step);
+        });
+        if (lane == kWave - 1) {
           s.pm[hh][wave] = m;
           s.ps[hh][wave] = sm;
           s.pi[hh][wave] = ninf;
@@ -435,7 +453,7 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     for (int k = 0; k < b; ++k) a += (tpc[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
     return a + ((incl[b >> 1] >> (16 * (b & 1))) & 0xFFFF);
   };
-  uint32_t* lk = uw + kTsListWord + int64_t(chunk) * 2 * kTsChunkCap;  // keys, then tokens
+  uint32_t* lk = uw + kTsListWord + int64_t(chunk) * 2 * kTsChunkCap;  // scores, then tokens
   if (tid == 0) store_coherent(reinterpret_cast<int32_t*>(uw + kTsCountWord + chunk), tot);
   if (tot <= kTsStage) {  // the same in every thread
     // staged in LDS without branches (a lane's non-candidates go to a slot of
@@ -446,10 +464,9 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
       int at = first_slot(b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = score_key(v[b][e]);
         const bool c = (cm >> (4 * b + e)) & 1u;
         const int a = c ? at : kTsStage + lane;
-        s.taken[a] = key;
+        s.taken[a] = __float_as_uint(v[b][e]);
         s.tied[a] = uint32_t(4 * q + e);
         at += c;
       }
@@ -466,10 +483,9 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
       int at = first_slot(b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = score_key(v[b][e]);
         if ((cm >> (4 * b + e)) & 1u) {
           if (at < kTsChunkCap) {
-            store_coherent(reinterpret_cast<int32_t*>(lk + at), int32_t(key));
+            store_coherent(reinterpret_cast<int32_t*>(lk + at), __float_as_int(v[b][e]));
             store_coherent(reinterpret_cast<int32_t*>(lk + kTsChunkCap + at), 4 * q + e);
           }
           ++at;
@@ -520,10 +536,11 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
       ck[j] = uint32_t(load_coherent(reinterpret_cast<const int32_t*>(l + off)));
       ct[j] = load_coherent(reinterpret_cast<const int32_t*>(l + kTsChunkCap + off));
     }
-    if (jn > 0) {  // only the last occupied j has slots past the list (all loads issued first)
 #pragma unroll
-      for (int j = 0; j < kTsPer; ++j)
-        if (j == jn - 1 && tid + kTsThreads * j >= nc) ct[j] = -1;
+    for (int j = 0; j < kTsPer; ++j) {  // after every load is issued
+      if (j >= jn) continue;
+      ck[j] = score_key(__uint_as_float(ck[j]));  // the lists hold the scores' bits
+      if (j == jn - 1 && tid + kTsThreads * j >= nc) ct[j] = -1;  // past the list
     }
     const TsCut cut = ts_radix(picks, [&](auto&& f) {
 #pragma unroll
@@ -539,15 +556,14 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
     // counts a run of 64 slots; wave 0 scans the runs' counts (taken and
     // tied, two 16-bit fields) into their bases, and a chosen slot's output
     // position is the taken slots before it plus min(ties before it, r_eq).
-    auto chosen = [&](int j, bool& gt, bool& eq) {
-      gt = ct[j] >= 0 && (cut.ge ? ck[j] >= cut.kge : ck[j] > cut.kgt);
-      eq = ct[j] >= 0 && !cut.ge && ck[j] == cut.keq;
-    };
+    uint32_t fgt = 0u, feq = 0u;  // bit j: slot j is above the cut, is a tie
 #pragma unroll
     for (int j = 0; j < kTsPer; ++j) {
       if (j >= jn) continue;
-      bool gt, eq;
-      chosen(j, gt, eq);
+      const bool gt = ct[j] >= 0 && (cut.ge ? ck[j] >= cut.kge : ck[j] > cut.kgt);
+      const bool eq = ct[j] >= 0 && !cut.ge && ck[j] == cut.keq;
+      fgt |= uint32_t(gt) << j;
+      feq |= uint32_t(eq) << j;
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
       if (lane == 0) s.slots[j * kTsWaves + wave] = uint32_t(__popcll(mg)) | uint32_t(__popcll(me)) << 16;
     }
@@ -560,12 +576,7 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
         c[i] = 4 * lane + i < kTsWaves * jn ? s.slots[4 * lane + i] : 0u;
         x += c[i];  // each field stays below 2^16: at most kTsCap slots
       }
-      uint32_t inc = x;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t n = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += n;
-      }
+      const uint32_t inc = uint32_t(ts_wave_scan(int(x)));
       uint32_t base = inc - x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -578,8 +589,7 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
 #pragma unroll
     for (int j = 0; j < kTsPer; ++j) {
       if (j >= jn) continue;
-      bool gt, eq;
-      chosen(j, gt, eq);
+      const bool gt = (fgt >> j) & 1u, eq = (feq >> j) & 1u;
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
       const uint32_t base = s.slots[j * kTsWaves + wave];
       const int pg = int(base & 0xFFFFu) +
