@@ -46,6 +46,35 @@ __global__ __launch_bounds__(256) void probe_vgpr_kernel(const uint8_t* __restri
   if (acc == kProbeMagic) sink[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Short tiles at scattered offsets (the token-mode attention's selected 256-byte
+// key and value rows): P = tile_bytes / 16 threads read one tile, one 16-byte
+// piece each (P divides 256), so the work-group covers 256 / P tiles per step,
+// UNROLL steps in flight per thread.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void probe_rows_kernel(const uint8_t* __restrict__ buf,
+                                                         const int64_t* __restrict__ tile_off,
+                                                         int64_t tile_bytes, int tiles_per_wg,
+                                                         int64_t n_tiles, uint32_t* sink) {
+  const int P = int(tile_bytes / 16);
+  const int per_step = 256 / P;
+  const int piece = threadIdx.x % P;
+  uint32_t acc = 0;
+  const int64_t t0 = int64_t(blockIdx.x) * tiles_per_wg;
+  const int64_t t1 = min(t0 + tiles_per_wg, n_tiles);
+  for (int64_t t = t0 + threadIdx.x / P; t < t1; t += int64_t(per_step) * UNROLL) {
+    uint4v x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t tt = t + int64_t(per_step) * u < t1 ? t + int64_t(per_step) * u : t;
+      const uint8_t* row = buf + (tile_off ? tile_off[tt] : tt * tile_bytes);
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(row) + piece);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+  }
+  if (acc == kProbeMagic) sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 // The same reads through LDS: wave w of the work-group takes the 1 KiB pieces
 // w, w + 4, ... of each tile (tile_bytes a multiple of 1 KiB) and keeps NSLOT
 // of them in flight in its ring.
@@ -116,6 +145,7 @@ int probe_read(const void* buf, int64_t buf_bytes, const int64_t* tile_off, int6
     return BSA_ERR_INVALID_ARG;
   if (!tile_off && n_tiles > buf_bytes / tile_bytes) return BSA_ERR_INVALID_ARG;
   if (mode == 1 && tile_bytes % 1024) return BSA_ERR_INVALID_ARG;
+  if (mode == 2 && (tile_bytes > 4096 || 4096 % tile_bytes)) return BSA_ERR_INVALID_ARG;
   const int64_t groups = (n_tiles + tiles_per_group - 1) / tiles_per_group;
   if (groups > 0x7FFFFFFF) return BSA_ERR_INVALID_ARG;
   const dim3 grid{static_cast<uint32_t>(groups)}, block{256};
@@ -137,6 +167,14 @@ int probe_read(const void* buf, int64_t buf_bytes, const int64_t* tile_off, int6
       case 8: BSA_PROBE(probe_lds_kernel, 8); break;
       case 16: BSA_PROBE(probe_lds_kernel, 16); break;
       case 32: BSA_PROBE(probe_lds_kernel, 32); break;
+      default: return BSA_ERR_UNSUPPORTED;
+    }
+  } else if (mode == 2) {
+    switch (depth) {
+      case 1: BSA_PROBE(probe_rows_kernel, 1); break;
+      case 2: BSA_PROBE(probe_rows_kernel, 2); break;
+      case 4: BSA_PROBE(probe_rows_kernel, 4); break;
+      case 8: BSA_PROBE(probe_rows_kernel, 8); break;
       default: return BSA_ERR_UNSUPPORTED;
     }
   } else {

@@ -39,6 +39,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 // with the non-temporal score stores this made the scan 4% (BF16) and 9% (FP8)
 // faster at 128K context, batch 8, 8 KV heads.
 constexpr int kTokPerWg = 16384;
+constexpr int kTokThreads = 256;  // threads of a token-scan work-group
+constexpr int kTokWaves = kTokThreads / kWave;
 constexpr int kTokStagger = 13;  // steps between the starting points of consecutive waves
 
 //
@@ -49,7 +51,7 @@ constexpr int kTokStagger = 13;  // steps between the starting points of consecu
 // hist_stride. Units where the selection takes nothing or everything (picks 0
 // or L) are not counted, as there.
 template <int R, bool FP8>
-__global__ __launch_bounds__(256) void scan_token_kernel(
+__global__ __launch_bounds__(kTokThreads) void scan_token_kernel(
     const _Float16* __restrict__ q, const void* __restrict__ kproj,
     const float* __restrict__ proj, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, int Hkv, int Hq, int G, int Tmax, float sigma,
@@ -60,11 +62,11 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   constexpr int kLpt = kRowBytes / 16;    // lanes per token (one 16-byte piece each)
   constexpr int kTps = kWave / kLpt;  // tokens per 1 KiB slice
   constexpr int kSlices = kLpt;       // slices per 64-token step
-  constexpr int kPerWave = kTokPerWg / 4;
+  constexpr int kPerWave = kTokPerWg / kTokWaves;
   __shared__ float qbar[kHeadDim];
-  __shared__ float part[256];
+  __shared__ float part[kTokThreads];
   __shared__ float p_lds[R];
-  __shared__ __attribute__((aligned(16))) float keep[4][kPerWave];  // the scores, until the end
+  __shared__ __attribute__((aligned(16))) float keep[kTokWaves][kPerWave];  // the scores, until the end
   __shared__ uint32_t h16[kTokHistBins / 2];  // bin d at half d & 1 of word d / 2
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.y;
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   const int picks = min(budget, L);
   const bool do_hist = hist0 != nullptr && picks > 0 && picks < L;  // uniform
   if (do_hist)
-    for (int w = threadIdx.x; w < kTokHistBins / 2; w += 256) h16[w] = 0u;  // before the barriers below
+    for (int w = threadIdx.x; w < kTokHistBins / 2; w += kTokThreads) h16[w] = 0u;  // before the barriers below
   const int t_wave = blockIdx.x * kTokPerWg + wave * kPerWave;
   const int t_end = min(t_wave + kPerWave, Tmax);
   const uint8_t* base = static_cast<const uint8_t*>(kproj) + int64_t(unit) * Tmax * kRowBytes;
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   const int nsteps = t_end > t_wave ? (t_end - t_wave + kWave - 1) / kWave : 0;
   const int k0 =
       nsteps > 0
-          ? int(((int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * 4 + wave) * kTokStagger % nsteps)
+          ? int(((int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * kTokWaves + wave) * kTokStagger %
+                nsteps)
           : 0;
   auto step_t = [&](int i) {  // first token of the wave's i-th step
     int k = k0 + i;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   // qbar = (sum of the group's queries) / G, then p = sigma * P^T qbar, in
   // float32. The thread's entries of P are loaded with the queries, before
   // the first barrier.
-  constexpr int kChunks = 256 / R;  // threads per output channel
+  constexpr int kChunks = kTokThreads / R;  // threads per output channel
   constexpr int kDPer = kHeadDim / kChunks;
   const int jj = threadIdx.x % R, ch = threadIdx.x / R;
   float pv[kDPer];
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void scan_token_kernel(
   if (do_hist) {
     __syncthreads();
     uint32_t* hist = hist0 + int64_t(unit) * hist_stride;
-    for (int w = threadIdx.x; w < kTokHistBins / 2; w += 256) {
+    for (int w = threadIdx.x; w < kTokHistBins / 2; w += kTokThreads) {
       const uint32_t x = h16[w];
       if (x & 0xFFFFu)
         __hip_atomic_fetch_add(&hist[2 * w], x & 0xFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -238,7 +241,7 @@ hipError_t launch_scan_token(const UnitGeom& g, float sigma, int rank, bool fp8,
                              int64_t hist_stride, int budget, hipStream_t s) {
   dim3 grid(ceil_div(g.Tmax, kTokPerWg), g.B * g.Hkv);
 #define BSA_SCAN_TOKEN(RK, F8)                                                                  \
-  hipLaunchKernelGGL((scan_token_kernel<RK, F8>), grid, dim3(256), 0, s, q, kproj, proj,         \
+  hipLaunchKernelGGL((scan_token_kernel<RK, F8>), grid, dim3(kTokThreads), 0, s, q, kproj, proj, \
                      seq_lens, scores, g.Hkv, g.Hq, g.G, g.Tmax, sigma, hist0, hist_stride, budget)
   if (fp8) {
     switch (rank) {

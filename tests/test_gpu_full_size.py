@@ -55,3 +55,45 @@ def test_full_size_sampled_units(name):
     PU.check_units(w, d, units)
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["jetqsparse", "token"])
+def test_full_size_every_unit_selection_and_output(name):
+    """Every unit of the bench's block and token workloads at full size, in the
+    bench's launch configuration: the selection is exactly the oracle's on the
+    GPU's own scores, and the partials, output and lse agree with the oracle's
+    attention over that selection (the scan's scores are checked against the
+    oracle's on the sampled units above, whose packing the oracle repeats)."""
+    import numpy as np
+
+    from oracle import decode as O
+
+    spec = W.SPECS[name]
+    print(f"[full-all] {name}: generating", flush=True)
+    w = W.generate(spec, threads=16)
+    d = upload(w)
+    d.pack()
+    for call in step_calls(d, default_form(spec.granularity)):
+        call()
+    torch.cuda.synchronize()
+    assert int(d.counters.abs().sum()) == 0
+    scores, idx, count = (t.cpu().numpy() for t in (d.scores, d.idx, d.count))
+    part_o, part_lse, out, out_lse = (t.cpu().numpy() for t in (d.part_o, d.part_lse, d.out,
+                                                                 d.out_lse))
+    G = spec.group
+    for b in range(spec.batch):
+        L = int(w.seq_lens[b])
+        for h in range(spec.kv_heads):
+            sg = scores[b, h].astype(np.float64)
+            if spec.granularity == "block":
+                ref_idx, ref_cnt = O.select_blocks_unit(sg, L, spec.n_tail, spec.budget)
+            else:
+                ref_idx, ref_cnt = O.select_tokens_unit(sg, L, spec.budget)
+            assert int(count[b, h]) == ref_cnt, (b, h)
+            assert np.array_equal(idx[b, h], ref_idx), f"selection differs at {(b, h)}"
+            rows = slice(h * G, (h + 1) * G)
+            PU.check_attention(w, b, h, idx[b, h], d.splits, part_o[b, rows], part_lse[b, rows],
+                               out[b, rows], out_lse[b, rows])
+        print(f"[full-all] {name}: sequence {b} ok", flush=True)
+    del d
+    torch.cuda.empty_cache()
