@@ -47,27 +47,31 @@ __global__ __launch_bounds__(256) void probe_vgpr_kernel(const uint8_t* __restri
 }
 
 // Short tiles at scattered offsets (the token-mode attention's selected 256-byte
-// key and value rows): P = tile_bytes / 16 threads read one tile, one 16-byte
-// piece each (P divides 256), so the work-group covers 256 / P tiles per step,
-// UNROLL steps in flight per thread.
+// key and value rows): the work-group's tile offsets are staged in LDS first
+// (as the attention stages its row indices), then P = tile_bytes / 16 threads
+// read one tile, one 16-byte piece each (P divides 256), so the work-group
+// covers 256 / P tiles per step, UNROLL steps in flight per thread.
+constexpr int kProbeRowsMax = 1024;  // tiles per work-group in this mode
 template <int UNROLL>
 __global__ __launch_bounds__(256) void probe_rows_kernel(const uint8_t* __restrict__ buf,
                                                          const int64_t* __restrict__ tile_off,
                                                          int64_t tile_bytes, int tiles_per_wg,
                                                          int64_t n_tiles, uint32_t* sink) {
+  __shared__ int64_t offs[kProbeRowsMax];
   const int P = int(tile_bytes / 16);
   const int per_step = 256 / P;
   const int piece = threadIdx.x % P;
-  uint32_t acc = 0;
   const int64_t t0 = int64_t(blockIdx.x) * tiles_per_wg;
-  const int64_t t1 = min(t0 + tiles_per_wg, n_tiles);
-  for (int64_t t = t0 + threadIdx.x / P; t < t1; t += int64_t(per_step) * UNROLL) {
+  const int n = int(min(int64_t(tiles_per_wg), n_tiles - t0));
+  for (int i = threadIdx.x; i < n; i += 256) offs[i] = tile_off ? tile_off[t0 + i] : (t0 + i) * tile_bytes;
+  __syncthreads();
+  uint32_t acc = 0;
+  for (int t = threadIdx.x / P; t < n; t += per_step * UNROLL) {
     uint4v x[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int64_t tt = t + int64_t(per_step) * u < t1 ? t + int64_t(per_step) * u : t;
-      const uint8_t* row = buf + (tile_off ? tile_off[tt] : tt * tile_bytes);
-      x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(row) + piece);
+      const int tt = t + per_step * u < n ? t + per_step * u : t;
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint4v*>(buf + offs[tt]) + piece);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
@@ -145,7 +149,8 @@ int probe_read(const void* buf, int64_t buf_bytes, const int64_t* tile_off, int6
     return BSA_ERR_INVALID_ARG;
   if (!tile_off && n_tiles > buf_bytes / tile_bytes) return BSA_ERR_INVALID_ARG;
   if (mode == 1 && tile_bytes % 1024) return BSA_ERR_INVALID_ARG;
-  if (mode == 2 && (tile_bytes > 4096 || 4096 % tile_bytes)) return BSA_ERR_INVALID_ARG;
+  if (mode == 2 && (tile_bytes > 4096 || 4096 % tile_bytes || tiles_per_group > kProbeRowsMax))
+    return BSA_ERR_INVALID_ARG;
   const int64_t groups = (n_tiles + tiles_per_group - 1) / tiles_per_group;
   if (groups > 0x7FFFFFFF) return BSA_ERR_INVALID_ARG;
   const dim3 grid{static_cast<uint32_t>(groups)}, block{256};

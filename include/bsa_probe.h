@@ -31,7 +31,8 @@ extern "C" {
  * mode 1: gfx950 global-to-LDS loads of 1 KiB per wave instruction, depth
  *         (4, 8, 16 or 32) of them in flight per wave;
  * mode 2: short tiles (tile_bytes divides 4096: the token-mode attention's
- *         256-byte key and value rows, JSSA Figure 6), tile_bytes / 16
+ *         256-byte key and value rows, JSSA Figure 6), tiles_per_group <=
+ *         1024: the group's offsets are staged in LDS, then tile_bytes / 16
  *         threads per tile, one 16-byte load each, depth (1, 2, 4 or 8)
  *         tiles in flight per thread.
  * sink: device uint32 [groups * 256] (written only in the case above).
