@@ -14,8 +14,10 @@ Prints one JSON line. `value` is (batch x KV heads) decode steps per second;
 cache and kernels, with the sparse step's speedup over it. `roofline` is the
 dominant kernel, the scan, measured with HIP events on the launch stream over
 the timed region (recorded on about 8 sampled steps, since each event record
-costs the GPU a marker); `cpu_baseline` is the CPU oracle timed on a bounded
-sample of the same workload.
+costs the GPU a marker); `components_us` splits a step into scoring, top-B
+selection and sparse attention, from an untimed pass of the step as separate
+calls; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload.
 """
 
 from __future__ import annotations
@@ -251,6 +253,47 @@ def event_stride(steps: int, layers: int, requested: int) -> int:
     return s
 
 
+def component_split(layers, cluster: bool, steps: int = 24):
+    """JSSA Figure 9's split of a decode step (candidate scoring, top-B
+    selection, sparse attention) from an untimed pass of the step as separate
+    calls (score_scan, select_topk, attend_combine; in cluster mode
+    score_clusters, select_clusters, attend and combine), every call bracketed
+    by HIP events on the launch stream. The scoring prep (the group's mean query
+    and its projection, or the block scan's query stage) runs inside the scoring
+    kernel's first microseconds."""
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_pack_amd.step import step_calls
+
+    form = "split" if cluster else "three"
+    parts = (["scoring", "top_selection", "sparse_attention", "sparse_attention"] if cluster
+             else ["scoring", "top_selection", "sparse_attention"])
+    stream = torch.cuda.current_stream()
+    for i in range(4):  # settle: one step per layer copy
+        for c in step_calls(layers[i % len(layers)], form):
+            c()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        for j, c in enumerate(step_calls(layers[i % len(layers)], form)):
+            c()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    out = {}
+    for name in dict.fromkeys(parts):
+        js = [j for j, p in enumerate(parts) if p == name]
+        ts = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for j in js) * 1e3 for i in range(1, steps)]
+        out[name] = round(float(np.median(ts)), 2)
+    out["calls"] = form
+    out["steps"] = steps - 1
+    out["statistic"] = "median of the per-step event times (the first step, after an idle queue, left out)"
+    return out
+
+
 def percentiles(xs):
     import numpy as np
 
@@ -435,6 +478,7 @@ def main() -> int:
         f"{len(sampled)} of {a.steps} timed steps (every {stride}th from step {sample0})",
         "warmup_run": {"steps": warm_steps, "ms": round(warm_ms, 1)},
         "roofline": roofline,
+        "components_us": component_split(layers, d0.cluster_mode),
     }
     if a.dense:
         log("[bench] timing dense attention on the same GPU")
