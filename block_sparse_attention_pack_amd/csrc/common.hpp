@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/bsa.h"
 
 namespace bsa {
@@ -190,6 +192,48 @@ __device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
 __device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Wave-wide scans and reductions with DPP moves (ALU lane exchanges, no LDS
+// round trip): four row shifts combine the lanes of each 16-lane row, then
+// lane 15 of rows 0 and 2 is broadcast into rows 1 and 3, and lane 31 into
+// rows 2 and 3. A lane whose source lies outside its row keeps `old`.
+constexpr int kDppRowShr = 0x110;      // + n: lane i takes lane i - n of its row
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row into the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+template <int CTRL, int ROWS>
+using DppStep = std::integral_constant<int, CTRL | ROWS << 16>;  // a step: control, rows written
+template <class Step>
+__device__ __forceinline__ int dpp_move(int old, int x, Step) {
+  return __builtin_amdgcn_update_dpp(old, x, Step::value & 0xFFFF, Step::value >> 16, 0xF, false);
+}
+template <class Op>
+__device__ __forceinline__ void wave_dpp_steps(Op&& op) {
+  op(DppStep<kDppRowShr + 1, 0xF>{});
+  op(DppStep<kDppRowShr + 2, 0xF>{});
+  op(DppStep<kDppRowShr + 4, 0xF>{});
+  op(DppStep<kDppRowShr + 8, 0xF>{});
+  op(DppStep<kDppRowBcast15, 0xA>{});
+  op(DppStep<kDppRowBcast31, 0xC>{});
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_scan_dpp(int x) {
+  wave_dpp_steps([&](auto step) { x += dpp_move(0, x, step); });
+  return x;
+}
+
+// The wave's minimum and maximum (the same in every lane).
+__device__ __forceinline__ void wave_minmax_dpp(uint32_t& lo, uint32_t& hi) {
+  wave_dpp_steps([&](auto step) {
+    const uint32_t l = uint32_t(dpp_move(int(lo), int(lo), step));
+    const uint32_t h = uint32_t(dpp_move(int(hi), int(hi), step));
+    lo = l < lo ? l : lo;
+    hi = h > hi ? h : hi;
+  });
+  lo = uint32_t(__builtin_amdgcn_readlane(int(lo), kWave - 1));
+  hi = uint32_t(__builtin_amdgcn_readlane(int(hi), kWave - 1));
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -10,7 +10,9 @@
 // boundary bucket. Each thread owns a contiguous range of candidate indices, so
 // one block-wide scan of the taken-by-key and tied counts places every chosen
 // index: the output is ascending, and of the candidates tied at kappa the lowest
-// indices are taken. The forced tail pages follow the scanned blocks.
+// indices are taken. The forced tail pages follow the scanned blocks. Wave-wide
+// scans and the key range use DPP moves, not LDS permutes: on a chain of six
+// dependent lane exchanges the permutes' LDS latency set the pace.
 #pragma once
 
 #include "common.hpp"
@@ -34,14 +36,8 @@ struct SelectLds {
 __device__ __forceinline__ void select_block_scan2(int& v, int& w, SelectLds& s, int& tv,
                                                    int& tw) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int nv = __shfl_up(v, off, kWave), nw = __shfl_up(w, off, kWave);
-    if (lane >= off) {
-      v += nv;
-      w += nw;
-    }
-  }
+  v = wave_scan_dpp(v);
+  w = wave_scan_dpp(w);
   if (lane == kWave - 1) {
     s.wave_tot[wave] = v;
     s.wave_tot2[wave] = w;
@@ -66,11 +62,7 @@ __device__ __forceinline__ void select_block_scan2(int& v, int& w, SelectLds& s,
 // Inclusive scan of one int per thread over the 256-thread work-group.
 __device__ __forceinline__ int select_block_scan(int v, SelectLds& s, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int n = __shfl_up(v, off, kWave);
-    if (lane >= off) v += n;
-  }
+  v = wave_scan_dpp(v);
   if (lane == kWave - 1) s.wave_tot[wave] = v;
   __syncthreads();
   int before = 0, tot = 0;
@@ -145,13 +137,7 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
       klo = key < klo ? key : klo;
       khi = key > khi ? key : khi;
     });
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t ol = uint32_t(__shfl_xor(int(klo), off, kWave));
-      const uint32_t oh = uint32_t(__shfl_xor(int(khi), off, kWave));
-      klo = ol < klo ? ol : klo;
-      khi = oh > khi ? oh : khi;
-    }
+    wave_minmax_dpp(klo, khi);
     if (lane == 0) {
       s.wave_lo[wave] = klo;
       s.wave_hi[wave] = khi;
@@ -199,12 +185,7 @@ __device__ __forceinline__ void select_unit_rows(const float* row, int C, int pi
           run += int(cur[255 - 4 * lane - i]);
           c[i] = run;
         }
-        int incl = run;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int n = __shfl_up(incl, off, kWave);
-          if (lane >= off) incl += n;
-        }
+        const int incl = wave_scan_dpp(run);
         const int P = incl - run;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -78,48 +78,6 @@ __device__ __forceinline__ float ts_key_floor(uint32_t T) {
   return __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
 }
 
-// Wave-wide scans and reductions with DPP moves (ALU lane exchanges, no LDS
-// round trip): four row shifts combine the lanes of each 16-lane row, then
-// lane 15 of rows 0 and 2 is broadcast into rows 1 and 3, and lane 31 into
-// rows 2 and 3. A lane whose source lies outside its row keeps `old`.
-constexpr int kDppRowShr = 0x110;      // + n: lane i takes lane i - n of its row
-constexpr int kDppRowBcast15 = 0x142;  // lane 15 of a row into the next row
-constexpr int kDppRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
-
-template <int CTRL, int ROWS>
-using TsDpp = std::integral_constant<int, CTRL | ROWS << 16>;  // a step: control, rows written
-template <class Step>
-__device__ __forceinline__ int ts_dpp(int old, int x, Step) {
-  return __builtin_amdgcn_update_dpp(old, x, Step::value & 0xFFFF, Step::value >> 16, 0xF, false);
-}
-template <class Op>
-__device__ __forceinline__ void ts_wave_steps(Op&& op) {
-  op(TsDpp<kDppRowShr + 1, 0xF>{});
-  op(TsDpp<kDppRowShr + 2, 0xF>{});
-  op(TsDpp<kDppRowShr + 4, 0xF>{});
-  op(TsDpp<kDppRowShr + 8, 0xF>{});
-  op(TsDpp<kDppRowBcast15, 0xA>{});
-  op(TsDpp<kDppRowBcast31, 0xC>{});
-}
-
-// Inclusive prefix sum over the wave's lanes.
-__device__ __forceinline__ int ts_wave_scan(int x) {
-  ts_wave_steps([&](auto step) { x += ts_dpp(0, x, step); });
-  return x;
-}
-
-// The wave's minimum and maximum (the same in every lane).
-__device__ __forceinline__ void ts_wave_minmax(uint32_t& lo, uint32_t& hi) {
-  ts_wave_steps([&](auto step) {
-    const uint32_t l = uint32_t(ts_dpp(int(lo), int(lo), step));
-    const uint32_t h = uint32_t(ts_dpp(int(hi), int(hi), step));
-    lo = l < lo ? l : lo;
-    hi = h > hi ? h : hi;
-  });
-  lo = uint32_t(__builtin_amdgcn_readlane(int(lo), kWave - 1));
-  hi = uint32_t(__builtin_amdgcn_readlane(int(hi), kWave - 1));
-}
-
 // (m, s) <- the log-sum-exp merge of (m, s) and (m2, s2): s a sum of exp(x - m)
 // (the exponentials by the hardware exp2: the shares they feed decide a count
 // within a tolerance of 1e-4, far above its few-ulp error)
@@ -142,7 +100,7 @@ __device__ __forceinline__ void ts_scan(int (&v)[N], int (&t)[N], TsLds& s) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
 #pragma unroll
-  for (int n = 0; n < N; ++n) v[n] = ts_wave_scan(v[n]);
+  for (int n = 0; n < N; ++n) v[n] = wave_scan_dpp(v[n]);
   if (lane == kWave - 1)
 #pragma unroll
     for (int n = 0; n < N; ++n) s.wtot[n][wave] = v[n];
@@ -150,7 +108,7 @@ __device__ __forceinline__ void ts_scan(int (&v)[N], int (&t)[N], TsLds& s) {
   // lane k < kTsWaves takes wave k's total: a scan over those lanes
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const int x = ts_wave_scan(lane < kTsWaves ? s.wtot[n][lane] : 0);
+    const int x = wave_scan_dpp(lane < kTsWaves ? s.wtot[n][lane] : 0);
     t[n] = __builtin_amdgcn_readlane(x, kTsWaves - 1);
     v[n] += wave > 0 ? __builtin_amdgcn_readlane(x, wave > 0 ? wave - 1 : 0) : 0;
   }
@@ -177,7 +135,7 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
     klo = key < klo ? key : klo;
     khi = key > khi ? key : khi;
   });
-  ts_wave_minmax(klo, khi);
+  wave_minmax_dpp(klo, khi);
   if (lane == 0) {
     s.wlo[wave] = klo;
     s.whi[wave] = khi;
@@ -186,7 +144,7 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
   __syncthreads();
   klo = lane < kTsWaves ? s.wlo[lane] : 0xFFFFFFFFu;  // lane k: wave k's
   khi = lane < kTsWaves ? s.whi[lane] : 0u;
-  ts_wave_minmax(klo, khi);
+  wave_minmax_dpp(klo, khi);
   const uint32_t diff = klo ^ khi;
   int hi = diff ? 32 - __builtin_clz(diff) : 0;  // bits [hi, 32) are common
   uint32_t prefix = hi < 32 ? khi >> hi : 0u;
@@ -237,7 +195,7 @@ __device__ __forceinline__ TsCut ts_radix(int picks, ForEach&& for_each_key, TsL
         run += int(cur[255 - 4 * lane - i]);
         c[i] = run;
       }
-      const int P = ts_wave_scan(run) - run;
+      const int P = wave_scan_dpp(run) - run;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int above = P + (i ? c[i - 1] : 0), ge = P + c[i];
@@ -376,11 +334,11 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
           }
         }
         // the wave's merge in lane 63 (an empty partner is (-inf, 0))
-        ts_wave_steps([&](auto step) {
-          const float m2 = __int_as_float(ts_dpp(__float_as_int(-__builtin_inff()), __float_as_int(m), step));
-          const float s2 = __int_as_float(ts_dpp(0, __float_as_int(sm), step));
+        wave_dpp_steps([&](auto step) {
+          const float m2 = __int_as_float(dpp_move(__float_as_int(-__builtin_inff()), __float_as_int(m), step));
+          const float s2 = __int_as_float(dpp_move(0, __float_as_int(sm), step));
           ts_lse_merge(m, sm, m2, s2);
-          ninf += ts_dpp(0, ninf, step);
+          ninf += dpp_move(0, ninf, step);
         });
         if (lane == kWave - 1) {
           s.pm[hh][wave] = m;
@@ -576,7 +534,7 @@ __global__ __launch_bounds__(kTsThreads) void tok_select_kernel(
         c[i] = 4 * lane + i < kTsWaves * jn ? s.slots[4 * lane + i] : 0u;
         x += c[i];  // each field stays below 2^16: at most kTsCap slots
       }
-      const uint32_t inc = uint32_t(ts_wave_scan(int(x)));
+      const uint32_t inc = uint32_t(wave_scan_dpp(int(x)));
       uint32_t base = inc - x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
