@@ -157,8 +157,8 @@ def test_token_select_when_the_sample_misleads(case):
 
 
 @pytest.mark.parametrize("pattern", ["random", "low_bits", "few_values", "specials", "all_equal"])
-@pytest.mark.parametrize("nb,budget,n_tail", [(1024, 64, 0), (2048, 130, 2), (4096, 1000, 1),
-                                              (4096, 4096, 0)])
+@pytest.mark.parametrize("nb,budget,n_tail", [(1024, 64, 0), (1000, 37, 1), (256, 256, 2),
+                                              (2048, 130, 2), (4096, 1000, 1), (4096, 4096, 0)])
 def test_block_select_matches_oracle(pattern, nb, budget, n_tail):
     T = nb * 128  # 2048 blocks fill the per-thread registers; 4096 re-read memory
     lengths = [T, T - 1, T // 2 + 5, 129, 128, 1, 0]
