@@ -364,7 +364,7 @@ def main() -> int:
     stages = forms_of(spec.granularity)[a.mode]
     calls = lambda d: step_calls(d, a.mode)
     # untimed warm-up: the --warmup steps, then more in batches of 16 until
-    # --warmup-ms of wall time has passed (the driver's short runs otherwise
+    # --warmup-ms of wall time has passed (short runs of a few steps otherwise
     # time a GPU whose clocks have not settled)
     t_warm = time.perf_counter()
     warm_steps = 0
