@@ -672,13 +672,14 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     lse_merge(m, s, __builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1]));
     ninf += int(p[2]);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(s, off, kWave);
+  // the wave's merge, complete in lane 63 (an empty partner is (-inf, 0))
+  wave_dpp_steps([&](auto step) {
+    const float m2 = __int_as_float(dpp_move(__float_as_int(-__builtin_inff()), __float_as_int(m), step));
+    const float s2 = __int_as_float(dpp_move(0, __float_as_int(s), step));
     lse_merge(m, s, m2, s2);
-    ninf += __shfl_xor(ninf, off, kWave);
-  }
-  if (lane == 0) {
+    ninf += dpp_move(0, ninf, step);
+  });
+  if (lane == kWave - 1) {
     red_m[wave] = m;
     red_s[wave] = s;
     red_i[wave] = ninf;
@@ -755,11 +756,12 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
       if (tid < 256) {
         v = hsum[255 - tid];
         incl = v;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const unsigned long long y = __shfl_up(incl, off, kWave);
-          if (lane >= off) incl += y;
-        }
+        // inclusive 64-bit scan: both halves move by DPP, the sum carries
+        wave_dpp_steps([&](auto step) {
+          const uint32_t lo = uint32_t(dpp_move(0, int(uint32_t(incl)), step));
+          const uint32_t hi = uint32_t(dpp_move(0, int(uint32_t(incl >> 32)), step));
+          incl += (uint64_t(hi) << 32) | lo;
+        });
         if (lane == kWave - 1) wtot[wave] = incl;
       }
       __syncthreads();
@@ -812,12 +814,7 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     const int k = tid * kTopPPer + j;
     tie_mine += (cutting && k < n && ekey[k] == kappa) ? 1 : 0;
   }
-  int tincl = tie_mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(tincl, off, kWave);
-    if (lane >= off) tincl += y;
-  }
+  const int tincl = wave_scan_dpp(tie_mine);
   if (lane == kWave - 1) red_i[wave] = tincl;
   __syncthreads();
   int tie_rank = tincl - tie_mine;
@@ -836,12 +833,7 @@ __global__ __launch_bounds__(kTopPThreads) void tok_topp_kernel(
     keep[j] = kp;
     mine += kp ? 1 : 0;
   }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_scan_dpp(mine);
   __syncthreads();  // red_i is reused
   if (lane == kWave - 1) red_i[wave] = incl;
   __syncthreads();
