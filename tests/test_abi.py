@@ -267,3 +267,20 @@ def test_noalloc_step_rejects_steps_beyond_its_scratch(lib):
                                      FAKE, None, None, None, FAKE, FAKE, FAKE, None, None, 9, FAKE,
                                      None, None)
     assert rc == -1 and "num_splits" in lib.bsa_last_error().decode()
+
+
+def test_probe_checks_its_arguments(lib):
+    fn = lib.bsa_probe_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    # (buf, buf_bytes, tile_off, n_tiles, tile_bytes, tiles_per_group, mode, depth, sink)
+    assert fn(None, 1 << 20, None, 4, 256, 4, 0, 8, FAKE, None) == -1      # no buffer
+    assert fn(FAKE, 1 << 20, None, 4, 250, 4, 0, 8, FAKE, None) == -1      # not 16-byte tiles
+    assert fn(FAKE, 1 << 10, None, 8, 256, 4, 0, 8, FAKE, None) == -1      # past the buffer
+    assert fn(FAKE, 1 << 20, None, 4, 4096 + 16, 4, 1, 8, FAKE, None) == -1  # LDS mode: KiB tiles
+    assert fn(FAKE, 1 << 20, None, 4, 48, 4, 2, 8, FAKE, None) == -1       # rows: divides 4096
+    assert fn(FAKE, 1 << 30, None, 4096, 256, 2048, 2, 8, FAKE, None) == -1  # rows: <= 1024 a group
+    assert fn(FAKE, 1 << 20, None, 4, 256, 4, 3, 8, FAKE, None) == -2      # no such mode
+    assert fn(FAKE, 1 << 20, None, 4, 256, 4, 0, 3, FAKE, None) == -2      # no such depth
